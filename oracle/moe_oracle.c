@@ -1,0 +1,412 @@
+/*
+ * moe_oracle.c -- plain, slow, fp64 reference of the fused MoE layer forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The product path (the
+ * HIP library under grouped_gemm_amd/) never calls, links or includes it, and
+ * this file includes nothing from there.
+ *
+ * What it computes, step by step, and where the pages describe it:
+ *
+ *  - top-k routing: per token, the k experts with the largest router score,
+ *    ties to the lower expert index, gate weights renormalised over the k
+ *    (Alpha-MoE news page, "How the megakernel works": routing and gating are
+ *    stages of the layer; LightMoE README, "MoE inference": top_k_ids are
+ *    int32 and distinct per token, top_k_weights are fp32);
+ *  - deterministic expert-major dispatch: per-expert counts, their exclusive
+ *    prefix sum m_indptr of length E+1 (zero-row experts allowed), and the
+ *    stable permutation of the T*k (token, slot) pairs into contiguous expert
+ *    row groups (LightMoE README, API table and "Grouped GEMM";
+ *    "MoE training": gather indices and inverse slots);
+ *  - the block-id -> (expert, row offset) table that lets one launch cover
+ *    variable-size expert groups without padding (pure-Triton MoE
+ *    commentary, second paragraph);
+ *  - dynamic activation quantisation before each expert GEMM and the
+ *    requantisation of the gated intermediate (LightMoE README, "MoE
+ *    inference": input quantisation and requantisation; Alpha-MoE news page,
+ *    "The MoE bottleneck": FP8 W8A8);
+ *  - per expert, out = A * B^T against [N, K] weights (LightMoE README,
+ *    "Dense GEMM"/"Grouped GEMM"), gate and up from the same input, SiLU(gate)
+ *    times up (pure-Triton MoE commentary, second paragraph), then the down
+ *    projection;
+ *  - routing-weight application and combine in a fixed order (LightMoE
+ *    README, "MoE inference").
+ *
+ * Everything is accumulated in double over exactly dequantised operands.
+ * Where the activations are quantised on the fly, the oracle applies the
+ * same rule the layer does (stated at oracle_quant_group) so that both
+ * sides multiply the same codes.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define SCORE_SOFTMAX 0
+#define SCORE_SIGMOID 1
+#define SCORE_PROBS 2
+#define W_BF16 0
+#define W_FP8_CHANNEL 1
+#define W_FP8_BLOCK128 2
+#define W_MXFP4 3
+#define A_BF16 0
+#define A_FP8_TOKEN 1
+#define A_FP8_G128 2
+#define A_MXFP8_G32 3
+
+/* ------------------------------------------------------------------ codecs */
+
+/* bf16: the top 16 bits of an IEEE binary32. */
+double oracle_bf16_decode(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* Round a double to the nearest bf16 value, ties to even (finite inputs). */
+double oracle_bf16_round(double v) {
+  if (v == 0.0 || !isfinite(v)) return v;
+  int e;
+  frexp(v, &e);                 /* |v| in [2^(e-1), 2^e) */
+  int emin = -126;              /* bf16 shares binary32's exponent range */
+  int q = (e - 1 < emin ? emin : e - 1) - 7;   /* 8 significant bits */
+  double ulp = ldexp(1.0, q);
+  double r = nearbyint(v / ulp); /* default rounding mode: ties to even */
+  return r * ulp;
+}
+
+/* OCP FP8 E4M3 ("fn"): 1 sign, 4 exponent (bias 7), 3 mantissa bits,
+ * no infinities, 0x7f/0xff are NaN, largest finite 448. */
+double oracle_e4m3_decode(uint8_t c) {
+  int s = c >> 7, ex = (c >> 3) & 0xF, m = c & 7;
+  double mag;
+  if (ex == 0xF && m == 7) return NAN;
+  if (ex == 0)
+    mag = ldexp((double)m, -9);            /* subnormal: m * 2^-6 / 8 */
+  else
+    mag = ldexp(1.0 + m / 8.0, ex - 7);
+  return s ? -mag : mag;
+}
+
+/* Nearest E4M3 value to v, ties to the even mantissa, saturating at +-448.
+ * Brute force over the 127 non-negative finite codes.  The sign bit is the
+ * input's sign, also when the magnitude rounds to zero (IEEE-style -0). */
+uint8_t oracle_e4m3_encode(double v) {
+  double a = fabs(v);
+  if (a > 448.0) a = 448.0;
+  int best = 0;
+  double bd = INFINITY;
+  for (int c = 0; c < 127; ++c) {
+    double d = fabs(oracle_e4m3_decode((uint8_t)c) - a);
+    if (d < bd || (d == bd && (c & 1) == 0)) {
+      bd = d;
+      best = c;
+    }
+  }
+  return (uint8_t)(best | (signbit(v) ? 0x80 : 0));
+}
+
+/* OCP E8M0 scale: 2^(c-127); 0xff is NaN. */
+double oracle_e8m0_decode(uint8_t c) {
+  if (c == 0xFF) return NAN;
+  return ldexp(1.0, (int)c - 127);
+}
+
+/* OCP FP4 E2M1: 1 sign, 2 exponent (bias 1), 1 mantissa bit. */
+double oracle_e2m1_decode(uint8_t nib) {
+  static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  double m = mag[nib & 7];
+  return (nib & 8) ? -m : m;
+}
+
+/* --------------------------------------------------- activation quantisation
+ * One group of n values (a token row, or a 1x128 or 1x32 slice of it):
+ *  FP8 with an fp32 scale (per-token and 1x128 groups):
+ *    a = max |v| ; s = fp32(a / 448), or 1 when a == 0 ;
+ *    q_i = e4m3_rne(clamp(fp32(v_i / s), -448, 448)) ; value = q_i * s.
+ *  MXFP8 (OCP MX v1.0, 32-element blocks with E4M3 elements):
+ *    X = 2^(floor(log2 a) - 8)  (8 = largest exponent of E4M3), X = 2^-127
+ *    when a == 0 ; q_i = e4m3_rne_saturating(v_i / X) ; value = q_i * X.
+ * Returns the scale as a double (exact: an fp32 value or a power of two);
+ * for MX groups *e8m0 receives the biased exponent.
+ */
+double oracle_quant_group(const double* v, int n, int a_format, uint8_t* q, uint8_t* e8m0) {
+  double a = 0.0;
+  for (int i = 0; i < n; ++i)
+    if (fabs(v[i]) > a) a = fabs(v[i]);
+  if (a_format == A_MXFP8_G32) {
+    int ex;
+    if (a == 0.0) {
+      ex = -127;
+    } else {
+      int e;
+      frexp(a, &e);            /* a in [2^(e-1), 2^e) => floor(log2 a) = e-1 */
+      ex = (e - 1) - 8;
+      if (ex < -127) ex = -127;
+      if (ex > 127) ex = 127;
+    }
+    double X = ldexp(1.0, ex);
+    for (int i = 0; i < n; ++i) q[i] = oracle_e4m3_encode((double)(float)(v[i] / X));
+    if (e8m0) *e8m0 = (uint8_t)(ex + 127);
+    return X;
+  }
+  float s = (a == 0.0) ? 1.0f : (float)((double)(float)a / 448.0);
+  for (int i = 0; i < n; ++i) {
+    float r = (float)(v[i] / (double)s);
+    if (r > 448.0f) r = 448.0f;
+    if (r < -448.0f) r = -448.0f;
+    q[i] = oracle_e4m3_encode((double)r);
+  }
+  return (double)s;
+}
+
+static int group_len(int a_format, int n) {
+  switch (a_format) {
+    case A_FP8_TOKEN: return n;
+    case A_FP8_G128: return 128;
+    case A_MXFP8_G32: return 32;
+    default: return 1;
+  }
+}
+
+/* Replace v[0..n) by its dequantised image under the activation format. */
+static void quant_dequant_row(double* v, int n, int a_format) {
+  if (a_format == A_BF16) {
+    for (int i = 0; i < n; ++i) v[i] = oracle_bf16_round(v[i]);
+    return;
+  }
+  int g = group_len(a_format, n);
+  uint8_t* q = (uint8_t*)malloc((size_t)g);
+  for (int i0 = 0; i0 < n; i0 += g) {
+    double s = oracle_quant_group(v + i0, g, a_format, q, NULL);
+    for (int i = 0; i < g; ++i) v[i0 + i] = oracle_e4m3_decode(q[i]) * s;
+  }
+  free(q);
+}
+
+/* Activation quantisation exposed for the test suite: row-major [rows, n]. */
+void oracle_quant_rows(const double* v, int rows, int n, int a_format, uint8_t* q,
+                       double* scales) {
+  int g = group_len(a_format, n);
+  for (int r = 0; r < rows; ++r)
+    for (int i0 = 0; i0 < n; i0 += g)
+      scales[(size_t)r * (n / g) + i0 / g] =
+          oracle_quant_group(v + (size_t)r * n + i0, g, a_format, q + (size_t)r * n + i0, NULL);
+}
+
+/* ------------------------------------------------------------------ routing
+ * Per token: repeatedly take the highest remaining score, the lower expert
+ * index winning a tie (scores are compared as given, fp32, +0 == -0).
+ * Gate weights are renormalised over the k chosen experts:
+ *   softmax: w_j = exp(l_j - l_max) / sum_sel exp(l_i - l_max)
+ *   sigmoid: w_j = sig(l_j) / sum_sel sig(l_i)
+ *   probs:   w_j = p_j / sum_sel p_i
+ */
+void oracle_route(const float* scores, int T, int E, int k, int score_fn, int32_t* ids,
+                  double* w) {
+  char* taken = (char*)malloc((size_t)E);
+  for (int t = 0; t < T; ++t) {
+    const float* row = scores + (size_t)t * E;
+    memset(taken, 0, (size_t)E);
+    for (int j = 0; j < k; ++j) {
+      int best = -1;
+      for (int e = 0; e < E; ++e) {
+        if (taken[e]) continue;
+        if (best < 0 || (double)row[e] > (double)row[best]) best = e;
+      }
+      taken[best] = 1;
+      ids[(size_t)t * k + j] = best;
+    }
+    double sum = 0.0, top = (double)row[ids[(size_t)t * k]];
+    double* wt = w + (size_t)t * k;
+    for (int j = 0; j < k; ++j) {
+      double l = (double)row[ids[(size_t)t * k + j]];
+      double v;
+      if (score_fn == SCORE_SOFTMAX)
+        v = exp(l - top);
+      else if (score_fn == SCORE_SIGMOID)
+        v = 1.0 / (1.0 + exp(-l));
+      else
+        v = l;
+      wt[j] = v;
+      sum += v;
+    }
+    for (int j = 0; j < k; ++j) wt[j] /= sum;
+  }
+  free(taken);
+}
+
+/* ----------------------------------------------------------------- dispatch
+ * counts[e] = number of (t, j) with ids[t, j] == e; m_indptr = exclusive
+ * prefix sum (length E+1).  Slots are ordered by expert, then by the flat
+ * index t*k + j (a stable counting sort).  gather[slot] = t*k + j and
+ * inv[t*k + j] = slot.
+ */
+void oracle_dispatch(const int32_t* ids, int T, int k, int E, int32_t* counts,
+                     int32_t* m_indptr, int32_t* gather, int32_t* inv) {
+  int S = T * k;
+  for (int e = 0; e < E; ++e) counts[e] = 0;
+  for (int p = 0; p < S; ++p) counts[ids[p]]++;
+  m_indptr[0] = 0;
+  for (int e = 0; e < E; ++e) m_indptr[e + 1] = m_indptr[e] + counts[e];
+  int32_t* next = (int32_t*)malloc(sizeof(int32_t) * (size_t)(E > 0 ? E : 1));
+  for (int e = 0; e < E; ++e) next[e] = m_indptr[e];
+  for (int p = 0; p < S; ++p) {
+    int slot = next[ids[p]]++;
+    gather[slot] = p;
+    inv[p] = slot;
+  }
+  free(next);
+}
+
+/* Block table for row blocks of height bm: for each expert in ascending
+ * order, ceil(counts[e] / bm) entries (e, r * bm).  Returns the entry count;
+ * writes at most cap entries as pairs into table. */
+int oracle_tile_table(const int32_t* counts, int E, int bm, int32_t* table, int cap) {
+  int n = 0;
+  for (int e = 0; e < E; ++e)
+    for (int r = 0; r * bm < counts[e]; ++r) {
+      if (n < cap) {
+        table[2 * n] = e;
+        table[2 * n + 1] = r * bm;
+      }
+      ++n;
+    }
+  return n;
+}
+
+/* ------------------------------------------------------------------ experts */
+typedef struct {
+  int w_format;
+  const void* codes;   /* one expert's [N, K] matrix */
+  const void* scales;  /* per format, or NULL */
+  int N, K;
+} oracle_mat;
+
+static void dequant_row(const oracle_mat* m, int n, double* out) {
+  int K = m->K;
+  if (m->w_format == W_BF16) {
+    const uint16_t* c = (const uint16_t*)m->codes + (size_t)n * K;
+    for (int i = 0; i < K; ++i) out[i] = oracle_bf16_decode(c[i]);
+  } else if (m->w_format == W_FP8_CHANNEL) {
+    const uint8_t* c = (const uint8_t*)m->codes + (size_t)n * K;
+    double s = ((const float*)m->scales)[n];
+    for (int i = 0; i < K; ++i) out[i] = oracle_e4m3_decode(c[i]) * s;
+  } else if (m->w_format == W_FP8_BLOCK128) {
+    const uint8_t* c = (const uint8_t*)m->codes + (size_t)n * K;
+    const float* s = (const float*)m->scales + (size_t)(n / 128) * (K / 128);
+    for (int i = 0; i < K; ++i) out[i] = oracle_e4m3_decode(c[i]) * (double)s[i / 128];
+  } else { /* W_MXFP4: two e2m1 codes per byte, element 2i in the low nibble */
+    const uint8_t* c = (const uint8_t*)m->codes + (size_t)n * (K / 2);
+    const uint8_t* s = (const uint8_t*)m->scales + (size_t)n * (K / 32);
+    for (int i = 0; i < K; ++i) {
+      uint8_t nib = (i & 1) ? (c[i / 2] >> 4) : (c[i / 2] & 0xF);
+      out[i] = oracle_e2m1_decode(nib) * oracle_e8m0_decode(s[i / 32]);
+    }
+  }
+}
+
+/* out[n] = sum_k a[k] * W[n, k] for every row n of an expert matrix. */
+static void matvec(const oracle_mat* m, const double* a, double* out) {
+#pragma omp parallel
+  {
+    double* row = (double*)malloc(sizeof(double) * (size_t)m->K);
+#pragma omp for schedule(static)
+    for (int n = 0; n < m->N; ++n) {
+      dequant_row(m, n, row);
+      double acc = 0.0;
+      for (int i = 0; i < m->K; ++i) acc += a[i] * row[i];
+      out[n] = acc;
+    }
+    free(row);
+  }
+}
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* One expert on one (already dequantised) token row: SwiGLU MLP with the
+ * intermediate requantised under the activation format.  o has H entries. */
+static void expert_forward(const oracle_mat* g, const oracle_mat* u, const oracle_mat* d,
+                           const double* xq, int a_format, double* o) {
+  int I = g->N;
+  double* gv = (double*)malloc(sizeof(double) * (size_t)I);
+  double* uv = (double*)malloc(sizeof(double) * (size_t)I);
+  matvec(g, xq, gv);
+  matvec(u, xq, uv);
+  for (int n = 0; n < I; ++n) gv[n] = silu(gv[n]) * uv[n];
+  quant_dequant_row(gv, I, a_format);
+  matvec(d, gv, o);
+  free(gv);
+  free(uv);
+}
+
+static size_t code_bytes(int w_format, int N, int K) {
+  if (w_format == W_BF16) return (size_t)N * K * 2;
+  if (w_format == W_MXFP4) return (size_t)N * K / 2;
+  return (size_t)N * K;
+}
+
+static size_t scale_bytes(int w_format, int N, int K) {
+  if (w_format == W_FP8_CHANNEL) return (size_t)N * 4;
+  if (w_format == W_FP8_BLOCK128) return (size_t)(N / 128) * (K / 128) * 4;
+  if (w_format == W_MXFP4) return (size_t)N * (K / 32);
+  return 0;
+}
+
+static oracle_mat expert_mat(int w_format, const void* codes, const void* scales, int e, int N,
+                             int K) {
+  oracle_mat m;
+  m.w_format = w_format;
+  m.N = N;
+  m.K = K;
+  m.codes = (const char*)codes + code_bytes(w_format, N, K) * (size_t)e;
+  m.scales = scales ? (const char*)scales + scale_bytes(w_format, N, K) * (size_t)e : NULL;
+  return m;
+}
+
+/*
+ * Layer output for a list of tokens.
+ *   x_bits  [T, H] bf16 activations
+ *   ids, w  [T, k] routing (from oracle_route, or any valid routing)
+ *   w_*     codes [E, N, K] and scales of the routed experts
+ *   sh_*    the always-on shared expert (weight 1, outside renormalisation)
+ *           when has_shared != 0
+ *   tokens  which rows of y to compute; y is [ntok, H] (fp64)
+ * y_t = sum_j w[t,j] * expert_{ids[t,j]}(x_t) (+ shared(x_t)), j ascending.
+ */
+void oracle_layer_forward(int H, int I, int E, int k, int w_format, int a_format,
+                          const void* wg, const void* sg, const void* wu, const void* su,
+                          const void* wd, const void* sd, int has_shared, int Is,
+                          const void* shg, const void* shsg, const void* shu, const void* shsu,
+                          const void* shd, const void* shsd, const uint16_t* x_bits,
+                          const int32_t* ids, const double* w, const int32_t* tokens, int ntok,
+                          double* y) {
+  double* xq = (double*)malloc(sizeof(double) * (size_t)H);
+  double* o = (double*)malloc(sizeof(double) * (size_t)H);
+  for (int i = 0; i < ntok; ++i) {
+    int t = tokens[i];
+    for (int h = 0; h < H; ++h) xq[h] = oracle_bf16_decode(x_bits[(size_t)t * H + h]);
+    if (a_format != A_BF16) quant_dequant_row(xq, H, a_format);
+    double* yt = y + (size_t)i * H;
+    for (int h = 0; h < H; ++h) yt[h] = 0.0;
+    for (int j = 0; j < k; ++j) {
+      int e = ids[(size_t)t * k + j];
+      oracle_mat g = expert_mat(w_format, wg, sg, e, I, H);
+      oracle_mat u = expert_mat(w_format, wu, su, e, I, H);
+      oracle_mat d = expert_mat(w_format, wd, sd, e, H, I);
+      expert_forward(&g, &u, &d, xq, a_format, o);
+      double wj = w[(size_t)t * k + j];
+      for (int h = 0; h < H; ++h) yt[h] += wj * o[h];
+    }
+    if (has_shared) {
+      oracle_mat g = expert_mat(w_format, shg, shsg, 0, Is, H);
+      oracle_mat u = expert_mat(w_format, shu, shsu, 0, Is, H);
+      oracle_mat d = expert_mat(w_format, shd, shsd, 0, H, Is);
+      expert_forward(&g, &u, &d, xq, a_format, o);
+      for (int h = 0; h < H; ++h) yt[h] += o[h];
+    }
+  }
+  free(xq);
+  free(o);
+}
