@@ -1,0 +1,22 @@
+"""gfx950 fused MoE layer forward: Python binding of libmoe.so.
+
+Argument marshalling only. Every step of the layer runs in the HIP kernels
+of ``libmoe.so`` (C ABI in ``include/moe.h``); PyTorch supplies device
+memory and the current stream. Importing this package fails loudly if the
+library has not been built; there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+from ._binding import (  # noqa: F401
+    A_BF16, A_FP8_G128, A_FP8_TOKEN, A_MXFP8_G32, OP_GATEUP_SWIGLU, OP_PLAIN, SCORE_PROBS,
+    SCORE_SIGMOID, SCORE_SOFTMAX, W_BF16, W_FP8_BLOCK128, W_FP8_CHANNEL, W_MXFP4, MoeError,
+    LayerDesc, Workspace, combine, config_rows, dispatch, grouped_gemm, layer_forward,
+    library_path, quantize_act, route_topk, symbols)
+
+__all__ = [
+    "LayerDesc", "Workspace", "MoeError", "route_topk", "dispatch", "grouped_gemm",
+    "quantize_act", "combine", "layer_forward", "config_rows", "library_path", "symbols",
+]

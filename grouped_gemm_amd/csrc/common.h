@@ -1,0 +1,163 @@
+// Device-side building blocks shared by the gfx950 kernels of the MoE layer.
+//
+// MFMA conventions used throughout (measured on gfx950):
+//  * v_mfma_*_16x16x128_f8f6f4: operand "A" supplies 16 rows, operand "B" 16
+//    columns, both over 128 K elements.  For 8-bit elements, lane l (row
+//    l%16, lane group g = l/16) holds K elements [16g, 16g+16) in its first
+//    four registers and [64+16g, 64+16g+16) in the next four.  For 4-bit
+//    elements lane group g holds K [32g, 32g+32), the even element in the low
+//    nibble.  The scale operand of lane l covers row l%16 and the 32-wide K
+//    block l/16.
+//  * the fp32 result: lane l holds D[4*(l/16) + i][l%16], i = 0..3.
+//  * v_mfma_f32_16x16x32_bf16: lane group g holds K [8g, 8g+8) of its row.
+// In every kernel here operand A is the expert weight (rows = output
+// channels) and operand B the token rows, so a lane ends up with four
+// consecutive output channels of one token.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Format enumerations (mirrored in the public header).
+#define MOE_W_BF16 0
+#define MOE_W_FP8_CHANNEL 1
+#define MOE_W_FP8_BLOCK128 2
+#define MOE_W_MXFP4 3
+#define MOE_A_BF16 0
+#define MOE_A_FP8_TOKEN 1
+#define MOE_A_FP8_G128 2
+#define MOE_A_MXFP8_G32 3
+
+// Weight/activation format pairs supported by the kernels.
+enum Fmt { F_BF16 = 0, F_FP8_CH = 1, F_FP8_BLK = 2, F_MX = 3 };
+
+#define DEVI __device__ __forceinline__
+
+// ---------------------------------------------------------------- scalars
+DEVI float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round to nearest even (finite inputs).
+DEVI uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Two fp32 -> two OCP e4m3 codes (RNE).  The hardware conversion is exact
+// round-to-nearest-even inside the finite range; inputs are clamped to
+// +-448 first because out-of-range inputs may produce the NaN code.
+DEVI uint32_t cvt2_e4m3(float a, float b) {
+  a = fminf(fmaxf(a, -448.f), 448.f);
+  b = fminf(fmaxf(b, -448.f), 448.f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+DEVI uint32_t cvt4_e4m3(float a, float b, float c, float d) {
+  a = fminf(fmaxf(a, -448.f), 448.f);
+  b = fminf(fmaxf(b, -448.f), 448.f);
+  c = fminf(fmaxf(c, -448.f), 448.f);
+  d = fminf(fmaxf(d, -448.f), 448.f);
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+  return (uint32_t)r;
+}
+
+DEVI float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// floor(log2(a)) for a finite a > 0 (exact, from the exponent field).
+DEVI int ilog2_floor(float a) {
+  uint32_t u = __float_as_uint(a);
+  int e = (int)((u >> 23) & 0xFF);
+  if (e == 0) {                       // subnormal: 2^-149 * mantissa
+    uint32_t m = u & 0x7FFFFF;
+    return -149 + (31 - __builtin_clz(m));
+  }
+  return e - 127;
+}
+
+// ---------------------------------------------------------------- wave reductions
+DEVI float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+DEVI float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------- MFMA
+DEVI f32x4 mfma_f8(const i32x8& a, const i32x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+// A = e2m1 (format 4), B = e4m3 (format 0), per-lane e8m0 scales.
+DEVI f32x4 mfma_f4f8_scaled(const i32x8& a, const i32x8& b, f32x4 c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, sa, 0, sb);
+}
+DEVI f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- fragments
+// One K step = 128 elements.  Per-lane operand bytes per step: fp8 32,
+// fp4 16, bf16 64 (four 16x16x32 sub-steps).
+template <int ELEM_BITS>
+struct Frag;
+
+template <>
+struct Frag<8> {
+  i32x8 v;
+  DEVI void load(const uint8_t* row, int k0, int g) {
+    const i32x4 lo = *(const i32x4*)(row + k0 + 16 * g);
+    const i32x4 hi = *(const i32x4*)(row + k0 + 64 + 16 * g);
+    v = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  DEVI void zero() { v = (i32x8){0, 0, 0, 0, 0, 0, 0, 0}; }
+};
+
+template <>
+struct Frag<4> {
+  i32x8 v;
+  DEVI void load(const uint8_t* row, int k0, int g) {   // row = packed bytes
+    const i32x4 q = *(const i32x4*)(row + (k0 >> 1) + 16 * g);
+    v = (i32x8){q[0], q[1], q[2], q[3], 0, 0, 0, 0};
+  }
+  DEVI void zero() { v = (i32x8){0, 0, 0, 0, 0, 0, 0, 0}; }
+};
+
+template <>
+struct Frag<16> {
+  bf16x8 v[4];
+  DEVI void load(const uint8_t* row, int k0, int g) {   // row = bf16 bytes
+#pragma unroll
+    for (int s = 0; s < 4; ++s) v[s] = *(const bf16x8*)(row + 2 * (k0 + 32 * s + 8 * g));
+  }
+  DEVI void zero() {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      for (int i = 0; i < 8; ++i) v[s][i] = (__bf16)0.0f;
+  }
+};
+
+// Bits per element of the weight (A) and activation (B) operands.
+template <int F> struct FmtBits;
+template <> struct FmtBits<F_BF16> { static constexpr int W = 16, X = 16; };
+template <> struct FmtBits<F_FP8_CH> { static constexpr int W = 8, X = 8; };
+template <> struct FmtBits<F_FP8_BLK> { static constexpr int W = 8, X = 8; };
+template <> struct FmtBits<F_MX> { static constexpr int W = 4, X = 8; };
+
+// Bytes of one operand row of K elements.
+template <int BITS> DEVI constexpr long row_bytes(int K) { return (long)K * BITS / 8; }
+
+// acc += A*B for one K step, for the unscaled formats.
+DEVI f32x4 mma_step(const Frag<8>& a, const Frag<8>& b, f32x4 c) { return mfma_f8(a.v, b.v, c); }
+DEVI f32x4 mma_step(const Frag<16>& a, const Frag<16>& b, f32x4 c) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) c = mfma_bf16(a.v[s], b.v[s], c);
+  return c;
+}

@@ -1,0 +1,163 @@
+// Dynamic activation quantisation and the weighted top-k combine.
+//
+// Quantisation (LightMoE README, "MoE inference": BF16 input quantisation
+// before the gate/up projection and requantisation of the intermediate;
+// Alpha-MoE news page, "The MoE bottleneck": FP8 W8A8).  Per group of a
+// row: a = max|v|; FP8 groups use the fp32 scale s = a/448 (1 when a = 0)
+// and q = e4m3_rne(clamp(v/s, +-448)) with IEEE division; MX groups (OCP MX
+// v1.0) use X = 2^(floor(log2 a) - 8) stored as e8m0, and q = e4m3_rne_sat(v/X).
+//
+// Combine (LightMoE README, "MoE inference": routing-weight application and
+// deterministic combine): y[t] = sum over j ascending of w[t,j] times the
+// slot output of (t, j), plus the shared expert's row, rounded to bf16 once.
+#include "layer.h"
+
+template <int AF>
+struct QGroup {
+  static constexpr int CHUNKS = AF == MOE_A_FP8_G128 ? 16 : AF == MOE_A_MXFP8_G32 ? 4 : 0;
+};
+
+// One 256-thread block per row; thread owns 8-element chunks c = tid + 256*j.
+template <int AF, bool IN_BF16, int MAXJ>
+__global__ void __launch_bounds__(256) k_quant(QuantArgs qa) {
+  const int row = blockIdx.x;
+  if (qa.nrows && row >= *qa.nrows) return;
+  const int n = qa.n, nch = n / 8;
+  const int tid = threadIdx.x;
+  float v[MAXJ][8];
+  float gmax[MAXJ];
+#pragma unroll
+  for (int j = 0; j < MAXJ; ++j) {
+    int c = tid + 256 * j;
+    gmax[j] = 0.f;
+    if (c < nch) {
+      if (IN_BF16) {
+        const uint16_t* src = (const uint16_t*)qa.in + (size_t)row * n + 8 * c;
+        uint4 raw = *(const uint4*)src;
+        uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[j][2 * i] = bf16_to_f32((uint16_t)(w4[i] & 0xFFFF));
+          v[j][2 * i + 1] = bf16_to_f32((uint16_t)(w4[i] >> 16));
+        }
+      } else {
+        const float* src = (const float*)qa.in + (size_t)row * n + 8 * c;
+        float4 a = *(const float4*)src, b = *(const float4*)(src + 4);
+        v[j][0] = a.x; v[j][1] = a.y; v[j][2] = a.z; v[j][3] = a.w;
+        v[j][4] = b.x; v[j][5] = b.y; v[j][6] = b.z; v[j][7] = b.w;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) gmax[j] = fmaxf(gmax[j], fabsf(v[j][i]));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[j][i] = 0.f;
+    }
+  }
+  if (AF == MOE_A_FP8_TOKEN) {
+    __shared__ float red[4];
+    float m = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j) m = fmaxf(m, gmax[j]);
+    m = wave_max(m);
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j) gmax[j] = m;
+  } else {
+    constexpr int CH = QGroup<AF>::CHUNKS;   // consecutive lanes sharing a group
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j)
+#pragma unroll
+      for (int o = 1; o < CH; o <<= 1) gmax[j] = fmaxf(gmax[j], __shfl_xor(gmax[j], o, 64));
+  }
+#pragma unroll
+  for (int j = 0; j < MAXJ; ++j) {
+    int c = tid + 256 * j;
+    if (c >= nch) continue;
+    float a = gmax[j];
+    uint32_t lo, hi;
+    if (AF == MOE_A_MXFP8_G32) {
+      int ex = a > 0.f ? ilog2_floor(a) - 8 : -127;
+      ex = ex < -127 ? -127 : (ex > 127 ? 127 : ex);
+      float inv = __builtin_ldexpf(1.0f, -ex);   // exact power of two
+      lo = cvt4_e4m3(v[j][0] * inv, v[j][1] * inv, v[j][2] * inv, v[j][3] * inv);
+      hi = cvt4_e4m3(v[j][4] * inv, v[j][5] * inv, v[j][6] * inv, v[j][7] * inv);
+      if ((c & 3) == 0) ((uint8_t*)qa.scale)[(size_t)row * (n / 32) + c / 4] = (uint8_t)(ex + 127);
+    } else {
+      float s = a > 0.f ? a / 448.0f : 1.0f;
+      lo = cvt4_e4m3(v[j][0] / s, v[j][1] / s, v[j][2] / s, v[j][3] / s);
+      hi = cvt4_e4m3(v[j][4] / s, v[j][5] / s, v[j][6] / s, v[j][7] / s);
+      if (AF == MOE_A_FP8_TOKEN) {
+        if (c == 0) ((float*)qa.scale)[row] = s;
+      } else if ((c & 15) == 0) {
+        ((float*)qa.scale)[(size_t)row * (n / 128) + c / 16] = s;
+      }
+    }
+    *(uint2*)(qa.q + (size_t)row * n + 8 * c) = make_uint2(lo, hi);
+  }
+}
+
+template <int AF, bool IN_BF16>
+static hipError_t quant_dispatch_j(const QuantArgs& q, hipStream_t st) {
+  int nch = q.n / 8, j = (nch + 255) / 256;
+  dim3 grid(q.R), block(256);
+  if (j <= 1) hipLaunchKernelGGL((k_quant<AF, IN_BF16, 1>), grid, block, 0, st, q);
+  else if (j <= 2) hipLaunchKernelGGL((k_quant<AF, IN_BF16, 2>), grid, block, 0, st, q);
+  else if (j <= 4) hipLaunchKernelGGL((k_quant<AF, IN_BF16, 4>), grid, block, 0, st, q);
+  else if (j <= 8) hipLaunchKernelGGL((k_quant<AF, IN_BF16, 8>), grid, block, 0, st, q);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_quant(const QuantArgs& q, hipStream_t st) {
+  if (q.R == 0) return hipSuccess;
+  switch (q.a_format) {
+    case MOE_A_FP8_TOKEN:
+      return q.in_bf16 ? quant_dispatch_j<MOE_A_FP8_TOKEN, true>(q, st)
+                       : quant_dispatch_j<MOE_A_FP8_TOKEN, false>(q, st);
+    case MOE_A_FP8_G128:
+      return q.in_bf16 ? quant_dispatch_j<MOE_A_FP8_G128, true>(q, st)
+                       : quant_dispatch_j<MOE_A_FP8_G128, false>(q, st);
+    case MOE_A_MXFP8_G32:
+      return q.in_bf16 ? quant_dispatch_j<MOE_A_MXFP8_G32, true>(q, st)
+                       : quant_dispatch_j<MOE_A_MXFP8_G32, false>(q, st);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+// ------------------------------------------------------------------ combine
+// One 256-thread block per token; thread owns 8-column chunks.
+__global__ void __launch_bounds__(256) k_combine(CombineArgs c) {
+  const int t = blockIdx.x, H = c.H, nch = H / 8;
+  const int S = c.T * c.k;
+  for (int ch = threadIdx.x; ch < nch; ch += 256) {
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = 0; j < c.k; ++j) {
+      int slot = c.inv[t * c.k + j];
+      float wj = c.w[t * c.k + j];
+      const float* o = c.out_slot + (size_t)slot * H + 8 * ch;
+      float4 a = *(const float4*)o, b = *(const float4*)(o + 4);
+      acc[0] += wj * a.x; acc[1] += wj * a.y; acc[2] += wj * a.z; acc[3] += wj * a.w;
+      acc[4] += wj * b.x; acc[5] += wj * b.y; acc[6] += wj * b.z; acc[7] += wj * b.w;
+    }
+    if (c.shared) {
+      const float* o = c.out_slot + (size_t)(S + t) * H + 8 * ch;
+      float4 a = *(const float4*)o, b = *(const float4*)(o + 4);
+      acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+      acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+    }
+    uint32_t p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      p[i] = (uint32_t)f32_to_bf16(acc[2 * i]) | ((uint32_t)f32_to_bf16(acc[2 * i + 1]) << 16);
+    *(uint4*)(c.y + (size_t)t * H + 8 * ch) = make_uint4(p[0], p[1], p[2], p[3]);
+  }
+}
+
+hipError_t launch_combine(const CombineArgs& c, hipStream_t st) {
+  if (c.T == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_combine, dim3(c.T), dim3(256), 0, st, c);
+  return hipGetLastError();
+}

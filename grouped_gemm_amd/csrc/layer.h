@@ -1,0 +1,109 @@
+// Internal declarations shared by the kernels and the host library.
+#pragma once
+#include "common.h"
+
+#define MOE_SCORE_SOFTMAX 0
+#define MOE_SCORE_SIGMOID 1
+#define MOE_SCORE_PROBS 2
+
+// meta[] words written by the dispatch step
+#define META_NACTIVE 0   // active row groups (experts with rows, plus the shared group)
+#define META_NTILES 1    // entries of the block table
+#define META_CFG 2       // chosen configuration
+#define META_MAXCNT 3    // largest group
+#define META_ROWS 4      // total rows (slots), shared group included
+#define META_BM 5        // row-block height of the table
+#define META_ERROR 6     // nonzero: the device rejected the group offsets
+#define META_WORDS 16
+
+// Slots up to which one 1024-thread block does the whole dispatch.
+#define SMALL_DISPATCH_SLOTS 8192
+
+// Tile configurations: 0 streams weights (decode-sized groups); the others
+// are LDS-tiled with the given row-block height.
+#define NUM_CFGS_MAX 4
+
+__host__ __device__ inline int cfg_rows(int cfg) {
+  switch (cfg) {
+    case 0: return 64;
+    case 1: return 32;
+    case 2: return 64;
+    case 3: return 128;
+    default: return 64;
+  }
+}
+
+struct DispatchArgs {
+  const float* scores;    // [T,E] or NULL when ids are given
+  const int32_t* ids_in;  // [T,k] when scores == NULL
+  int32_t* ids;           // [T,k] routing output (when scores != NULL)
+  float* w;               // [T,k]
+  int T, E, k, score_fn, shared;
+  int32_t* counts;        // [G]
+  int32_t* indptr;        // [G+1]
+  int32_t* gather;        // [S + shared*T]
+  int32_t* inv;           // [S]
+  int32_t* active;        // [G]
+  int32_t* tiles;         // [2 * max tiles]
+  int32_t* meta;          // [META_WORDS]
+  int32_t* chunk;         // [ceil(S/1024) * E]
+  int force_cfg;          // -1: choose from the histogram
+  int H, I, wbits, xbits; // for the cost model
+  int num_cfgs;           // configurations the library has kernels for
+};
+
+// Grouped GEMM over expert-major row groups.
+struct GemmArgs {
+  const uint8_t* w0;      // routed weights [E, N, K] (gate or down)
+  const uint8_t* w1;      // routed up weights (gate/up op)
+  const void* w0s;        // weight scales per format
+  const void* w1s;
+  const uint8_t* sh_w0;   // shared expert (group E), or NULL
+  const uint8_t* sh_w1;
+  const void* sh_w0s;
+  const void* sh_w1s;
+  int E;                  // routed groups; group E is the shared expert
+  int N, K;
+  const uint8_t* a;       // activation rows (bf16 or e4m3 codes)
+  const void* a_scale;    // per format
+  const int32_t* gather;  // NULL: row = slot; else row = gather[slot] / gather_div
+  int gather_div;
+  const int32_t* counts;
+  const int32_t* indptr;
+  const int32_t* active;
+  const int32_t* tiles;
+  const int32_t* meta;
+  int cfg_self;           // this launch runs only if meta[META_CFG] == cfg_self (or -1)
+  void* out;              // gate/up: bf16 h or fp32 h staging; down: fp32 [rows, N]
+  int max_groups;         // grid bound on active groups (streaming kernel)
+};
+
+struct QuantArgs {
+  const void* in;         // rows [R, n], bf16 (in_bf16) or fp32
+  int in_bf16;
+  int R, n;
+  const int32_t* nrows;   // optional device row count (NULL: R)
+  uint8_t* q;             // [R, n] e4m3
+  void* scale;            // fp32 [R] / fp32 [R, n/128] / uint8 [R, n/32]
+  int a_format;
+};
+
+struct CombineArgs {
+  const float* out_slot;  // [S + shared*T, H]
+  const float* w;         // [T,k]
+  const int32_t* inv;     // [T*k]
+  int T, k, H, shared;
+  uint16_t* y;            // [T,H] bf16
+};
+
+hipError_t launch_route(const float* scores, int T, int E, int k, int score_fn, int32_t* ids,
+                        float* w, hipStream_t st);
+hipError_t launch_dispatch(const DispatchArgs& d, hipStream_t st);
+size_t dispatch_small_lds(int T, int k, int G);
+hipError_t launch_quant(const QuantArgs& q, hipStream_t st);
+hipError_t launch_combine(const CombineArgs& c, hipStream_t st);
+hipError_t launch_indptr_table(const int32_t* user_indptr, int cap, const DispatchArgs& d,
+                               hipStream_t st);
+// Streaming (decode) grouped GEMM; fmt = Fmt, gateup = fused SwiGLU op.
+hipError_t launch_gemm_stream(int fmt, bool gateup, const GemmArgs& g, hipStream_t st);
+hipError_t launch_gemm_tiled(int fmt, bool gateup, int cfg, const GemmArgs& g, hipStream_t st);

@@ -1,0 +1,486 @@
+// Top-k routing, deterministic expert-major dispatch, the block table and
+// the on-device tile-configuration choice.
+//
+// Routing follows the Alpha-MoE news page ("How the megakernel works":
+// routing and gating are stages of the layer) and the LightMoE README ("MoE
+// inference": int32 ids distinct per token, fp32 weights).  Dispatch follows
+// the LightMoE README (API table: deterministic expert-major dispatch;
+// "Grouped GEMM": m_indptr of E+1 entries, zero-row experts valid; "MoE
+// training": gather indices and inverse slots).  The block table is the
+// block-id -> (expert, row offset) map of the pure-Triton MoE commentary
+// (second paragraph).  The configuration is chosen from the runtime expert
+// histogram as in the RaMP abstract.
+//
+// Determinism: integer counts are order-independent sums; every slot
+// position comes from a stable rank (count of earlier equal ids), computed
+// with wave ballots and per-wave prefix sums, never from atomic arrival order.
+#include "layer.h"
+
+// Order-preserving map of an fp32 score to uint32 (+0 and -0 compare equal).
+DEVI uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if (u == 0x80000000u) u = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+DEVI uint64_t shfl_xor_u64(uint64_t v, int m) {
+  uint32_t lo = __shfl_xor((uint32_t)v, m, 64);
+  uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// One wave routes one token.  Each lane keeps up to four candidate experts
+// (e = lane + 64*i) as 64-bit keys (score key, 0xFFFF - e): the maximum key
+// is the highest score with the lowest index among equals.
+DEVI void route_one_token(const float* row, int E, int k, int score_fn, int lane, int32_t* ids_out,
+                          float* w_out, int32_t* ids_lds) {
+  uint64_t key[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int e = lane + 64 * i;
+    key[i] = (e < E) ? (((uint64_t)score_key(row[e]) << 32) | (uint32_t)(0xFFFF - e)) : 0ull;
+  }
+  int my_id = 0;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) best = key[i] > best ? key[i] : best;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      uint64_t other = shfl_xor_u64(best, o);
+      best = other > best ? other : best;
+    }
+    int be = 0xFFFF - (int)(best & 0xFFFFu);
+    if (lane == (be & 63)) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i == (be >> 6)) key[i] = 0ull;
+    }
+    if (lane == j) my_id = be;
+  }
+  // gate weights over the chosen k, renormalised
+  float l = (lane < k) ? row[my_id] : 0.f;
+  float top = __shfl(l, 0, 64);
+  float v = 0.f;
+  if (lane < k) {
+    if (score_fn == MOE_SCORE_SOFTMAX)
+      v = expf(l - top);
+    else if (score_fn == MOE_SCORE_SIGMOID)
+      v = 1.0f / (1.0f + expf(-l));
+    else
+      v = l;
+  }
+  float sum = wave_sum(v);
+  if (lane < k) {
+    ids_out[lane] = my_id;
+    w_out[lane] = v / sum;
+    if (ids_lds) ids_lds[lane] = my_id;
+  }
+}
+
+__global__ void __launch_bounds__(256) k_route(const float* __restrict__ scores, int T, int E, int k,
+                                               int score_fn, int32_t* __restrict__ ids,
+                                               float* __restrict__ w) {
+  int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  route_one_token(scores + (size_t)t * E, E, k, score_fn, lane, ids + (size_t)t * k,
+                  w + (size_t)t * k, nullptr);
+}
+
+// ------------------------------------------------------------------ ranks
+// For lanes holding key e (valid), the number of lower lanes with the same
+// key, the number of lanes with that key, and whether this lane is the
+// highest one of its key.
+DEVI void wave_match(int e, bool valid, int lane, int& rank, int& cnt, bool& last) {
+  uint64_t todo = __ballot(valid);
+  rank = 0;
+  cnt = 0;
+  last = false;
+  while (todo) {
+    int leader = __ffsll((unsigned long long)todo) - 1;
+    int le = __shfl(e, leader, 64);
+    bool mine = valid && e == le;
+    uint64_t m = __ballot(mine);
+    if (mine) {
+      rank = __popcll(m & ((1ull << lane) - 1ull));
+      cnt = __popcll(m);
+      last = lane == (63 - __clzll(m));
+    }
+    todo &= ~m;
+  }
+}
+
+// Stable ranks of up to 1024 keys held one per thread of a 1024-thread
+// block (thread order = slot order).  wcnt is LDS [16][G] and must be zero
+// on entry; it is zero again on exit.  Returns each valid thread's rank
+// among lower threads with the same key; if `totals` is given, adds each
+// key's count in this round to totals[key].
+DEVI int block_stable_rank(int e, bool valid, int32_t* wcnt, int G, int32_t* totals) {
+  int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int rank, cnt;
+  bool last;
+  wave_match(e, valid, lane, rank, cnt, last);
+  if (valid && last) wcnt[wave * G + e] = cnt;
+  __syncthreads();
+  int pre = 0;
+  if (valid)
+    for (int w = 0; w < wave; ++w) pre += wcnt[w * G + e];
+  __syncthreads();
+  for (int g = tid; g < G; g += blockDim.x) {
+    int s = 0;
+    for (int w = 0; w < 16; ++w) {
+      s += wcnt[w * G + g];
+      wcnt[w * G + g] = 0;
+    }
+    if (totals) totals[g] += s;
+  }
+  __syncthreads();
+  return pre + rank;
+}
+
+// Exclusive prefix sum of n <= 1024 ints in LDS, in place, by one wave
+// (wave 0); returns nothing, result visible after the caller's barrier.
+DEVI void wave0_exclusive_scan(int32_t* a, int n, int32_t* total) {
+  int tid = threadIdx.x;
+  if (tid >= 64) return;
+  constexpr int PER = 16;
+  int base = tid * PER;
+  int loc[PER];
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    loc[i] = (base + i < n) ? a[base + i] : 0;
+    s += loc[i];
+  }
+  int inc = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int v = __shfl_up(inc, o, 64);
+    if (tid >= o) inc += v;
+  }
+  int run = inc - s;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (base + i < n) a[base + i] = run;
+    run += loc[i];
+  }
+  if (tid == 63 && total) *total = inc;
+}
+
+// ---------------------------------------------------------------- config choice
+// Cost of running the two projections with configuration cfg, from the
+// grid geometry (RaMP abstract: the cost depends on the CTA grid the
+// histogram induces).  Each configuration is priced as
+//   waves(cfg) * wave_time(cfg) + fixed(cfg)
+// where a "wave" is one round of workgroups over all CUs, and a workgroup's
+// time is the larger of its HBM bytes at the per-CU share of bandwidth and
+// its MFMA work at the per-CU share of peak.  Streaming (cfg 0) re-reads an
+// expert's weights once per 64-row chunk; tiled configurations read the
+// weight tile once per row block.
+DEVI float config_cost(int cfg, const int32_t* cnt, int G, int H, int I, int wbits, int xbits,
+                       int lane) {
+  const float cus = 256.f, bw_cu = 8.0e12f / 256.f;          // bytes/s per CU
+  const float mfma_cu = (wbits == 16 ? 2.5e15f : 5.0e15f) / 256.f;
+  float t = 0.f;
+  if (cfg == 0) {
+    // GEMM1 + GEMM2 weight bytes per 64-row pass of each active group
+    float wbytes = 3.f * H * (float)I * wbits / 8.f;
+    float passes = 0.f;
+    for (int g = lane; g < G; g += 64) passes += (float)((cnt[g] + 63) / 64);
+    passes = wave_sum(passes);
+    t = passes * wbytes / (bw_cu * cus) + 8e-6f;
+  } else {
+    int bm = cfg_rows(cfg), bn = 128;
+    float tiles = 0.f;
+    for (int g = lane; g < G; g += 64) tiles += (float)((cnt[g] + bm - 1) / bm);
+    tiles = wave_sum(tiles);
+    // gate/up tile: 2*bn weight rows x H; down tile: bn rows x I
+    float tiles1 = tiles * (I / bn), tiles2 = tiles * (H / bn);
+    float by1 = (2.f * bn * H * wbits + (float)bm * H * xbits) / 8.f;
+    float fl1 = 4.f * bm * bn * (float)H;
+    float by2 = ((float)bn * I * wbits + (float)bm * I * xbits) / 8.f;
+    float fl2 = 2.f * bm * bn * (float)I;
+    float t1 = fmaxf(by1 / bw_cu, fl1 / mfma_cu), t2 = fmaxf(by2 / bw_cu, fl2 / mfma_cu);
+    t = ceilf(tiles1 / cus) * t1 + ceilf(tiles2 / cus) * t2 + 12e-6f;
+  }
+  return t;
+}
+
+// Shared tail of both dispatch paths.  cnt (LDS, G entries) holds the
+// group counts; writes counts, m_indptr, the active-group list, the chosen
+// configuration, its block table and meta.  All threads of a 1024-thread
+// block must call it.
+DEVI void finalize_dispatch(const DispatchArgs& d, int32_t* cnt, int32_t* scan_buf,
+                            int32_t* flag_buf, int32_t* tiles_buf, int G, int S_total) {
+  int tid = threadIdx.x;
+  __shared__ int32_t s_total, s_active, s_cfg, s_max, s_ntiles;
+  for (int g = tid; g < G; g += blockDim.x) {
+    scan_buf[g] = cnt[g];
+    flag_buf[g] = cnt[g] > 0 ? 1 : 0;
+    d.counts[g] = cnt[g];
+  }
+  __syncthreads();
+  wave0_exclusive_scan(scan_buf, G, &s_total);
+  __syncthreads();
+  if (tid >= 64 && tid < 128) {
+    // a second wave scans the active flags concurrently
+    int l = tid - 64;
+    constexpr int PER = 16;
+    int base = l * PER, loc[PER], s = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      loc[i] = (base + i < G) ? flag_buf[base + i] : 0;
+      s += loc[i];
+    }
+    int inc = s;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      int v = __shfl_up(inc, o, 64);
+      if (l >= o) inc += v;
+    }
+    int run = inc - s;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (base + i < G && loc[i]) d.active[run] = base + i;
+      run += loc[i];
+    }
+    if (l == 63) s_active = inc;
+  }
+  if (tid >= 128 && tid < 192) {
+    // one wave evaluates every configuration's cost over the histogram
+    int l = tid - 128, mx = 0;
+    for (int g = l; g < G; g += 64) mx = cnt[g] > mx ? cnt[g] : mx;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      int v = __shfl_xor(mx, o, 64);
+      mx = v > mx ? v : mx;
+    }
+    int cfg = d.force_cfg;
+    if (cfg < 0) {
+      float best = 3.0e38f;
+      for (int c = 0; c < d.num_cfgs; ++c) {
+        float cost = config_cost(c, cnt, G, d.H, d.I, d.wbits, d.xbits, l);
+        if (cost < best) {
+          best = cost;
+          cfg = c;
+        }
+      }
+    }
+    if (l == 0) {
+      s_max = mx;
+      s_cfg = cfg;
+    }
+  }
+  __syncthreads();
+  for (int g = tid; g <= G; g += blockDim.x) d.indptr[g] = (g < G) ? scan_buf[g] : s_total;
+  // block table for the chosen row-block height
+  int bm = cfg_rows(s_cfg);
+  for (int g = tid; g < G; g += blockDim.x) tiles_buf[g] = (cnt[g] + bm - 1) / bm;
+  __syncthreads();
+  wave0_exclusive_scan(tiles_buf, G, &s_ntiles);
+  __syncthreads();
+  for (int g = tid; g < G; g += blockDim.x) {
+    int n = (cnt[g] + bm - 1) / bm, base = tiles_buf[g];
+    for (int r = 0; r < n; ++r) {
+      d.tiles[2 * (base + r)] = g;
+      d.tiles[2 * (base + r) + 1] = r * bm;
+    }
+  }
+  if (tid == 0) {
+    d.meta[META_NACTIVE] = s_active;
+    d.meta[META_NTILES] = s_ntiles;
+    d.meta[META_CFG] = s_cfg;
+    d.meta[META_MAXCNT] = s_max;
+    d.meta[META_ROWS] = S_total;
+    d.meta[META_BM] = bm;
+    d.meta[META_ERROR] = 0;
+  }
+}
+
+// ---------------------------------------------------------------- small path
+// One 1024-thread block: (optionally) routing, then counts, scan, stable
+// scatter, active list, configuration and block table.  For S = T*k <= 8192.
+__global__ void __launch_bounds__(1024) k_dispatch_small(DispatchArgs d) {
+  extern __shared__ int32_t smem[];
+  const int G = d.E + d.shared;
+  const int S = d.T * d.k;
+  int32_t* ids_l = smem;                       // [S]
+  int32_t* cnt = ids_l + S;                    // [G]
+  int32_t* run = cnt + G;                      // [G] running offsets
+  int32_t* wcnt = run + G;                     // [16*G]
+  int32_t* scan_buf = wcnt + 16 * G;           // [G]
+  int32_t* flag_buf = scan_buf + G;            // [G]
+  int32_t* tiles_buf = flag_buf + G;           // [G]
+  int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  if (d.scores) {
+    for (int t = wave; t < d.T; t += 16)
+      route_one_token(d.scores + (size_t)t * d.E, d.E, d.k, d.score_fn, lane, d.ids + (size_t)t * d.k,
+                      d.w + (size_t)t * d.k, ids_l + t * d.k);
+  } else {
+    for (int p = tid; p < S; p += blockDim.x) ids_l[p] = d.ids_in[p];
+  }
+  for (int g = tid; g < G; g += blockDim.x) {
+    cnt[g] = 0;
+    run[g] = 0;
+  }
+  for (int i = tid; i < 16 * G; i += blockDim.x) wcnt[i] = 0;
+  __syncthreads();
+  for (int p = tid; p < S; p += blockDim.x) atomicAdd(&cnt[ids_l[p]], 1);
+  __syncthreads();
+  if (tid == 0 && d.shared) cnt[d.E] = d.T;
+  __syncthreads();
+  finalize_dispatch(d, cnt, scan_buf, flag_buf, tiles_buf, G, S + (d.shared ? d.T : 0));
+  __syncthreads();
+  // Stable scatter, 1024 slots per round.  scan_buf[g] is the next free
+  // slot of group g; `run` collects this round's per-group totals.
+  for (int base = 0; base < S; base += 1024) {
+    int p = base + tid;
+    bool valid = p < S;
+    int e = valid ? ids_l[p] : 0;
+    int r = block_stable_rank(e, valid, wcnt, G, run);
+    if (valid) {
+      int slot = scan_buf[e] + r;
+      d.gather[slot] = p;
+      d.inv[p] = slot;
+    }
+    __syncthreads();
+    for (int g = tid; g < G; g += blockDim.x) {
+      scan_buf[g] += run[g];
+      run[g] = 0;
+    }
+    __syncthreads();
+  }
+  if (d.shared)
+    for (int t = tid; t < d.T; t += blockDim.x) d.gather[S + t] = t * d.k;
+}
+
+// ---------------------------------------------------------------- large path
+// 1) per-chunk histograms (1024 slots per chunk)
+__global__ void __launch_bounds__(1024) k_dispatch_hist(DispatchArgs d) {
+  extern __shared__ int32_t smem[];
+  int32_t* cnt = smem;   // [E]
+  int S = d.T * d.k, c = blockIdx.x, tid = threadIdx.x;
+  for (int e = tid; e < d.E; e += blockDim.x) cnt[e] = 0;
+  __syncthreads();
+  int p = c * 1024 + tid;
+  if (p < S) atomicAdd(&cnt[d.ids_in[p]], 1);
+  __syncthreads();
+  for (int e = tid; e < d.E; e += blockDim.x) d.chunk[(size_t)c * d.E + e] = cnt[e];
+}
+
+// 2) one block: chunk bases, group counts, scan, active list, config, table
+__global__ void __launch_bounds__(1024) k_dispatch_scan(DispatchArgs d) {
+  extern __shared__ int32_t smem[];
+  const int G = d.E + d.shared;
+  int32_t* cnt = smem;
+  int32_t* scan_buf = cnt + G;
+  int32_t* flag_buf = scan_buf + G;
+  int32_t* tiles_buf = flag_buf + G;
+  int S = d.T * d.k, nchunks = (S + 1023) / 1024, tid = threadIdx.x;
+  for (int e = tid; e < d.E; e += blockDim.x) {
+    int run = 0;
+    for (int c = 0; c < nchunks; ++c) {
+      int v = d.chunk[(size_t)c * d.E + e];
+      d.chunk[(size_t)c * d.E + e] = run;
+      run += v;
+    }
+    cnt[e] = run;
+  }
+  if (tid == 0 && d.shared) cnt[d.E] = d.T;
+  __syncthreads();
+  finalize_dispatch(d, cnt, scan_buf, flag_buf, tiles_buf, G, S + (d.shared ? d.T : 0));
+  if (d.shared)
+    for (int t = blockIdx.x * blockDim.x + tid; t < d.T; t += blockDim.x) d.gather[S + t] = t * d.k;
+}
+
+// 3) stable scatter of each chunk
+__global__ void __launch_bounds__(1024) k_dispatch_scatter(DispatchArgs d) {
+  extern __shared__ int32_t smem[];
+  const int G = d.E;
+  int32_t* wcnt = smem;  // [16*E]
+  int S = d.T * d.k, c = blockIdx.x, tid = threadIdx.x;
+  for (int i = tid; i < 16 * G; i += blockDim.x) wcnt[i] = 0;
+  __syncthreads();
+  int p = c * 1024 + tid;
+  bool valid = p < S;
+  int e = valid ? d.ids_in[p] : 0;
+  int r = block_stable_rank(e, valid, wcnt, G, nullptr);
+  if (valid) {
+    int slot = d.indptr[e] + d.chunk[(size_t)c * d.E + e] + r;
+    d.gather[slot] = p;
+    d.inv[p] = slot;
+  }
+}
+
+// ---------------------------------------------------------------- host launchers
+size_t dispatch_small_lds(int T, int k, int G) {
+  return sizeof(int32_t) * ((size_t)T * k + 2 * G + 16 * G + 3 * G);
+}
+
+hipError_t launch_route(const float* scores, int T, int E, int k, int score_fn, int32_t* ids,
+                        float* w, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_route, dim3((T + 3) / 4), dim3(256), 0, st, scores, T, E, k, score_fn, ids, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch(const DispatchArgs& d, hipStream_t st) {
+  const int G = d.E + d.shared;
+  const int S = d.T * d.k;
+  if (S <= SMALL_DISPATCH_SLOTS) {
+    hipLaunchKernelGGL(k_dispatch_small, dim3(1), dim3(1024), dispatch_small_lds(d.T, d.k, G), st, d);
+    return hipGetLastError();
+  }
+  // large path: routing (if requested) runs as its own grid first
+  DispatchArgs d2 = d;
+  if (d.scores) {
+    hipError_t e = launch_route(d.scores, d.T, d.E, d.k, d.score_fn, d.ids, d.w, st);
+    if (e != hipSuccess) return e;
+    d2.scores = nullptr;
+    d2.ids_in = d.ids;
+  }
+  int nchunks = (S + 1023) / 1024;
+  hipLaunchKernelGGL(k_dispatch_hist, dim3(nchunks), dim3(1024), sizeof(int32_t) * d.E, st, d2);
+  hipLaunchKernelGGL(k_dispatch_scan, dim3(1), dim3(1024), sizeof(int32_t) * 4 * G, st, d2);
+  hipLaunchKernelGGL(k_dispatch_scatter, dim3(nchunks), dim3(1024), sizeof(int32_t) * 16 * d.E, st,
+                     d2);
+  return hipGetLastError();
+}
+
+// Block table, counts and active list from a caller-supplied m_indptr (the
+// standalone grouped GEMM).  Rejects (runs nothing) when m_indptr is not
+// non-decreasing from 0 or exceeds `cap` rows.
+__global__ void __launch_bounds__(1024) k_indptr_table(const int32_t* __restrict__ user_indptr,
+                                                       int cap, DispatchArgs d) {
+  extern __shared__ int32_t smem[];
+  const int G = d.E;
+  int32_t* cnt = smem;
+  int32_t* scan_buf = cnt + G;
+  int32_t* flag_buf = scan_buf + G;
+  int32_t* tiles_buf = flag_buf + G;
+  __shared__ int bad;
+  int tid = threadIdx.x;
+  if (tid == 0) bad = (user_indptr[0] != 0 || user_indptr[G] > cap) ? 1 : 0;
+  __syncthreads();
+  for (int g = tid; g < G; g += blockDim.x) {
+    int c = user_indptr[g + 1] - user_indptr[g];
+    if (c < 0) atomicOr(&bad, 1);
+    cnt[g] = c;
+  }
+  __syncthreads();
+  if (bad) {
+    for (int g = tid; g < G; g += blockDim.x) cnt[g] = 0;
+    __syncthreads();
+  }
+  finalize_dispatch(d, cnt, scan_buf, flag_buf, tiles_buf, G, bad ? 0 : user_indptr[G]);
+  if (tid == 0 && bad) d.meta[META_ERROR] = 1;
+}
+
+hipError_t launch_indptr_table(const int32_t* user_indptr, int cap, const DispatchArgs& d,
+                               hipStream_t st) {
+  hipLaunchKernelGGL(k_indptr_table, dim3(1), dim3(1024), sizeof(int32_t) * 4 * d.E, st,
+                     user_indptr, cap, d);
+  return hipGetLastError();
+}

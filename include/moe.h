@@ -1,0 +1,217 @@
+/*
+ * moe.h -- C ABI of the gfx950 fused Mixture-of-Experts layer forward.
+ *
+ * The layer: top-k routing -> expert-major token dispatch -> grouped GEMM
+ * with the gate and up projections fused over one input tile and SwiGLU
+ * applied to the accumulators -> down-projection grouped GEMM -> weighted
+ * top-k combine, for one GPU that holds every expert.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are device pointers unless their name starts with host_.
+ *  - All work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
+ *    the default stream).  The returned status reports argument validation
+ *    and launch errors only; a fault inside a kernel surfaces at the
+ *    caller's next synchronisation.
+ *  - The caller owns every buffer: inputs, outputs, weights and the
+ *    workspace memory.  No entry point allocates device memory, except
+ *    moe_layer_forward's one-time graph instantiation per token count
+ *    (decode sizes only; see moe_workspace_set_graphs).
+ *  - A workspace serves one stream at a time (LightMoE README, "MoE
+ *    inference": one plan per concurrent stream because workspaces are
+ *    reused).  Calls that share a workspace on different streams race.
+ *  - Matrices are row-major.  Expert weights are [E, N, K] with K
+ *    contiguous, so every projection computes out = A * B^T (LightMoE README,
+ *    "Dense GEMM" and "Grouped GEMM").
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
+#endif
+
+/* Status codes. */
+#define MOE_OK 0
+#define MOE_EINVAL 1        /* bad argument (null pointer, bad size, bad enum) */
+#define MOE_EUNSUPPORTED 2  /* well-formed but outside what the kernels cover */
+#define MOE_ECAPACITY 3     /* exceeds the workspace's max_tokens / capacity */
+#define MOE_EHIP 4          /* a HIP runtime call failed */
+
+/* Router score functions (top-k always compares the given fp32 scores). */
+#define MOE_SCORE_SOFTMAX 0 /* scores are logits; weights = softmax over the k chosen */
+#define MOE_SCORE_SIGMOID 1 /* scores are logits; weights = sigmoid, renormalised over k */
+#define MOE_SCORE_PROBS 2   /* scores are probabilities; weights = p / sum of the k */
+
+/* Weight formats (stored codes, quantised offline by the caller). */
+#define MOE_W_BF16 0         /* bf16 [E,N,K] */
+#define MOE_W_FP8_CHANNEL 1  /* e4m3 [E,N,K] + fp32 scale per output row [E,N] */
+#define MOE_W_FP8_BLOCK128 2 /* e4m3 [E,N,K] + fp32 scale per 128x128 block [E,N/128,K/128] */
+#define MOE_W_MXFP4 3        /* e2m1 packed [E,N,K/2] (element 2i in the low nibble)
+                                + e8m0 scale per 1x32 block [E,N,K/32] (OCP MX v1.0) */
+
+/* Activation formats (quantised on the fly by the layer). */
+#define MOE_A_BF16 0         /* no quantisation; the intermediate is rounded to bf16 */
+#define MOE_A_FP8_TOKEN 1    /* e4m3, one fp32 scale per row (amax/448) */
+#define MOE_A_FP8_G128 2     /* e4m3, one fp32 scale per 1x128 group */
+#define MOE_A_MXFP8_G32 3    /* e4m3, one e8m0 scale per 1x32 group (OCP MX v1.0) */
+
+/* Grouped GEMM operations. */
+#define MOE_OP_PLAIN 0          /* out[r, n] = sum_k A[r,k] * B0[e,n,k], fp32 out */
+#define MOE_OP_GATEUP_SWIGLU 1  /* out[r, n] = SiLU(A*B0^T) * (A*B1^T), activation format */
+
+typedef struct moe_ws moe_ws; /* opaque host handle */
+
+/* Shape and formats of one MoE layer (fixed at workspace creation). */
+typedef struct moe_layer_desc {
+  int hidden;          /* H: multiple of 128 */
+  int inter;           /* I: multiple of 128 */
+  int num_experts;     /* E: 1..256 routed experts */
+  int top_k;           /* k: 1..min(E,16) */
+  int shared_experts;  /* 0 or 1 always-on shared expert (weight 1, outside renormalisation) */
+  int shared_inter;    /* I of the shared expert; must equal `inter` when shared_experts = 1 */
+  int score_fn;        /* MOE_SCORE_* */
+  int renormalize;     /* must be 1 (gate weights renormalised over the k chosen) */
+  int w_format;        /* MOE_W_* */
+  int a_format;        /* MOE_A_*; pairs: BF16/BF16, FP8_CHANNEL/FP8_TOKEN,
+                          FP8_BLOCK128/FP8_G128, MXFP4/MXFP8_G32 */
+  int max_tokens;      /* T capacity; T*top_k must not exceed 1,048,576 */
+} moe_layer_desc;
+
+/* Caller-owned expert weights, layout [E, N, K] K-contiguous (see formats). */
+typedef struct moe_weights {
+  const void *w_gate, *w_up, *w_down;   /* [E,I,H], [E,I,H], [E,H,I] codes */
+  const void *s_gate, *s_up, *s_down;   /* scales per format, or NULL for bf16 */
+  const void *sh_gate, *sh_up, *sh_down;/* shared expert [1,Is,H],[1,Is,H],[1,H,Is] or NULL */
+  const void *ss_gate, *ss_up, *ss_down;
+} moe_weights;
+
+/* Human-readable text for a status code (static storage). */
+MOE_API const char* moe_status_string(int status);
+/* Detail of the last error on the calling thread (thread-local storage). */
+MOE_API const char* moe_last_error(void);
+
+/* Bytes of device memory a workspace for `desc` needs.  Errors: EINVAL,
+ * EUNSUPPORTED for a shape or format pair outside the validation rules. */
+MOE_API int moe_workspace_size(const moe_layer_desc* desc, size_t* host_bytes);
+
+/* Build a workspace handle over caller-owned device memory `dev_buf` of
+ * `bytes` (at least moe_workspace_size, 256-byte aligned).  The handle is
+ * host memory owned by the library; the device buffer stays the caller's and
+ * must outlive the handle.  Also loads the kernels on the current device. */
+MOE_API int moe_workspace_create(const moe_layer_desc* desc, void* dev_buf, size_t bytes, moe_ws** out);
+
+/* Release the handle (and any graphs it instantiated).  NULL is a no-op. */
+MOE_API int moe_workspace_destroy(moe_ws* ws);
+
+/* Top-k routing (Alpha-MoE news page, "How the megakernel works": routing
+ * and gating; LightMoE README, "MoE inference": int32 ids distinct per
+ * token, fp32 weights).
+ *   scores     [T, E] fp32: logits (SOFTMAX/SIGMOID) or probabilities (PROBS)
+ *   topk_ids   [T, k] int32 out: the k largest scores in descending order,
+ *              ties broken towards the lower expert index (+0 == -0)
+ *   topk_w     [T, k] fp32 out: gate weights renormalised over the k
+ * T = 0 is a no-op.  Errors: EINVAL (nulls, k < 1, k > min(E,16), E > 256). */
+MOE_API int moe_route_topk(const float* scores, int T, int E, int k, int score_fn, int32_t* topk_ids,
+                   float* topk_w, void* stream);
+
+/* Deterministic expert-major dispatch (LightMoE README, API table and "MoE
+ * training": gather indices, m_indptr, inverse slots; "Grouped GEMM":
+ * m_indptr has E+1 entries and zero-row experts are valid).  Slots are
+ * ordered by expert, then by flat index t*k+j.
+ *   topk_ids  [T, k] int32 in, each in [0, E)
+ *   counts    [E]   int32 out: rows per expert
+ *   m_indptr  [E+1] int32 out: exclusive prefix sum of counts
+ *   gather    [T*k] int32 out: slot -> t*k+j
+ *   inv       [T*k] int32 out: t*k+j -> slot
+ * E must equal the workspace's num_experts and T <= max_tokens.  The
+ * workspace supplies scratch (per-chunk histograms).  Errors: EINVAL,
+ * ECAPACITY. */
+MOE_API int moe_dispatch(moe_ws* ws, const int32_t* topk_ids, int T, int k, int E, int32_t* counts,
+                 int32_t* m_indptr, int32_t* gather, int32_t* inv, void* stream);
+
+/* Grouped GEMM over expert-major rows, one launch for all experts and no
+ * padding (pure-Triton MoE commentary, second paragraph: block-id ->
+ * (expert, offset) map; LightMoE README, "Grouped GEMM").
+ *   op        MOE_OP_PLAIN or MOE_OP_GATEUP_SWIGLU
+ *   a         activation rows in the workspace's activation format:
+ *             bf16 [rows, K] for A_BF16, else e4m3 codes [rows, K]
+ *   a_scale   activation scales: fp32 [rows] (FP8_TOKEN), fp32 [rows, K/128]
+ *             (FP8_G128), uint8 e8m0 [rows, K/32] (MXFP8_G32); NULL for bf16
+ *   a_gather  NULL: row r of group e is a[m_indptr[e] + r]; else it is
+ *             a[a_gather[m_indptr[e] + r] / gather_div] (pass moe_dispatch's
+ *             gather and top_k to read token rows in place)
+ *   m_indptr  [E+1] int32, m_indptr[E] = total rows R (<= workspace capacity)
+ *   N, K      output columns and contraction length; b0/b1 are [E, N, K]
+ *             in the workspace's weight format with scales b0_scale/b1_scale
+ *             (b1 only for GATEUP_SWIGLU)
+ *   out       PLAIN: fp32 [R, N].  GATEUP_SWIGLU: h in the activation
+ *             format (bf16 [R, N], or e4m3 codes [R, N] + out_scale as for
+ *             a_scale with K replaced by N)
+ * Errors: EINVAL, EUNSUPPORTED (N or K not a multiple of 128), ECAPACITY. */
+MOE_API int moe_grouped_gemm(moe_ws* ws, int op, const void* a, const void* a_scale,
+                     const int32_t* a_gather, int gather_div, const int32_t* m_indptr, int E,
+                     int N, int K, const void* b0, const void* b0_scale, const void* b1,
+                     const void* b1_scale, void* out, void* out_scale, void* stream);
+
+/* Dynamic activation quantisation of bf16 rows x [T, H] into the
+ * workspace's activation format (LightMoE README, "MoE inference": input
+ * quantisation): per group, s = amax/448 in fp32 (1 when amax = 0) and
+ * q = e4m3_rne(clamp(x/s, +-448)); MX groups use X = 2^(floor(log2 amax)-8).
+ *   q [T, H] e4m3 codes out, scale as a_scale of moe_grouped_gemm.
+ * Errors: EINVAL, EUNSUPPORTED (bf16 format: nothing to quantise). */
+MOE_API int moe_quantize_act(moe_ws* ws, const uint16_t* x_bf16, int T, uint8_t* q, void* scale,
+                     void* stream);
+
+/* Weighted top-k combine (LightMoE README, "MoE inference": routing-weight
+ * application and deterministic combine):
+ *   y[t] = bf16( sum_{j<k} w[t,j] * out_slot[inv[t*k+j]] (+ out_slot[T*k+t]
+ *          when the layer has a shared expert) ), j ascending, fp32 sums.
+ *   out_slot [T*k (+T), H] fp32; y [T, H] bf16 out. */
+MOE_API int moe_combine(moe_ws* ws, const float* out_slot, const float* topk_w, const int32_t* inv, int T,
+                uint16_t* y_bf16, void* stream);
+
+/* The whole layer: x bf16 [T, H] and router scores [T, E] -> y bf16 [T, H].
+ * Runs routing, dispatch, activation quantisation, the fused gate/up SwiGLU
+ * grouped GEMM, intermediate requantisation, the down grouped GEMM and the
+ * combine.  The tile configuration is chosen on the device from the expert
+ * histogram (RaMP abstract: configuration from the runtime routing
+ * distribution, not batch size alone).  T = 0 is a no-op.
+ * Errors: EINVAL, ECAPACITY (T > max_tokens), EHIP. */
+MOE_API int moe_layer_forward(moe_ws* ws, const moe_weights* w, const uint16_t* x_bf16,
+                      const float* scores, int T, uint16_t* y_bf16, void* stream);
+
+/* Routing results of the workspace's last moe_layer_forward (device
+ * pointers into the workspace, valid until the next call):
+ * topk_ids [T,k], topk_w [T,k], counts [E(+1)], m_indptr [E+2 with the
+ * shared group], gather, inv.  Any out pointer may be NULL. */
+MOE_API int moe_workspace_routing(const moe_ws* ws, const int32_t** topk_ids, const float** topk_w,
+                          const int32_t** counts, const int32_t** m_indptr,
+                          const int32_t** gather, const int32_t** inv);
+
+/* Force the tile configuration (tests and cost-model fitting): -1 = choose
+ * from the histogram (default); 0 = streaming decode kernels; 1.. = tiled
+ * kernels with a row-block height given by moe_config_rows(cfg). */
+MOE_API int moe_workspace_force_config(moe_ws* ws, int cfg_id);
+/* Configuration used by the last moe_layer_forward (synchronises `stream`). */
+MOE_API int moe_workspace_last_config(const moe_ws* ws, int* host_cfg_id, void* stream);
+/* Row-block height of a configuration, or -1 if unknown. */
+MOE_API int moe_config_rows(int cfg_id);
+
+/* Enable (1, default) or disable (0) hipGraph capture of moe_layer_forward
+ * for decode token counts (T <= 128): the first call at each T captures
+ * and instantiates a graph, later calls with the same pointers replay it. */
+MOE_API int moe_workspace_set_graphs(moe_ws* ws, int enable);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -120,18 +120,15 @@ def _e4m3_bits(a32: np.ndarray) -> np.ndarray:
     return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
-_E2M1_MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
-
-
 def _e2m1_codes(v: np.ndarray) -> np.ndarray:
-    """Nearest e2m1 code (ties to the even code), saturating at 6."""
-    a = np.minimum(np.abs(v.astype(np.float64)), 6.0)
-    idx = np.searchsorted(_E2M1_MAG, a)            # first magnitude >= a
-    idx = np.clip(idx, 1, 7)
-    lo, hi = _E2M1_MAG[idx - 1], _E2M1_MAG[idx]
-    pick_hi = (a - lo > hi - a) | ((a - lo == hi - a) & (idx % 2 == 0))
-    code = np.where(pick_hi, idx, idx - 1).astype(np.uint8)
-    code = np.where(a == 0, 0, code).astype(np.uint8)
+    """Nearest e2m1 code (ties to the even code), saturating at 6.
+
+    The magnitudes are 0, .5, 1, 1.5, 2, 3, 4, 6 (codes 0..7); the code is
+    the number of midpoints the magnitude passes, where a value exactly on a
+    midpoint goes to the even code."""
+    a = np.abs(v)
+    code = ((a > 0.25).astype(np.uint8) + (a >= 0.75) + (a > 1.25) + (a >= 1.75)
+            + (a > 2.5) + (a >= 3.5) + (a > 5.0)).astype(np.uint8)
     sign = (np.signbit(v) & (code != 0)).astype(np.uint8) << 3
     return code | sign
 
@@ -154,16 +151,13 @@ def store_matrix(w32: np.ndarray, w_format: int):
         return q, s
     if w_format == W_MXFP4:
         assert k % 32 == 0
-        g = w32.reshape(n, k // 32, 32).astype(np.float64)
+        g = w32.reshape(n, k // 32, 32)
         amax = np.abs(g).max(axis=2)
-        with np.errstate(divide="ignore"):
-            e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))), -127.0)
-        # a few amax values sit just below a power of two in float64 log2
-        e = np.where((amax > 0) & (np.exp2(e + 1) <= amax), e + 1, e)
-        e = np.where((amax > 0) & (np.exp2(e) > amax), e - 1, e)
-        xe = np.where(amax > 0, e - 2, -127.0)
-        xe = np.clip(xe, -127, 127)
-        codes = _e2m1_codes(g / np.exp2(xe)[:, :, None]).reshape(n, k)
+        _, e = np.frexp(amax)                 # amax = m * 2^e, m in [0.5, 1)
+        xe = np.where(amax > 0, e.astype(np.int32) - 1 - 2, -127)   # floor(log2 amax) - 2
+        xe = np.clip(xe, -127, 127).astype(np.int32)
+        scaled = g * np.ldexp(np.float32(1.0), -xe)[:, :, None].astype(np.float32)
+        codes = _e2m1_codes(scaled).reshape(n, k)
         packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
         return packed, (xe + 127).astype(np.uint8)
     raise ValueError(w_format)

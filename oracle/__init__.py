@@ -67,6 +67,8 @@ def lib():
         L.oracle_layer_forward.restype = None
         L.oracle_layer_forward.argtypes = [i, i, i, i, i, i, P, P, P, P, P, P, i, i,
                                            P, P, P, P, P, P, P, P, P, P, i, P]
+        L.oracle_grouped_gemm.restype = None
+        L.oracle_grouped_gemm.argtypes = [i, i, i, P, P, P, i, P, i, i, i, P, P, P, P, P]
         _lib = L
     return _lib
 
@@ -178,3 +180,21 @@ def layer_forward(weights, x_bits, ids, w, tokens=None) -> np.ndarray:
         _p(weights.sh_down), _p(weights.ss_down),
         _p(x_bits), _p(ids), _p(w), _p(toks), len(toks), _p(y))
     return y
+
+
+def grouped_gemm(w_format, a_format, op, a, a_scale, a_gather, gather_div, m_indptr, N, K,
+                 b0, b0s, b1=None, b1s=None) -> np.ndarray:
+    """fp64 grouped projection (op 0 plain, op 1 SwiGLU of gate/up)."""
+    m_indptr = _c(m_indptr, np.int32)
+    E = len(m_indptr) - 1
+    R = int(m_indptr[-1])
+    out = np.zeros((R, N), dtype=np.float64)
+    ag = None if a_gather is None else _c(a_gather, np.int32)
+    lib().oracle_grouped_gemm(w_format, a_format, op, _p(np.ascontiguousarray(a)),
+                              None if a_scale is None else _p(np.ascontiguousarray(a_scale)),
+                              _p(ag), int(gather_div), _p(m_indptr), E, N, K,
+                              _p(np.ascontiguousarray(b0)),
+                              None if b0s is None else _p(np.ascontiguousarray(b0s)),
+                              None if b1 is None else _p(np.ascontiguousarray(b1)),
+                              None if b1s is None else _p(np.ascontiguousarray(b1s)), _p(out))
+    return out

@@ -410,3 +410,53 @@ void oracle_layer_forward(int H, int I, int E, int k, int w_format, int a_format
   free(xq);
   free(o);
 }
+
+/* ------------------------------------------------------------ grouped GEMM
+ * The grouped projection on its own (LightMoE README, "Grouped GEMM":
+ * contiguous expert-major rows delimited by m_indptr; out = A * B^T per
+ * expert).  Row r of group e (m_indptr[e] <= r < m_indptr[e+1]) reads
+ * activation row a_gather ? a_gather[r] / gather_div : r, dequantised under
+ * a_format (codes times the row's, group's or block's scale).
+ *   op 0: out[r, n] = sum_k a[r, k] * B0[e, n, k]
+ *   op 1: out[r, n] = SiLU(sum_k a B0) * (sum_k a B1), not requantised.
+ * out is fp64 [m_indptr[E], N]. */
+void oracle_grouped_gemm(int w_format, int a_format, int op, const void* a, const void* a_scale,
+                         const int32_t* a_gather, int gather_div, const int32_t* m_indptr, int E,
+                         int N, int K, const void* b0, const void* b0s, const void* b1,
+                         const void* b1s, double* out) {
+  double* arow = (double*)malloc(sizeof(double) * (size_t)K);
+  double* g = (double*)malloc(sizeof(double) * (size_t)N);
+  double* u = (double*)malloc(sizeof(double) * (size_t)N);
+  for (int e = 0; e < E; ++e) {
+    oracle_mat B0 = expert_mat(w_format, b0, b0s, e, N, K);
+    oracle_mat B1 = expert_mat(w_format, b1 ? b1 : b0, b1 ? b1s : b0s, e, N, K);
+    for (int r = m_indptr[e]; r < m_indptr[e + 1]; ++r) {
+      long src = a_gather ? a_gather[r] / gather_div : r;
+      for (int k = 0; k < K; ++k) {
+        if (a_format == A_BF16) {
+          arow[k] = oracle_bf16_decode(((const uint16_t*)a)[src * K + k]);
+          continue;
+        }
+        double q = oracle_e4m3_decode(((const uint8_t*)a)[src * K + k]);
+        double s;
+        if (a_format == A_FP8_TOKEN)
+          s = ((const float*)a_scale)[src];
+        else if (a_format == A_FP8_G128)
+          s = ((const float*)a_scale)[src * (K / 128) + k / 128];
+        else
+          s = oracle_e8m0_decode(((const uint8_t*)a_scale)[src * (K / 32) + k / 32]);
+        arow[k] = q * s;
+      }
+      matvec(&B0, arow, g);
+      if (op == 1) {
+        matvec(&B1, arow, u);
+        for (int n = 0; n < N; ++n) out[(size_t)r * N + n] = silu(g[n]) * u[n];
+      } else {
+        for (int n = 0; n < N; ++n) out[(size_t)r * N + n] = g[n];
+      }
+    }
+  }
+  free(arow);
+  free(g);
+  free(u);
+}

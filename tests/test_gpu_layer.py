@@ -1,0 +1,136 @@
+"""GPU parity of the whole layer (moe_layer_forward through the C ABI).
+
+Small shapes (oracle on every token) span several 16-channel blocks, several
+K steps and ragged token tails for every format; full-size shapes (the
+benchmarked layer shapes) are checked on sampled tokens.  Routing, counts,
+offsets and the permutation are bit-exact; the output is within the
+relative-Frobenius tolerance of its format.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth as ms
+import oracle
+from gpu_util import (bf16_to_f64, check_routing, dev_weights, relerr, run_layer, say, tol_for,
+                      workspace, ws_routing)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    ("bf16", ms.small_shape("tiny", hidden=512, inter=384, experts=6, top_k=2), 37),
+    ("fp8_channel", ms.small_shape("mixtral", hidden=512, inter=768, experts=8, top_k=2), 45),
+    ("fp8_block", ms.small_shape("qwen", hidden=384, inter=256, experts=12, top_k=4), 53),
+    ("fp8_block_shared", ms.small_shape("dsv3", hidden=512, inter=256, experts=16, top_k=3,
+                                        shared_inter=256), 29),
+    ("mxfp4", ms.small_shape("imbalance", hidden=384, inter=512, experts=10, top_k=3), 41),
+    ("tiny_cfg", ms.CONFIGS["tiny"], 32),
+]
+
+
+@pytest.mark.parametrize("name,sh,T", SMALL, ids=[c[0] for c in SMALL])
+def test_layer_small_matches_oracle(name, sh, T):
+    say("layer small", name, T)
+    W = ms.gen_weights(sh)
+    B = ms.gen_batch(sh, T)
+    ws = workspace(sh, T)
+    y = run_layer(ws, dev_weights(W), B.x_bits, B.scores)
+    ids, w = check_routing(sh, T, ws_routing(ws, sh, T), B.scores)
+    ref = oracle.layer_forward(W, B.x_bits, ids, w)
+    err = relerr(bf16_to_f64(y), ref)
+    say("  relerr", err)
+    assert np.all(np.isfinite(bf16_to_f64(y)))
+    assert err <= tol_for(sh)
+
+
+def test_layer_is_deterministic_and_graph_replay_matches_eager():
+    sh = SMALL[1][1]
+    T = 24
+    W = ms.gen_weights(sh)
+    B = ms.gen_batch(sh, T)
+    dW = dev_weights(W)
+    ws = workspace(sh, T)
+    ws.set_graphs(False)
+    y0 = run_layer(ws, dW, B.x_bits, B.scores)
+    y1 = run_layer(ws, dW, B.x_bits, B.scores)
+    np.testing.assert_array_equal(y0, y1)
+    ws.set_graphs(True)
+    st = torch.cuda.Stream()
+    x = torch.from_numpy(B.x_bits.view(np.int16)).cuda()
+    s = torch.from_numpy(B.scores).cuda()
+    import grouped_gemm_amd as g
+    for rep in range(4):
+        y = torch.zeros(T, sh.hidden, dtype=torch.int16, device="cuda")
+        torch.cuda.synchronize()
+        with torch.cuda.stream(st):
+            yg = torch.empty(T, sh.hidden, dtype=torch.int16, device="cuda")
+            g.layer_forward(ws, dW, x, s, yg, stream=st)
+        st.synchronize()
+        # eager work between replays
+        y.copy_(yg)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(y.cpu().numpy().view(np.uint16), y0)
+
+
+def test_zero_token_experts_with_nan_weights_are_inert():
+    sh = SMALL[1][1]
+    T = 20
+    W = ms.gen_weights(sh)
+    B = ms.gen_batch(sh, T)
+    s = B.scores.copy()
+    s[:, 3] -= 100.0
+    s[:, 5] -= 100.0
+    ws = workspace(sh, T)
+    ws.set_graphs(False)
+    y0 = run_layer(ws, dev_weights(W), B.x_bits, s)
+    for e in (3, 5):
+        W.w_gate[e] = 0x7F
+        W.w_up[e] = 0x7F
+        W.w_down[e] = 0x7F
+        W.s_gate[e] = np.nan
+        W.s_down[e] = np.nan
+    y1 = run_layer(ws, dev_weights(W), B.x_bits, s)
+    assert np.all(np.isfinite(bf16_to_f64(y1)))
+    np.testing.assert_array_equal(y0, y1)
+
+
+def test_all_tokens_one_expert():
+    sh = ms.small_shape("qwen", hidden=256, inter=256, experts=8, top_k=1)
+    T = 150   # more than one 64-row chunk in one group
+    W = ms.gen_weights(sh)
+    B = ms.gen_batch(sh, T)
+    s = B.scores.copy()
+    s[:, 2] += 100.0
+    ws = workspace(sh, T)
+    y = run_layer(ws, dev_weights(W), B.x_bits, s)
+    ids, w = check_routing(sh, T, ws_routing(ws, sh, T), s)
+    assert np.all(ids == 2)
+    ref = oracle.layer_forward(W, B.x_bits, ids, w)
+    assert relerr(bf16_to_f64(y), ref) <= tol_for(sh)
+
+
+# Full-size layer shapes; tokens sampled for the oracle.
+FULL = [("mixtral", 1), ("mixtral", 32), ("mixtral", 128), ("tiny", 32), ("qwen", 8192),
+        ("dsv3", 1), ("dsv3", 16), ("dsv3", 256), ("dsv3", 4096), ("imbalance", 2048)]
+
+
+@pytest.mark.parametrize("name,T", FULL, ids=[f"{n}-T{t}" for n, t in FULL])
+def test_layer_full_size_sampled(name, T):
+    sh = ms.CONFIGS[name]
+    say("layer full", name, T)
+    B = ms.gen_batch(sh, T)
+    ids_ref, _ = oracle.route(B.scores, sh.top_k, sh.score_fn)
+    active = sorted(set(np.unique(ids_ref).tolist()))
+    W = ms.gen_weights(sh, experts=active)      # inactive experts stay zero (never read)
+    say("  weights ready,", len(active), "active experts")
+    ws = workspace(sh, T)
+    y = run_layer(ws, dev_weights(W), B.x_bits, B.scores)
+    ids, w = check_routing(sh, T, ws_routing(ws, sh, T), B.scores)
+    rng = np.random.default_rng(T)
+    n = min(T, 12)
+    toks = np.unique(np.concatenate([[0, T - 1], rng.choice(T, size=n, replace=False)]))
+    ref = oracle.layer_forward(W, B.x_bits, ids, w, tokens=toks)
+    err = relerr(bf16_to_f64(y[toks]), ref)
+    say("  sampled relerr", err, "tokens", len(toks))
+    assert np.all(np.isfinite(bf16_to_f64(y)))
+    assert err <= tol_for(sh)

@@ -1,0 +1,113 @@
+"""GPU parity: routing, dispatch and activation quantisation, bit-exact
+against the oracle (integer and code outputs), gate weights within 1e-6."""
+import numpy as np
+import pytest
+import torch
+
+import grouped_gemm_amd as g
+import moe_synth as ms
+import oracle
+from gpu_util import dev, say, workspace
+
+pytestmark = pytest.mark.gpu
+
+ROUTE_CASES = [
+    ("tiny", 37), ("mixtral", 128), ("qwen", 301), ("dsv3", 16), ("imbalance", 300),
+]
+
+
+@pytest.mark.parametrize("name,T", ROUTE_CASES)
+def test_route_topk_matches_oracle(name, T):
+    sh = ms.CONFIGS[name]
+    say("route", name, T)
+    B = ms.gen_batch(sh, T)
+    s = B.scores.copy()
+    # plant exact ties, including +0/-0, on a few tokens
+    s[0, :] = 0.0
+    s[1, ::2] = -0.0
+    s[2, : min(6, sh.experts)] = s[2, 0]
+    ids_ref, w_ref = oracle.route(s, sh.top_k, sh.score_fn)
+    ds = dev(s)
+    ids = torch.empty(T, sh.top_k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, sh.top_k, dtype=torch.float32, device="cuda")
+    g.route_topk(ds, sh.top_k, sh.score_fn, ids, w)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ids.cpu().numpy(), ids_ref)
+    wn = w.cpu().numpy().astype(np.float64)
+    np.testing.assert_allclose(wn, w_ref, rtol=0, atol=1e-6)
+    # an all-zero probability row has no defined weights (0/0 on both sides)
+    ok = ~np.isnan(w_ref).any(axis=1)
+    np.testing.assert_array_equal(np.isnan(wn).any(axis=1), ~ok)
+    np.testing.assert_allclose(wn[ok].sum(1), 1.0, rtol=0, atol=1e-6)
+
+
+@pytest.mark.parametrize("name,T", [("mixtral", 128), ("dsv3", 1000), ("qwen", 8192),
+                                    ("imbalance", 2048), ("tiny", 1)])
+def test_dispatch_matches_oracle(name, T):
+    sh = ms.CONFIGS[name]
+    say("dispatch", name, T)
+    B = ms.gen_batch(sh, T)
+    ids_ref, _ = oracle.route(B.scores, sh.top_k, sh.score_fn)
+    counts, indptr, gather, inv = oracle.dispatch(ids_ref, sh.experts)
+    ws = workspace(sh.with_(shared=0, shared_inter=0), T)
+    E, S = sh.experts, T * sh.top_k
+    d_c = torch.empty(E, dtype=torch.int32, device="cuda")
+    d_i = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    d_g = torch.empty(S, dtype=torch.int32, device="cuda")
+    d_v = torch.empty(S, dtype=torch.int32, device="cuda")
+    g.dispatch(ws, dev(ids_ref), E, d_c, d_i, d_g, d_v)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(d_c.cpu().numpy(), counts)
+    np.testing.assert_array_equal(d_i.cpu().numpy(), indptr)
+    np.testing.assert_array_equal(d_g.cpu().numpy(), gather)
+    np.testing.assert_array_equal(d_v.cpu().numpy(), inv)
+
+
+def test_dispatch_all_tokens_one_expert_and_empty_experts():
+    sh = ms.CONFIGS["qwen"]
+    for T in (5, 2000):          # one-block path and multi-block path
+        ids = np.zeros((T, sh.top_k), dtype=np.int32)
+        ids[:, :] = np.arange(sh.top_k, dtype=np.int32)[None, :] * 31   # 8 experts, 248 empty
+        counts, indptr, gather, inv = oracle.dispatch(ids, sh.experts)
+        ws = workspace(sh, T)
+        E, S = sh.experts, T * sh.top_k
+        d_c = torch.empty(E, dtype=torch.int32, device="cuda")
+        d_i = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+        d_g = torch.empty(S, dtype=torch.int32, device="cuda")
+        d_v = torch.empty(S, dtype=torch.int32, device="cuda")
+        g.dispatch(ws, dev(ids), E, d_c, d_i, d_g, d_v)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(d_c.cpu().numpy(), counts)
+        np.testing.assert_array_equal(d_i.cpu().numpy(), indptr)
+        np.testing.assert_array_equal(d_g.cpu().numpy(), gather)
+        np.testing.assert_array_equal(d_v.cpu().numpy(), inv)
+
+
+@pytest.mark.parametrize("name", ["mixtral", "qwen", "imbalance", "dsv3"])
+def test_quantize_act_bit_exact(name):
+    sh = ms.CONFIGS[name]
+    say("quant", name)
+    T = 19
+    B = ms.gen_batch(sh, T)
+    x = B.x_bits.copy()
+    x[3] = 0                                  # all-zero row
+    x[4, :7] = np.array([0x3F80, 0xBF80, 0x0001, 0x8001, 0x7F00, 0xFF00, 0x0000], np.uint16)
+    xv = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    q_ref, s_ref = oracle.quant_rows(xv, sh.a_format)
+    ws = workspace(sh, T)
+    H = sh.hidden
+    q = torch.empty(T, H, dtype=torch.uint8, device="cuda")
+    if sh.a_format == ms.A_FP8_TOKEN:
+        sc = torch.empty(T, dtype=torch.float32, device="cuda")
+    elif sh.a_format == ms.A_FP8_G128:
+        sc = torch.empty(T, H // 128, dtype=torch.float32, device="cuda")
+    else:
+        sc = torch.empty(T, H // 32, dtype=torch.uint8, device="cuda")
+    g.quantize_act(ws, dev(x.view(np.int16)), q, sc)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(q.cpu().numpy(), q_ref)
+    if sh.a_format == ms.A_MXFP8_G32:
+        np.testing.assert_array_equal(2.0 ** (sc.cpu().numpy().astype(np.float64) - 127), s_ref)
+    else:
+        np.testing.assert_array_equal(sc.cpu().numpy().astype(np.float64).reshape(s_ref.shape),
+                                      s_ref)

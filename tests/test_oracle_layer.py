@@ -180,3 +180,50 @@ def test_subset_of_tokens_matches_full():
     y = oracle.layer_forward(W, B.x_bits, ids, w)
     ys = oracle.layer_forward(W, B.x_bits, ids, w, tokens=np.array([6, 1, 3]))
     np.testing.assert_array_equal(ys, y[[6, 1, 3]])
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("op", [0, 1])
+def test_grouped_gemm_matches_dense_per_group(name, op):
+    """The oracle's grouped projection equals, group by group, a torch fp64
+    matmul over the dequantised rows and weights (and SiLU(g)*u for op 1)."""
+    sh = SMALL[name]
+    W = ms.gen_weights(sh)
+    H, I, E = sh.hidden, sh.inter, sh.experts
+    rng = np.random.default_rng(4)
+    counts = rng.integers(0, 5, size=E).astype(np.int32)
+    counts[0] = 0
+    indptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(indptr[-1])
+    T, kdiv = 9, 2
+    gather = rng.integers(0, T * kdiv, size=R).astype(np.int32)
+    x = ms.gen_batch(sh, T).x_bits
+    xv = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(torch.float64)
+    if sh.a_format == ms.A_BF16:
+        a, a_s, xq = x, None, xv
+    else:
+        q, s = oracle.quant_rows(xv.numpy(), sh.a_format)
+        g = {ms.A_FP8_TOKEN: H, ms.A_FP8_G128: 128, ms.A_MXFP8_G32: 32}[sh.a_format]
+        xq = torch.from_numpy(q).view(torch.float8_e4m3fn).to(torch.float64) * \
+            torch.from_numpy(np.repeat(s, g, axis=1))
+        a = q
+        if sh.a_format == ms.A_FP8_TOKEN:
+            a_s = s[:, 0].astype(np.float32)
+        elif sh.a_format == ms.A_FP8_G128:
+            a_s = s.astype(np.float32)
+        else:
+            a_s = (np.log2(s) + 127).astype(np.uint8)
+    out = oracle.grouped_gemm(sh.w_format, sh.a_format, op, a, a_s, gather, kdiv, indptr, I, H,
+                              W.w_gate, W.s_gate, W.w_up if op else None,
+                              W.s_up if op else None)
+    for e in range(E):
+        rows = gather[indptr[e]:indptr[e + 1]] // kdiv
+        if len(rows) == 0:
+            continue
+        Wg = deq_weight(W.w_gate[e], None if W.s_gate is None else W.s_gate[e], sh.w_format, I, H)
+        ref = xq[rows] @ Wg.T
+        if op:
+            Wu = deq_weight(W.w_up[e], None if W.s_up is None else W.s_up[e], sh.w_format, I, H)
+            ref = F.silu(ref) * (xq[rows] @ Wu.T)
+        np.testing.assert_allclose(out[indptr[e]:indptr[e + 1]], ref.numpy(), rtol=1e-10,
+                                   atol=1e-14)
