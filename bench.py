@@ -1,0 +1,231 @@
+"""Benchmark of the fused MoE layer forward on one MI355X.
+
+Default workload: the Mixtral-8x7B-shaped layer (H 4096, I 14336, 8 experts,
+top-2, SwiGLU) in FP8 e4m3 W8A8 (per-output-channel weight scales, dynamic
+per-token activation scales) at T = 128 tokens, the largest decode batch
+the layer is quoted at; T = 32 is timed in the same run as a second point.
+A step is one moe_layer_forward call: routing, dispatch, input
+quantisation, fused gate/up + SwiGLU grouped GEMM, requantisation, down
+grouped GEMM and combine, on inputs already resident in HBM (replayed as a
+hipGraph, the decode launch path).
+
+Printed: one JSON line.  `value` is the algorithmic HBM throughput of the
+layer (GB/s): bytes the method must move (weights and scales of the experts
+that receive tokens, x read once, y written once, the FP8 intermediate
+written and read once) over the measured time per step.  Also reported:
+layer microseconds and active TFLOP/s (6*H*I*rows), the roofline of the
+dominant kernel (its duration measured with HIP events recorded around it
+on the launch stream, eager path, right after the timed steps), and the CPU
+oracle timed on a bounded sample of the same batch.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("MoE layer µs + active TFLOP/s / HBM GB/s (FP8 W8A8) at 32, 128, 8192 tokens")
+HBM_PEAK_GBS = 8000.0
+STAGES = ["route+dispatch", "quant_x", "gemm_gateup_swiglu", "quant_h", "gemm_down", "combine"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def layer_bytes(sh, T, n_active):
+    """Algorithmic bytes of one layer call (see module docstring) and of one
+    launch of the gate/up kernel; also the number of expert rows."""
+    H, I = sh.hidden, sh.inter
+    wbits = {0: 16, 1: 8, 2: 8, 3: 4}[sh.w_format]
+    abytes = 2 if sh.a_format == 0 else 1
+
+    def mat_scales(n, k):           # weight scale bytes of one [n, k] matrix
+        return {0: 0, 1: n * 4, 2: (n // 128) * (k // 128) * 4, 3: n * k // 32}[sh.w_format]
+
+    def act_scales(rows, k):        # activation scale bytes of [rows, k]
+        return rows * {0: 0, 1: 4, 2: (k // 128) * 4, 3: k // 32}[sh.a_format]
+
+    groups = n_active + sh.shared
+    rows = T * sh.top_k + (T if sh.shared else 0)
+    gateup = groups * 2 * (H * I * wbits / 8 + mat_scales(I, H))
+    down = groups * (H * I * wbits / 8 + mat_scales(H, I))
+    x_in = T * H * 2                                   # bf16 x read once
+    y_out = T * H * 2                                  # bf16 y written once
+    h_rt = 2 * (rows * I * abytes + act_scales(rows, I))
+    total = gateup + down + x_in + y_out + h_rt
+    g1 = gateup + T * H * abytes + act_scales(T, H) + rows * I * abytes + act_scales(rows, I)
+    return total, g1, rows
+
+
+def setup(name, T, seed_dev="cuda"):
+    import torch
+    import grouped_gemm_amd as g
+    import moe_synth as ms
+    sh = ms.CONFIGS[name]
+    B = ms.gen_batch(sh, T)
+    # experts that receive tokens (stable argsort of the scores, top k)
+    order = np.argsort(-B.scores.astype(np.float64), axis=1, kind="stable")[:, :sh.top_k]
+    active = sorted(set(order.ravel().tolist()))
+    t0 = time.time()
+    W = ms.gen_weights(sh, experts=active)
+    log(f"[bench] {name} T={T}: {len(active)} active experts, weights drawn in "
+        f"{time.time() - t0:.1f}s")
+    dW = {n: (torch.from_numpy(np.ascontiguousarray(getattr(W, n))).to(seed_dev)
+              if getattr(W, n) is not None else None)
+          for n in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
+                    "sh_gate", "sh_up", "sh_down", "ss_gate", "ss_up", "ss_down")}
+    ws = g.Workspace(sh.hidden, sh.inter, sh.experts, sh.top_k, T, shared_experts=sh.shared,
+                     shared_inter=sh.shared_inter, score_fn=sh.score_fn, w_format=sh.w_format,
+                     a_format=sh.a_format)
+    x = torch.from_numpy(B.x_bits.view(np.int16)).to(seed_dev)
+    s = torch.from_numpy(B.scores).to(seed_dev)
+    y = torch.empty(T, sh.hidden, dtype=torch.int16, device=seed_dev)
+    return sh, B, W, dW, ws, x, s, y, len(active)
+
+
+def time_point(name, T, steps, warmup):
+    import torch
+    import grouped_gemm_amd as g
+    sh, B, W, dW, ws, x, s, y, n_active = setup(name, T)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            g.layer_forward(ws, dW, x, s, y, stream=stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for _ in range(steps):
+            g.layer_forward(ws, dW, x, s, y, stream=stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / steps
+    cfg = ws.last_config(stream)
+    # per-stage durations, eager path, events on the launch stream
+    evs = []
+    with torch.cuda.stream(stream):
+        for _ in range(steps):
+            pair = []
+            for st in range(6):
+                b = torch.cuda.Event(enable_timing=True)
+                e = torch.cuda.Event(enable_timing=True)
+                b.record(stream)
+                e.record(stream)
+                ws.set_stage_events(st, b, e)
+                pair.append((b, e))
+            g.layer_forward(ws, dW, x, s, y, stream=stream)
+            evs.append(pair)
+    torch.cuda.synchronize()
+    for st in range(6):
+        ws.set_stage_events(st, None, None)
+    stage_ms = [float(np.mean([p[st][0].elapsed_time(p[st][1]) for p in evs])) for st in range(6)]
+    total_b, g1_b, rows = layer_bytes(sh, T, n_active)
+    flops = 6.0 * sh.hidden * sh.inter * rows
+    us = ms_step * 1e3
+    return dict(sh=sh, B=B, W=W, T=T, us=us, ms=ms_step, gbs=total_b / (us * 1e-6) / 1e9,
+                tflops=flops / (us * 1e-6) / 1e12, bytes=total_b, g1_bytes=g1_b, flops=flops,
+                stage_ms=stage_ms, cfg=cfg, n_active=n_active, rows=rows)
+
+
+def cpu_baseline(pt, n_tokens):
+    import oracle
+    sh, B, W, T = pt["sh"], pt["B"], pt["W"], pt["T"]
+    ids, w = oracle.route(B.scores, sh.top_k, sh.score_fn)
+    toks = np.linspace(0, T - 1, n_tokens).astype(np.int32)
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    t0 = time.perf_counter()
+    oracle.layer_forward(W, B.x_bits, ids, w, tokens=toks)
+    dt = time.perf_counter() - t0
+    full = dt * T / n_tokens
+    return {"value": round(pt["bytes"] / full / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n_tokens} of the {T} tokens of the timed batch (same weights, "
+                      f"routing and activations), {dt:.1f}s wall, scaled to the full batch "
+                      f"({full:.1f}s per layer call)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mixtral")
+    ap.add_argument("--tokens", type=int, default=0)
+    ap.add_argument("--cpu-tokens", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the layer holds every expert on one device); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import grouped_gemm_amd  # noqa: F401  (fails loudly if the library is not built)
+
+    import moe_synth as ms
+    sh0 = ms.CONFIGS[args.workload]
+    T_main = args.tokens or max(sh0.tokens)
+    points = []
+    extra_T = [t for t in sh0.tokens if t != T_main and t >= 16] if not args.tokens else []
+    for T in extra_T:
+        p = time_point(args.workload, T, args.steps, args.warmup)
+        points.append(p)
+        log(f"[bench] T={T}: {p['us']:.1f} us, {p['gbs']:.0f} GB/s, {p['tflops']:.2f} TFLOP/s")
+    main_pt = time_point(args.workload, T_main, args.steps, args.warmup)
+    points.append(main_pt)
+    log(f"[bench] T={T_main}: {main_pt['us']:.1f} us, {main_pt['gbs']:.0f} GB/s, "
+        f"{main_pt['tflops']:.2f} TFLOP/s, stages(ms)={[round(v, 4) for v in main_pt['stage_ms']]}")
+    dom = int(np.argmax(main_pt["stage_ms"]))
+    dom_ms = main_pt["stage_ms"][dom]
+    if dom == 2:
+        dom_bytes = main_pt["g1_bytes"]
+    else:
+        dom_bytes = None
+    roof = None
+    if dom_bytes is not None:
+        ach = dom_bytes / (dom_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "k_gemm_stream (gate/up + SwiGLU)", "avg_ms": round(dom_ms, 5),
+                "bytes_per_launch": int(dom_bytes)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(main_pt, args.cpu_tokens)
+        log(f"[bench] cpu oracle: {cpu}")
+    sh = main_pt["sh"]
+    out = {
+        "metric": METRIC, "value": round(main_pt["gbs"], 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(main_pt["ms"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": f"{sh.name}-shaped MoE layer H{sh.hidden} I{sh.inter} "
+                               f"E{sh.experts} top{sh.top_k}, T={T_main}",
+                   "tokens": T_main, "hidden": sh.hidden, "inter": sh.inter,
+                   "experts": sh.experts, "top_k": sh.top_k, "w_format": sh.w_format,
+                   "a_format": sh.a_format, "tile_config": main_pt["cfg"]},
+        "points": [{"tokens": p["T"], "layer_us": round(p["us"], 2),
+                    "active_tflops": round(p["tflops"], 3), "hbm_gbs": round(p["gbs"], 1),
+                    "hbm_frac": round(p["gbs"] / HBM_PEAK_GBS, 4),
+                    "stage_ms": {STAGES[i]: round(v, 5) for i, v in enumerate(p["stage_ms"])}}
+                   for p in points],
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -17,7 +17,7 @@ SYMBOLS = (
     "moe_workspace_destroy", "moe_route_topk", "moe_dispatch", "moe_grouped_gemm",
     "moe_quantize_act", "moe_combine", "moe_layer_forward", "moe_workspace_routing",
     "moe_workspace_force_config", "moe_workspace_last_config", "moe_config_rows",
-    "moe_workspace_set_graphs",
+    "moe_workspace_set_graphs", "moe_workspace_set_stage_events",
 )
 
 
@@ -71,6 +71,7 @@ def _load():
     L.moe_workspace_last_config.argtypes = [P, C.POINTER(i), P]
     L.moe_config_rows.argtypes = [i]
     L.moe_workspace_set_graphs.argtypes = [P, i]
+    L.moe_workspace_set_stage_events.argtypes = [P, i, P, P]
     for n in SYMBOLS:
         if n not in ("moe_status_string", "moe_last_error"):
             getattr(L, n).restype = i
@@ -147,6 +148,13 @@ class Workspace:
 
     def set_graphs(self, enable: bool):
         _check(_load().moe_workspace_set_graphs(self.handle, int(bool(enable))))
+
+    def set_stage_events(self, stage: int, ev_begin=None, ev_end=None):
+        """Record torch.cuda.Event pairs (enable_timing=True, already recorded
+        once so that they exist) around one stage of layer_forward."""
+        b = None if ev_begin is None else C.c_void_p(ev_begin.cuda_event)
+        e = None if ev_end is None else C.c_void_p(ev_end.cuda_event)
+        _check(_load().moe_workspace_set_stage_events(self.handle, stage, b, e))
 
     def last_config(self, stream=None) -> int:
         v = C.c_int(-1)

@@ -144,6 +144,12 @@ struct moe_ws {
   int graphs = 1;
   int device = 0;
   std::map<GraphKey, hipGraphExec_t> execs;
+  hipEvent_t stage_ev[6][2] = {};
+  bool any_stage_events() const {
+    for (auto& p : stage_ev)
+      if (p[0] || p[1]) return true;
+    return false;
+  }
   template <class T>
   T* at(size_t off) const {
     return reinterpret_cast<T*>(base + off);
@@ -211,13 +217,21 @@ int enqueue_layer(moe_ws* ws, const moe_weights* w, const uint16_t* x, const flo
   const Layout& L = ws->L;
   const int S = T * d.top_k, S_tot = S + (d.shared_experts ? T : 0);
   const int G = (int)L.G;
+  auto mark = [&](int stage, int which) -> hipError_t {
+    hipEvent_t e = ws->stage_ev[stage][which];
+    return e ? hipEventRecord(e, st) : hipSuccess;
+  };
   DispatchArgs da = dispatch_args(ws, T);
   da.scores = scores;
+  HIP_TRY(mark(0, 0), "event record");
   HIP_TRY(launch_dispatch(da, st), "dispatch launch");
+  HIP_TRY(mark(0, 1), "event record");
   const bool quant = ws->fmt != F_BF16;
   if (quant) {
     QuantArgs q{x, 1, T, d.hidden, nullptr, ws->at<uint8_t>(L.xq), ws->at<void>(L.xs), d.a_format};
+    HIP_TRY(mark(1, 0), "event record");
     HIP_TRY(launch_quant(q, st), "input quantisation launch");
+    HIP_TRY(mark(1, 1), "event record");
   }
   int max_groups = d.num_experts < S ? d.num_experts : S;
   max_groups += d.shared_experts;
@@ -239,11 +253,15 @@ int enqueue_layer(moe_ws* ws, const moe_weights* w, const uint16_t* x, const flo
   g1.gather_div = d.top_k;
   g1.out = ws->at<void>(L.h);
   g1.max_groups = max_groups;
+  HIP_TRY(mark(2, 0), "event record");
   HIP_TRY(run_gemm(ws, true, g1, st), "gate/up grouped GEMM launch");
+  HIP_TRY(mark(2, 1), "event record");
   if (quant) {
     QuantArgs q{ws->at<void>(L.h), 0, S_tot, d.inter, nullptr, ws->at<uint8_t>(L.hq),
                 ws->at<void>(L.hs), d.a_format};
+    HIP_TRY(mark(3, 0), "event record");
     HIP_TRY(launch_quant(q, st), "intermediate quantisation launch");
+    HIP_TRY(mark(3, 1), "event record");
   }
   GemmArgs g2 = gemm_args(ws);
   g2.w0 = (const uint8_t*)w->w_down;
@@ -258,10 +276,14 @@ int enqueue_layer(moe_ws* ws, const moe_weights* w, const uint16_t* x, const flo
   g2.gather_div = 1;
   g2.out = ws->at<void>(L.out_slot);
   g2.max_groups = max_groups;
+  HIP_TRY(mark(4, 0), "event record");
   HIP_TRY(run_gemm(ws, false, g2, st), "down grouped GEMM launch");
+  HIP_TRY(mark(4, 1), "event record");
   CombineArgs c{ws->at<float>(L.out_slot), ws->at<float>(L.w), ws->at<int32_t>(L.inv), T,
                 d.top_k, d.hidden, d.shared_experts, y};
+  HIP_TRY(mark(5, 0), "event record");
   HIP_TRY(launch_combine(c, st), "combine launch");
+  HIP_TRY(mark(5, 1), "event record");
   return MOE_OK;
 }
 
@@ -452,7 +474,7 @@ int moe_layer_forward(moe_ws* ws, const moe_weights* w, const uint16_t* x, const
   int rc = check_weights(ws, w);
   if (rc) return rc;
   hipStream_t st = (hipStream_t)stream;
-  const bool use_graph = ws->graphs && st != nullptr && T <= 128;
+  const bool use_graph = ws->graphs && st != nullptr && T <= 128 && !ws->any_stage_events();
   if (!use_graph) return enqueue_layer(ws, w, x, scores, T, y, st);
   GraphKey key{};
   key.T = T;
@@ -523,6 +545,14 @@ int moe_workspace_set_graphs(moe_ws* ws, int enable) {
     for (auto& kv : ws->execs) hipGraphExecDestroy(kv.second);
     ws->execs.clear();
   }
+  return MOE_OK;
+}
+
+int moe_workspace_set_stage_events(moe_ws* ws, int stage, void* ev_begin, void* ev_end) {
+  if (!ws) return fail(MOE_EINVAL, "workspace is NULL");
+  if (stage < 0 || stage > 5) return fail(MOE_EINVAL, "stage must be in [0, 5]");
+  ws->stage_ev[stage][0] = (hipEvent_t)ev_begin;
+  ws->stage_ev[stage][1] = (hipEvent_t)ev_end;
   return MOE_OK;
 }
 

@@ -211,6 +211,14 @@ MOE_API int moe_config_rows(int cfg_id);
  * and instantiates a graph, later calls with the same pointers replay it. */
 MOE_API int moe_workspace_set_graphs(moe_ws* ws, int enable);
 
+/* Profiling: record the caller's HIP events (hipEvent_t, created with
+ * timing enabled) immediately before and after the launches of one stage of
+ * moe_layer_forward.  Stages: 0 routing + dispatch, 1 input quantisation,
+ * 2 gate/up grouped GEMM, 3 intermediate requantisation, 4 down grouped
+ * GEMM, 5 combine.  NULL events clear the stage.  While any stage has
+ * events, moe_layer_forward runs its eager path (no graph replay). */
+MOE_API int moe_workspace_set_stage_events(moe_ws* ws, int stage, void* ev_begin, void* ev_end);
+
 #ifdef __cplusplus
 }
 #endif
