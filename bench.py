@@ -91,10 +91,12 @@ def setup(name, T, seed_dev="cuda"):
     return sh, B, W, dW, ws, x, s, y, len(active)
 
 
-def time_point(name, T, steps, warmup):
+def time_point(name, T, steps, warmup, force_cfg=-1):
     import torch
     import grouped_gemm_amd as g
     sh, B, W, dW, ws, x, s, y, n_active = setup(name, T)
+    if force_cfg >= 0:
+        ws.force_config(force_cfg)
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         for _ in range(warmup):
@@ -164,6 +166,8 @@ def main():
     ap.add_argument("--tokens", type=int, default=0)
     ap.add_argument("--cpu-tokens", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--force-config", type=int, default=-1,
+                    help="tile configuration (default: chosen on the device)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the layer holds every expert on one device); "
@@ -181,10 +185,10 @@ def main():
     points = []
     extra_T = [t for t in sh0.tokens if t != T_main and t >= 16] if not args.tokens else []
     for T in extra_T:
-        p = time_point(args.workload, T, args.steps, args.warmup)
+        p = time_point(args.workload, T, args.steps, args.warmup, args.force_config)
         points.append(p)
         log(f"[bench] T={T}: {p['us']:.1f} us, {p['gbs']:.0f} GB/s, {p['tflops']:.2f} TFLOP/s")
-    main_pt = time_point(args.workload, T_main, args.steps, args.warmup)
+    main_pt = time_point(args.workload, T_main, args.steps, args.warmup, args.force_config)
     points.append(main_pt)
     log(f"[bench] T={T_main}: {main_pt['us']:.1f} us, {main_pt['gbs']:.0f} GB/s, "
         f"{main_pt['tflops']:.2f} TFLOP/s, stages(ms)={[round(v, 4) for v in main_pt['stage_ms']]}")

@@ -21,6 +21,7 @@ struct QGroup {
 template <int AF, bool IN_BF16, int MAXJ>
 __global__ void __launch_bounds__(256) k_quant(QuantArgs qa) {
   const int row = blockIdx.x;
+  if (qa.meta && qa.meta[META_CFG] != qa.only_cfg) return;
   if (qa.nrows && row >= *qa.nrows) return;
   const int n = qa.n, nch = n / 8;
   const int tid = threadIdx.x;

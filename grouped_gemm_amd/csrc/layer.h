@@ -74,8 +74,10 @@ struct GemmArgs {
   const int32_t* tiles;
   const int32_t* meta;
   int cfg_self;           // this launch runs only if meta[META_CFG] == cfg_self (or -1)
-  void* out;              // gate/up: bf16 h or fp32 h staging; down: fp32 [rows, N]
-  int max_groups;         // grid bound on active groups (streaming kernel)
+  void* out;              // gate/up: bf16 h, fp32 h staging or e4m3 h; down: fp32 [rows, N]
+  void* out_scale;        // gate/up with in-kernel requantisation: h scales
+  int max_groups;         // grid bound on active groups
+  int max_rows;           // grid bound on rows (all groups)
 };
 
 struct QuantArgs {
@@ -86,6 +88,8 @@ struct QuantArgs {
   uint8_t* q;             // [R, n] e4m3
   void* scale;            // fp32 [R] / fp32 [R, n/128] / uint8 [R, n/32]
   int a_format;
+  const int32_t* meta;    // optional: run only if meta[META_CFG] == only_cfg
+  int only_cfg;
 };
 
 struct CombineArgs {

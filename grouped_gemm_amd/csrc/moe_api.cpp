@@ -37,8 +37,11 @@ int hip_fail(hipError_t e, const char* what) {
     if (e_ != hipSuccess) return hip_fail(e_, what); \
   } while (0)
 
-// Tile configurations the library has kernels for (cfg 0 = streaming).
-constexpr int kNumCfgs = 1;
+// Tile configurations the library has kernels for: 0 = streaming, 1..3 =
+// tiled with row blocks of cfg_rows(cfg).  bf16 stops at 64-row blocks (a
+// 128-row bf16 token tile would not leave registers for the accumulators).
+constexpr int kNumCfgs = 4;
+int num_cfgs(int fmt) { return fmt == F_BF16 ? 3 : kNumCfgs; }
 
 int fmt_of(const moe_layer_desc& d) {
   if (d.w_format == MOE_W_BF16 && d.a_format == MOE_A_BF16) return F_BF16;
@@ -181,7 +184,7 @@ DispatchArgs dispatch_args(const moe_ws* ws, int T) {
   a.I = d.inter;
   a.wbits = wbits_of(ws->fmt);
   a.xbits = xbits_of(ws->fmt);
-  a.num_cfgs = kNumCfgs;
+  a.num_cfgs = num_cfgs(ws->fmt);
   return a;
 }
 
@@ -197,13 +200,21 @@ GemmArgs gemm_args(const moe_ws* ws) {
   return g;
 }
 
-// Run both projections with every configuration that has kernels; each
-// launch returns at once unless the device chose its configuration.
-hipError_t run_gemm(const moe_ws* ws, bool gateup, GemmArgs g, hipStream_t st) {
-  g.cfg_self = kNumCfgs > 1 ? 0 : -1;
+// Run a projection with every configuration that has kernels; each launch
+// returns at once unless the device chose its configuration.  `tiled_out`
+// and `tiled_scale` redirect the fused gate/up output of the tiled kernels,
+// which requantise the intermediate in their epilogue for the 1x128 and
+// MX formats.
+hipError_t run_gemm(const moe_ws* ws, bool gateup, GemmArgs g, void* tiled_out, void* tiled_scale,
+                    hipStream_t st) {
+  g.cfg_self = 0;
   hipError_t e = launch_gemm_stream(ws->fmt, gateup, g, st);
   if (e != hipSuccess) return e;
-  for (int c = 1; c < kNumCfgs; ++c) {
+  if (tiled_out) {
+    g.out = tiled_out;
+    g.out_scale = tiled_scale;
+  }
+  for (int c = 1; c < num_cfgs(ws->fmt); ++c) {
     g.cfg_self = c;
     e = launch_gemm_tiled(ws->fmt, gateup, c, g, st);
     if (e != hipSuccess) return e;
@@ -253,12 +264,21 @@ int enqueue_layer(moe_ws* ws, const moe_weights* w, const uint16_t* x, const flo
   g1.gather_div = d.top_k;
   g1.out = ws->at<void>(L.h);
   g1.max_groups = max_groups;
+  g1.max_rows = S_tot;
+  // the tiled kernels requantise 1x128 and MX intermediates themselves
+  const bool fused_requant = ws->fmt == F_FP8_BLK || ws->fmt == F_MX;
   HIP_TRY(mark(2, 0), "event record");
-  HIP_TRY(run_gemm(ws, true, g1, st), "gate/up grouped GEMM launch");
+  HIP_TRY(run_gemm(ws, true, g1, fused_requant ? ws->at<void>(L.hq) : nullptr,
+                   fused_requant ? ws->at<void>(L.hs) : nullptr, st),
+          "gate/up grouped GEMM launch");
   HIP_TRY(mark(2, 1), "event record");
   if (quant) {
     QuantArgs q{ws->at<void>(L.h), 0, S_tot, d.inter, nullptr, ws->at<uint8_t>(L.hq),
                 ws->at<void>(L.hs), d.a_format};
+    if (fused_requant) {   // only the streaming configuration left fp32 h behind
+      q.meta = ws->at<int32_t>(L.meta);
+      q.only_cfg = 0;
+    }
     HIP_TRY(mark(3, 0), "event record");
     HIP_TRY(launch_quant(q, st), "intermediate quantisation launch");
     HIP_TRY(mark(3, 1), "event record");
@@ -276,8 +296,9 @@ int enqueue_layer(moe_ws* ws, const moe_weights* w, const uint16_t* x, const flo
   g2.gather_div = 1;
   g2.out = ws->at<void>(L.out_slot);
   g2.max_groups = max_groups;
+  g2.max_rows = S_tot;
   HIP_TRY(mark(4, 0), "event record");
-  HIP_TRY(run_gemm(ws, false, g2, st), "down grouped GEMM launch");
+  HIP_TRY(run_gemm(ws, false, g2, nullptr, nullptr, st), "down grouped GEMM launch");
   HIP_TRY(mark(4, 1), "event record");
   CombineArgs c{ws->at<float>(L.out_slot), ws->at<float>(L.w), ws->at<int32_t>(L.inv), T,
                 d.top_k, d.hidden, d.shared_experts, y};
@@ -348,7 +369,7 @@ int moe_workspace_create(const moe_layer_desc* desc, void* dev_buf, size_t bytes
 
 int moe_workspace_destroy(moe_ws* ws) {
   if (!ws) return MOE_OK;
-  for (auto& kv : ws->execs) hipGraphExecDestroy(kv.second);
+  for (auto& kv : ws->execs) (void)hipGraphExecDestroy(kv.second);
   delete ws;
   return MOE_OK;
 }
@@ -425,6 +446,7 @@ int moe_grouped_gemm(moe_ws* ws, int op, const void* a, const void* a_scale,
   g.gather = a_gather;
   g.gather_div = a_gather ? gather_div : 1;
   g.max_groups = E;
+  g.max_rows = (int)cap;
   g.cfg_self = -1;
   if (gateup && quant) {
     g.out = ws->at<void>(ws->L.h);
@@ -492,13 +514,13 @@ int moe_layer_forward(moe_ws* ws, const moe_weights* w, const uint16_t* x, const
     rc = enqueue_layer(ws, w, x, scores, T, y, st);
     hipError_t e = hipStreamEndCapture(st, &graph);
     if (rc) {
-      if (e == hipSuccess) hipGraphDestroy(graph);
+      if (e == hipSuccess) (void)hipGraphDestroy(graph);
       return rc;
     }
     if (e != hipSuccess) return hip_fail(e, "end capture");
     hipGraphExec_t exec;
     e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
-    hipGraphDestroy(graph);
+    (void)hipGraphDestroy(graph);
     if (e != hipSuccess) return hip_fail(e, "graph instantiate");
     it = ws->execs.emplace(key, exec).first;
   }
@@ -521,9 +543,10 @@ int moe_workspace_routing(const moe_ws* ws, const int32_t** ids, const float** w
 
 int moe_workspace_force_config(moe_ws* ws, int cfg) {
   if (!ws) return fail(MOE_EINVAL, "workspace is NULL");
-  if (cfg < -1 || cfg >= kNumCfgs) return fail(MOE_EINVAL, "cfg must be in [-1, %d)", kNumCfgs);
+  if (cfg < -1 || cfg >= num_cfgs(ws->fmt))
+    return fail(MOE_EINVAL, "cfg must be in [-1, %d)", num_cfgs(ws->fmt));
   ws->force_cfg = cfg;
-  for (auto& kv : ws->execs) hipGraphExecDestroy(kv.second);
+  for (auto& kv : ws->execs) (void)hipGraphExecDestroy(kv.second);
   ws->execs.clear();
   return MOE_OK;
 }
@@ -542,7 +565,7 @@ int moe_workspace_set_graphs(moe_ws* ws, int enable) {
   if (!ws) return fail(MOE_EINVAL, "workspace is NULL");
   ws->graphs = enable ? 1 : 0;
   if (!enable) {
-    for (auto& kv : ws->execs) hipGraphExecDestroy(kv.second);
+    for (auto& kv : ws->execs) (void)hipGraphExecDestroy(kv.second);
     ws->execs.clear();
   }
   return MOE_OK;

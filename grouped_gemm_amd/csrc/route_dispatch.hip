@@ -169,40 +169,53 @@ DEVI void wave0_exclusive_scan(int32_t* a, int n, int32_t* total) {
 }
 
 // ---------------------------------------------------------------- config choice
-// Cost of running the two projections with configuration cfg, from the
-// grid geometry (RaMP abstract: the cost depends on the CTA grid the
-// histogram induces).  Each configuration is priced as
-//   waves(cfg) * wave_time(cfg) + fixed(cfg)
-// where a "wave" is one round of workgroups over all CUs, and a workgroup's
-// time is the larger of its HBM bytes at the per-CU share of bandwidth and
-// its MFMA work at the per-CU share of peak.  Streaming (cfg 0) re-reads an
-// expert's weights once per 64-row chunk; tiled configurations read the
-// weight tile once per row block.
+// Predicted time of the two projections under configuration cfg, from the
+// grid geometry the histogram induces (RaMP abstract: a wave cost model over
+// the CTA grid selects the configuration from the runtime expert histogram).
+// Per projection, a configuration is priced as
+//   rounds * (per-item time) + fixed launch cost,
+// rounds = ceil(items / concurrent items), and an item's time is the larger
+// of its streamed bytes at its share of HBM bandwidth and its MFMA work
+// (padding rows included) at its share of the matrix-core peak, each
+// derated by an efficiency factor of the kernel family.  Streaming (cfg 0):
+// an item is 16 output channels of one group, one 64-row pass; it streams
+// the weight rows once per pass.  Tiled (cfg >= 1): an item is a BM-row block
+// of one group times 128 (gate/up) or 128 (down) channels; weights of a
+// group are read from HBM once (later row blocks hit L2), tokens per item.
 DEVI float config_cost(int cfg, const int32_t* cnt, int G, int H, int I, int wbits, int xbits,
                        int lane) {
-  const float cus = 256.f, bw_cu = 8.0e12f / 256.f;          // bytes/s per CU
-  const float mfma_cu = (wbits == 16 ? 2.5e15f : 5.0e15f) / 256.f;
+  const float cus = 256.f, bw = 8.0e12f, peak = (wbits == 16 ? 2.5e15f : 5.0e15f);
   float t = 0.f;
   if (cfg == 0) {
-    // GEMM1 + GEMM2 weight bytes per 64-row pass of each active group
-    float wbytes = 3.f * H * (float)I * wbits / 8.f;
-    float passes = 0.f;
-    for (int g = lane; g < G; g += 64) passes += (float)((cnt[g] + 63) / 64);
+    const float eff_bw = 0.60f;
+    float passes = 0.f, rows = 0.f;
+    for (int g = lane; g < G; g += 64) {
+      passes += (float)((cnt[g] + 63) / 64);
+      rows += (float)cnt[g];
+    }
     passes = wave_sum(passes);
-    t = passes * wbytes / (bw_cu * cus) + 8e-6f;
+    rows = wave_sum(rows);
+    float wbytes = passes * 3.f * H * (float)I * wbits / 8.f;
+    float flops = 6.f * H * (float)I * 64.f * passes;
+    t = fmaxf(wbytes / (bw * eff_bw), flops / (peak * 0.05f)) + 6e-6f;
   } else {
-    int bm = cfg_rows(cfg), bn = 128;
-    float tiles = 0.f;
-    for (int g = lane; g < G; g += 64) tiles += (float)((cnt[g] + bm - 1) / bm);
+    const int bm = cfg_rows(cfg);
+    const float eff_bw = 0.55f, eff_mfma = 0.45f;
+    float tiles = 0.f, groups = 0.f;
+    for (int g = lane; g < G; g += 64) {
+      tiles += (float)((cnt[g] + bm - 1) / bm);
+      groups += cnt[g] > 0 ? 1.f : 0.f;
+    }
     tiles = wave_sum(tiles);
-    // gate/up tile: 2*bn weight rows x H; down tile: bn rows x I
-    float tiles1 = tiles * (I / bn), tiles2 = tiles * (H / bn);
-    float by1 = (2.f * bn * H * wbits + (float)bm * H * xbits) / 8.f;
-    float fl1 = 4.f * bm * bn * (float)H;
-    float by2 = ((float)bn * I * wbits + (float)bm * I * xbits) / 8.f;
-    float fl2 = 2.f * bm * bn * (float)I;
-    float t1 = fmaxf(by1 / bw_cu, fl1 / mfma_cu), t2 = fmaxf(by2 / bw_cu, fl2 / mfma_cu);
-    t = ceilf(tiles1 / cus) * t1 + ceilf(tiles2 / cus) * t2 + 12e-6f;
+    groups = wave_sum(groups);
+    float wbytes = groups * 3.f * H * (float)I * wbits / 8.f;
+    float xbytes = tiles * bm * (H * (I / 128.f) + I * (H / 128.f)) * xbits / 8.f;
+    float flops = 6.f * H * (float)I * bm * tiles;
+    float items = tiles * (I / 128.f + H / 128.f);
+    float rounds = ceilf(items / (2.f * cus));
+    float per_item = fmaxf((wbytes + xbytes) / items / (bw * eff_bw / (2.f * cus)),
+                           flops / items / (peak * eff_mfma / (2.f * cus)));
+    t = rounds * per_item + 10e-6f;
   }
   return t;
 }

@@ -134,3 +134,36 @@ def test_layer_full_size_sampled(name, T):
     say("  sampled relerr", err, "tokens", len(toks))
     assert np.all(np.isfinite(bf16_to_f64(y)))
     assert err <= tol_for(sh)
+
+
+FORCED = [(n, sh, T) for n, sh, T in SMALL if n != "tiny_cfg"] + [
+    ("fp8_block_big", ms.small_shape("qwen", hidden=512, inter=256, experts=6, top_k=2), 300),
+    ("mxfp4_big", ms.small_shape("imbalance", hidden=512, inter=256, experts=4, top_k=2), 200),
+    ("fp8_channel_big", ms.small_shape("mixtral", hidden=256, inter=512, experts=3, top_k=2), 170),
+]
+
+
+@pytest.mark.parametrize("name,sh,T", FORCED, ids=[c[0] for c in FORCED])
+def test_layer_every_config_matches_oracle(name, sh, T):
+    """Every tile configuration (streaming and each tiled row-block height)
+    gives the oracle's routing bit-exact and an output within tolerance."""
+    W = ms.gen_weights(sh)
+    B = ms.gen_batch(sh, T)
+    dW = dev_weights(W)
+    ws = workspace(sh, T)
+    ws.set_graphs(False)
+    ids, w = oracle.route(B.scores, sh.top_k, sh.score_fn)
+    ref = oracle.layer_forward(W, B.x_bits, ids, w)
+    ncfg = 3 if sh.w_format == ms.W_BF16 else 4
+    outs = []
+    for cfg in range(ncfg):
+        ws.force_config(cfg)
+        y = run_layer(ws, dW, B.x_bits, B.scores)
+        assert ws.last_config() == cfg
+        check_routing(sh, T, ws_routing(ws, sh, T), B.scores)
+        err = relerr(bf16_to_f64(y), ref)
+        say("  cfg", cfg, "relerr", err)
+        assert np.all(np.isfinite(bf16_to_f64(y)))
+        assert err <= tol_for(sh), (cfg, err)
+        outs.append(y)
+    ws.force_config(-1)
