@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libmoe.so")
 BUILD = os.path.join(HERE, "_build")
 SOURCES = ["route_dispatch.hip", "elementwise.hip", "gemm_stream.hip", "gemm_tiled.hip",
-           "moe_api.cpp"]
+           "gemm_pipe.hip", "moe_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -161,3 +161,23 @@ DEVI f32x4 mma_step(const Frag<16>& a, const Frag<16>& b, f32x4 c) {
   for (int s = 0; s < 4; ++s) c = mfma_bf16(a.v[s], b.v[s], c);
   return c;
 }
+
+// ---------------------------------------------------------------- XCD-aware work split
+// Workgroups of a launch are dealt to the 8 XCDs of the chip in turn
+// (workgroup b runs on XCD b % 8), and each XCD has its own L2.  A
+// persistent grid therefore gives every XCD one contiguous range of the
+// (expert-major) work items, walked by that XCD's workgroups, so the items
+// that share an expert's weights and a row block's tokens meet in one L2.
+struct ItemRange {
+  int begin, end, step;
+};
+DEVI ItemRange xcd_items(int n_items) {
+  constexpr int NX = 8;
+  const int grid = gridDim.x;
+  if (grid % NX) return {(int)blockIdx.x, n_items, grid};
+  const int x = blockIdx.x % NX, j = blockIdx.x / NX, per = grid / NX;
+  const int chunk = (n_items + NX - 1) / NX;
+  const int b = x * chunk;
+  const int e = b + chunk < n_items ? b + chunk : n_items;
+  return {b + j, e, per};
+}

@@ -129,25 +129,47 @@ hipError_t launch_quant(const QuantArgs& q, hipStream_t st) {
 }
 
 // ------------------------------------------------------------------ combine
-// One 256-thread block per token; thread owns 8-column chunks.
+// One 256-thread block per token; thread owns 8-column chunks.  Slot rows
+// are either fp32 (weights applied here) or bf16 already scaled by their
+// routing weight in the down projection's epilogue; either way the k rows
+// (then the shared expert's) are added in a fixed order in fp32 and the sum
+// is rounded to bf16 once.
+DEVI void load8(const void* base, size_t row, int H, int ch, bool bf16, float (&v)[8]) {
+  if (bf16) {
+    const uint4 r = *(const uint4*)((const uint16_t*)base + row * H + 8 * ch);
+    const uint32_t w4[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_to_f32((uint16_t)(w4[i] & 0xFFFF));
+      v[2 * i + 1] = bf16_to_f32((uint16_t)(w4[i] >> 16));
+    }
+  } else {
+    const float* o = (const float*)base + row * H + 8 * ch;
+    const float4 a = *(const float4*)o, b = *(const float4*)(o + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
 __global__ void __launch_bounds__(256) k_combine(CombineArgs c) {
   const int t = blockIdx.x, H = c.H, nch = H / 8;
   const int S = c.T * c.k;
+  const bool wb = c.weighted_bf16 != 0;
   for (int ch = threadIdx.x; ch < nch; ch += 256) {
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int j = 0; j < c.k; ++j) {
-      int slot = c.inv[t * c.k + j];
-      float wj = c.w[t * c.k + j];
-      const float* o = c.out_slot + (size_t)slot * H + 8 * ch;
-      float4 a = *(const float4*)o, b = *(const float4*)(o + 4);
-      acc[0] += wj * a.x; acc[1] += wj * a.y; acc[2] += wj * a.z; acc[3] += wj * a.w;
-      acc[4] += wj * b.x; acc[5] += wj * b.y; acc[6] += wj * b.z; acc[7] += wj * b.w;
+      const int slot = c.inv[t * c.k + j];
+      const float wj = wb ? 1.0f : c.w[t * c.k + j];
+      float v[8];
+      load8(c.out_slot, (size_t)slot, H, ch, wb, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += wj * v[i];
     }
     if (c.shared) {
-      const float* o = c.out_slot + (size_t)(S + t) * H + 8 * ch;
-      float4 a = *(const float4*)o, b = *(const float4*)(o + 4);
-      acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
-      acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+      float v[8];
+      load8(c.out_slot, (size_t)(S + t), H, ch, wb, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
     }
     uint32_t p[4];
 #pragma unroll

@@ -181,7 +181,7 @@ __global__ void __launch_bounds__(WAVES * 64) k_gemm_stream(GemmArgs p) {
             *(f32x4*)((float*)p.out + (size_t)slot * N + n0) = h;
           }
         } else {
-          *(f32x4*)((float*)p.out + (size_t)slot * N + n0) = v0;
+          store_down(p, slot, n0, v0);
         }
       }
     }

@@ -69,7 +69,8 @@ __global__ void __launch_bounds__(THREADS) k_gemm_tiled(GemmArgs p) {
   const int nsteps = K / 128;
   float* amax_l = (float*)(lds + 2 * Lds<F, BM>::BUF);
 
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+  const ItemRange ir = xcd_items(n_items);
+  for (int item = ir.begin; item < ir.end; item += ir.step) {
     const int tile = item / nblk, nb = item - tile * nblk;
     const int g = p.tiles[2 * tile], r0 = p.tiles[2 * tile + 1];
     const int m0 = p.indptr[g] + r0;
@@ -268,9 +269,8 @@ __global__ void __launch_bounds__(THREADS) k_gemm_tiled(GemmArgs p) {
       for (int t = 0; t < TT; ++t) {
         const int r = t * 16 + r16;
         if (r >= M) continue;
-        float* orow = (float*)p.out + (size_t)(m0 + r) * N;
 #pragma unroll
-        for (int rt = 0; rt < RTW; ++rt) *(f32x4*)(orow + nw0 + rt * 16 + 4 * lg) = acc[0][rt][t];
+        for (int rt = 0; rt < RTW; ++rt) store_down(p, m0 + r, nw0 + rt * 16 + 4 * lg, acc[0][rt][t]);
       }
     } else {
       // h = SiLU(gate) * up, in place in acc[0]
@@ -416,8 +416,14 @@ hipError_t launch_bm(int bm, const GemmArgs& g, hipStream_t st) {
     case 32: return launch_one<F, GATEUP, 32, 2>(g, st);
     case 64: return launch_one<F, GATEUP, 64, 2>(g, st);
     case 128:
-      if constexpr (F == F_BF16) return hipErrorInvalidValue;   // see num_cfgs
-      else return launch_one<F, GATEUP, 128, 2>(g, st);
+      if constexpr (F == F_BF16) {
+        return hipErrorInvalidValue;   // see num_cfgs
+      } else {
+        // the pipelined kernel covers 256 down-projection channels per item
+        if (GATEUP || g.N % 256 == 0) return launch_gemm_pipe(F, GATEUP, g, st);
+        if constexpr (!GATEUP) return launch_one<F, false, 128, 2>(g, st);
+        return hipErrorInvalidValue;
+      }
   }
   return hipErrorInvalidValue;
 }

@@ -16,8 +16,12 @@
 #define META_ERROR 6     // nonzero: the device rejected the group offsets
 #define META_WORDS 16
 
-// Slots up to which one 1024-thread block does the whole dispatch.
+// Slots up to which one 1024-thread block does the whole dispatch; it also
+// routes (scores staged in LDS) when everything fits in DISPATCH_LDS_MAX.
 #define SMALL_DISPATCH_SLOTS 8192
+#define DISPATCH_LDS_MAX (64 * 1024)
+// LDS ints the multi-block scan stages per pass of chunk counts
+#define SCAN_STAGE_INTS 12288
 
 // Tile configurations: 0 streams weights (decode-sized groups); the others
 // are LDS-tiled with the given row-block height.
@@ -78,7 +82,26 @@ struct GemmArgs {
   void* out_scale;        // gate/up with in-kernel requantisation: h scales
   int max_groups;         // grid bound on active groups
   int max_rows;           // grid bound on rows (all groups)
+  // down projection of the layer: when row_w is set, row `slot` is scaled by
+  // its routing weight row_w[row_w_idx[slot]] (1 for slot >= row_w_n, the
+  // shared expert) and stored as bf16; otherwise stored as fp32
+  const float* row_w;
+  const int32_t* row_w_idx;
+  int row_w_n;
 };
+
+// Store four consecutive down-projection outputs of one row.
+DEVI void store_down(const GemmArgs& p, int slot, int n0, f32x4 v) {
+  if (p.row_w) {
+    const float w = slot < p.row_w_n ? p.row_w[p.row_w_idx[slot]] : 1.0f;
+    v = v * w;
+    uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    *(uint2*)((uint16_t*)p.out + (size_t)slot * p.N + n0) = make_uint2(lo, hi);
+  } else {
+    *(f32x4*)((float*)p.out + (size_t)slot * p.N + n0) = v;
+  }
+}
 
 struct QuantArgs {
   const void* in;         // rows [R, n], bf16 (in_bf16) or fp32
@@ -93,17 +116,18 @@ struct QuantArgs {
 };
 
 struct CombineArgs {
-  const float* out_slot;  // [S + shared*T, H]
+  const void* out_slot;   // [S + shared*T, H]: fp32 unweighted, or bf16 pre-weighted
   const float* w;         // [T,k]
   const int32_t* inv;     // [T*k]
   int T, k, H, shared;
   uint16_t* y;            // [T,H] bf16
+  int weighted_bf16;      // out_slot rows are bf16 and already carry w[t,j]
 };
 
 hipError_t launch_route(const float* scores, int T, int E, int k, int score_fn, int32_t* ids,
                         float* w, hipStream_t st);
 hipError_t launch_dispatch(const DispatchArgs& d, hipStream_t st);
-size_t dispatch_small_lds(int T, int k, int G);
+size_t dispatch_small_lds(int T, int k, int G, int E, bool route);
 hipError_t launch_quant(const QuantArgs& q, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& c, hipStream_t st);
 hipError_t launch_indptr_table(const int32_t* user_indptr, int cap, const DispatchArgs& d,
@@ -111,3 +135,5 @@ hipError_t launch_indptr_table(const int32_t* user_indptr, int cap, const Dispat
 // Streaming (decode) grouped GEMM; fmt = Fmt, gateup = fused SwiGLU op.
 hipError_t launch_gemm_stream(int fmt, bool gateup, const GemmArgs& g, hipStream_t st);
 hipError_t launch_gemm_tiled(int fmt, bool gateup, int cfg, const GemmArgs& g, hipStream_t st);
+// Pipelined 128-row-block grouped GEMM (FP8 and MX formats).
+hipError_t launch_gemm_pipe(int fmt, bool gateup, const GemmArgs& g, hipStream_t st);

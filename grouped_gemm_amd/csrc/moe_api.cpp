@@ -297,11 +297,14 @@ int enqueue_layer(moe_ws* ws, const moe_weights* w, const uint16_t* x, const flo
   g2.out = ws->at<void>(L.out_slot);
   g2.max_groups = max_groups;
   g2.max_rows = S_tot;
+  g2.row_w = ws->at<float>(L.w);          // weight of slot = w[gather[slot]]
+  g2.row_w_idx = ws->at<int32_t>(L.gather);
+  g2.row_w_n = S;
   HIP_TRY(mark(4, 0), "event record");
   HIP_TRY(run_gemm(ws, false, g2, nullptr, nullptr, st), "down grouped GEMM launch");
   HIP_TRY(mark(4, 1), "event record");
-  CombineArgs c{ws->at<float>(L.out_slot), ws->at<float>(L.w), ws->at<int32_t>(L.inv), T,
-                d.top_k, d.hidden, d.shared_experts, y};
+  CombineArgs c{ws->at<void>(L.out_slot), ws->at<float>(L.w), ws->at<int32_t>(L.inv), T,
+                d.top_k, d.hidden, d.shared_experts, y, 1};
   HIP_TRY(mark(5, 0), "event record");
   HIP_TRY(launch_combine(c, st), "combine launch");
   HIP_TRY(mark(5, 1), "event record");
@@ -481,7 +484,7 @@ int moe_combine(moe_ws* ws, const float* out_slot, const float* topk_w, const in
   if (T > ws->d.max_tokens) return fail(MOE_ECAPACITY, "T=%d exceeds max_tokens", T);
   if (T == 0) return MOE_OK;
   if (!out_slot || !topk_w || !inv || !y) return fail(MOE_EINVAL, "null pointer");
-  CombineArgs c{out_slot, topk_w, inv, T, ws->d.top_k, ws->d.hidden, ws->d.shared_experts, y};
+  CombineArgs c{out_slot, topk_w, inv, T, ws->d.top_k, ws->d.hidden, ws->d.shared_experts, y, 0};
   HIP_TRY(launch_combine(c, (hipStream_t)stream), "combine launch");
   return MOE_OK;
 }

@@ -325,11 +325,16 @@ __global__ void __launch_bounds__(1024) k_dispatch_small(DispatchArgs d) {
   int32_t* scan_buf = wcnt + 16 * G;           // [G]
   int32_t* flag_buf = scan_buf + G;            // [G]
   int32_t* tiles_buf = flag_buf + G;           // [G]
+  float* sc_l = (float*)(tiles_buf + G);       // [T*E] router scores (routing fused)
   int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   if (d.scores) {
+    // all scores into LDS with coalesced loads, then one wave per token
+    const int n = d.T * d.E;
+    for (int i = tid; i < n; i += blockDim.x) sc_l[i] = d.scores[i];
+    __syncthreads();
     for (int t = wave; t < d.T; t += 16)
-      route_one_token(d.scores + (size_t)t * d.E, d.E, d.k, d.score_fn, lane, d.ids + (size_t)t * d.k,
+      route_one_token(sc_l + t * d.E, d.E, d.k, d.score_fn, lane, d.ids + (size_t)t * d.k,
                       d.w + (size_t)t * d.k, ids_l + t * d.k);
   } else {
     for (int p = tid; p < S; p += blockDim.x) ids_l[p] = d.ids_in[p];
@@ -383,7 +388,9 @@ __global__ void __launch_bounds__(1024) k_dispatch_hist(DispatchArgs d) {
   for (int e = tid; e < d.E; e += blockDim.x) d.chunk[(size_t)c * d.E + e] = cnt[e];
 }
 
-// 2) one block: chunk bases, group counts, scan, active list, config, table
+// 2) one block: chunk bases, group counts, scan, active list, config, table.
+// The per-chunk counts are staged through LDS in coalesced passes of CG
+// chunks, so no thread walks a chain of dependent global loads.
 __global__ void __launch_bounds__(1024) k_dispatch_scan(DispatchArgs d) {
   extern __shared__ int32_t smem[];
   const int G = d.E + d.shared;
@@ -391,21 +398,29 @@ __global__ void __launch_bounds__(1024) k_dispatch_scan(DispatchArgs d) {
   int32_t* scan_buf = cnt + G;
   int32_t* flag_buf = scan_buf + G;
   int32_t* tiles_buf = flag_buf + G;
+  int32_t* stage = tiles_buf + G;                 // [CG][E]
+  const int CG = SCAN_STAGE_INTS / d.E;
   int S = d.T * d.k, nchunks = (S + 1023) / 1024, tid = threadIdx.x;
-  for (int e = tid; e < d.E; e += blockDim.x) {
-    int run = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      int v = d.chunk[(size_t)c * d.E + e];
-      d.chunk[(size_t)c * d.E + e] = run;
-      run += v;
+  int run = 0;
+  for (int c0 = 0; c0 < nchunks; c0 += CG) {
+    const int n = min(CG, nchunks - c0);
+    for (int i = tid; i < n * d.E; i += blockDim.x) stage[i] = d.chunk[(size_t)c0 * d.E + i];
+    __syncthreads();
+    if (tid < d.E) {
+      for (int c = 0; c < n; ++c) {
+        const int v = stage[c * d.E + tid];
+        d.chunk[(size_t)(c0 + c) * d.E + tid] = run;
+        run += v;
+      }
     }
-    cnt[e] = run;
+    __syncthreads();
   }
+  if (tid < d.E) cnt[tid] = run;
   if (tid == 0 && d.shared) cnt[d.E] = d.T;
   __syncthreads();
   finalize_dispatch(d, cnt, scan_buf, flag_buf, tiles_buf, G, S + (d.shared ? d.T : 0));
   if (d.shared)
-    for (int t = blockIdx.x * blockDim.x + tid; t < d.T; t += blockDim.x) d.gather[S + t] = t * d.k;
+    for (int t = tid; t < d.T; t += blockDim.x) d.gather[S + t] = t * d.k;
 }
 
 // 3) stable scatter of each chunk
@@ -428,8 +443,8 @@ __global__ void __launch_bounds__(1024) k_dispatch_scatter(DispatchArgs d) {
 }
 
 // ---------------------------------------------------------------- host launchers
-size_t dispatch_small_lds(int T, int k, int G) {
-  return sizeof(int32_t) * ((size_t)T * k + 2 * G + 16 * G + 3 * G);
+size_t dispatch_small_lds(int T, int k, int G, int E, bool route) {
+  return sizeof(int32_t) * ((size_t)T * k + 2 * G + 16 * G + 3 * G + (route ? (size_t)T * E : 0));
 }
 
 hipError_t launch_route(const float* scores, int T, int E, int k, int score_fn, int32_t* ids,
@@ -443,7 +458,19 @@ hipError_t launch_dispatch(const DispatchArgs& d, hipStream_t st) {
   const int G = d.E + d.shared;
   const int S = d.T * d.k;
   if (S <= SMALL_DISPATCH_SLOTS) {
-    hipLaunchKernelGGL(k_dispatch_small, dim3(1), dim3(1024), dispatch_small_lds(d.T, d.k, G), st, d);
+    // routing is fused into the block when the scores fit in its LDS
+    if (d.scores && dispatch_small_lds(d.T, d.k, G, d.E, true) > DISPATCH_LDS_MAX) {
+      hipError_t e = launch_route(d.scores, d.T, d.E, d.k, d.score_fn, d.ids, d.w, st);
+      if (e != hipSuccess) return e;
+      DispatchArgs d2 = d;
+      d2.scores = nullptr;
+      d2.ids_in = d.ids;
+      hipLaunchKernelGGL(k_dispatch_small, dim3(1), dim3(1024),
+                         dispatch_small_lds(d.T, d.k, G, d.E, false), st, d2);
+      return hipGetLastError();
+    }
+    hipLaunchKernelGGL(k_dispatch_small, dim3(1), dim3(1024),
+                       dispatch_small_lds(d.T, d.k, G, d.E, d.scores != nullptr), st, d);
     return hipGetLastError();
   }
   // large path: routing (if requested) runs as its own grid first
@@ -456,7 +483,8 @@ hipError_t launch_dispatch(const DispatchArgs& d, hipStream_t st) {
   }
   int nchunks = (S + 1023) / 1024;
   hipLaunchKernelGGL(k_dispatch_hist, dim3(nchunks), dim3(1024), sizeof(int32_t) * d.E, st, d2);
-  hipLaunchKernelGGL(k_dispatch_scan, dim3(1), dim3(1024), sizeof(int32_t) * 4 * G, st, d2);
+  hipLaunchKernelGGL(k_dispatch_scan, dim3(1), dim3(1024),
+                     sizeof(int32_t) * (4 * G + SCAN_STAGE_INTS), st, d2);
   hipLaunchKernelGGL(k_dispatch_scatter, dim3(nchunks), dim3(1024), sizeof(int32_t) * 16 * d.E, st,
                      d2);
   return hipGetLastError();
