@@ -6,24 +6,26 @@
 // launch, no padding between groups).
 //
 // Per K step of 128 elements a workgroup stages, in a ring of NSTAGE LDS
-// buffers, the 128 token rows of its block and the 256 weight rows of its
-// channel block.  Both are copied by asynchronous global->LDS loads
+// buffers, the BM token rows of its block and the NR weight rows of its
+// channel block (gate rows then up rows for the fused op).  Both are copied by asynchronous global->LDS loads
 // (global_load_lds_dwordx4), so loads of the next NSTAGE-1 steps are in
 // flight while the MFMAs of the current step run and no registers are held
 // by them.  Rows land in LDS with their 16-byte chunks XOR-swizzled by the
 // row index, which makes the MFMA fragment reads (16 rows, same chunk)
 // bank-conflict free without padding.
 //
-// The four waves form a 2x2 grid: a wave owns 64 tokens and 128 weight rows
-// (64 gate + 64 up rows for the fused op, so each lane holds matching gate
-// and up values; 128 output channels for the down projection).
+// The four waves form a WM x WN grid over (tokens, channels): a wave owns
+// BM/WM tokens and NBC/WN output channels (the matching gate and up rows for
+// the fused op, so each lane holds gate and up values of the same channel).
+// Large blocks (BM = 128, NR = 256) serve prefill; BM = 32/64 with deep rings
+// serve decode, where the kernel is a stream of weight bytes with several
+// K steps of every workgroup in flight.
 #include "layer.h"
 
 namespace {
 
 constexpr int PTHREADS = 256;
-constexpr int PBM = 128;       // token rows per item
-constexpr int PNR = 256;       // weight rows per item
+constexpr int LDS_RING_BUDGET = 150 * 1024;   // bytes of LDS for the stage ring
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -34,7 +36,8 @@ DEVI void lds_dma4(const void* src, uint8_t* lds_block) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_block, 4, 0, 0);
 }
 
-// Wait until at most n vector-memory operations of this wave are pending.
+// Wait until at most n vector-memory operations of this wave are pending
+// (n is wave-uniform; the counter field holds 0..63).
 DEVI void wait_vm(int n) {
   switch (n) {
     case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
@@ -54,10 +57,53 @@ DEVI void wait_vm(int n) {
     case 14: asm volatile("s_waitcnt vmcnt(14)" ::: "memory"); break;
     case 15: asm volatile("s_waitcnt vmcnt(15)" ::: "memory"); break;
     case 16: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+    case 17: asm volatile("s_waitcnt vmcnt(17)" ::: "memory"); break;
+    case 18: asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); break;
+    case 19: asm volatile("s_waitcnt vmcnt(19)" ::: "memory"); break;
     case 20: asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); break;
+    case 21: asm volatile("s_waitcnt vmcnt(21)" ::: "memory"); break;
+    case 22: asm volatile("s_waitcnt vmcnt(22)" ::: "memory"); break;
+    case 23: asm volatile("s_waitcnt vmcnt(23)" ::: "memory"); break;
     case 24: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
+    case 25: asm volatile("s_waitcnt vmcnt(25)" ::: "memory"); break;
     case 26: asm volatile("s_waitcnt vmcnt(26)" ::: "memory"); break;
+    case 27: asm volatile("s_waitcnt vmcnt(27)" ::: "memory"); break;
+    case 28: asm volatile("s_waitcnt vmcnt(28)" ::: "memory"); break;
+    case 29: asm volatile("s_waitcnt vmcnt(29)" ::: "memory"); break;
     case 30: asm volatile("s_waitcnt vmcnt(30)" ::: "memory"); break;
+    case 31: asm volatile("s_waitcnt vmcnt(31)" ::: "memory"); break;
+    case 32: asm volatile("s_waitcnt vmcnt(32)" ::: "memory"); break;
+    case 33: asm volatile("s_waitcnt vmcnt(33)" ::: "memory"); break;
+    case 34: asm volatile("s_waitcnt vmcnt(34)" ::: "memory"); break;
+    case 35: asm volatile("s_waitcnt vmcnt(35)" ::: "memory"); break;
+    case 36: asm volatile("s_waitcnt vmcnt(36)" ::: "memory"); break;
+    case 37: asm volatile("s_waitcnt vmcnt(37)" ::: "memory"); break;
+    case 38: asm volatile("s_waitcnt vmcnt(38)" ::: "memory"); break;
+    case 39: asm volatile("s_waitcnt vmcnt(39)" ::: "memory"); break;
+    case 40: asm volatile("s_waitcnt vmcnt(40)" ::: "memory"); break;
+    case 41: asm volatile("s_waitcnt vmcnt(41)" ::: "memory"); break;
+    case 42: asm volatile("s_waitcnt vmcnt(42)" ::: "memory"); break;
+    case 43: asm volatile("s_waitcnt vmcnt(43)" ::: "memory"); break;
+    case 44: asm volatile("s_waitcnt vmcnt(44)" ::: "memory"); break;
+    case 45: asm volatile("s_waitcnt vmcnt(45)" ::: "memory"); break;
+    case 46: asm volatile("s_waitcnt vmcnt(46)" ::: "memory"); break;
+    case 47: asm volatile("s_waitcnt vmcnt(47)" ::: "memory"); break;
+    case 48: asm volatile("s_waitcnt vmcnt(48)" ::: "memory"); break;
+    case 49: asm volatile("s_waitcnt vmcnt(49)" ::: "memory"); break;
+    case 50: asm volatile("s_waitcnt vmcnt(50)" ::: "memory"); break;
+    case 51: asm volatile("s_waitcnt vmcnt(51)" ::: "memory"); break;
+    case 52: asm volatile("s_waitcnt vmcnt(52)" ::: "memory"); break;
+    case 53: asm volatile("s_waitcnt vmcnt(53)" ::: "memory"); break;
+    case 54: asm volatile("s_waitcnt vmcnt(54)" ::: "memory"); break;
+    case 55: asm volatile("s_waitcnt vmcnt(55)" ::: "memory"); break;
+    case 56: asm volatile("s_waitcnt vmcnt(56)" ::: "memory"); break;
+    case 57: asm volatile("s_waitcnt vmcnt(57)" ::: "memory"); break;
+    case 58: asm volatile("s_waitcnt vmcnt(58)" ::: "memory"); break;
+    case 59: asm volatile("s_waitcnt vmcnt(59)" ::: "memory"); break;
+    case 60: asm volatile("s_waitcnt vmcnt(60)" ::: "memory"); break;
+    case 61: asm volatile("s_waitcnt vmcnt(61)" ::: "memory"); break;
+    case 62: asm volatile("s_waitcnt vmcnt(62)" ::: "memory"); break;
+    case 63: asm volatile("s_waitcnt vmcnt(63)" ::: "memory"); break;
     default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
   }
 }
@@ -72,20 +118,31 @@ DEVI void raw_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int F>
-struct PipeFmt {
-  static constexpr int WB = FmtBits<F>::W;            // 8 or 4
+template <int F, bool GATEUP, int BM, int NR, int WM>
+struct PipeCfg {
+  static constexpr int WN = 4 / WM;
+  static constexpr int WB = FmtBits<F>::W;             // 8 or 4
   static constexpr int WROWB = 128 * WB / 8;           // weight bytes per row per step
-  static constexpr int TOKB = PBM * 128;               // token bytes per stage
-  static constexpr int WTB = PNR * WROWB;              // weight bytes per stage
+  static constexpr int TOKB = BM * 128;                // token bytes per stage
+  static constexpr int WTB = NR * WROWB;               // weight bytes per stage
   static constexpr bool ASC = F == F_FP8_BLK || F == F_MX;   // activation scales per step
   static constexpr int ASB = ASC ? 4 * 256 : 0;        // 256 dword slots (4 waves x 64)
-  static constexpr int WSB = F == F_MX ? 4 * PNR : 0;  // e8m0 weight scales, dword per row
+  static constexpr int WSB = F == F_MX ? 4 * 256 : 0;  // e8m0 weight scales, dword per row
   static constexpr int STAGE = TOKB + WTB + ASB + WSB;
+  static constexpr int NSTAGE_FIT = LDS_RING_BUDGET / STAGE;
+  static constexpr int NSTAGE = NSTAGE_FIT > 8 ? 8 : NSTAGE_FIT;
+  static constexpr int NBC = GATEUP ? NR / 2 : NR;     // output channels per item
+  static constexpr int TT = BM / WM / 16;              // 16-token tiles per wave
+  static constexpr int RT = NBC / WN / 16;             // 16-row tiles per matrix per wave
   // per-wave DMA instructions per stage (vmcnt units)
-  static constexpr int NTOK = TOKB / 1024 / 4;
-  static constexpr int NWT = WTB / 1024 / 4;
+  static constexpr int NTOK = TOKB / 4096;
+  static constexpr int NWT = WTB / 4096;
   static constexpr int LOADS = NTOK + NWT + (ASC ? 1 : 0) + (F == F_MX ? 1 : 0);
+  static_assert(NSTAGE >= 2, "stage ring does not fit");
+  static_assert(TT >= 1 && RT >= 1 && NTOK >= 1 && NWT >= 1, "tile shape");
+  static_assert(!(GATEUP && F == F_FP8_BLK) || NBC == 128, "1x128 requantisation needs 128 channels");
+  static_assert(!(GATEUP && F == F_MX) || RT % 2 == 0, "MX requantisation needs 32-channel groups");
+  static_assert((NSTAGE - 2) * LOADS <= 63, "vmcnt range");
 };
 
 // byte offset of (row, 16-byte chunk) in a swizzled [rows][128 B] block
@@ -95,16 +152,14 @@ DEVI int swz64(int row, int chunk) { return row * 64 + 16 * (chunk ^ ((row >> 1)
 
 }  // namespace
 
-template <int F, bool GATEUP, int NSTAGE>
+template <int F, bool GATEUP, int BM, int NR, int WM>
 __global__ void __launch_bounds__(PTHREADS) k_gemm_pipe(GemmArgs p) {
-  using PF = PipeFmt<F>;
-  constexpr int WB = PF::WB;
+  using PC = PipeCfg<F, GATEUP, BM, NR, WM>;
+  constexpr int WB = PC::WB, WN = PC::WN, NSTAGE = PC::NSTAGE;
   constexpr int NM = GATEUP ? 2 : 1;
-  constexpr int RT = GATEUP ? 4 : 8;           // 16-row weight tiles per matrix per wave
-  constexpr int TT = 4;                        // 16-token tiles per wave
-  constexpr int NBC = GATEUP ? 128 : 256;      // output channels per item
+  constexpr int RT = PC::RT, TT = PC::TT, NBC = PC::NBC;
   constexpr int WSC_MAX = 128;                 // K steps covered by the scale table
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * PF::STAGE + 2 * PBM * 4 + 2 * 2 * WSC_MAX * 4];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * PC::STAGE + 4 * BM * 4 + 2 * WSC_MAX * 4];
 
   if (p.cfg_self >= 0 && p.meta[META_CFG] != p.cfg_self) return;
   const int ntiles = p.meta[META_NTILES];
@@ -113,19 +168,19 @@ __global__ void __launch_bounds__(PTHREADS) k_gemm_pipe(GemmArgs p) {
   const int n_items = ntiles * nblk;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WM, wn = wave / WM;
   const int r16 = lane & 15, lg = lane >> 4;
   const long wrow = row_bytes<WB>(K), xrow = K;   // token rows are e4m3 here
   const int nsteps = K / 128;
-  float* amax_l = (float*)(lds + NSTAGE * PF::STAGE);
-  float* wsc_l = amax_l + 2 * PBM;            // [matrix][block of this item][K step]
+  float* amax_l = (float*)(lds + NSTAGE * PC::STAGE);   // [WN][BM]
+  float* wsc_l = amax_l + 4 * BM;                        // [2][K steps]
 
   const ItemRange ir = xcd_items(n_items);
   for (int item = ir.begin; item < ir.end; item += ir.step) {
     const int tile = item / nblk, nb = item - tile * nblk;
     const int g = p.tiles[2 * tile], r0 = p.tiles[2 * tile + 1];
     const int m0 = p.indptr[g] + r0;
-    const int M = min(PBM, p.counts[g] - r0);
+    const int M = min(BM, p.counts[g] - r0);
     const bool sh = g >= p.E;
     const uint8_t* W0 = sh ? p.sh_w0 : p.w0 + (size_t)g * N * wrow;
     const uint8_t* W1 = GATEUP ? (sh ? p.sh_w1 : p.w1 + (size_t)g * N * wrow) : nullptr;
@@ -137,71 +192,59 @@ __global__ void __launch_bounds__(PTHREADS) k_gemm_pipe(GemmArgs p) {
     }
     const uint8_t* S0 = (const uint8_t*)(sh ? p.sh_w0s : p.w0s) + s_off;
     const uint8_t* S1 = GATEUP ? (const uint8_t*)(sh ? p.sh_w1s : p.w1s) + s_off : nullptr;
+    const int cbase = nb * NBC;                 // first output channel of the item
 
     // --- source addresses of this lane's DMA slots (fixed for the item)
-    // tokens: instruction i of this wave fills LDS token rows (wave*NTOK+i)*8 .. +8
-    const uint8_t* tsrc[PF::NTOK];
+    const uint8_t* tsrc[PC::NTOK];
 #pragma unroll
-    for (int i = 0; i < PF::NTOK; ++i) {
-      const int row = (wave * PF::NTOK + i) * 8 + (lane >> 3);
+    for (int i = 0; i < PC::NTOK; ++i) {
+      const int row = (wave * PC::NTOK + i) * 8 + (lane >> 3);
       const int slot = m0 + (row < M ? row : 0);
       const int r = p.gather ? p.gather[slot] / p.gather_div : slot;
       const int chunk = (lane & 7) ^ (row & 7);
       tsrc[i] = p.a + (size_t)r * xrow + 16 * chunk;
     }
-    // weights: LDS weight row R -> global row
-    const uint8_t* wsrc[PF::NWT];
+    const uint8_t* wsrc[PC::NWT];
 #pragma unroll
-    for (int j = 0; j < PF::NWT; ++j) {
+    for (int j = 0; j < PC::NWT; ++j) {
       int R, chunk;
       if constexpr (WB == 8) {
-        R = (wave * PF::NWT + j) * 8 + (lane >> 3);
+        R = (wave * PC::NWT + j) * 8 + (lane >> 3);
         chunk = (lane & 7) ^ (R & 7);
       } else {
-        R = (wave * PF::NWT + j) * 16 + (lane >> 2);
+        R = (wave * PC::NWT + j) * 16 + (lane >> 2);
         chunk = (lane & 3) ^ ((R >> 1) & 3);
       }
-      const uint8_t* base;
-      int grow;
-      if (GATEUP) {
-        base = R < 128 ? W0 : W1;
-        grow = nb * 128 + (R & 127);
-      } else {
-        base = W0;
-        grow = nb * 256 + R;
-      }
+      const uint8_t* base = (GATEUP && R >= NBC) ? W1 : W0;
+      const int grow = cbase + (GATEUP ? R % NBC : R);
       wsrc[j] = base + (size_t)grow * wrow + 16 * chunk;
     }
-    // activation scales: lane covers token row wave*64 + lane (rows >= BM unused)
     const uint8_t* asrc = nullptr;
-    if constexpr (PF::ASC) {
+    if constexpr (PC::ASC) {
       const int row = wave * 64 + lane;
       const int slot = m0 + (row < M ? row : 0);
       const int r = p.gather ? p.gather[slot] / p.gather_div : slot;
       if (F == F_FP8_BLK) asrc = (const uint8_t*)p.a_scale + ((size_t)r * (K / 128)) * 4;
       else asrc = (const uint8_t*)p.a_scale + (size_t)r * (K / 32);
     }
-    // MX weight scales: lane covers weight row wave*64 + lane
     const uint8_t* wssrc = nullptr;
     if constexpr (F == F_MX) {
-      const int R = wave * 64 + lane;
-      const uint8_t* sb = GATEUP ? (R < 128 ? S0 : S1) : S0;
-      const int grow = GATEUP ? nb * 128 + (R & 127) : nb * 256 + R;
+      const int R0 = wave * 64 + lane;
+      const int R = R0 < NR ? R0 : 0;           // slots beyond NR load row 0, unused
+      const uint8_t* sb = (GATEUP && R >= NBC) ? S1 : S0;
+      const int grow = cbase + (GATEUP ? R % NBC : R);
       wssrc = sb + (size_t)grow * (K / 32);
     }
 
     auto issue = [&](int s) {
-      uint8_t* st = lds + (s % NSTAGE) * PF::STAGE;
+      uint8_t* st = lds + (s % NSTAGE) * PC::STAGE;
 #pragma unroll
-      for (int i = 0; i < PF::NTOK; ++i) lds_dma16(tsrc[i] + (size_t)s * 128, st + (wave * PF::NTOK + i) * 1024);
+      for (int i = 0; i < PC::NTOK; ++i) lds_dma16(tsrc[i] + (size_t)s * 128, st + (wave * PC::NTOK + i) * 1024);
 #pragma unroll
-      for (int j = 0; j < PF::NWT; ++j)
-        lds_dma16(wsrc[j] + (size_t)s * PF::WROWB, st + PF::TOKB + (wave * PF::NWT + j) * 1024);
-      if constexpr (F == F_FP8_BLK) lds_dma4(asrc + 4 * s, st + PF::TOKB + PF::WTB + wave * 256);
-      if constexpr (F == F_MX) {
-        lds_dma4(asrc + 4 * s, st + PF::TOKB + PF::WTB + wave * 256);
-        lds_dma4(wssrc + 4 * s, st + PF::TOKB + PF::WTB + PF::ASB + wave * 256);
-      }
+      for (int j = 0; j < PC::NWT; ++j)
+        lds_dma16(wsrc[j] + (size_t)s * PC::WROWB, st + PC::TOKB + (wave * PC::NWT + j) * 1024);
+      if constexpr (PC::ASC) lds_dma4(asrc + 4 * s, st + PC::TOKB + PC::WTB + wave * 256);
+      if constexpr (F == F_MX) lds_dma4(wssrc + 4 * s, st + PC::TOKB + PC::WTB + PC::ASB + wave * 256);
     };
 
     f32x4 acc[NM][RT][TT];
@@ -213,13 +256,14 @@ __global__ void __launch_bounds__(PTHREADS) k_gemm_pipe(GemmArgs p) {
         for (int t = 0; t < TT; ++t) acc[m][rt][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
     if constexpr (F == F_FP8_BLK) {
-      // the item's 128x128 weight block scales for every K step, into LDS
-      // (gate/up: blocks nb of both matrices; down: blocks 2nb and 2nb+1)
+      // the item's 128x128 weight block scales for every K step, into LDS:
+      // gate/up: block cbase/128 of both matrices; down: the wave's block
+      // (NR/WN rows, inside one 128-row block) for each of NR/128 blocks
       for (int i = tid; i < 2 * nsteps; i += PTHREADS) {
         const int which = i / nsteps, ks = i - which * nsteps;
-        float v;
-        if (GATEUP) v = ((const float*)(which == 0 ? S0 : S1))[(size_t)nb * (K / 128) + ks];
-        else v = ((const float*)S0)[(size_t)(2 * nb + which) * (K / 128) + ks];
+        float v = 0.f;
+        if (GATEUP) v = ((const float*)(which == 0 ? S0 : S1))[(size_t)(cbase / 128) * (K / 128) + ks];
+        else if (which * 128 < NR) v = ((const float*)S0)[(size_t)(cbase / 128 + which) * (K / 128) + ks];
         wsc_l[which * WSC_MAX + ks] = v;
       }
       __syncthreads();
@@ -230,17 +274,18 @@ __global__ void __launch_bounds__(PTHREADS) k_gemm_pipe(GemmArgs p) {
     for (int s = 0; s < NSTAGE - 1; ++s)
       if (s < nsteps) issue(s);
 
+    const int trow0 = wm * (BM / WM);                      // first token row of the wave
+    const int wrow0 = wn * (NBC / WN);                     // first weight row (per matrix)
     for (int s = 0; s < nsteps; ++s) {
       const int ahead = min(NSTAGE - 2, nsteps - 1 - s);   // later stages still loading
-      wait_vm(ahead * PF::LOADS);
+      wait_vm(ahead * PC::LOADS);
       raw_barrier();
       if (s + NSTAGE - 1 < nsteps) issue(s + NSTAGE - 1);
-      const uint8_t* st = lds + (s % NSTAGE) * PF::STAGE;
-      // token fragments of this wave (64 tokens)
+      const uint8_t* st = lds + (s % NSTAGE) * PC::STAGE;
       i32x8 bfr[TT];
 #pragma unroll
       for (int t = 0; t < TT; ++t) {
-        const int row = wm * 64 + t * 16 + r16;
+        const int row = trow0 + t * 16 + r16;
         const i32x4 lo = *(const i32x4*)(st + swz128(row, lg));
         const i32x4 hi = *(const i32x4*)(st + swz128(row, lg + 4));
         bfr[t] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -249,32 +294,30 @@ __global__ void __launch_bounds__(PTHREADS) k_gemm_pipe(GemmArgs p) {
       int sbx[TT];
       if constexpr (F == F_FP8_BLK) {
 #pragma unroll
-        for (int t = 0; t < TT; ++t)
-          sx[t] = ((const float*)(st + PF::TOKB + PF::WTB))[wm * 64 + t * 16 + r16];
+        for (int t = 0; t < TT; ++t) sx[t] = ((const float*)(st + PC::TOKB + PC::WTB))[trow0 + t * 16 + r16];
       }
       if constexpr (F == F_MX) {
 #pragma unroll
-        for (int t = 0; t < TT; ++t)
-          sbx[t] = (st + PF::TOKB + PF::WTB)[(wm * 64 + t * 16 + r16) * 4 + lg];
+        for (int t = 0; t < TT; ++t) sbx[t] = (st + PC::TOKB + PC::WTB)[(trow0 + t * 16 + r16) * 4 + lg];
       }
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         float wsc = 1.f;
-        if constexpr (F == F_FP8_BLK) wsc = wsc_l[(GATEUP ? m : wn) * WSC_MAX + s];
+        if constexpr (F == F_FP8_BLK)
+          wsc = wsc_l[(GATEUP ? m : (wrow0 / 128)) * WSC_MAX + s];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-          // LDS weight row of this lane for tile rt
-          const int R = GATEUP ? (m * 128 + wn * 64 + rt * 16 + r16) : (wn * 128 + rt * 16 + r16);
+          const int R = m * NBC + wrow0 + rt * 16 + r16;     // LDS weight row of this lane
           i32x8 afr;
           int sw = 0;
           if constexpr (WB == 8) {
-            const i32x4 lo = *(const i32x4*)(st + PF::TOKB + swz128(R, lg));
-            const i32x4 hi = *(const i32x4*)(st + PF::TOKB + swz128(R, lg + 4));
+            const i32x4 lo = *(const i32x4*)(st + PC::TOKB + swz128(R, lg));
+            const i32x4 hi = *(const i32x4*)(st + PC::TOKB + swz128(R, lg + 4));
             afr = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           } else {
-            const i32x4 q = *(const i32x4*)(st + PF::TOKB + swz64(R, lg));
+            const i32x4 q = *(const i32x4*)(st + PC::TOKB + swz64(R, lg));
             afr = (i32x8){q[0], q[1], q[2], q[3], 0, 0, 0, 0};
-            sw = (st + PF::TOKB + PF::WTB + PF::ASB)[R * 4 + lg];
+            sw = (st + PC::TOKB + PC::WTB + PC::ASB)[R * 4 + lg];
           }
 #pragma unroll
           for (int t = 0; t < TT; ++t) {
@@ -293,12 +336,12 @@ __global__ void __launch_bounds__(PTHREADS) k_gemm_pipe(GemmArgs p) {
     __syncthreads();   // every wave is done with the ring before it is refilled
 
     // ------------------------------------------------------------ epilogue
-    // lane: channel c0 + rt*16 + 4*lg + i, token row wm*64 + t*16 + r16
-    const int c0 = GATEUP ? nb * 128 + wn * 64 : nb * 256 + wn * 128;
+    // lane: channel c0 + rt*16 + 4*lg + i, token row trow0 + t*16 + r16
+    const int c0 = cbase + wrow0;
     int tok[TT];
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
-      const int r = wm * 64 + t * 16 + r16;
+      const int r = trow0 + t * 16 + r16;
       const int slot = m0 + (r < M ? r : 0);
       tok[t] = p.gather ? p.gather[slot] / p.gather_div : slot;
     }
@@ -318,10 +361,23 @@ __global__ void __launch_bounds__(PTHREADS) k_gemm_pipe(GemmArgs p) {
     if constexpr (!GATEUP) {
 #pragma unroll
       for (int t = 0; t < TT; ++t) {
-        const int r = wm * 64 + t * 16 + r16;
+        const int r = trow0 + t * 16 + r16;
         if (r >= M) continue;
+        const int slot = m0 + r;
+        const float w = p.row_w ? (slot < p.row_w_n ? p.row_w[p.row_w_idx[slot]] : 1.0f) : 1.0f;
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) store_down(p, m0 + r, c0 + rt * 16 + 4 * lg, acc[0][rt][t]);
+        for (int rt = 0; rt < RT; ++rt) {
+          const f32x4 v = acc[0][rt][t];
+          const int n0 = c0 + rt * 16 + 4 * lg;
+          if (p.row_w) {
+            const f32x4 vw = v * w;
+            const uint32_t lo = (uint32_t)f32_to_bf16(vw[0]) | ((uint32_t)f32_to_bf16(vw[1]) << 16);
+            const uint32_t hi = (uint32_t)f32_to_bf16(vw[2]) | ((uint32_t)f32_to_bf16(vw[3]) << 16);
+            *(uint2*)((uint16_t*)p.out + (size_t)slot * N + n0) = make_uint2(lo, hi);
+          } else {
+            *(f32x4*)((float*)p.out + (size_t)slot * N + n0) = v;
+          }
+        }
       }
     } else {
 #pragma unroll
@@ -333,14 +389,14 @@ __global__ void __launch_bounds__(PTHREADS) k_gemm_pipe(GemmArgs p) {
       if constexpr (F == F_FP8_CH) {
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
-          const int r = wm * 64 + t * 16 + r16;
+          const int r = trow0 + t * 16 + r16;
           if (r >= M) continue;
           float* orow = (float*)p.out + (size_t)(m0 + r) * N;
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) *(f32x4*)(orow + c0 + rt * 16 + 4 * lg) = acc[0][rt][t];
         }
       } else if constexpr (F == F_FP8_BLK) {
-        // 1x128 group = this item's 128 channels = the two waves wn = 0, 1
+        // 1x128 group = the item's 128 channels, spread over the WN waves
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
           float mx = 0.f;
@@ -350,13 +406,15 @@ __global__ void __launch_bounds__(PTHREADS) k_gemm_pipe(GemmArgs p) {
             for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(acc[0][rt][t][i]));
           mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
           mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-          if (lg == 0) amax_l[wn * PBM + wm * 64 + t * 16 + r16] = mx;
+          if (lg == 0) amax_l[wn * BM + trow0 + t * 16 + r16] = mx;
         }
         __syncthreads();
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
-          const int r = wm * 64 + t * 16 + r16;
-          const float a = fmaxf(amax_l[r], amax_l[PBM + r]);
+          const int r = trow0 + t * 16 + r16;
+          float a = 0.f;
+#pragma unroll
+          for (int w = 0; w < WN; ++w) a = fmaxf(a, amax_l[w * BM + r]);
           const float sc = a > 0.f ? a / 448.0f : 1.0f;
           if (r < M) {
             uint8_t* orow = (uint8_t*)p.out + (size_t)(m0 + r) * N;
@@ -373,7 +431,7 @@ __global__ void __launch_bounds__(PTHREADS) k_gemm_pipe(GemmArgs p) {
       } else {   // F_MX: 32-channel groups = row-tile pairs of this wave
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
-          const int r = wm * 64 + t * 16 + r16;
+          const int r = trow0 + t * 16 + r16;
 #pragma unroll
           for (int gp = 0; gp < RT / 2; ++gp) {
             float mx = 0.f;
@@ -416,26 +474,51 @@ int pipe_cus() {
   return n;
 }
 
-template <int F, bool GATEUP>
+template <int F, bool GATEUP, int BM, int NR, int WM>
 hipError_t launch_pipe_t(const GemmArgs& g, hipStream_t st) {
-  constexpr int NBC = GATEUP ? 128 : 256;
-  if (g.N % NBC || g.K % 128 || g.K > 128 * 128) return hipErrorInvalidValue;
-  long max_tiles = (long)g.max_rows / PBM + g.max_groups;
-  long items = max_tiles * (g.N / NBC);
+  using PC = PipeCfg<F, GATEUP, BM, NR, WM>;
+  if (g.N % PC::NBC || g.K % 128 || g.K > 128 * 128) return hipErrorInvalidValue;
+  long max_tiles = (long)g.max_rows / BM + g.max_groups;
+  long items = max_tiles * (g.N / PC::NBC);
   long grid = pipe_cus();
   if (grid > items) grid = items;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL((k_gemm_pipe<F, GATEUP, 3>), dim3((unsigned)grid), dim3(PTHREADS), 0, st, g);
+  hipLaunchKernelGGL((k_gemm_pipe<F, GATEUP, BM, NR, WM>), dim3((unsigned)grid), dim3(PTHREADS), 0, st, g);
   return hipGetLastError();
+}
+
+// Tile shape per (format, op, row-block height).
+template <int F, bool GATEUP>
+hipError_t launch_pipe_bm(int bm, const GemmArgs& g, hipStream_t st) {
+  if constexpr (GATEUP) {
+    switch (bm) {
+      case 128: return launch_pipe_t<F, true, 128, 256, 2>(g, st);
+      case 64:
+        if constexpr (F == F_FP8_CH) return launch_pipe_t<F, true, 64, 128, 1>(g, st);
+        else return launch_pipe_t<F, true, 64, 256, 1>(g, st);
+      case 32:
+        if constexpr (F == F_FP8_CH) return launch_pipe_t<F, true, 32, 128, 1>(g, st);
+        else return launch_pipe_t<F, true, 32, 256, 1>(g, st);
+    }
+  } else {
+    switch (bm) {
+      case 128:
+        if (g.N % 256 == 0) return launch_pipe_t<F, false, 128, 256, 2>(g, st);
+        return launch_pipe_t<F, false, 128, 128, 2>(g, st);
+      case 64: return launch_pipe_t<F, false, 64, 128, 1>(g, st);
+      case 32: return launch_pipe_t<F, false, 32, 128, 1>(g, st);
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_gemm_pipe(int fmt, bool gateup, const GemmArgs& g, hipStream_t st) {
+hipError_t launch_gemm_pipe(int fmt, bool gateup, int bm, const GemmArgs& g, hipStream_t st) {
   switch (fmt) {
-    case F_FP8_CH: return gateup ? launch_pipe_t<F_FP8_CH, true>(g, st) : launch_pipe_t<F_FP8_CH, false>(g, st);
-    case F_FP8_BLK: return gateup ? launch_pipe_t<F_FP8_BLK, true>(g, st) : launch_pipe_t<F_FP8_BLK, false>(g, st);
-    case F_MX: return gateup ? launch_pipe_t<F_MX, true>(g, st) : launch_pipe_t<F_MX, false>(g, st);
+    case F_FP8_CH: return gateup ? launch_pipe_bm<F_FP8_CH, true>(bm, g, st) : launch_pipe_bm<F_FP8_CH, false>(bm, g, st);
+    case F_FP8_BLK: return gateup ? launch_pipe_bm<F_FP8_BLK, true>(bm, g, st) : launch_pipe_bm<F_FP8_BLK, false>(bm, g, st);
+    case F_MX: return gateup ? launch_pipe_bm<F_MX, true>(bm, g, st) : launch_pipe_bm<F_MX, false>(bm, g, st);
   }
   return hipErrorInvalidValue;
 }

@@ -412,20 +412,16 @@ hipError_t launch_one(const GemmArgs& g, hipStream_t st) {
 
 template <int F, bool GATEUP>
 hipError_t launch_bm(int bm, const GemmArgs& g, hipStream_t st) {
-  switch (bm) {
-    case 32: return launch_one<F, GATEUP, 32, 2>(g, st);
-    case 64: return launch_one<F, GATEUP, 64, 2>(g, st);
-    case 128:
-      if constexpr (F == F_BF16) {
-        return hipErrorInvalidValue;   // see num_cfgs
-      } else {
-        // the pipelined kernel covers 256 down-projection channels per item
-        if (GATEUP || g.N % 256 == 0) return launch_gemm_pipe(F, GATEUP, g, st);
-        if constexpr (!GATEUP) return launch_one<F, false, 128, 2>(g, st);
-        return hipErrorInvalidValue;
-      }
+  if constexpr (F != F_BF16) {
+    // FP8 and MX formats run the pipelined kernel at every row-block height
+    return launch_gemm_pipe(F, GATEUP, bm, g, st);
+  } else {
+    switch (bm) {
+      case 32: return launch_one<F, GATEUP, 32, 2>(g, st);
+      case 64: return launch_one<F, GATEUP, 64, 2>(g, st);
+    }
+    return hipErrorInvalidValue;   // bf16 stops at 64-row blocks
   }
-  return hipErrorInvalidValue;
 }
 
 }  // namespace

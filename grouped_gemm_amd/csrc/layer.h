@@ -135,5 +135,5 @@ hipError_t launch_indptr_table(const int32_t* user_indptr, int cap, const Dispat
 // Streaming (decode) grouped GEMM; fmt = Fmt, gateup = fused SwiGLU op.
 hipError_t launch_gemm_stream(int fmt, bool gateup, const GemmArgs& g, hipStream_t st);
 hipError_t launch_gemm_tiled(int fmt, bool gateup, int cfg, const GemmArgs& g, hipStream_t st);
-// Pipelined 128-row-block grouped GEMM (FP8 and MX formats).
-hipError_t launch_gemm_pipe(int fmt, bool gateup, const GemmArgs& g, hipStream_t st);
+// Pipelined grouped GEMM (FP8 and MX formats), row blocks of bm = 32/64/128.
+hipError_t launch_gemm_pipe(int fmt, bool gateup, int bm, const GemmArgs& g, hipStream_t st);
