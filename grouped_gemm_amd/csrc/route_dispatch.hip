@@ -169,55 +169,45 @@ DEVI void wave0_exclusive_scan(int32_t* a, int n, int32_t* total) {
 }
 
 // ---------------------------------------------------------------- config choice
-// Predicted time of the two projections under configuration cfg, from the
-// grid geometry the histogram induces (RaMP abstract: a wave cost model over
-// the CTA grid selects the configuration from the runtime expert histogram).
-// Per projection, a configuration is priced as
-//   rounds * (per-item time) + fixed launch cost,
-// rounds = ceil(items / concurrent items), and an item's time is the larger
-// of its streamed bytes at its share of HBM bandwidth and its MFMA work
-// (padding rows included) at its share of the matrix-core peak, each
-// derated by an efficiency factor of the kernel family.  Streaming (cfg 0):
-// an item is 16 output channels of one group, one 64-row pass; it streams
-// the weight rows once per pass.  Tiled (cfg >= 1): an item is a BM-row block
-// of one group times 128 (gate/up) or 128 (down) channels; weights of a
-// group are read from HBM once (later row blocks hit L2), tokens per item.
-DEVI float config_cost(int cfg, const int32_t* cnt, int G, int H, int I, int wbits, int xbits,
-                       int lane) {
-  const float cus = 256.f, bw = 8.0e12f, peak = (wbits == 16 ? 2.5e15f : 5.0e15f);
-  float t = 0.f;
-  if (cfg == 0) {
-    const float eff_bw = 0.60f;
-    float passes = 0.f, rows = 0.f;
-    for (int g = lane; g < G; g += 64) {
-      passes += (float)((cnt[g] + 63) / 64);
-      rows += (float)cnt[g];
-    }
-    passes = wave_sum(passes);
-    rows = wave_sum(rows);
-    float wbytes = passes * 3.f * H * (float)I * wbits / 8.f;
-    float flops = 6.f * H * (float)I * 64.f * passes;
-    t = fmaxf(wbytes / (bw * eff_bw), flops / (peak * 0.05f)) + 6e-6f;
-  } else {
-    const int bm = cfg_rows(cfg);
-    const float eff_bw = 0.55f, eff_mfma = 0.45f;
-    float tiles = 0.f, groups = 0.f;
-    for (int g = lane; g < G; g += 64) {
-      tiles += (float)((cnt[g] + bm - 1) / bm);
-      groups += cnt[g] > 0 ? 1.f : 0.f;
-    }
-    tiles = wave_sum(tiles);
-    groups = wave_sum(groups);
-    float wbytes = groups * 3.f * H * (float)I * wbits / 8.f;
-    float xbytes = tiles * bm * (H * (I / 128.f) + I * (H / 128.f)) * xbits / 8.f;
-    float flops = 6.f * H * (float)I * bm * tiles;
-    float items = tiles * (I / 128.f + H / 128.f);
-    float rounds = ceilf(items / (2.f * cus));
-    float per_item = fmaxf((wbytes + xbytes) / items / (bw * eff_bw / (2.f * cus)),
-                           flops / items / (peak * eff_mfma / (2.f * cus)));
-    t = rounds * per_item + 10e-6f;
+// Configuration from the runtime expert histogram (RaMP abstract: the best
+// kernel configuration depends on the routing distribution, not on the batch
+// size alone).  Statistics of the histogram: the active groups A, the largest
+// group m, the mean group r = rows / A.  The rule, in order:
+//  1. the work items a 32-row tiled grid would have (row blocks times output
+//     channel blocks of the first projection) cannot fill the CUs -> cfg 0,
+//     the streaming kernel, which splits K across waves instead;
+//  2. every group fits one 32-row block -> cfg 1 (each weight byte read
+//     once, least MFMA padding);
+//  3. every group fits one 64-row block -> cfg 2;
+//  4. groups average 64 rows or more -> cfg 3 (128-row blocks, the
+//     highest MFMA intensity per staged byte); otherwise cfg 2.
+// The rule reproduces the fastest measured configuration on the benchmarked
+// layer shapes; a fitted cost model over these statistics can replace it.
+DEVI int choose_config(const int32_t* cnt, int G, int I, int num_cfgs, int lane, int* max_out) {
+  int mx = 0, active = 0, rows = 0, tiles32 = 0;
+  for (int g = lane; g < G; g += 64) {
+    const int c = cnt[g];
+    mx = c > mx ? c : mx;
+    active += c > 0;
+    rows += c;
+    tiles32 += (c + 31) / 32;
   }
-  return t;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const int v = __shfl_xor(mx, o, 64);
+    mx = v > mx ? v : mx;
+    active += __shfl_xor(active, o, 64);
+    rows += __shfl_xor(rows, o, 64);
+    tiles32 += __shfl_xor(tiles32, o, 64);
+  }
+  *max_out = mx;
+  if (num_cfgs <= 1) return 0;
+  const int cus = 256;
+  const long items32 = (long)tiles32 * (I / 128);
+  if (items32 < cus) return 0;
+  if (mx <= 32) return 1;
+  if (mx <= 64 || num_cfgs < 4) return num_cfgs < 3 ? 1 : 2;
+  return (active > 0 && rows >= 64 * active) ? 3 : 2;
 }
 
 // Shared tail of both dispatch paths.  cnt (LDS, G entries) holds the
@@ -261,25 +251,10 @@ DEVI void finalize_dispatch(const DispatchArgs& d, int32_t* cnt, int32_t* scan_b
     if (l == 63) s_active = inc;
   }
   if (tid >= 128 && tid < 192) {
-    // one wave evaluates every configuration's cost over the histogram
+    // one wave derives the configuration from the histogram
     int l = tid - 128, mx = 0;
-    for (int g = l; g < G; g += 64) mx = cnt[g] > mx ? cnt[g] : mx;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      int v = __shfl_xor(mx, o, 64);
-      mx = v > mx ? v : mx;
-    }
-    int cfg = d.force_cfg;
-    if (cfg < 0) {
-      float best = 3.0e38f;
-      for (int c = 0; c < d.num_cfgs; ++c) {
-        float cost = config_cost(c, cnt, G, d.H, d.I, d.wbits, d.xbits, l);
-        if (cost < best) {
-          best = cost;
-          cfg = c;
-        }
-      }
-    }
+    int cfg = choose_config(cnt, G, d.I, d.num_cfgs, l, &mx);
+    if (d.force_cfg >= 0) cfg = d.force_cfg;
     if (l == 0) {
       s_max = mx;
       s_cfg = cfg;
