@@ -152,16 +152,21 @@ DEVI int swz64(int row, int chunk) { return row * 64 + 16 * (chunk ^ ((row >> 1)
 
 }  // namespace
 
+// LDS bytes one tile shape needs: stage ring, cross-wave amax, scale table.
 template <int F, bool GATEUP, int BM, int NR, int WM>
-__global__ void __launch_bounds__(PTHREADS) k_gemm_pipe(GemmArgs p) {
+constexpr int pipe_lds_bytes() {
+  return PipeCfg<F, GATEUP, BM, NR, WM>::NSTAGE * PipeCfg<F, GATEUP, BM, NR, WM>::STAGE +
+         4 * BM * 4 + 2 * 128 * 4;
+}
+
+template <int F, bool GATEUP, int BM, int NR, int WM>
+DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
   using PC = PipeCfg<F, GATEUP, BM, NR, WM>;
   constexpr int WB = PC::WB, WN = PC::WN, NSTAGE = PC::NSTAGE;
   constexpr int NM = GATEUP ? 2 : 1;
   constexpr int RT = PC::RT, TT = PC::TT, NBC = PC::NBC;
   constexpr int WSC_MAX = 128;                 // K steps covered by the scale table
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * PC::STAGE + 4 * BM * 4 + 2 * WSC_MAX * 4];
 
-  if (p.cfg_self >= 0 && p.meta[META_CFG] != p.cfg_self) return;
   const int ntiles = p.meta[META_NTILES];
   const int N = p.N, K = p.K;
   const int nblk = N / NBC;
@@ -461,6 +466,49 @@ __global__ void __launch_bounds__(PTHREADS) k_gemm_pipe(GemmArgs p) {
   }
 }
 
+// Tile shape of each row-block height (per format and op):
+//   gate/up: 128 channels (256 weight rows) per item; 2x2 waves at 128 rows,
+//            1x4 waves below; per-channel FP8 at 32/64 rows uses 64-channel
+//            items (it requantises in a separate pass, so the 1x128 group
+//            constraint does not apply);
+//   down:    256 channels per item (2x2 waves) at 128 rows when H allows,
+//            else 128; 128 channels with 1x4 waves at 32/64 rows.
+template <int F, bool GATEUP>
+struct PipeShapes {
+  static constexpr int NR_SMALL = (GATEUP && F != F_FP8_CH) ? 256 : 128;
+  static constexpr int LDS = [] {
+    int m = pipe_lds_bytes<F, GATEUP, 32, NR_SMALL, 1>();
+    int b = pipe_lds_bytes<F, GATEUP, 64, NR_SMALL, 1>();
+    int c = pipe_lds_bytes<F, GATEUP, 128, 256, 2>();
+    int d = 0;
+    if constexpr (!GATEUP) d = pipe_lds_bytes<F, GATEUP, 128, 128, 2>();
+    m = m > b ? m : b;
+    m = m > c ? m : c;
+    return m > d ? m : d;
+  }();
+};
+
+// One kernel for every row-block height: the configuration the dispatch
+// step wrote into meta selects the tile shape, so a single launch serves
+// configurations 1..3 and returns at once when configuration 0 (the
+// streaming kernel) was chosen.
+template <int F, bool GATEUP>
+__global__ void __launch_bounds__(PTHREADS) k_gemm_pipe(GemmArgs p) {
+  using SH = PipeShapes<F, GATEUP>;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[SH::LDS];
+  const int cfg = p.meta[META_CFG];
+  if (p.cfg_self >= 0 && cfg != p.cfg_self) return;
+  switch (cfg_rows(cfg) * (cfg > 0)) {
+    case 32: pipe_body<F, GATEUP, 32, SH::NR_SMALL, 1>(p, lds); break;
+    case 64: pipe_body<F, GATEUP, 64, SH::NR_SMALL, 1>(p, lds); break;
+    case 128:
+      if (GATEUP || p.N % 256 == 0) pipe_body<F, GATEUP, 128, 256, 2>(p, lds);
+      else if constexpr (!GATEUP) pipe_body<F, GATEUP, 128, 128, 2>(p, lds);
+      break;
+    default: break;
+  }
+}
+
 namespace {
 
 int pipe_cus() {
@@ -474,51 +522,24 @@ int pipe_cus() {
   return n;
 }
 
-template <int F, bool GATEUP, int BM, int NR, int WM>
-hipError_t launch_pipe_t(const GemmArgs& g, hipStream_t st) {
-  using PC = PipeCfg<F, GATEUP, BM, NR, WM>;
-  if (g.N % PC::NBC || g.K % 128 || g.K > 128 * 128) return hipErrorInvalidValue;
-  long max_tiles = (long)g.max_rows / BM + g.max_groups;
-  long items = max_tiles * (g.N / PC::NBC);
-  long grid = pipe_cus();
-  if (grid > items) grid = items;
-  if (grid < 1) grid = 1;
-  hipLaunchKernelGGL((k_gemm_pipe<F, GATEUP, BM, NR, WM>), dim3((unsigned)grid), dim3(PTHREADS), 0, st, g);
-  return hipGetLastError();
-}
-
-// Tile shape per (format, op, row-block height).
 template <int F, bool GATEUP>
-hipError_t launch_pipe_bm(int bm, const GemmArgs& g, hipStream_t st) {
-  if constexpr (GATEUP) {
-    switch (bm) {
-      case 128: return launch_pipe_t<F, true, 128, 256, 2>(g, st);
-      case 64:
-        if constexpr (F == F_FP8_CH) return launch_pipe_t<F, true, 64, 128, 1>(g, st);
-        else return launch_pipe_t<F, true, 64, 256, 1>(g, st);
-      case 32:
-        if constexpr (F == F_FP8_CH) return launch_pipe_t<F, true, 32, 128, 1>(g, st);
-        else return launch_pipe_t<F, true, 32, 256, 1>(g, st);
-    }
-  } else {
-    switch (bm) {
-      case 128:
-        if (g.N % 256 == 0) return launch_pipe_t<F, false, 128, 256, 2>(g, st);
-        return launch_pipe_t<F, false, 128, 128, 2>(g, st);
-      case 64: return launch_pipe_t<F, false, 64, 128, 1>(g, st);
-      case 32: return launch_pipe_t<F, false, 32, 128, 1>(g, st);
-    }
-  }
-  return hipErrorInvalidValue;
+hipError_t launch_pipe_t(const GemmArgs& g, hipStream_t st) {
+  if (g.N % (GATEUP ? 64 : 128) || g.K % 128 || g.K > 128 * 128) return hipErrorInvalidValue;
+  if (GATEUP && F != F_FP8_CH && g.N % 128) return hipErrorInvalidValue;
+  // persistent grid: one workgroup per CU (the stage ring fills the LDS),
+  // a multiple of the 8 XCDs
+  long grid = pipe_cus();
+  hipLaunchKernelGGL((k_gemm_pipe<F, GATEUP>), dim3((unsigned)grid), dim3(PTHREADS), 0, st, g);
+  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gemm_pipe(int fmt, bool gateup, int bm, const GemmArgs& g, hipStream_t st) {
+hipError_t launch_gemm_pipe(int fmt, bool gateup, const GemmArgs& g, hipStream_t st) {
   switch (fmt) {
-    case F_FP8_CH: return gateup ? launch_pipe_bm<F_FP8_CH, true>(bm, g, st) : launch_pipe_bm<F_FP8_CH, false>(bm, g, st);
-    case F_FP8_BLK: return gateup ? launch_pipe_bm<F_FP8_BLK, true>(bm, g, st) : launch_pipe_bm<F_FP8_BLK, false>(bm, g, st);
-    case F_MX: return gateup ? launch_pipe_bm<F_MX, true>(bm, g, st) : launch_pipe_bm<F_MX, false>(bm, g, st);
+    case F_FP8_CH: return gateup ? launch_pipe_t<F_FP8_CH, true>(g, st) : launch_pipe_t<F_FP8_CH, false>(g, st);
+    case F_FP8_BLK: return gateup ? launch_pipe_t<F_FP8_BLK, true>(g, st) : launch_pipe_t<F_FP8_BLK, false>(g, st);
+    case F_MX: return gateup ? launch_pipe_t<F_MX, true>(g, st) : launch_pipe_t<F_MX, false>(g, st);
   }
   return hipErrorInvalidValue;
 }

@@ -413,8 +413,7 @@ hipError_t launch_one(const GemmArgs& g, hipStream_t st) {
 template <int F, bool GATEUP>
 hipError_t launch_bm(int bm, const GemmArgs& g, hipStream_t st) {
   if constexpr (F != F_BF16) {
-    // FP8 and MX formats run the pipelined kernel at every row-block height
-    return launch_gemm_pipe(F, GATEUP, bm, g, st);
+    return hipErrorInvalidValue;   // FP8 and MX formats use launch_gemm_pipe
   } else {
     switch (bm) {
       case 32: return launch_one<F, GATEUP, 32, 2>(g, st);

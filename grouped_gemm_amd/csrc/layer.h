@@ -20,6 +20,8 @@
 // routes (scores staged in LDS) when everything fits in DISPATCH_LDS_MAX.
 #define SMALL_DISPATCH_SLOTS 8192
 #define DISPATCH_LDS_MAX (64 * 1024)
+// Expert counts up to which one thread routes a token (above: one wave)
+#define SMALL_E_THREAD_ROUTE 32
 // LDS ints the multi-block scan stages per pass of chunk counts
 #define SCAN_STAGE_INTS 12288
 
@@ -54,6 +56,7 @@ struct DispatchArgs {
   int force_cfg;          // -1: choose from the histogram
   int H, I, wbits, xbits; // for the cost model
   int num_cfgs;           // configurations the library has kernels for
+  int cus;                // compute units of the device (configuration rule)
 };
 
 // Grouped GEMM over expert-major row groups.
@@ -135,5 +138,7 @@ hipError_t launch_indptr_table(const int32_t* user_indptr, int cap, const Dispat
 // Streaming (decode) grouped GEMM; fmt = Fmt, gateup = fused SwiGLU op.
 hipError_t launch_gemm_stream(int fmt, bool gateup, const GemmArgs& g, hipStream_t st);
 hipError_t launch_gemm_tiled(int fmt, bool gateup, int cfg, const GemmArgs& g, hipStream_t st);
-// Pipelined grouped GEMM (FP8 and MX formats), row blocks of bm = 32/64/128.
-hipError_t launch_gemm_pipe(int fmt, bool gateup, int bm, const GemmArgs& g, hipStream_t st);
+// Pipelined grouped GEMM (FP8 and MX formats): one launch covers the tiled
+// configurations 1..3 (row blocks of 32/64/128); g.cfg_self = -1 runs
+// whichever of them the device chose, a value >= 1 only that one.
+hipError_t launch_gemm_pipe(int fmt, bool gateup, const GemmArgs& g, hipStream_t st);

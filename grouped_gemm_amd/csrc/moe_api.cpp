@@ -161,6 +161,17 @@ struct moe_ws {
 
 namespace {
 
+int device_cus() {
+  static int n = 0;
+  if (!n) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+  }
+  return n;
+}
+
 DispatchArgs dispatch_args(const moe_ws* ws, int T) {
   DispatchArgs a{};
   const moe_layer_desc& d = ws->d;
@@ -185,6 +196,7 @@ DispatchArgs dispatch_args(const moe_ws* ws, int T) {
   a.wbits = wbits_of(ws->fmt);
   a.xbits = xbits_of(ws->fmt);
   a.num_cfgs = num_cfgs(ws->fmt);
+  a.cus = device_cus();
   return a;
 }
 
@@ -200,23 +212,49 @@ GemmArgs gemm_args(const moe_ws* ws) {
   return g;
 }
 
-// Run a projection with every configuration that has kernels; each launch
-// returns at once unless the device chose its configuration.  `tiled_out`
-// and `tiled_scale` redirect the fused gate/up output of the tiled kernels,
-// which requantise the intermediate in their epilogue for the 1x128 and
-// MX formats.
+// Which kernel families the device's choice can land on, from bounds the
+// host knows without reading the histogram: rows_tot rows spread over at
+// most min(G, rows_tot) groups.  The device rule picks the streaming kernel
+// exactly when a 32-row tiled grid would have fewer items than CUs, with
+// items = (sum over groups of ceil(rows/32)) * (I/128), and that sum lies in
+// [ceil(rows_tot/32), ceil(rows_tot/32) + groups].  A forced configuration
+// is known outright.
+struct Candidates {
+  bool stream, tiled;
+};
+Candidates candidates(const moe_ws* ws, long rows_tot) {
+  if (ws->force_cfg >= 0) return {ws->force_cfg == 0, ws->force_cfg > 0};
+  const long cus = device_cus(), cb = ws->d.inter / 128;
+  const long groups = rows_tot < ws->L.G ? rows_tot : ws->L.G;
+  const long lo = (rows_tot + 31) / 32, hi = lo + groups;
+  return {lo * cb < cus, hi * cb >= cus};
+}
+
+// Run a projection with the kernel families the configuration can land on;
+// a launch whose family the device did not choose returns at once.
+// `tiled_out` and `tiled_scale` redirect the fused gate/up output of the
+// tiled kernels, which requantise the intermediate in their epilogue for the
+// 1x128 and MX formats.
 hipError_t run_gemm(const moe_ws* ws, bool gateup, GemmArgs g, void* tiled_out, void* tiled_scale,
-                    hipStream_t st) {
-  g.cfg_self = 0;
-  hipError_t e = launch_gemm_stream(ws->fmt, gateup, g, st);
-  if (e != hipSuccess) return e;
+                    long rows_tot, hipStream_t st) {
+  const Candidates cand = candidates(ws, rows_tot);
+  if (cand.stream) {
+    g.cfg_self = 0;
+    hipError_t e = launch_gemm_stream(ws->fmt, gateup, g, st);
+    if (e != hipSuccess) return e;
+  }
+  if (!cand.tiled) return hipSuccess;
   if (tiled_out) {
     g.out = tiled_out;
     g.out_scale = tiled_scale;
   }
+  if (ws->fmt != F_BF16) {
+    g.cfg_self = ws->force_cfg > 0 ? ws->force_cfg : -1;   // any tiled configuration
+    return launch_gemm_pipe(ws->fmt, gateup, g, st);
+  }
   for (int c = 1; c < num_cfgs(ws->fmt); ++c) {
     g.cfg_self = c;
-    e = launch_gemm_tiled(ws->fmt, gateup, c, g, st);
+    hipError_t e = launch_gemm_tiled(ws->fmt, gateup, c, g, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -269,7 +307,7 @@ int enqueue_layer(moe_ws* ws, const moe_weights* w, const uint16_t* x, const flo
   const bool fused_requant = ws->fmt == F_FP8_BLK || ws->fmt == F_MX;
   HIP_TRY(mark(2, 0), "event record");
   HIP_TRY(run_gemm(ws, true, g1, fused_requant ? ws->at<void>(L.hq) : nullptr,
-                   fused_requant ? ws->at<void>(L.hs) : nullptr, st),
+                   fused_requant ? ws->at<void>(L.hs) : nullptr, S_tot, st),
           "gate/up grouped GEMM launch");
   HIP_TRY(mark(2, 1), "event record");
   if (quant) {
@@ -301,7 +339,7 @@ int enqueue_layer(moe_ws* ws, const moe_weights* w, const uint16_t* x, const flo
   g2.row_w_idx = ws->at<int32_t>(L.gather);
   g2.row_w_n = S;
   HIP_TRY(mark(4, 0), "event record");
-  HIP_TRY(run_gemm(ws, false, g2, nullptr, nullptr, st), "down grouped GEMM launch");
+  HIP_TRY(run_gemm(ws, false, g2, nullptr, nullptr, S_tot, st), "down grouped GEMM launch");
   HIP_TRY(mark(4, 1), "event record");
   CombineArgs c{ws->at<void>(L.out_slot), ws->at<float>(L.w), ws->at<int32_t>(L.inv), T,
                 d.top_k, d.hidden, d.shared_experts, y, 1};

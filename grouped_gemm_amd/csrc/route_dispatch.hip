@@ -78,6 +78,50 @@ DEVI void route_one_token(const float* row, int E, int k, int score_fn, int lane
   }
 }
 
+// One thread routes one token (small expert counts): k passes over the E
+// scores, each taking the largest remaining key (score, then lowest index),
+// exactly the order route_one_token produces.
+DEVI void route_token_thread(const float* row, int E, int k, int score_fn, int32_t* ids_out,
+                             float* w_out, int32_t* ids_lds) {
+  uint64_t taken = 0;
+  int first = 0;
+  for (int j = 0; j < k; ++j) {
+    int best = -1;
+    uint32_t bk = 0;
+    for (int e = 0; e < E; ++e) {
+      if ((taken >> e) & 1ull) continue;
+      const uint32_t key = score_key(row[e]);
+      if (best < 0 || key > bk) {
+        best = e;
+        bk = key;
+      }
+    }
+    taken |= 1ull << best;
+    ids_out[j] = best;
+    if (ids_lds) ids_lds[j] = best;
+    if (j == 0) first = best;
+  }
+  const float top = row[first];
+  float sum = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const float l = row[ids_out[j]];
+    float v = score_fn == MOE_SCORE_SOFTMAX ? expf(l - top)
+              : score_fn == MOE_SCORE_SIGMOID ? 1.0f / (1.0f + expf(-l)) : l;
+    w_out[j] = v;
+    sum += v;
+  }
+  for (int j = 0; j < k; ++j) w_out[j] = w_out[j] / sum;
+}
+
+__global__ void __launch_bounds__(256) k_route_thread(const float* __restrict__ scores, int T, int E,
+                                                      int k, int score_fn, int32_t* __restrict__ ids,
+                                                      float* __restrict__ w) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  route_token_thread(scores + (size_t)t * E, E, k, score_fn, ids + (size_t)t * k, w + (size_t)t * k,
+                     nullptr);
+}
+
 __global__ void __launch_bounds__(256) k_route(const float* __restrict__ scores, int T, int E, int k,
                                                int score_fn, int32_t* __restrict__ ids,
                                                float* __restrict__ w) {
@@ -183,7 +227,8 @@ DEVI void wave0_exclusive_scan(int32_t* a, int n, int32_t* total) {
 //     highest MFMA intensity per staged byte); otherwise cfg 2.
 // The rule reproduces the fastest measured configuration on the benchmarked
 // layer shapes; a fitted cost model over these statistics can replace it.
-DEVI int choose_config(const int32_t* cnt, int G, int I, int num_cfgs, int lane, int* max_out) {
+DEVI int choose_config(const int32_t* cnt, int G, int I, int num_cfgs, int cus, int lane,
+                      int* max_out) {
   int mx = 0, active = 0, rows = 0, tiles32 = 0;
   for (int g = lane; g < G; g += 64) {
     const int c = cnt[g];
@@ -202,7 +247,6 @@ DEVI int choose_config(const int32_t* cnt, int G, int I, int num_cfgs, int lane,
   }
   *max_out = mx;
   if (num_cfgs <= 1) return 0;
-  const int cus = 256;
   const long items32 = (long)tiles32 * (I / 128);
   if (items32 < cus) return 0;
   if (mx <= 32) return 1;
@@ -253,7 +297,7 @@ DEVI void finalize_dispatch(const DispatchArgs& d, int32_t* cnt, int32_t* scan_b
   if (tid >= 128 && tid < 192) {
     // one wave derives the configuration from the histogram
     int l = tid - 128, mx = 0;
-    int cfg = choose_config(cnt, G, d.I, d.num_cfgs, l, &mx);
+    int cfg = choose_config(cnt, G, d.I, d.num_cfgs, d.cus, l, &mx);
     if (d.force_cfg >= 0) cfg = d.force_cfg;
     if (l == 0) {
       s_max = mx;
@@ -308,9 +352,15 @@ __global__ void __launch_bounds__(1024) k_dispatch_small(DispatchArgs d) {
     const int n = d.T * d.E;
     for (int i = tid; i < n; i += blockDim.x) sc_l[i] = d.scores[i];
     __syncthreads();
-    for (int t = wave; t < d.T; t += 16)
-      route_one_token(sc_l + t * d.E, d.E, d.k, d.score_fn, lane, d.ids + (size_t)t * d.k,
-                      d.w + (size_t)t * d.k, ids_l + t * d.k);
+    if (d.E <= SMALL_E_THREAD_ROUTE) {
+      for (int t = tid; t < d.T; t += blockDim.x)
+        route_token_thread(sc_l + t * d.E, d.E, d.k, d.score_fn, d.ids + (size_t)t * d.k,
+                           d.w + (size_t)t * d.k, ids_l + t * d.k);
+    } else {
+      for (int t = wave; t < d.T; t += 16)
+        route_one_token(sc_l + t * d.E, d.E, d.k, d.score_fn, lane, d.ids + (size_t)t * d.k,
+                        d.w + (size_t)t * d.k, ids_l + t * d.k);
+    }
   } else {
     for (int p = tid; p < S; p += blockDim.x) ids_l[p] = d.ids_in[p];
   }
@@ -425,7 +475,11 @@ size_t dispatch_small_lds(int T, int k, int G, int E, bool route) {
 hipError_t launch_route(const float* scores, int T, int E, int k, int score_fn, int32_t* ids,
                         float* w, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_route, dim3((T + 3) / 4), dim3(256), 0, st, scores, T, E, k, score_fn, ids, w);
+  if (E <= SMALL_E_THREAD_ROUTE)
+    hipLaunchKernelGGL(k_route_thread, dim3((T + 255) / 256), dim3(256), 0, st, scores, T, E, k,
+                       score_fn, ids, w);
+  else
+    hipLaunchKernelGGL(k_route, dim3((T + 3) / 4), dim3(256), 0, st, scores, T, E, k, score_fn, ids, w);
   return hipGetLastError();
 }
 
