@@ -203,7 +203,10 @@ def main():
         ach = dom_bytes / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "k_gemm_stream (gate/up + SwiGLU)", "avg_ms": round(dom_ms, 5),
+                "kernel": ("k_gemm_stream (gate/up + SwiGLU)" if main_pt["cfg"] == 0 else
+                           "k_gemm_pipe (gate/up + SwiGLU, %d-row blocks)"
+                           % {1: 32, 2: 64, 3: 128}.get(main_pt["cfg"], 0)),
+                "avg_ms": round(dom_ms, 5),
                 "bytes_per_launch": int(dom_bytes)}
     cpu = None
     if not args.no_cpu_baseline:
