@@ -32,6 +32,23 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = ("MoE layer µs + active TFLOP/s / HBM GB/s (FP8 W8A8) at 32, 128, 8192 tokens")
+
+# HBM bytes per launch of the dominant kernel measured with rocprofv3
+# FETCH_SIZE / WRITE_SIZE counters, scaled by the same counters on a plain
+# copy of known size (profiles/mixtral_fp8_T128_traffic_counters.md).  A
+# figure is only reported while the kernel sources still hash to the value
+# they had when the counters were taken.
+TRAFFIC = {
+    ("mixtral", 128, 2): {"bytes": 962603267, "src_sha": "da19cc0b662f4461"},
+}
+KERNEL_SRC = ["grouped_gemm_amd/csrc/gemm_pipe.hip", "grouped_gemm_amd/csrc/common.h",
+              "grouped_gemm_amd/csrc/layer.h"]
+
+
+def kernel_src_sha() -> str:
+    import hashlib
+    data = b"".join(open(os.path.join(ROOT, f), "rb").read() for f in KERNEL_SRC)
+    return hashlib.sha256(data).hexdigest()[:16]
 HBM_PEAK_GBS = 8000.0
 STAGES = ["route+dispatch", "quant_x", "gemm_gateup_swiglu", "quant_h", "gemm_down", "combine"]
 
@@ -168,6 +185,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--force-config", type=int, default=-1,
                     help="tile configuration (default: chosen on the device)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain elementwise copy of 256 MiB (fp32 in, fp32 out), "
+                         "whose known byte counts calibrate hardware traffic counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the layer holds every expert on one device); "
@@ -180,6 +200,16 @@ def main():
     import grouped_gemm_amd  # noqa: F401  (fails loudly if the library is not built)
 
     import moe_synth as ms
+    if args.copy_calibration:
+        n = 64 * 1024 * 1024
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: 3 x elementwise copy, {4 * n} bytes read and "
+            f"{4 * n} bytes written per launch")
+        del a, b
     sh0 = ms.CONFIGS[args.workload]
     T_main = args.tokens or max(sh0.tokens)
     points = []
@@ -201,8 +231,10 @@ def main():
     roof = None
     if dom_bytes is not None:
         ach = dom_bytes / (dom_ms * 1e-3) / 1e9
+        tr = TRAFFIC.get((args.workload, T_main, main_pt["cfg"]))
+        traffic = tr["bytes"] if tr and tr["src_sha"] == kernel_src_sha() else None
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": ("k_gemm_stream (gate/up + SwiGLU)" if main_pt["cfg"] == 0 else
                            "k_gemm_pipe (gate/up + SwiGLU, %d-row blocks)"
                            % {1: 32, 2: 64, 3: 128}.get(main_pt["cfg"], 0)),
