@@ -23,9 +23,15 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
          "-fvisibility=hidden", "-Wno-unused-result"]
 
 
+# per-file code generation options: the pipelined GEMM keeps MFMA results in
+# ordinary VGPRs, so its per-block scaling reads them without copies out of
+# the accumulation registers
+EXTRA = {"gemm_pipe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)

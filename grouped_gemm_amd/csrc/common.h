@@ -66,7 +66,9 @@ DEVI uint32_t cvt4_e4m3(float a, float b, float c, float d) {
   return (uint32_t)r;
 }
 
-DEVI float silu(float z) { return z / (1.0f + __expf(-z)); }
+// z * sigmoid(z); the reciprocal is the hardware one (1 ulp), far inside the
+// rounding of the bf16 / e4m3 values the result is stored as.
+DEVI float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // floor(log2(a)) for a finite a > 0 (exact, from the exponent field).
 DEVI int ilog2_floor(float a) {
@@ -150,6 +152,12 @@ template <> struct FmtBits<F_BF16> { static constexpr int W = 16, X = 16; };
 template <> struct FmtBits<F_FP8_CH> { static constexpr int W = 8, X = 8; };
 template <> struct FmtBits<F_FP8_BLK> { static constexpr int W = 8, X = 8; };
 template <> struct FmtBits<F_MX> { static constexpr int W = 4, X = 8; };
+
+// Load from a wave-uniform address through the scalar data cache.  Only for
+// arrays that the running kernel never writes (routing tables, scales).
+template <class T> DEVI T ldu(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
 
 // Bytes of one operand row of K elements.
 template <int BITS> DEVI constexpr long row_bytes(int K) { return (long)K * BITS / 8; }

@@ -108,6 +108,29 @@ DEVI void wait_vm(int n) {
   }
 }
 
+// The same with a compile-time count (no dispatch on the value).
+template <int N>
+DEVI void wait_vm_c() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait for a*L + b*M outstanding operations, a = A, A-1, ..., 0 tried in
+// that order (the first is the steady state), b in {0, 1}.
+template <int L, int M, int A>
+DEVI void wait_vm_ab(int a, bool b) {
+  if constexpr (A >= 0) {
+    if (a == A) {
+      if (b) wait_vm_c<A * L + M>();
+      else wait_vm_c<A * L>();
+    } else {
+      wait_vm_ab<L, M, A - 1>(a, b);
+    }
+  } else {
+    wait_vm_c<0>();
+  }
+}
+
 // Workgroup barrier without the memory fence of __syncthreads(): the fence
 // would wait for every outstanding vector-memory operation, including the
 // asynchronous stage loads that must stay in flight.  Callers wait for what
@@ -125,24 +148,30 @@ struct PipeCfg {
   static constexpr int WROWB = 128 * WB / 8;           // weight bytes per row per step
   static constexpr int TOKB = BM * 128;                // token bytes per stage
   static constexpr int WTB = NR * WROWB;               // weight bytes per stage
-  static constexpr bool ASC = F == F_FP8_BLK || F == F_MX;   // activation scales per step
-  static constexpr int ASB = ASC ? 4 * 256 : 0;        // 256 dword slots (4 waves x 64)
+  static constexpr bool ASC = F == F_FP8_BLK || F == F_MX;   // per-step scale slots
+  static constexpr int ASB = ASC ? 4 * 256 : 0;        // 64 dwords per wave
   static constexpr int WSB = F == F_MX ? 4 * 256 : 0;  // e8m0 weight scales, dword per row
   static constexpr int STAGE = TOKB + WTB + ASB + WSB;
   static constexpr int NSTAGE_FIT = LDS_RING_BUDGET / STAGE;
   static constexpr int NSTAGE = NSTAGE_FIT > 8 ? 8 : NSTAGE_FIT;
   static constexpr int NBC = GATEUP ? NR / 2 : NR;     // output channels per item
+  static constexpr int NM_ = GATEUP ? 2 : 1;           // weight matrices
   static constexpr int TT = BM / WM / 16;              // 16-token tiles per wave
   static constexpr int RT = NBC / WN / 16;             // 16-row tiles per matrix per wave
-  // per-wave DMA instructions per stage (vmcnt units)
+  static constexpr int RB = BM > 64 ? BM : 64;         // rows per row-metadata buffer
+  // per-wave DMA instructions per stage (vmcnt units), and per item start
   static constexpr int NTOK = TOKB / 4096;
   static constexpr int NWT = WTB / 4096;
   static constexpr int LOADS = NTOK + NWT + (ASC ? 1 : 0) + (F == F_MX ? 1 : 0);
+  static constexpr int NMETA = 4;
   static_assert(NSTAGE >= 2, "stage ring does not fit");
   static_assert(TT >= 1 && RT >= 1 && NTOK >= 1 && NWT >= 1, "tile shape");
   static_assert(!(GATEUP && F == F_FP8_BLK) || NBC == 128, "1x128 requantisation needs 128 channels");
   static_assert(!(GATEUP && F == F_MX) || RT % 2 == 0, "MX requantisation needs 32-channel groups");
-  static_assert((NSTAGE - 2) * LOADS <= 63, "vmcnt range");
+  static_assert(F != F_FP8_BLK || BM <= 192, "the fourth wave's scale slot carries weight scales");
+  static_assert(F != F_MX || !GATEUP || NR == 256, "MX gate/up scale rows: one matrix per wave pair");
+  static_assert((NSTAGE - 2) * (LOADS + NMETA) <= 63, "vmcnt range");
+  static_assert(NM_ * NBC <= 256 && NBC % 64 == 0, "channel scales: one per lane of the four waves");
 };
 
 // byte offset of (row, 16-byte chunk) in a swizzled [rows][128 B] block
@@ -152,213 +181,366 @@ DEVI int swz64(int row, int chunk) { return row * 64 + 16 * (chunk ^ ((row >> 1)
 
 }  // namespace
 
-// LDS bytes one tile shape needs: stage ring, cross-wave amax, scale table.
+// LDS bytes one tile shape needs: stage ring, cross-wave amax, item
+// metadata (double-buffered row indices, activation scales, routing weights
+// and per-channel weight scales) and a sink for the metadata loads of waves
+// that carry none.
 template <int F, bool GATEUP, int BM, int NR, int WM>
 constexpr int pipe_lds_bytes() {
-  return PipeCfg<F, GATEUP, BM, NR, WM>::NSTAGE * PipeCfg<F, GATEUP, BM, NR, WM>::STAGE +
-         4 * BM * 4 + 2 * 128 * 4;
+  using PC = PipeCfg<F, GATEUP, BM, NR, WM>;
+  return PC::NSTAGE * PC::STAGE + 4 * BM * 4 + 3 * 2 * PC::RB * 4 + 2 * 256 * 4 + 4 * 256;
 }
 
+// One persistent workgroup walks its items (row block x channel block) as a
+// single stream of K steps: the ring runs on across item boundaries, so the
+// first stages of the next item load while the current item finishes and
+// writes its outputs.  Per item, the rows' metadata (gather indices, then
+// per-row activation scales and routing weights) is also brought into LDS by
+// asynchronous loads issued ahead of the item's first stage.
+//
+// All DMA sources are a wave-uniform base (advanced per step in scalar
+// registers) plus a fixed 32-bit per-lane offset.
 template <int F, bool GATEUP, int BM, int NR, int WM>
 DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
   using PC = PipeCfg<F, GATEUP, BM, NR, WM>;
   constexpr int WB = PC::WB, WN = PC::WN, NSTAGE = PC::NSTAGE;
   constexpr int NM = GATEUP ? 2 : 1;
-  constexpr int RT = PC::RT, TT = PC::TT, NBC = PC::NBC;
-  constexpr int WSC_MAX = 128;                 // K steps covered by the scale table
+  constexpr int RT = PC::RT, TT = PC::TT, NBC = PC::NBC, RB = PC::RB;
+  constexpr int NTOK = PC::NTOK, NWT = PC::NWT, LOADS = PC::LOADS, NMETA = PC::NMETA;
+  constexpr int MW = (BM + 63) / 64;             // waves whose lanes carry item rows
 
-  const int ntiles = p.meta[META_NTILES];
   const int N = p.N, K = p.K;
   const int nblk = N / NBC;
-  const int n_items = ntiles * nblk;
+  const int n_items = ldu(p.meta + META_NTILES) * nblk;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % WM, wn = wave / WM;
   const int r16 = lane & 15, lg = lane >> 4;
-  const long wrow = row_bytes<WB>(K), xrow = K;   // token rows are e4m3 here
-  const int nsteps = K / 128;
+  const uint32_t wrow = (uint32_t)row_bytes<WB>(K), xrow = (uint32_t)K;   // token rows: e4m3
+  const int ns = K / 128;
+  // activation-scale bytes per token row
+  const uint32_t srow = F == F_FP8_BLK ? (uint32_t)(K / 128) * 4 : (uint32_t)(K / 32);
+
   float* amax_l = (float*)(lds + NSTAGE * PC::STAGE);   // [WN][BM]
-  float* wsc_l = amax_l + 4 * BM;                        // [2][K steps]
+  int32_t* idx_l = (int32_t*)(amax_l + 4 * BM);          // [2][RB] row index source values
+  float* as_l = (float*)(idx_l + 2 * RB);                // [2][RB] per-row activation scale (FP8 per channel)
+  float* rw_l = as_l + 2 * RB;                           // [2][RB] routing weight of the row's slot
+  float* cs_l = rw_l + 2 * RB;                           // [2][256] channel scales (FP8 per channel)
+  uint8_t* sink_l = (uint8_t*)(cs_l + 2 * 256);          // [4][256]
 
   const ItemRange ir = xcd_items(n_items);
-  for (int item = ir.begin; item < ir.end; item += ir.step) {
+  if (ir.begin >= ir.end) return;
+  const int nit = (ir.end - ir.begin + ir.step - 1) / ir.step;
+  const int nq = nit * ns;                               // K steps of this workgroup
+  const int D = min(NSTAGE - 1, ns);                     // stages loaded ahead
+
+  // array whose values select the rows of an item: the activation gather, or
+  // (down projection) the slot -> routing-weight index
+  const int32_t* rowsrc = p.gather ? p.gather : (p.row_w ? p.row_w_idx : nullptr);
+
+  struct It {
+    int g, m0, M, cbase;
+    bool sh;
+  };
+  auto info = [&](int j) {
+    const int item = ir.begin + j * ir.step;
     const int tile = item / nblk, nb = item - tile * nblk;
-    const int g = p.tiles[2 * tile], r0 = p.tiles[2 * tile + 1];
-    const int m0 = p.indptr[g] + r0;
-    const int M = min(BM, p.counts[g] - r0);
-    const bool sh = g >= p.E;
-    const uint8_t* W0 = sh ? p.sh_w0 : p.w0 + (size_t)g * N * wrow;
-    const uint8_t* W1 = GATEUP ? (sh ? p.sh_w1 : p.w1 + (size_t)g * N * wrow) : nullptr;
-    size_t s_off = 0;
-    if (!sh) {
-      if (F == F_FP8_CH) s_off = (size_t)g * N * 4;
-      if (F == F_FP8_BLK) s_off = (size_t)g * (N / 128) * (K / 128) * 4;
-      if (F == F_MX) s_off = (size_t)g * N * (K / 32);
-    }
-    const uint8_t* S0 = (const uint8_t*)(sh ? p.sh_w0s : p.w0s) + s_off;
-    const uint8_t* S1 = GATEUP ? (const uint8_t*)(sh ? p.sh_w1s : p.w1s) + s_off : nullptr;
-    const int cbase = nb * NBC;                 // first output channel of the item
+    It r;
+    r.g = ldu(p.tiles + 2 * tile);
+    const int r0 = ldu(p.tiles + 2 * tile + 1);
+    r.m0 = ldu(p.indptr + r.g) + r0;
+    r.M = min(BM, ldu(p.counts + r.g) - r0);
+    r.sh = r.g >= p.E;
+    r.cbase = nb * NBC;
+    return r;
+  };
 
-    // --- source addresses of this lane's DMA slots (fixed for the item)
-    const uint8_t* tsrc[PC::NTOK];
-#pragma unroll
-    for (int i = 0; i < PC::NTOK; ++i) {
-      const int row = (wave * PC::NTOK + i) * 8 + (lane >> 3);
-      const int slot = m0 + (row < M ? row : 0);
-      const int r = p.gather ? p.gather[slot] / p.gather_div : slot;
-      const int chunk = (lane & 7) ^ (row & 7);
-      tsrc[i] = p.a + (size_t)r * xrow + 16 * chunk;
+  // ---- per-lane DMA offsets that are the same for every item.  The weight
+  // rows of one wave belong to one matrix (gate or up) and its DMA
+  // instructions differ by a whole number of row groups, so one lane offset
+  // serves all of them; the rest is a wave-uniform base.
+  constexpr int RPI = WB == 8 ? 8 : 16;                  // weight rows per DMA instruction
+  static_assert(!GATEUP || NBC % (NWT * RPI) == 0, "a wave's weight rows lie in one matrix");
+  const int wr0 = wave * NWT * RPI;                      // first weight row of this wave
+  const bool wup = GATEUP && wr0 >= NBC;                 // wave loads up rows
+  uint32_t woff;
+  if constexpr (WB == 8) woff = (uint32_t)(lane >> 3) * wrow + 16 * ((lane & 7) ^ ((lane >> 3) & 7));
+  else woff = (uint32_t)(lane >> 2) * wrow + 16 * ((lane & 3) ^ ((lane >> 3) & 3));
+  const size_t wrel = (size_t)(wup ? wr0 - NBC : wr0) * wrow;   // wave's rows in its matrix
+  uint32_t wsoff = 0;        // MX: e8m0 scale row of this lane's weight row
+  if constexpr (F == F_MX) {
+    const int R0 = wave * 64 + lane;
+    const int R = R0 < NR ? R0 : 0;
+    wsoff = (uint32_t)(GATEUP && R >= NBC ? R - NBC : R) * (uint32_t)(K / 32);
+  }
+
+  // ---- issue-side state: bases advanced by one K step per issued stage
+  const uint8_t* ib_tok = nullptr;         // token rows (uniform)
+  const uint8_t* ib_w = nullptr;           // this wave's weight rows
+  const uint8_t* ib_a = nullptr;           // activation scales
+  const uint8_t* ib_ws = nullptr;          // weight scales (BLK: lane-selected block; MX: wave's matrix)
+  uint32_t toff[NTOK];
+  uint32_t aoff = 0;
+
+  const int mrow = wave * 64 + lane;       // metadata row of this lane
+  const bool mwave = wave < MW;
+
+  // row-index values of item jn -> idx_l[jn&1] (sink when absent)
+  auto meta_rows = [&](int jn) {
+    const int32_t* src = p.meta;
+    uint8_t* dst = sink_l + wave * 256;
+    if (jn < nit && rowsrc && mwave) {
+      const It n = info(jn);
+      src = rowsrc + n.m0 + min(mrow, n.M - 1);
+      dst = (uint8_t*)(idx_l + (jn & 1) * RB + wave * 64);
     }
-    const uint8_t* wsrc[PC::NWT];
+    lds_dma4(src, dst);
+  };
+
+  // build the issue-side state of item j (its row indices are in idx_l) and
+  // issue its per-item metadata: per-row activation scale (per-channel FP8),
+  // routing weight of the down projection's weighted store, and the
+  // per-channel weight scales
+  auto begin_item = [&](int j) {
+    const It it = info(j);
+    const int32_t* ix = idx_l + (j & 1) * RB;
+    const bool gat = p.gather != nullptr;
+    ib_tok = gat ? p.a : p.a + (size_t)it.m0 * xrow;
 #pragma unroll
-    for (int j = 0; j < PC::NWT; ++j) {
-      int R, chunk;
-      if constexpr (WB == 8) {
-        R = (wave * PC::NWT + j) * 8 + (lane >> 3);
-        chunk = (lane & 7) ^ (R & 7);
-      } else {
-        R = (wave * PC::NWT + j) * 16 + (lane >> 2);
-        chunk = (lane & 3) ^ ((R >> 1) & 3);
-      }
-      const uint8_t* base = (GATEUP && R >= NBC) ? W1 : W0;
-      const int grow = cbase + (GATEUP ? R % NBC : R);
-      wsrc[j] = base + (size_t)grow * wrow + 16 * chunk;
+    for (int i = 0; i < NTOK; ++i) {
+      const int row = (wave * NTOK + i) * 8 + (lane >> 3);
+      const int rr = min(row, it.M - 1);
+      const uint32_t r = gat ? (uint32_t)(ix[rr] / p.gather_div) : (uint32_t)rr;
+      toff[i] = r * xrow + 16 * ((lane & 7) ^ (row & 7));
     }
-    const uint8_t* asrc = nullptr;
+    const int rr = min(mrow, it.M - 1);
+    const uint32_t rm = gat ? (uint32_t)(ix[rr] / p.gather_div) : (uint32_t)rr;
     if constexpr (PC::ASC) {
-      const int row = wave * 64 + lane;
-      const int slot = m0 + (row < M ? row : 0);
-      const int r = p.gather ? p.gather[slot] / p.gather_div : slot;
-      if (F == F_FP8_BLK) asrc = (const uint8_t*)p.a_scale + ((size_t)r * (K / 128)) * 4;
-      else asrc = (const uint8_t*)p.a_scale + (size_t)r * (K / 32);
+      ib_a = gat ? (const uint8_t*)p.a_scale : (const uint8_t*)p.a_scale + (size_t)it.m0 * srow;
+      aoff = rm * srow;
     }
-    const uint8_t* wssrc = nullptr;
+    const size_t wexp = (size_t)it.g * N * wrow;
+    const uint8_t* wm0 = wup ? (it.sh ? p.sh_w1 : p.w1 + wexp) : (it.sh ? p.sh_w0 : p.w0 + wexp);
+    ib_w = wm0 + (size_t)it.cbase * wrow + wrel;
+    if constexpr (F == F_FP8_BLK) {
+      // lane 0: block of the gate (down: first 128 rows), lane 1: up (down:
+      // the second 128 rows when the item has them)
+      const size_t so = it.sh ? 0 : (size_t)it.g * (N / 128) * (K / 128) * 4;
+      const size_t blk = (size_t)(it.cbase / 128) * (K / 128) * 4;
+      const uint8_t* s0 = (const uint8_t*)(it.sh ? p.sh_w0s : p.w0s) + so + blk;
+      const uint8_t* s1;
+      if (GATEUP) s1 = (const uint8_t*)(it.sh ? p.sh_w1s : p.w1s) + so + blk;
+      else s1 = NR > 128 ? s0 + (size_t)(K / 128) * 4 : s0;
+      ib_ws = (lane & 1) ? s1 : s0;
+    }
     if constexpr (F == F_MX) {
-      const int R0 = wave * 64 + lane;
-      const int R = R0 < NR ? R0 : 0;           // slots beyond NR load row 0, unused
-      const uint8_t* sb = (GATEUP && R >= NBC) ? S1 : S0;
-      const int grow = cbase + (GATEUP ? R % NBC : R);
-      wssrc = sb + (size_t)grow * (K / 32);
+      const size_t so = it.sh ? 0 : (size_t)it.g * N * (K / 32);
+      const size_t ro = (size_t)it.cbase * (K / 32);
+      const bool up = GATEUP && wave * 64 >= NBC;
+      ib_ws = (const uint8_t*)(up ? (it.sh ? p.sh_w1s : p.w1s) : (it.sh ? p.sh_w0s : p.w0s)) + so + ro;
     }
+    const void* as_src = p.meta;
+    uint8_t* as_dst = sink_l + wave * 256;
+    const void* rw_src = p.meta;
+    uint8_t* rw_dst = sink_l + wave * 256;
+    if (mwave) {
+      if (F == F_FP8_CH) {
+        as_src = gat ? (const float*)p.a_scale + rm : (const float*)p.a_scale + it.m0 + rr;
+        as_dst = (uint8_t*)(as_l + (j & 1) * RB + wave * 64);
+      }
+      if (p.row_w) {
+        const int slot = it.m0 + rr;
+        rw_src = slot < p.row_w_n ? p.row_w + ix[rr] : p.row_w;
+        rw_dst = (uint8_t*)(rw_l + (j & 1) * RB + wave * 64);
+      }
+    }
+    lds_dma4(as_src, as_dst);
+    lds_dma4(rw_src, rw_dst);
+    const void* cs_src = p.meta;
+    uint8_t* cs_dst = sink_l + wave * 256;
+    if (F == F_FP8_CH && wave * 64 < NM * NBC) {
+      const int m = wave * 64 / NBC;          // the matrix is uniform per wave (NBC % 64 == 0)
+      const size_t so = it.sh ? 0 : (size_t)it.g * N;
+      const void* sbase;
+      if (m == 0) sbase = it.sh ? p.sh_w0s : p.w0s;
+      else sbase = it.sh ? p.sh_w1s : p.w1s;
+      cs_src = (const float*)sbase + so + it.cbase + (wave * 64 - m * NBC) + lane;
+      cs_dst = (uint8_t*)(cs_l + (j & 1) * 256 + wave * 64);
+    }
+    lds_dma4(cs_src, cs_dst);
+  };
 
-    auto issue = [&](int s) {
-      uint8_t* st = lds + (s % NSTAGE) * PC::STAGE;
+  // one stage into ring slot `slot`, then advance the bases by one K step
+  auto issue = [&](int slot) {
+    uint8_t* st = lds + slot * PC::STAGE;
 #pragma unroll
-      for (int i = 0; i < PC::NTOK; ++i) lds_dma16(tsrc[i] + (size_t)s * 128, st + (wave * PC::NTOK + i) * 1024);
+    for (int i = 0; i < NTOK; ++i) lds_dma16(ib_tok + toff[i], st + (wave * NTOK + i) * 1024);
+    // the offset is re-materialised as a 32-bit value in the loop, so the
+    // loads take the scalar base + 32-bit lane offset form
+    uint32_t wo = woff;
+    asm volatile("" : "+v"(wo));
 #pragma unroll
-      for (int j = 0; j < PC::NWT; ++j)
-        lds_dma16(wsrc[j] + (size_t)s * PC::WROWB, st + PC::TOKB + (wave * PC::NWT + j) * 1024);
-      if constexpr (PC::ASC) lds_dma4(asrc + 4 * s, st + PC::TOKB + PC::WTB + wave * 256);
-      if constexpr (F == F_MX) lds_dma4(wssrc + 4 * s, st + PC::TOKB + PC::WTB + PC::ASB + wave * 256);
-    };
+    for (int jj = 0; jj < NWT; ++jj)
+      lds_dma16(ib_w + (size_t)jj * RPI * wrow + wo, st + PC::TOKB + (wave * NWT + jj) * 1024);
+    if constexpr (F == F_FP8_BLK) {
+      if (wave == 3)   // the step's weight block scales (lanes 0 and 1)
+        lds_dma4(ib_ws, st + PC::TOKB + PC::WTB + 3 * 256);
+      else
+        lds_dma4(ib_a + aoff, st + PC::TOKB + PC::WTB + wave * 256);
+    }
+    if constexpr (F == F_MX) {
+      lds_dma4(ib_a + aoff, st + PC::TOKB + PC::WTB + wave * 256);
+      lds_dma4(ib_ws + wsoff, st + PC::TOKB + PC::WTB + PC::ASB + wave * 256);
+    }
+    ib_tok += 128;
+    ib_w += PC::WROWB;
+    ib_a += 4;
+    ib_ws += 4;
+  };
 
-    f32x4 acc[NM][RT][TT];
+  // ---- start: row indices of the first item, then the first D stages
+  meta_rows(0);
+  wait_vm(0);
+  raw_barrier();
+  begin_item(0);
+  meta_rows(1);
+  for (int q = 0; q < D; ++q) issue(q);
+
+  f32x4 acc[NM][RT][TT];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int t = 0; t < TT; ++t) acc[m][rt][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  const int trow0 = wm * (BM / WM);                      // first token row of the wave
+  const int wrow0 = wn * (NBC / WN);                     // first weight row (per matrix)
+  // compute position (item j, step s, ring slot cs); issue position (item
+  // ji, step si, ring slot is_) runs D stages ahead, at most one item ahead
+  int j = 0, s = 0, cs = 0;
+  int ji = D == ns ? 1 : 0, si = D == ns ? 0 : D, is_ = D % NSTAGE;
+  for (int q = 0; q < nq; ++q) {
+    // Stages q+1 .. q+ahead may stay in flight.  Metadata loads issued
+    // with an item start among them are not counted, so there the wait also
+    // covers a few loads of the next stage (once per item).  At an item's
+    // first step everything is waited for: the previous item's output
+    // stores share the counter with the loads.
+    {
+      const int ahead = min(D - 1, nq - 1 - q);
+      if ((s == 0 && j > 0) || ahead == 0) wait_vm_c<0>();
+      else if (ahead == NSTAGE - 2) wait_vm_c<(NSTAGE - 2) * LOADS>();
+      else wait_vm_ab<LOADS, 0, NSTAGE - 3>(ahead, false);
+    }
+    raw_barrier();
+    if (ji < nit) {
+      if (si == 0) {
+        begin_item(ji);
+        meta_rows(ji + 1);
+      }
+      issue(is_);
+      is_ = is_ + 1 == NSTAGE ? 0 : is_ + 1;
+      if (++si == ns) {
+        si = 0;
+        ++ji;
+      }
+    }
+    const uint8_t* st = lds + cs * PC::STAGE;
+    cs = cs + 1 == NSTAGE ? 0 : cs + 1;
+    // every fragment of the step is read from LDS up front, so the reads
+    // overlap each other and the MFMAs wait only for their own operands
+    i32x8 bfr[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      const int row = trow0 + t * 16 + r16;
+      const i32x4 lo = *(const i32x4*)(st + swz128(row, lg));
+      const i32x4 hi = *(const i32x4*)(st + swz128(row, lg + 4));
+      bfr[t] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    i32x8 afr[NM][RT];
+    int sw[NM][RT];
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int t = 0; t < TT; ++t) acc[m][rt][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
+      for (int rt = 0; rt < RT; ++rt) {
+        const int R = m * NBC + wrow0 + rt * 16 + r16;     // LDS weight row of this lane
+        sw[m][rt] = 0;
+        if constexpr (WB == 8) {
+          const i32x4 lo = *(const i32x4*)(st + PC::TOKB + swz128(R, lg));
+          const i32x4 hi = *(const i32x4*)(st + PC::TOKB + swz128(R, lg + 4));
+          afr[m][rt] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        } else {
+          const i32x4 qv = *(const i32x4*)(st + PC::TOKB + swz64(R, lg));
+          afr[m][rt] = (i32x8){qv[0], qv[1], qv[2], qv[3], 0, 0, 0, 0};
+          sw[m][rt] = (st + PC::TOKB + PC::WTB + PC::ASB)[R * 4 + lg];
+        }
+      }
     if constexpr (F == F_FP8_BLK) {
-      // the item's 128x128 weight block scales for every K step, into LDS:
-      // gate/up: block cbase/128 of both matrices; down: the wave's block
-      // (NR/WN rows, inside one 128-row block) for each of NR/128 blocks
-      for (int i = tid; i < 2 * nsteps; i += PTHREADS) {
-        const int which = i / nsteps, ks = i - which * nsteps;
-        float v = 0.f;
-        if (GATEUP) v = ((const float*)(which == 0 ? S0 : S1))[(size_t)(cbase / 128) * (K / 128) + ks];
-        else if (which * 128 < NR) v = ((const float*)S0)[(size_t)(cbase / 128 + which) * (K / 128) + ks];
-        wsc_l[which * WSC_MAX + ks] = v;
-      }
-      __syncthreads();
-    }
-
-    // prologue: NSTAGE-1 steps in flight
+      // 128x128 block scaling: each K step is one scale block, so every
+      // product is formed unscaled and then added with its row's
+      // (activation scale x weight block scale).  Products of one weight
+      // row tile go to one of two register sets, and the scaling of one
+      // set runs while the MFMAs of the other are in flight.
+      const float* scl = (const float*)(st + PC::TOKB + PC::WTB);
+      float sc[NM][TT];
 #pragma unroll
-    for (int s = 0; s < NSTAGE - 1; ++s)
-      if (s < nsteps) issue(s);
-
-    const int trow0 = wm * (BM / WM);                      // first token row of the wave
-    const int wrow0 = wn * (NBC / WN);                     // first weight row (per matrix)
-    for (int s = 0; s < nsteps; ++s) {
-      const int ahead = min(NSTAGE - 2, nsteps - 1 - s);   // later stages still loading
-      wait_vm(ahead * PC::LOADS);
-      raw_barrier();
-      if (s + NSTAGE - 1 < nsteps) issue(s + NSTAGE - 1);
-      const uint8_t* st = lds + (s % NSTAGE) * PC::STAGE;
-      i32x8 bfr[TT];
+      for (int m = 0; m < NM; ++m) {
+        const float wsc = scl[3 * 64 + (GATEUP ? m : (wrow0 / 128))];
 #pragma unroll
-      for (int t = 0; t < TT; ++t) {
-        const int row = trow0 + t * 16 + r16;
-        const i32x4 lo = *(const i32x4*)(st + swz128(row, lg));
-        const i32x4 hi = *(const i32x4*)(st + swz128(row, lg + 4));
-        bfr[t] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        for (int t = 0; t < TT; ++t) sc[m][t] = scl[trow0 + t * 16 + r16] * wsc;
       }
-      float sx[TT];
+      constexpr int NC = NM * RT;
+      f32x4 d[2][TT];
+#pragma unroll
+      for (int c = 0; c <= NC; ++c) {
+        if (c < NC) {
+#pragma unroll
+          for (int t = 0; t < TT; ++t)
+            d[c & 1][t] = mfma_f8(afr[c / RT][c % RT], bfr[t], (f32x4){0.f, 0.f, 0.f, 0.f});
+        }
+        if (c > 0) {
+          const int pc = c - 1, pm = pc / RT, prt = pc % RT;
+#pragma unroll
+          for (int t = 0; t < TT; ++t) acc[pm][prt][t] += d[pc & 1][t] * sc[pm][t];
+        }
+      }
+    } else {
       int sbx[TT];
-      if constexpr (F == F_FP8_BLK) {
-#pragma unroll
-        for (int t = 0; t < TT; ++t) sx[t] = ((const float*)(st + PC::TOKB + PC::WTB))[trow0 + t * 16 + r16];
-      }
       if constexpr (F == F_MX) {
 #pragma unroll
         for (int t = 0; t < TT; ++t) sbx[t] = (st + PC::TOKB + PC::WTB)[(trow0 + t * 16 + r16) * 4 + lg];
       }
 #pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        float wsc = 1.f;
-        if constexpr (F == F_FP8_BLK)
-          wsc = wsc_l[(GATEUP ? m : (wrow0 / 128)) * WSC_MAX + s];
+      for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          const int R = m * NBC + wrow0 + rt * 16 + r16;     // LDS weight row of this lane
-          i32x8 afr;
-          int sw = 0;
-          if constexpr (WB == 8) {
-            const i32x4 lo = *(const i32x4*)(st + PC::TOKB + swz128(R, lg));
-            const i32x4 hi = *(const i32x4*)(st + PC::TOKB + swz128(R, lg + 4));
-            afr = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          } else {
-            const i32x4 q = *(const i32x4*)(st + PC::TOKB + swz64(R, lg));
-            afr = (i32x8){q[0], q[1], q[2], q[3], 0, 0, 0, 0};
-            sw = (st + PC::TOKB + PC::WTB + PC::ASB)[R * 4 + lg];
-          }
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
           for (int t = 0; t < TT; ++t) {
-            if constexpr (F == F_FP8_BLK) {
-              f32x4 d = mfma_f8(afr, bfr[t], (f32x4){0.f, 0.f, 0.f, 0.f});
-              acc[m][rt][t] += d * (sx[t] * wsc);
-            } else if constexpr (F == F_MX) {
-              acc[m][rt][t] = mfma_f4f8_scaled(afr, bfr[t], acc[m][rt][t], sw, sbx[t]);
-            } else {
-              acc[m][rt][t] = mfma_f8(afr, bfr[t], acc[m][rt][t]);
-            }
+            if constexpr (F == F_MX)
+              acc[m][rt][t] = mfma_f4f8_scaled(afr[m][rt], bfr[t], acc[m][rt][t], sw[m][rt], sbx[t]);
+            else
+              acc[m][rt][t] = mfma_f8(afr[m][rt], bfr[t], acc[m][rt][t]);
           }
-        }
-      }
     }
-    __syncthreads();   // every wave is done with the ring before it is refilled
+    if (++s < ns) continue;
 
     // ------------------------------------------------------------ epilogue
     // lane: channel c0 + rt*16 + 4*lg + i, token row trow0 + t*16 + r16
-    const int c0 = cbase + wrow0;
-    int tok[TT];
-#pragma unroll
-    for (int t = 0; t < TT; ++t) {
-      const int r = trow0 + t * 16 + r16;
-      const int slot = m0 + (r < M ? r : 0);
-      tok[t] = p.gather ? p.gather[slot] / p.gather_div : slot;
-    }
+    const It cur = info(j);
+    const int m0 = cur.m0, M = cur.M;
+    const int c0 = cur.cbase + wrow0;
+    const float* asj = as_l + (j & 1) * RB;
+    const float* rwj = rw_l + (j & 1) * RB;
     if constexpr (F == F_FP8_CH) {
+      const float* csj = cs_l + (j & 1) * 256;
 #pragma unroll
       for (int t = 0; t < TT; ++t) {
-        const float sxt = ((const float*)p.a_scale)[tok[t]];
+        const float sxt = asj[trow0 + t * 16 + r16];
 #pragma unroll
         for (int m = 0; m < NM; ++m)
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) {
-            const f32x4 wsv = *(const f32x4*)((const float*)(m == 0 ? S0 : S1) + c0 + rt * 16 + 4 * lg);
+            const f32x4 wsv = *(const f32x4*)(csj + m * NBC + wrow0 + rt * 16 + 4 * lg);
             acc[m][rt][t] = acc[m][rt][t] * sxt * wsv;
           }
       }
@@ -369,12 +551,12 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
         const int r = trow0 + t * 16 + r16;
         if (r >= M) continue;
         const int slot = m0 + r;
-        const float w = p.row_w ? (slot < p.row_w_n ? p.row_w[p.row_w_idx[slot]] : 1.0f) : 1.0f;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           const f32x4 v = acc[0][rt][t];
           const int n0 = c0 + rt * 16 + 4 * lg;
           if (p.row_w) {
+            const float w = slot < p.row_w_n ? rwj[r] : 1.0f;
             const f32x4 vw = v * w;
             const uint32_t lo = (uint32_t)f32_to_bf16(vw[0]) | ((uint32_t)f32_to_bf16(vw[1]) << 16);
             const uint32_t hi = (uint32_t)f32_to_bf16(vw[2]) | ((uint32_t)f32_to_bf16(vw[3]) << 16);
@@ -413,7 +595,10 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
           mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
           if (lg == 0) amax_l[wn * BM + trow0 + t * 16 + r16] = mx;
         }
-        __syncthreads();
+        // LDS-only exchange: the stage loads in flight must not be waited for
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        raw_barrier();
+        const int nb = cur.cbase / 128;
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
           const int r = trow0 + t * 16 + r16;
@@ -421,18 +606,18 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
 #pragma unroll
           for (int w = 0; w < WN; ++w) a = fmaxf(a, amax_l[w * BM + r]);
           const float sc = a > 0.f ? a / 448.0f : 1.0f;
+          const float isc = 1.0f / sc;
           if (r < M) {
             uint8_t* orow = (uint8_t*)p.out + (size_t)(m0 + r) * N;
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
               const f32x4 h = acc[0][rt][t];
               *(uint32_t*)(orow + c0 + rt * 16 + 4 * lg) =
-                  cvt4_e4m3(h[0] / sc, h[1] / sc, h[2] / sc, h[3] / sc);
+                  cvt4_e4m3(h[0] * isc, h[1] * isc, h[2] * isc, h[3] * isc);
             }
             if (wn == 0 && lg == 0) ((float*)p.out_scale)[(size_t)(m0 + r) * (N / 128) + nb] = sc;
           }
         }
-        __syncthreads();
       } else {   // F_MX: 32-channel groups = row-tile pairs of this wave
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
@@ -441,9 +626,9 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
           for (int gp = 0; gp < RT / 2; ++gp) {
             float mx = 0.f;
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
+            for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
-              for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(acc[0][2 * gp + q][t][i]));
+              for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(acc[0][2 * gp + qq][t][i]));
             mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
             mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
             int ex = mx > 0.f ? ilog2_floor(mx) - 8 : -127;
@@ -452,9 +637,9 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
             if (r < M) {
               uint8_t* orow = (uint8_t*)p.out + (size_t)(m0 + r) * N;
 #pragma unroll
-              for (int q = 0; q < 2; ++q) {
-                const f32x4 h = acc[0][2 * gp + q][t];
-                *(uint32_t*)(orow + c0 + (2 * gp + q) * 16 + 4 * lg) =
+              for (int qq = 0; qq < 2; ++qq) {
+                const f32x4 h = acc[0][2 * gp + qq][t];
+                *(uint32_t*)(orow + c0 + (2 * gp + qq) * 16 + 4 * lg) =
                     cvt4_e4m3(h[0] * inv, h[1] * inv, h[2] * inv, h[3] * inv);
               }
               if (lg == 0) ((uint8_t*)p.out_scale)[(size_t)(m0 + r) * (N / 32) + (c0 + 32 * gp) / 32] = (uint8_t)(ex + 127);
@@ -463,6 +648,14 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
         }
       }
     }
+    s = 0;
+    ++j;
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int t = 0; t < TT; ++t) acc[m][rt][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
 }
 
