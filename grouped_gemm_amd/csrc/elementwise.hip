@@ -17,14 +17,17 @@ struct QGroup {
   static constexpr int CHUNKS = AF == MOE_A_FP8_G128 ? 16 : AF == MOE_A_MXFP8_G32 ? 4 : 0;
 };
 
-// One 256-thread block per row; thread owns 8-element chunks c = tid + 256*j.
+// A 256-thread block quantises one row at a time and strides over the rows
+// (the grid is bounded, so a launch whose rows are absent or that the chosen
+// configuration skips costs a few blocks); thread owns 8-element chunks
+// c = tid + 256*j.
 template <int AF, bool IN_BF16, int MAXJ>
 __global__ void __launch_bounds__(256) k_quant(QuantArgs qa) {
-  const int row = blockIdx.x;
   if (qa.meta && qa.meta[META_CFG] != qa.only_cfg) return;
-  if (qa.nrows && row >= *qa.nrows) return;
+  const int nrows = qa.nrows ? min(*qa.nrows, qa.R) : qa.R;
   const int n = qa.n, nch = n / 8;
   const int tid = threadIdx.x;
+  for (int row = blockIdx.x; row < nrows; row += gridDim.x) {
   float v[MAXJ][8];
   float gmax[MAXJ];
 #pragma unroll
@@ -97,12 +100,26 @@ __global__ void __launch_bounds__(256) k_quant(QuantArgs qa) {
     }
     *(uint2*)(qa.q + (size_t)row * n + 8 * c) = make_uint2(lo, hi);
   }
+  if (AF == MOE_A_FP8_TOKEN) __syncthreads();   // red[] is reused by the next row
+  }
+}
+
+// bounded persistent grid: a few blocks per compute unit
+static int elementwise_grid(int rows) {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+  }
+  return rows < 8 * cus ? rows : 8 * cus;
 }
 
 template <int AF, bool IN_BF16>
 static hipError_t quant_dispatch_j(const QuantArgs& q, hipStream_t st) {
   int nch = q.n / 8, j = (nch + 255) / 256;
-  dim3 grid(q.R), block(256);
+  dim3 grid(elementwise_grid(q.R)), block(256);
   if (j <= 1) hipLaunchKernelGGL((k_quant<AF, IN_BF16, 1>), grid, block, 0, st, q);
   else if (j <= 2) hipLaunchKernelGGL((k_quant<AF, IN_BF16, 2>), grid, block, 0, st, q);
   else if (j <= 4) hipLaunchKernelGGL((k_quant<AF, IN_BF16, 4>), grid, block, 0, st, q);
@@ -151,36 +168,56 @@ DEVI void load8(const void* base, size_t row, int H, int ch, bool bf16, float (&
   }
 }
 
+// Blocks stride over the tokens.  The k slot rows of a chunk are loaded in
+// groups of up to CK (all loads of a group in flight together) and added in
+// ascending j.
+template <int CK>
 __global__ void __launch_bounds__(256) k_combine(CombineArgs c) {
-  const int t = blockIdx.x, H = c.H, nch = H / 8;
-  const int S = c.T * c.k;
+  const int H = c.H, nch = H / 8, k = c.k;
+  const int S = c.T * k;
   const bool wb = c.weighted_bf16 != 0;
-  for (int ch = threadIdx.x; ch < nch; ch += 256) {
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int j = 0; j < c.k; ++j) {
-      const int slot = c.inv[t * c.k + j];
-      const float wj = wb ? 1.0f : c.w[t * c.k + j];
-      float v[8];
-      load8(c.out_slot, (size_t)slot, H, ch, wb, v);
+  for (int t = blockIdx.x; t < c.T; t += gridDim.x) {
+    for (int ch = threadIdx.x; ch < nch; ch += 256) {
+      float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      for (int j0 = 0; j0 < k; j0 += CK) {
+        float v[CK][8];
+        float wj[CK];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += wj * v[i];
+        for (int u = 0; u < CK; ++u) {
+          if (j0 + u < k) {
+            const int slot = ldu(c.inv + (size_t)t * k + j0 + u);
+            wj[u] = wb ? 1.0f : ldu(c.w + (size_t)t * k + j0 + u);
+            load8(c.out_slot, (size_t)slot, H, ch, wb, v[u]);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < CK; ++u) {
+          if (j0 + u < k) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] += wj[u] * v[u][i];
+          }
+        }
+      }
+      if (c.shared) {
+        float v[8];
+        load8(c.out_slot, (size_t)(S + t), H, ch, wb, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += v[i];
+      }
+      uint32_t p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        p[i] = (uint32_t)f32_to_bf16(acc[2 * i]) | ((uint32_t)f32_to_bf16(acc[2 * i + 1]) << 16);
+      *(uint4*)(c.y + (size_t)t * H + 8 * ch) = make_uint4(p[0], p[1], p[2], p[3]);
     }
-    if (c.shared) {
-      float v[8];
-      load8(c.out_slot, (size_t)(S + t), H, ch, wb, v);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += v[i];
-    }
-    uint32_t p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      p[i] = (uint32_t)f32_to_bf16(acc[2 * i]) | ((uint32_t)f32_to_bf16(acc[2 * i + 1]) << 16);
-    *(uint4*)(c.y + (size_t)t * H + 8 * ch) = make_uint4(p[0], p[1], p[2], p[3]);
   }
 }
 
 hipError_t launch_combine(const CombineArgs& c, hipStream_t st) {
   if (c.T == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_combine, dim3(c.T), dim3(256), 0, st, c);
+  const dim3 grid(elementwise_grid(c.T)), block(256);
+  if (c.k <= 2) hipLaunchKernelGGL(k_combine<2>, grid, block, 0, st, c);
+  else if (c.k <= 4) hipLaunchKernelGGL(k_combine<4>, grid, block, 0, st, c);
+  else hipLaunchKernelGGL(k_combine<8>, grid, block, 0, st, c);
   return hipGetLastError();
 }

@@ -24,7 +24,6 @@
 
 namespace {
 
-constexpr int PTHREADS = 256;
 constexpr int LDS_RING_BUDGET = 150 * 1024;   // bytes of LDS for the stage ring
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -141,16 +140,16 @@ DEVI void raw_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int F, bool GATEUP, int BM, int NR, int WM>
+template <int F, bool GATEUP, int BM, int NR, int WM, int NW>
 struct PipeCfg {
-  static constexpr int WN = 4 / WM;
+  static constexpr int WN = NW / WM;
   static constexpr int WB = FmtBits<F>::W;             // 8 or 4
   static constexpr int WROWB = 128 * WB / 8;           // weight bytes per row per step
   static constexpr int TOKB = BM * 128;                // token bytes per stage
   static constexpr int WTB = NR * WROWB;               // weight bytes per stage
   static constexpr bool ASC = F == F_FP8_BLK || F == F_MX;   // per-step scale slots
-  static constexpr int ASB = ASC ? 4 * 256 : 0;        // 64 dwords per wave
-  static constexpr int WSB = F == F_MX ? 4 * 256 : 0;  // e8m0 weight scales, dword per row
+  static constexpr int ASB = ASC ? NW * 256 : 0;       // 64 dwords per wave
+  static constexpr int WSB = F == F_MX ? NW * 256 : 0; // e8m0 weight scales, dword per row
   static constexpr int STAGE = TOKB + WTB + ASB + WSB;
   static constexpr int NSTAGE_FIT = LDS_RING_BUDGET / STAGE;
   static constexpr int NSTAGE = NSTAGE_FIT > 8 ? 8 : NSTAGE_FIT;
@@ -160,18 +159,19 @@ struct PipeCfg {
   static constexpr int RT = NBC / WN / 16;             // 16-row tiles per matrix per wave
   static constexpr int RB = BM > 64 ? BM : 64;         // rows per row-metadata buffer
   // per-wave DMA instructions per stage (vmcnt units), and per item start
-  static constexpr int NTOK = TOKB / 4096;
-  static constexpr int NWT = WTB / 4096;
+  static constexpr int NTOK = TOKB / (NW * 1024);
+  static constexpr int NWT = WTB / (NW * 1024);
   static constexpr int LOADS = NTOK + NWT + (ASC ? 1 : 0) + (F == F_MX ? 1 : 0);
   static constexpr int NMETA = 4;
   static_assert(NSTAGE >= 2, "stage ring does not fit");
   static_assert(TT >= 1 && RT >= 1 && NTOK >= 1 && NWT >= 1, "tile shape");
   static_assert(!(GATEUP && F == F_FP8_BLK) || NBC == 128, "1x128 requantisation needs 128 channels");
   static_assert(!(GATEUP && F == F_MX) || RT % 2 == 0, "MX requantisation needs 32-channel groups");
-  static_assert(F != F_FP8_BLK || BM <= 192, "the fourth wave's scale slot carries weight scales");
+  static_assert(F != F_FP8_BLK || BM <= (NW - 1) * 64, "the last wave's scale slot carries weight scales");
+  static_assert(TOKB % (NW * 1024) == 0 && WTB % (NW * 1024) == 0, "whole DMA instructions per wave");
   static_assert(F != F_MX || !GATEUP || NR == 256, "MX gate/up scale rows: one matrix per wave pair");
   static_assert((NSTAGE - 2) * (LOADS + NMETA) <= 63, "vmcnt range");
-  static_assert(NM_ * NBC <= 256 && NBC % 64 == 0, "channel scales: one per lane of the four waves");
+  static_assert(NM_ * NBC <= NW * 64 && NBC % 64 == 0, "channel scales: one per lane of the waves");
 };
 
 // byte offset of (row, 16-byte chunk) in a swizzled [rows][128 B] block
@@ -185,10 +185,10 @@ DEVI int swz64(int row, int chunk) { return row * 64 + 16 * (chunk ^ ((row >> 1)
 // metadata (double-buffered row indices, activation scales, routing weights
 // and per-channel weight scales) and a sink for the metadata loads of waves
 // that carry none.
-template <int F, bool GATEUP, int BM, int NR, int WM>
+template <int F, bool GATEUP, int BM, int NR, int WM, int NW>
 constexpr int pipe_lds_bytes() {
-  using PC = PipeCfg<F, GATEUP, BM, NR, WM>;
-  return PC::NSTAGE * PC::STAGE + 4 * BM * 4 + 3 * 2 * PC::RB * 4 + 2 * 256 * 4 + 4 * 256;
+  using PC = PipeCfg<F, GATEUP, BM, NR, WM, NW>;
+  return PC::NSTAGE * PC::STAGE + PC::WN * BM * 4 + 3 * 2 * PC::RB * 4 + 2 * 256 * 4 + NW * 256;
 }
 
 // One persistent workgroup walks its items (row block x channel block) as a
@@ -200,9 +200,9 @@ constexpr int pipe_lds_bytes() {
 //
 // All DMA sources are a wave-uniform base (advanced per step in scalar
 // registers) plus a fixed 32-bit per-lane offset.
-template <int F, bool GATEUP, int BM, int NR, int WM>
+template <int F, bool GATEUP, int BM, int NR, int WM, int NW>
 DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
-  using PC = PipeCfg<F, GATEUP, BM, NR, WM>;
+  using PC = PipeCfg<F, GATEUP, BM, NR, WM, NW>;
   constexpr int WB = PC::WB, WN = PC::WN, NSTAGE = PC::NSTAGE;
   constexpr int NM = GATEUP ? 2 : 1;
   constexpr int RT = PC::RT, TT = PC::TT, NBC = PC::NBC, RB = PC::RB;
@@ -222,11 +222,11 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
   const uint32_t srow = F == F_FP8_BLK ? (uint32_t)(K / 128) * 4 : (uint32_t)(K / 32);
 
   float* amax_l = (float*)(lds + NSTAGE * PC::STAGE);   // [WN][BM]
-  int32_t* idx_l = (int32_t*)(amax_l + 4 * BM);          // [2][RB] row index source values
+  int32_t* idx_l = (int32_t*)(amax_l + WN * BM);         // [2][RB] row index source values
   float* as_l = (float*)(idx_l + 2 * RB);                // [2][RB] per-row activation scale (FP8 per channel)
   float* rw_l = as_l + 2 * RB;                           // [2][RB] routing weight of the row's slot
   float* cs_l = rw_l + 2 * RB;                           // [2][256] channel scales (FP8 per channel)
-  uint8_t* sink_l = (uint8_t*)(cs_l + 2 * 256);          // [4][256]
+  uint8_t* sink_l = (uint8_t*)(cs_l + 2 * 256);          // [NW][256]
 
   const ItemRange ir = xcd_items(n_items);
   if (ir.begin >= ir.end) return;
@@ -383,8 +383,8 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
     for (int jj = 0; jj < NWT; ++jj)
       lds_dma16(ib_w + (size_t)jj * RPI * wrow + wo, st + PC::TOKB + (wave * NWT + jj) * 1024);
     if constexpr (F == F_FP8_BLK) {
-      if (wave == 3)   // the step's weight block scales (lanes 0 and 1)
-        lds_dma4(ib_ws, st + PC::TOKB + PC::WTB + 3 * 256);
+      if (wave == NW - 1)   // the step's weight block scales (lanes 0 and 1)
+        lds_dma4(ib_ws, st + PC::TOKB + PC::WTB + (NW - 1) * 256);
       else
         lds_dma4(ib_a + aoff, st + PC::TOKB + PC::WTB + wave * 256);
     }
@@ -421,14 +421,19 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
   int j = 0, s = 0, cs = 0;
   int ji = D == ns ? 1 : 0, si = D == ns ? 0 : D, is_ = D % NSTAGE;
   for (int q = 0; q < nq; ++q) {
-    // Stages q+1 .. q+ahead may stay in flight.  Metadata loads issued
-    // with an item start among them are not counted, so there the wait also
-    // covers a few loads of the next stage (once per item).  At an item's
-    // first step everything is waited for: the previous item's output
-    // stores share the counter with the loads.
+    // Wait for stage q; stages q+1 .. q+ahead may stay in flight.  The
+    // count is the number of stage loads issued after stage q, n.  Loads
+    // complete in order, so while stage q is incomplete all n later loads
+    // are outstanding too and the counter stays above n: the wait is exact
+    // for loads.  The epilogues' output stores share the counter and may
+    // complete in any order; counted nowhere, they can only keep the
+    // counter higher (a longer wait), never let it pass early.  Metadata
+    // loads issued with an item start among the stages ahead are not
+    // counted either (the wait then also covers a few loads of the next
+    // stage, once per item).
     {
       const int ahead = min(D - 1, nq - 1 - q);
-      if ((s == 0 && j > 0) || ahead == 0) wait_vm_c<0>();
+      if (ahead == 0) wait_vm_c<0>();
       else if (ahead == NSTAGE - 2) wait_vm_c<(NSTAGE - 2) * LOADS>();
       else wait_vm_ab<LOADS, 0, NSTAGE - 3>(ahead, false);
     }
@@ -485,7 +490,7 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
       float sc[NM][TT];
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
-        const float wsc = scl[3 * 64 + (GATEUP ? m : (wrow0 / 128))];
+        const float wsc = scl[(NW - 1) * 64 + (GATEUP ? m : (wrow0 / 128))];
 #pragma unroll
         for (int t = 0; t < TT; ++t) sc[m][t] = scl[trow0 + t * 16 + r16] * wsc;
       }
@@ -574,7 +579,7 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[0][rt][t][i] = silu(acc[0][rt][t][i]) * acc[1][rt][t][i];
       if constexpr (F == F_FP8_CH) {
-#pragma unroll
+  #pragma unroll
         for (int t = 0; t < TT; ++t) {
           const int r = trow0 + t * 16 + r16;
           if (r >= M) continue;
@@ -598,7 +603,7 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
         // LDS-only exchange: the stage loads in flight must not be waited for
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         raw_barrier();
-        const int nb = cur.cbase / 128;
+          const int nb = cur.cbase / 128;
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
           const int r = trow0 + t * 16 + r16;
@@ -619,7 +624,7 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
           }
         }
       } else {   // F_MX: 32-channel groups = row-tile pairs of this wave
-#pragma unroll
+  #pragma unroll
         for (int t = 0; t < TT; ++t) {
           const int r = trow0 + t * 16 + r16;
 #pragma unroll
@@ -660,46 +665,51 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
 }
 
 // Tile shape of each row-block height (per format and op):
-//   gate/up: 128 channels (256 weight rows) per item; 2x2 waves at 128 rows,
-//            1x4 waves below; per-channel FP8 at 32/64 rows uses 64-channel
-//            items (it requantises in a separate pass, so the 1x128 group
-//            constraint does not apply);
-//   down:    256 channels per item (2x2 waves) at 128 rows when H allows,
-//            else 128; 128 channels with 1x4 waves at 32/64 rows.
+//   32/64 rows (decode-sized groups), four waves as 1x4: gate/up items of
+//            128 channels (256 weight rows), or 64 channels for per-channel
+//            FP8 (it requantises in a separate pass, so the 1x128 group
+//            constraint does not apply); down items of 128 channels;
+//   128 rows (prefill), eight waves as 2x4, two per SIMD, so one wave's
+//            waits for LDS and loads are covered by the other's MFMAs:
+//            gate/up items of 128 channels, down items of 256 channels when
+//            H allows, else 128.
 template <int F, bool GATEUP>
 struct PipeShapes {
   static constexpr int NR_SMALL = (GATEUP && F != F_FP8_CH) ? 256 : 128;
-  static constexpr int LDS = [] {
-    int m = pipe_lds_bytes<F, GATEUP, 32, NR_SMALL, 1>();
-    int b = pipe_lds_bytes<F, GATEUP, 64, NR_SMALL, 1>();
-    int c = pipe_lds_bytes<F, GATEUP, 128, 256, 2>();
+  static constexpr int LDS4 = [] {
+    const int a = pipe_lds_bytes<F, GATEUP, 32, NR_SMALL, 1, 4>();
+    const int b = pipe_lds_bytes<F, GATEUP, 64, NR_SMALL, 1, 4>();
+    return a > b ? a : b;
+  }();
+  static constexpr int LDS8 = [] {
+    const int c = pipe_lds_bytes<F, GATEUP, 128, 256, 2, 8>();
     int d = 0;
-    if constexpr (!GATEUP) d = pipe_lds_bytes<F, GATEUP, 128, 128, 2>();
-    m = m > b ? m : b;
-    m = m > c ? m : c;
-    return m > d ? m : d;
+    if constexpr (!GATEUP) d = pipe_lds_bytes<F, GATEUP, 128, 128, 2, 8>();
+    return c > d ? c : d;
   }();
 };
 
-// One kernel for every row-block height: the configuration the dispatch
-// step wrote into meta selects the tile shape, so a single launch serves
-// configurations 1..3 and returns at once when configuration 0 (the
-// streaming kernel) was chosen.
+// The device's configuration choice (meta) selects the tile shape: this
+// kernel serves configurations 1 and 2 and returns at once for the others.
 template <int F, bool GATEUP>
-__global__ void __launch_bounds__(PTHREADS) k_gemm_pipe(GemmArgs p) {
+__global__ void __launch_bounds__(256) k_gemm_pipe(GemmArgs p) {
   using SH = PipeShapes<F, GATEUP>;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[SH::LDS];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[SH::LDS4];
   const int cfg = p.meta[META_CFG];
   if (p.cfg_self >= 0 && cfg != p.cfg_self) return;
-  switch (cfg_rows(cfg) * (cfg > 0)) {
-    case 32: pipe_body<F, GATEUP, 32, SH::NR_SMALL, 1>(p, lds); break;
-    case 64: pipe_body<F, GATEUP, 64, SH::NR_SMALL, 1>(p, lds); break;
-    case 128:
-      if (GATEUP || p.N % 256 == 0) pipe_body<F, GATEUP, 128, 256, 2>(p, lds);
-      else if constexpr (!GATEUP) pipe_body<F, GATEUP, 128, 128, 2>(p, lds);
-      break;
-    default: break;
-  }
+  if (cfg == 1) pipe_body<F, GATEUP, 32, SH::NR_SMALL, 1, 4>(p, lds);
+  else if (cfg == 2) pipe_body<F, GATEUP, 64, SH::NR_SMALL, 1, 4>(p, lds);
+}
+
+// Configuration 3 (128-row blocks), eight waves.
+template <int F, bool GATEUP>
+__global__ void __launch_bounds__(512) k_gemm_pipe8(GemmArgs p) {
+  using SH = PipeShapes<F, GATEUP>;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[SH::LDS8];
+  const int cfg = p.meta[META_CFG];
+  if (cfg != 3 || (p.cfg_self >= 0 && cfg != p.cfg_self)) return;
+  if (GATEUP || p.N % 256 == 0) pipe_body<F, GATEUP, 128, 256, 2, 8>(p, lds);
+  else if constexpr (!GATEUP) pipe_body<F, GATEUP, 128, 128, 2, 8>(p, lds);
 }
 
 namespace {
@@ -716,23 +726,27 @@ int pipe_cus() {
 }
 
 template <int F, bool GATEUP>
-hipError_t launch_pipe_t(const GemmArgs& g, hipStream_t st) {
-  if (g.N % (GATEUP ? 64 : 128) || g.K % 128 || g.K > 128 * 128) return hipErrorInvalidValue;
+hipError_t launch_pipe_t(int family, const GemmArgs& g, hipStream_t st) {
+  if (g.N % (GATEUP ? 64 : 128) || g.K % 128) return hipErrorInvalidValue;
   if (GATEUP && F != F_FP8_CH && g.N % 128) return hipErrorInvalidValue;
   // persistent grid: one workgroup per CU (the stage ring fills the LDS),
   // a multiple of the 8 XCDs
-  long grid = pipe_cus();
-  hipLaunchKernelGGL((k_gemm_pipe<F, GATEUP>), dim3((unsigned)grid), dim3(PTHREADS), 0, st, g);
+  const unsigned grid = (unsigned)pipe_cus();
+  if (family == 0) hipLaunchKernelGGL((k_gemm_pipe<F, GATEUP>), dim3(grid), dim3(256), 0, st, g);
+  else hipLaunchKernelGGL((k_gemm_pipe8<F, GATEUP>), dim3(grid), dim3(512), 0, st, g);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gemm_pipe(int fmt, bool gateup, const GemmArgs& g, hipStream_t st) {
+hipError_t launch_gemm_pipe(int fmt, bool gateup, int family, const GemmArgs& g, hipStream_t st) {
   switch (fmt) {
-    case F_FP8_CH: return gateup ? launch_pipe_t<F_FP8_CH, true>(g, st) : launch_pipe_t<F_FP8_CH, false>(g, st);
-    case F_FP8_BLK: return gateup ? launch_pipe_t<F_FP8_BLK, true>(g, st) : launch_pipe_t<F_FP8_BLK, false>(g, st);
-    case F_MX: return gateup ? launch_pipe_t<F_MX, true>(g, st) : launch_pipe_t<F_MX, false>(g, st);
+    case F_FP8_CH:
+      return gateup ? launch_pipe_t<F_FP8_CH, true>(family, g, st) : launch_pipe_t<F_FP8_CH, false>(family, g, st);
+    case F_FP8_BLK:
+      return gateup ? launch_pipe_t<F_FP8_BLK, true>(family, g, st) : launch_pipe_t<F_FP8_BLK, false>(family, g, st);
+    case F_MX:
+      return gateup ? launch_pipe_t<F_MX, true>(family, g, st) : launch_pipe_t<F_MX, false>(family, g, st);
   }
   return hipErrorInvalidValue;
 }

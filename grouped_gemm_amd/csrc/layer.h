@@ -138,7 +138,11 @@ hipError_t launch_indptr_table(const int32_t* user_indptr, int cap, const Dispat
 // Streaming (decode) grouped GEMM; fmt = Fmt, gateup = fused SwiGLU op.
 hipError_t launch_gemm_stream(int fmt, bool gateup, const GemmArgs& g, hipStream_t st);
 hipError_t launch_gemm_tiled(int fmt, bool gateup, int cfg, const GemmArgs& g, hipStream_t st);
-// Pipelined grouped GEMM (FP8 and MX formats): one launch covers the tiled
-// configurations 1..3 (row blocks of 32/64/128); g.cfg_self = -1 runs
-// whichever of them the device chose, a value >= 1 only that one.
-hipError_t launch_gemm_pipe(int fmt, bool gateup, const GemmArgs& g, hipStream_t st);
+// Pipelined grouped GEMM (FP8 and MX formats).  Family 0 covers the tiled
+// configurations 1 and 2 (row blocks of 32/64, four waves), family 1
+// configuration 3 (128-row blocks, eight waves); g.cfg_self = -1 runs
+// whichever of the family's configurations the device chose, a value >= 1
+// only that one.
+hipError_t launch_gemm_pipe(int fmt, bool gateup, int family, const GemmArgs& g, hipStream_t st);
+// Rows from which the 128-row configuration may be chosen.
+#define CFG3_MIN_ROWS 4096

@@ -220,14 +220,22 @@ GemmArgs gemm_args(const moe_ws* ws) {
 // [ceil(rows_tot/32), ceil(rows_tot/32) + groups].  A forced configuration
 // is known outright.
 struct Candidates {
-  bool stream, tiled;
+  bool stream, small, big;   // streaming kernel; tiled configurations 1-2; configuration 3
 };
 Candidates candidates(const moe_ws* ws, long rows_tot) {
-  if (ws->force_cfg >= 0) return {ws->force_cfg == 0, ws->force_cfg > 0};
+  if (ws->force_cfg >= 0)
+    return {ws->force_cfg == 0, ws->force_cfg == 1 || ws->force_cfg == 2, ws->force_cfg == 3};
   const long cus = device_cus(), cb = ws->d.inter / 128;
-  const long groups = rows_tot < ws->L.G ? rows_tot : ws->L.G;
+  const long G = ws->L.G;
+  const long groups = rows_tot < G ? rows_tot : G;
   const long lo = (rows_tot + 31) / 32, hi = lo + groups;
-  return {lo * cb < cus, hi * cb >= cus};
+  const bool tiled = hi * cb >= cus;
+  // configuration 3 needs a group above 64 rows, at least 64 rows per
+  // active group and CFG3_MIN_ROWS rows; it is certain when every group
+  // count bound forces it (mean over all groups above 64, enough items)
+  const bool big = tiled && num_cfgs(ws->fmt) > 3 && rows_tot >= CFG3_MIN_ROWS && rows_tot > 64;
+  const bool big_certain = big && lo * cb >= cus && rows_tot > 64 * G;
+  return {lo * cb < cus, tiled && !big_certain, big};
 }
 
 // Run a projection with the kernel families the configuration can land on;
@@ -243,14 +251,19 @@ hipError_t run_gemm(const moe_ws* ws, bool gateup, GemmArgs g, void* tiled_out, 
     hipError_t e = launch_gemm_stream(ws->fmt, gateup, g, st);
     if (e != hipSuccess) return e;
   }
-  if (!cand.tiled) return hipSuccess;
+  if (!cand.small && !cand.big) return hipSuccess;
   if (tiled_out) {
     g.out = tiled_out;
     g.out_scale = tiled_scale;
   }
   if (ws->fmt != F_BF16) {
     g.cfg_self = ws->force_cfg > 0 ? ws->force_cfg : -1;   // any tiled configuration
-    return launch_gemm_pipe(ws->fmt, gateup, g, st);
+    if (cand.small) {
+      hipError_t e = launch_gemm_pipe(ws->fmt, gateup, 0, g, st);
+      if (e != hipSuccess) return e;
+    }
+    if (cand.big) return launch_gemm_pipe(ws->fmt, gateup, 1, g, st);
+    return hipSuccess;
   }
   for (int c = 1; c < num_cfgs(ws->fmt); ++c) {
     g.cfg_self = c;

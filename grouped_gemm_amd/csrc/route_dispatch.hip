@@ -251,7 +251,7 @@ DEVI int choose_config(const int32_t* cnt, int G, int I, int num_cfgs, int cus, 
   if (items32 < cus) return 0;
   if (mx <= 32) return 1;
   if (mx <= 64 || num_cfgs < 4) return num_cfgs < 3 ? 1 : 2;
-  return (active > 0 && rows >= 64 * active) ? 3 : 2;
+  return (active > 0 && rows >= 64 * active && rows >= CFG3_MIN_ROWS) ? 3 : 2;
 }
 
 // Shared tail of both dispatch paths.  cnt (LDS, G entries) holds the
