@@ -19,6 +19,8 @@
 // Slots up to which one 1024-thread block does the whole dispatch; it also
 // routes (scores staged in LDS) when everything fits in DISPATCH_LDS_MAX.
 #define SMALL_DISPATCH_SLOTS 8192
+// Slots up to which one wave does the whole dispatch (at most 64 groups)
+#define TINY_DISPATCH_SLOTS 1024
 #define DISPATCH_LDS_MAX (64 * 1024)
 // Expert counts up to which one thread routes a token (above: one wave)
 #define SMALL_E_THREAD_ROUTE 32

@@ -399,6 +399,112 @@ __global__ void __launch_bounds__(1024) k_dispatch_small(DispatchArgs d) {
     for (int t = tid; t < d.T; t += blockDim.x) d.gather[S + t] = t * d.k;
 }
 
+// ---------------------------------------------------------------- tiny path
+// One wave does everything for decode-sized batches (S <= 1024 slots, at
+// most 64 groups): thread-per-token routing, stable ranks over 64-slot
+// chunks (one ballot per distinct id present in the chunk; group g's running
+// count lives in lane g), the group scan, the active list, the configuration
+// and its block table -- with no workgroup barrier.
+__global__ void __launch_bounds__(64) k_dispatch_tiny(DispatchArgs d) {
+  __shared__ int32_t ids_l[TINY_DISPATCH_SLOTS];
+  __shared__ int32_t cnt_l[64];
+  const int lane = threadIdx.x;
+  const int G = d.E + d.shared;
+  const int S = d.T * d.k;
+  if (d.scores) {
+    for (int t = lane; t < d.T; t += 64)
+      route_token_thread(d.scores + (size_t)t * d.E, d.E, d.k, d.score_fn, d.ids + (size_t)t * d.k,
+                         d.w + (size_t)t * d.k, ids_l + t * d.k);
+  } else {
+    for (int p = lane; p < S; p += 64) ids_l[p] = d.ids_in[p];
+  }
+  __syncthreads();
+  // ranks, chunk by chunk in slot order
+  constexpr int MAXC = TINY_DISPATCH_SLOTS / 64;
+  int rk[MAXC];
+  int run = 0;                               // lane g: rows of group g so far
+  const int nch = (S + 63) / 64;
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    rk[c] = 0;
+    if (c >= nch) continue;
+    const int p = c * 64 + lane;
+    const bool valid = p < S;
+    const int e = valid ? ids_l[p] : -1;
+    uint64_t todo = __ballot(valid);
+    while (todo) {
+      const int leader = __ffsll((unsigned long long)todo) - 1;
+      const int le = __shfl(e, leader, 64);
+      const uint64_t m = __ballot(e == le);
+      const int base = __shfl(run, le, 64);
+      if (e == le) rk[c] = base + __popcll(m & ((1ull << lane) - 1ull));
+      if (lane == le) run += __popcll(m);
+      todo &= ~m;
+    }
+  }
+  const int cnt = lane < d.E ? run : (lane < G ? d.T : 0);   // group E is the shared expert
+  // exclusive scan of the counts
+  int inc = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += v;
+  }
+  const int excl = inc - cnt;
+  const int total = __shfl(inc, 63, 64);
+  if (lane < G) {
+    d.counts[lane] = cnt;
+    d.indptr[lane] = excl;
+    cnt_l[lane] = cnt;
+  }
+  if (lane == 0) d.indptr[G] = total;
+  // active list
+  const uint64_t act = __ballot(lane < G && cnt > 0);
+  if (lane < G && cnt > 0) d.active[__popcll(act & ((1ull << lane) - 1ull))] = lane;
+  __syncthreads();
+  int mx = 0;
+  int cfg = choose_config(cnt_l, G, d.I, d.num_cfgs, d.cus, lane, &mx);
+  if (d.force_cfg >= 0) cfg = d.force_cfg;
+  // block table for the chosen row-block height
+  const int bm = cfg_rows(cfg);
+  const int nt = lane < G ? (cnt + bm - 1) / bm : 0;
+  int tinc = nt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(tinc, o, 64);
+    if (lane >= o) tinc += v;
+  }
+  for (int r = 0, b = tinc - nt; r < nt; ++r) {
+    d.tiles[2 * (b + r)] = lane;
+    d.tiles[2 * (b + r) + 1] = r * bm;
+  }
+  const int ntiles = __shfl(tinc, 63, 64);   // every lane takes part in the shuffle
+  if (lane == 0) {
+    d.meta[META_NACTIVE] = __popcll(act);
+    d.meta[META_NTILES] = ntiles;
+    d.meta[META_CFG] = cfg;
+    d.meta[META_MAXCNT] = mx;
+    d.meta[META_ROWS] = total;
+    d.meta[META_BM] = bm;
+    d.meta[META_ERROR] = 0;
+  }
+  // gather / inverse slots
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    if (c >= nch) continue;
+    const int p = c * 64 + lane;
+    const bool valid = p < S;
+    const int e = valid ? ids_l[p] : 0;
+    const int slot = __shfl(excl, e, 64) + rk[c];
+    if (valid) {
+      d.gather[slot] = p;
+      d.inv[p] = slot;
+    }
+  }
+  if (d.shared)
+    for (int t = lane; t < d.T; t += 64) d.gather[S + t] = t * d.k;
+}
+
 // ---------------------------------------------------------------- large path
 // 1) per-chunk histograms (1024 slots per chunk)
 __global__ void __launch_bounds__(1024) k_dispatch_hist(DispatchArgs d) {
@@ -486,6 +592,10 @@ hipError_t launch_route(const float* scores, int T, int E, int k, int score_fn, 
 hipError_t launch_dispatch(const DispatchArgs& d, hipStream_t st) {
   const int G = d.E + d.shared;
   const int S = d.T * d.k;
+  if (S <= TINY_DISPATCH_SLOTS && G <= 64 && (!d.scores || d.E <= SMALL_E_THREAD_ROUTE)) {
+    hipLaunchKernelGGL(k_dispatch_tiny, dim3(1), dim3(64), 0, st, d);
+    return hipGetLastError();
+  }
   if (S <= SMALL_DISPATCH_SLOTS) {
     // routing is fused into the block when the scores fit in its LDS
     if (d.scores && dispatch_small_lds(d.T, d.k, G, d.E, true) > DISPATCH_LDS_MAX) {

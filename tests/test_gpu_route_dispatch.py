@@ -42,7 +42,8 @@ def test_route_topk_matches_oracle(name, T):
 
 
 @pytest.mark.parametrize("name,T", [("mixtral", 128), ("dsv3", 1000), ("qwen", 8192),
-                                    ("imbalance", 2048), ("tiny", 1)])
+                                    ("imbalance", 2048), ("tiny", 1), ("tiny", 333),
+                                    ("tiny", 512), ("tiny", 513)])
 def test_dispatch_matches_oracle(name, T):
     sh = ms.CONFIGS[name]
     say("dispatch", name, T)
@@ -81,6 +82,29 @@ def test_dispatch_all_tokens_one_expert_and_empty_experts():
         np.testing.assert_array_equal(d_i.cpu().numpy(), indptr)
         np.testing.assert_array_equal(d_g.cpu().numpy(), gather)
         np.testing.assert_array_equal(d_v.cpu().numpy(), inv)
+
+
+@pytest.mark.parametrize("E,k,T", [(64, 4, 256), (63, 5, 201), (2, 1, 1000), (64, 16, 64)])
+def test_dispatch_random_ids_one_wave_limits(E, k, T):
+    """Distinct random ids at the limits of the one-wave path (64 groups,
+    1024 slots) and just past them."""
+    say("dispatch ids", E, k, T)
+    rng = np.random.default_rng(E * 1000 + T)
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    counts, indptr, gather, inv = oracle.dispatch(ids, E)
+    sh = ms.small_shape("mixtral", hidden=256, inter=256, experts=E, top_k=k)
+    ws = workspace(sh, T)
+    S = T * k
+    d_c = torch.empty(E, dtype=torch.int32, device="cuda")
+    d_i = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    d_g = torch.empty(S, dtype=torch.int32, device="cuda")
+    d_v = torch.empty(S, dtype=torch.int32, device="cuda")
+    g.dispatch(ws, dev(ids), E, d_c, d_i, d_g, d_v)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(d_c.cpu().numpy(), counts)
+    np.testing.assert_array_equal(d_i.cpu().numpy(), indptr)
+    np.testing.assert_array_equal(d_g.cpu().numpy(), gather)
+    np.testing.assert_array_equal(d_v.cpu().numpy(), inv)
 
 
 @pytest.mark.parametrize("name", ["mixtral", "qwen", "imbalance", "dsv3"])
