@@ -11,6 +11,7 @@
 // deterministic combine): y[t] = sum over j ascending of w[t,j] times the
 // slot output of (t, j), plus the shared expert's row, rounded to bf16 once.
 #include "layer.h"
+#include "quant_row.h"
 
 template <int AF>
 struct QGroup {
@@ -143,6 +144,21 @@ hipError_t launch_quant(const QuantArgs& q, hipStream_t st) {
     default:
       return hipErrorInvalidValue;
   }
+}
+
+// bf16 rows, one wave per row: the same device code the routing launches
+// run on their spare waves
+__global__ void __launch_bounds__(256) k_quant_rows(QuantArgs q) {
+  quant_rows_waves(q, (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6), (int)gridDim.x * 4,
+                   threadIdx.x & 63);
+}
+
+hipError_t launch_quant_rows(const QuantArgs& q, hipStream_t st) {
+  if (q.R == 0) return hipSuccess;
+  if (!q.in_bf16) return hipErrorInvalidValue;
+  const int blocks = (q.R + 3) / 4;
+  hipLaunchKernelGGL(k_quant_rows, dim3(blocks < 2048 ? blocks : 2048), dim3(256), 0, st, q);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ combine

@@ -21,6 +21,8 @@
 #define SMALL_DISPATCH_SLOTS 8192
 // Slots up to which one wave does the whole dispatch (at most 64 groups)
 #define TINY_DISPATCH_SLOTS 1024
+// Router scores (floats) the one-wave path stages in LDS before routing
+#define TINY_SCORE_LDS 4096
 #define DISPATCH_LDS_MAX (64 * 1024)
 // Expert counts up to which one thread routes a token (above: one wave)
 #define SMALL_E_THREAD_ROUTE 32
@@ -41,6 +43,18 @@ __host__ __device__ inline int cfg_rows(int cfg) {
   }
 }
 
+struct QuantArgs {
+  const void* in;         // rows [R, n], bf16 (in_bf16) or fp32
+  int in_bf16;
+  int R, n;
+  const int32_t* nrows;   // optional device row count (NULL: R)
+  uint8_t* q;             // [R, n] e4m3
+  void* scale;            // fp32 [R] / fp32 [R, n/128] / uint8 [R, n/32]
+  int a_format;
+  const int32_t* meta;    // optional: run only if meta[META_CFG] == only_cfg
+  int only_cfg;
+};
+
 struct DispatchArgs {
   const float* scores;    // [T,E] or NULL when ids are given
   const int32_t* ids_in;  // [T,k] when scores == NULL
@@ -59,6 +73,8 @@ struct DispatchArgs {
   int H, I, wbits, xbits; // for the cost model
   int num_cfgs;           // configurations the library has kernels for
   int cus;                // compute units of the device (configuration rule)
+  QuantArgs fq;           // activation rows the routing launch quantises on
+                          // its spare waves (fq.R = 0: none)
 };
 
 // Grouped GEMM over expert-major row groups.
@@ -108,17 +124,6 @@ DEVI void store_down(const GemmArgs& p, int slot, int n0, f32x4 v) {
   }
 }
 
-struct QuantArgs {
-  const void* in;         // rows [R, n], bf16 (in_bf16) or fp32
-  int in_bf16;
-  int R, n;
-  const int32_t* nrows;   // optional device row count (NULL: R)
-  uint8_t* q;             // [R, n] e4m3
-  void* scale;            // fp32 [R] / fp32 [R, n/128] / uint8 [R, n/32]
-  int a_format;
-  const int32_t* meta;    // optional: run only if meta[META_CFG] == only_cfg
-  int only_cfg;
-};
 
 struct CombineArgs {
   const void* out_slot;   // [S + shared*T, H]: fp32 unweighted, or bf16 pre-weighted
@@ -130,10 +135,12 @@ struct CombineArgs {
 };
 
 hipError_t launch_route(const float* scores, int T, int E, int k, int score_fn, int32_t* ids,
-                        float* w, hipStream_t st);
+                        float* w, const QuantArgs& fq, hipStream_t st);
 hipError_t launch_dispatch(const DispatchArgs& d, hipStream_t st);
 size_t dispatch_small_lds(int T, int k, int G, int E, bool route);
 hipError_t launch_quant(const QuantArgs& q, hipStream_t st);
+// bf16 activation rows, one wave per row (the routing launches' quantiser)
+hipError_t launch_quant_rows(const QuantArgs& q, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& c, hipStream_t st);
 hipError_t launch_indptr_table(const int32_t* user_indptr, int cap, const DispatchArgs& d,
                                hipStream_t st);

@@ -285,16 +285,17 @@ int enqueue_layer(moe_ws* ws, const moe_weights* w, const uint16_t* x, const flo
   };
   DispatchArgs da = dispatch_args(ws, T);
   da.scores = scores;
+  const bool quant = ws->fmt != F_BF16;
+  // the input quantisation rides on the routing launch's spare waves (its
+  // stage events stay empty)
+  if (quant)
+    da.fq = QuantArgs{x, 1, T, d.hidden, nullptr, ws->at<uint8_t>(L.xq), ws->at<void>(L.xs),
+                      d.a_format};
   HIP_TRY(mark(0, 0), "event record");
   HIP_TRY(launch_dispatch(da, st), "dispatch launch");
   HIP_TRY(mark(0, 1), "event record");
-  const bool quant = ws->fmt != F_BF16;
-  if (quant) {
-    QuantArgs q{x, 1, T, d.hidden, nullptr, ws->at<uint8_t>(L.xq), ws->at<void>(L.xs), d.a_format};
-    HIP_TRY(mark(1, 0), "event record");
-    HIP_TRY(launch_quant(q, st), "input quantisation launch");
-    HIP_TRY(mark(1, 1), "event record");
-  }
+  HIP_TRY(mark(1, 0), "event record");
+  HIP_TRY(mark(1, 1), "event record");
   int max_groups = d.num_experts < S ? d.num_experts : S;
   max_groups += d.shared_experts;
   if (max_groups > G) max_groups = G;
@@ -437,7 +438,8 @@ int moe_route_topk(const float* scores, int T, int E, int k, int score_fn, int32
   if (score_fn < 0 || score_fn > 2) return fail(MOE_EINVAL, "unknown score_fn");
   if (T == 0) return MOE_OK;
   if (!scores || !ids || !w) return fail(MOE_EINVAL, "null pointer");
-  HIP_TRY(launch_route(scores, T, E, k, score_fn, ids, w, (hipStream_t)stream), "route launch");
+  HIP_TRY(launch_route(scores, T, E, k, score_fn, ids, w, QuantArgs{}, (hipStream_t)stream),
+          "route launch");
   return MOE_OK;
 }
 
@@ -524,7 +526,7 @@ int moe_quantize_act(moe_ws* ws, const uint16_t* x, int T, uint8_t* q, void* sca
   if (T == 0) return MOE_OK;
   if (!x || !q || !scale) return fail(MOE_EINVAL, "null pointer");
   QuantArgs qa{x, 1, T, ws->d.hidden, nullptr, q, scale, ws->d.a_format};
-  HIP_TRY(launch_quant(qa, (hipStream_t)stream), "quantisation launch");
+  HIP_TRY(launch_quant_rows(qa, (hipStream_t)stream), "quantisation launch");
   return MOE_OK;
 }
 

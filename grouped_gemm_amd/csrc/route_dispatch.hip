@@ -15,6 +15,7 @@
 // position comes from a stable rank (count of earlier equal ids), computed
 // with wave ballots and per-wave prefix sums, never from atomic arrival order.
 #include "layer.h"
+#include "quant_row.h"
 
 // Order-preserving map of an fp32 score to uint32 (+0 and -0 compare equal).
 DEVI uint32_t score_key(float s) {
@@ -113,9 +114,17 @@ DEVI void route_token_thread(const float* row, int E, int k, int score_fn, int32
   for (int j = 0; j < k; ++j) w_out[j] = w_out[j] / sum;
 }
 
+// Routing grids carry the input quantisation on blocks past the routed
+// tokens (fq.R = 0: none).
 __global__ void __launch_bounds__(256) k_route_thread(const float* __restrict__ scores, int T, int E,
                                                       int k, int score_fn, int32_t* __restrict__ ids,
-                                                      float* __restrict__ w) {
+                                                      float* __restrict__ w, QuantArgs fq) {
+  const int rb = (T + 255) / 256;
+  if ((int)blockIdx.x >= rb) {
+    quant_rows_waves(fq, ((int)blockIdx.x - rb) * 4 + (threadIdx.x >> 6), ((int)gridDim.x - rb) * 4,
+                     threadIdx.x & 63);
+    return;
+  }
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= T) return;
   route_token_thread(scores + (size_t)t * E, E, k, score_fn, ids + (size_t)t * k, w + (size_t)t * k,
@@ -124,9 +133,14 @@ __global__ void __launch_bounds__(256) k_route_thread(const float* __restrict__ 
 
 __global__ void __launch_bounds__(256) k_route(const float* __restrict__ scores, int T, int E, int k,
                                                int score_fn, int32_t* __restrict__ ids,
-                                               float* __restrict__ w) {
-  int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  int t = blockIdx.x * 4 + wave;
+                                               float* __restrict__ w, QuantArgs fq) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rb = (T + 3) / 4;
+  if ((int)blockIdx.x >= rb) {
+    quant_rows_waves(fq, ((int)blockIdx.x - rb) * 4 + wave, ((int)gridDim.x - rb) * 4, lane);
+    return;
+  }
+  const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
   route_one_token(scores + (size_t)t * E, E, k, score_fn, lane, ids + (size_t)t * k,
                   w + (size_t)t * k, nullptr);
@@ -333,6 +347,7 @@ DEVI void finalize_dispatch(const DispatchArgs& d, int32_t* cnt, int32_t* scan_b
 // ---------------------------------------------------------------- small path
 // One 1024-thread block: (optionally) routing, then counts, scan, stable
 // scatter, active list, configuration and block table.  For S = T*k <= 8192.
+// Blocks past the first quantise the activation rows.
 __global__ void __launch_bounds__(1024) k_dispatch_small(DispatchArgs d) {
   extern __shared__ int32_t smem[];
   const int G = d.E + d.shared;
@@ -346,6 +361,10 @@ __global__ void __launch_bounds__(1024) k_dispatch_small(DispatchArgs d) {
   int32_t* tiles_buf = flag_buf + G;           // [G]
   float* sc_l = (float*)(tiles_buf + G);       // [T*E] router scores (routing fused)
   int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (blockIdx.x != 0) {   // blocks past the first quantise the activation rows
+    quant_rows_waves(d.fq, ((int)blockIdx.x - 1) * 16 + wave, ((int)gridDim.x - 1) * 16, lane);
+    return;
+  }
 
   if (d.scores) {
     // all scores into LDS with coalesced loads, then one wave per token
@@ -400,25 +419,45 @@ __global__ void __launch_bounds__(1024) k_dispatch_small(DispatchArgs d) {
 }
 
 // ---------------------------------------------------------------- tiny path
+// LDS ordering inside one wave: its LDS operations complete in order, so
+// waiting for them (and keeping the compiler from moving memory operations
+// across) publishes every lane's writes to the other lanes.
+DEVI void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // One wave does everything for decode-sized batches (S <= 1024 slots, at
-// most 64 groups): thread-per-token routing, stable ranks over 64-slot
-// chunks (one ballot per distinct id present in the chunk; group g's running
-// count lives in lane g), the group scan, the active list, the configuration
-// and its block table -- with no workgroup barrier.
-__global__ void __launch_bounds__(64) k_dispatch_tiny(DispatchArgs d) {
+// most 64 groups): thread-per-token routing (scores staged in LDS by
+// coalesced loads when they fit), stable ranks over 64-slot chunks (one
+// ballot per distinct id present in the chunk; group g's running count
+// lives in lane g), the group scan, the active list, the configuration and
+// its block table -- with no workgroup barrier.  The other waves of the
+// grid quantise the activation rows meanwhile.
+__global__ void __launch_bounds__(256) k_dispatch_tiny(DispatchArgs d) {
   __shared__ int32_t ids_l[TINY_DISPATCH_SLOTS];
   __shared__ int32_t cnt_l[64];
-  const int lane = threadIdx.x;
+  __shared__ float sc_l[TINY_SCORE_LDS];
+  const int lane = threadIdx.x & 63;
+  if (blockIdx.x != 0 || threadIdx.x >= 64) {
+    quant_rows_waves(d.fq, (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6) - 1, (int)gridDim.x * 4 - 1,
+                     lane);
+    return;
+  }
   const int G = d.E + d.shared;
   const int S = d.T * d.k;
   if (d.scores) {
+    const int n = d.T * d.E;
+    const float* src = d.scores;
+    if (n <= TINY_SCORE_LDS) {
+      for (int i = lane; i < n; i += 64) sc_l[i] = d.scores[i];
+      wave_lds_sync();
+      src = sc_l;
+    }
     for (int t = lane; t < d.T; t += 64)
-      route_token_thread(d.scores + (size_t)t * d.E, d.E, d.k, d.score_fn, d.ids + (size_t)t * d.k,
+      route_token_thread(src + (size_t)t * d.E, d.E, d.k, d.score_fn, d.ids + (size_t)t * d.k,
                          d.w + (size_t)t * d.k, ids_l + t * d.k);
   } else {
     for (int p = lane; p < S; p += 64) ids_l[p] = d.ids_in[p];
   }
-  __syncthreads();
+  wave_lds_sync();
   // ranks, chunk by chunk in slot order
   constexpr int MAXC = TINY_DISPATCH_SLOTS / 64;
   int rk[MAXC];
@@ -461,7 +500,7 @@ __global__ void __launch_bounds__(64) k_dispatch_tiny(DispatchArgs d) {
   // active list
   const uint64_t act = __ballot(lane < G && cnt > 0);
   if (lane < G && cnt > 0) d.active[__popcll(act & ((1ull << lane) - 1ull))] = lane;
-  __syncthreads();
+  wave_lds_sync();
   int mx = 0;
   int cfg = choose_config(cnt_l, G, d.I, d.num_cfgs, d.cus, lane, &mx);
   if (d.force_cfg >= 0) cfg = d.force_cfg;
@@ -578,14 +617,28 @@ size_t dispatch_small_lds(int T, int k, int G, int E, bool route) {
   return sizeof(int32_t) * ((size_t)T * k + 2 * G + 16 * G + 3 * G + (route ? (size_t)T * E : 0));
 }
 
+// Blocks (of `wpb` waves) to add to a launch so its spare waves quantise
+// fq.R rows: about one wave per row, at most a few blocks per CU.
+static int quant_blocks(const QuantArgs& fq, int wpb, int spare_waves) {
+  if (fq.R <= 0) return 0;
+  const int need = fq.R - spare_waves;
+  if (need <= 0) return spare_waves > 0 ? 0 : 1;
+  const int b = (need + wpb - 1) / wpb;
+  return b < 2048 ? b : 2048;
+}
+
 hipError_t launch_route(const float* scores, int T, int E, int k, int score_fn, int32_t* ids,
-                        float* w, hipStream_t st) {
+                        float* w, const QuantArgs& fq, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  if (E <= SMALL_E_THREAD_ROUTE)
-    hipLaunchKernelGGL(k_route_thread, dim3((T + 255) / 256), dim3(256), 0, st, scores, T, E, k,
-                       score_fn, ids, w);
-  else
-    hipLaunchKernelGGL(k_route, dim3((T + 3) / 4), dim3(256), 0, st, scores, T, E, k, score_fn, ids, w);
+  if (E <= SMALL_E_THREAD_ROUTE) {
+    const int rb = (T + 255) / 256;
+    hipLaunchKernelGGL(k_route_thread, dim3(rb + quant_blocks(fq, 4, 0)), dim3(256), 0, st, scores,
+                       T, E, k, score_fn, ids, w, fq);
+  } else {
+    const int rb = (T + 3) / 4;
+    hipLaunchKernelGGL(k_route, dim3(rb + quant_blocks(fq, 4, 0)), dim3(256), 0, st, scores, T, E, k,
+                       score_fn, ids, w, fq);
+  }
   return hipGetLastError();
 }
 
@@ -593,32 +646,40 @@ hipError_t launch_dispatch(const DispatchArgs& d, hipStream_t st) {
   const int G = d.E + d.shared;
   const int S = d.T * d.k;
   if (S <= TINY_DISPATCH_SLOTS && G <= 64 && (!d.scores || d.E <= SMALL_E_THREAD_ROUTE)) {
-    hipLaunchKernelGGL(k_dispatch_tiny, dim3(1), dim3(64), 0, st, d);
+    const int grid = 1 + quant_blocks(d.fq, 4, 3);
+    hipLaunchKernelGGL(k_dispatch_tiny, dim3(grid), dim3(256), 0, st, d);
     return hipGetLastError();
   }
   if (S <= SMALL_DISPATCH_SLOTS) {
     // routing is fused into the block when the scores fit in its LDS
     if (d.scores && dispatch_small_lds(d.T, d.k, G, d.E, true) > DISPATCH_LDS_MAX) {
-      hipError_t e = launch_route(d.scores, d.T, d.E, d.k, d.score_fn, d.ids, d.w, st);
+      hipError_t e = launch_route(d.scores, d.T, d.E, d.k, d.score_fn, d.ids, d.w, d.fq, st);
       if (e != hipSuccess) return e;
       DispatchArgs d2 = d;
       d2.scores = nullptr;
       d2.ids_in = d.ids;
+      d2.fq.R = 0;
       hipLaunchKernelGGL(k_dispatch_small, dim3(1), dim3(1024),
                          dispatch_small_lds(d.T, d.k, G, d.E, false), st, d2);
       return hipGetLastError();
     }
-    hipLaunchKernelGGL(k_dispatch_small, dim3(1), dim3(1024),
+    const int grid = 1 + quant_blocks(d.fq, 16, 0);
+    hipLaunchKernelGGL(k_dispatch_small, dim3(grid), dim3(1024),
                        dispatch_small_lds(d.T, d.k, G, d.E, d.scores != nullptr), st, d);
     return hipGetLastError();
   }
-  // large path: routing (if requested) runs as its own grid first
+  // large path: routing (if requested, with the input quantisation) runs as
+  // its own grid first
   DispatchArgs d2 = d;
+  d2.fq.R = 0;
   if (d.scores) {
-    hipError_t e = launch_route(d.scores, d.T, d.E, d.k, d.score_fn, d.ids, d.w, st);
+    hipError_t e = launch_route(d.scores, d.T, d.E, d.k, d.score_fn, d.ids, d.w, d.fq, st);
     if (e != hipSuccess) return e;
     d2.scores = nullptr;
     d2.ids_in = d.ids;
+  } else if (d.fq.R > 0) {
+    hipError_t e = launch_quant(d.fq, st);
+    if (e != hipSuccess) return e;
   }
   int nchunks = (S + 1023) / 1024;
   hipLaunchKernelGGL(k_dispatch_hist, dim3(nchunks), dim3(1024), sizeof(int32_t) * d.E, st, d2);

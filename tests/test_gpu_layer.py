@@ -25,6 +25,11 @@ SMALL = [
                                         shared_inter=256), 29),
     ("mxfp4", ms.small_shape("imbalance", hidden=384, inter=512, experts=10, top_k=3), 41),
     ("tiny_cfg", ms.CONFIGS["tiny"], 32),
+    # more slots than the one-wave dispatch takes: one-block dispatch with
+    # routing fused (700), and the multi-block path with thread routing (4200);
+    # both quantise x on the routing launch's spare waves
+    ("fp8_channel_700", ms.small_shape("mixtral", hidden=256, inter=256, experts=8, top_k=2), 700),
+    ("fp8_channel_4200", ms.small_shape("mixtral", hidden=256, inter=256, experts=8, top_k=2), 4200),
 ]
 
 
