@@ -79,43 +79,75 @@ DEVI void route_one_token(const float* row, int E, int k, int score_fn, int lane
   }
 }
 
-// One thread routes one token (small expert counts): k passes over the E
-// scores, each taking the largest remaining key (score, then lowest index),
-// exactly the order route_one_token produces.
+// One thread routes one token (small expert counts, E <= 32): k passes over
+// the E scores, each taking the largest remaining key (score, then lowest
+// index) -- exactly the order route_one_token produces.  Compact rolled
+// loops, for scores staged in LDS.
 DEVI void route_token_thread(const float* row, int E, int k, int score_fn, int32_t* ids_out,
                              float* w_out, int32_t* ids_lds) {
-  uint64_t taken = 0;
-  int first = 0;
+  uint32_t taken = 0;
+  float top = 0.f, sum = 0.f;
   for (int j = 0; j < k; ++j) {
     int best = -1;
     uint32_t bk = 0;
     for (int e = 0; e < E; ++e) {
-      if ((taken >> e) & 1ull) continue;
+      if ((taken >> e) & 1u) continue;
       const uint32_t key = score_key(row[e]);
       if (best < 0 || key > bk) {
         best = e;
         bk = key;
       }
     }
-    taken |= 1ull << best;
+    taken |= 1u << best;
     ids_out[j] = best;
     if (ids_lds) ids_lds[j] = best;
-    if (j == 0) first = best;
-  }
-  const float top = row[first];
-  float sum = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const float l = row[ids_out[j]];
-    float v = score_fn == MOE_SCORE_SOFTMAX ? expf(l - top)
-              : score_fn == MOE_SCORE_SIGMOID ? 1.0f / (1.0f + expf(-l)) : l;
-    w_out[j] = v;
-    sum += v;
+    const float l = row[best];
+    if (j == 0) top = l;
+    const float x = score_fn == MOE_SCORE_SOFTMAX ? expf(l - top)
+                    : score_fn == MOE_SCORE_SIGMOID ? 1.0f / (1.0f + expf(-l)) : l;
+    w_out[j] = x;
+    sum += x;
   }
   for (int j = 0; j < k; ++j) w_out[j] = w_out[j] / sum;
 }
 
-// Routing grids carry the input quantisation on blocks past the routed
-// tokens (fq.R = 0: none).
+// The same selection with the token's scores held in registers (all loads
+// issued at once), for scores read from global memory.
+DEVI void route_token_regs(const float* row, int E, int k, int score_fn, int32_t* ids_out,
+                           float* w_out, int32_t* ids_lds) {
+  float v[SMALL_E_THREAD_ROUTE];
+#pragma unroll
+  for (int e = 0; e < SMALL_E_THREAD_ROUTE; ++e) v[e] = e < E ? row[e] : 0.f;
+  uint32_t key[SMALL_E_THREAD_ROUTE];
+#pragma unroll
+  for (int e = 0; e < SMALL_E_THREAD_ROUTE; ++e) key[e] = score_key(v[e]);
+  uint32_t taken = 0;
+  float top = 0.f, sum = 0.f;
+  // the pass loop stays rolled (short code); unnormalised weights go to
+  // w_out and are divided by their sum once all k are known
+  for (int j = 0; j < k; ++j) {
+    int best = -1;
+    uint32_t bk = 0;
+    float bv = 0.f;
+#pragma unroll
+    for (int e = 0; e < SMALL_E_THREAD_ROUTE; ++e) {
+      const bool ok = e < E && !((taken >> e) & 1u) && (best < 0 || key[e] > bk);
+      best = ok ? e : best;
+      bk = ok ? key[e] : bk;
+      bv = ok ? v[e] : bv;
+    }
+    taken |= 1u << best;
+    ids_out[j] = best;
+    if (ids_lds) ids_lds[j] = best;
+    if (j == 0) top = bv;
+    const float x = score_fn == MOE_SCORE_SOFTMAX ? expf(bv - top)
+                    : score_fn == MOE_SCORE_SIGMOID ? 1.0f / (1.0f + expf(-bv)) : bv;
+    w_out[j] = x;
+    sum += x;
+  }
+  for (int j = 0; j < k; ++j) w_out[j] = w_out[j] / sum;
+}
+
 __global__ void __launch_bounds__(256) k_route_thread(const float* __restrict__ scores, int T, int E,
                                                       int k, int score_fn, int32_t* __restrict__ ids,
                                                       float* __restrict__ w, QuantArgs fq) {
@@ -127,7 +159,7 @@ __global__ void __launch_bounds__(256) k_route_thread(const float* __restrict__ 
   }
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= T) return;
-  route_token_thread(scores + (size_t)t * E, E, k, score_fn, ids + (size_t)t * k, w + (size_t)t * k,
+  route_token_regs(scores + (size_t)t * E, E, k, score_fn, ids + (size_t)t * k, w + (size_t)t * k,
                      nullptr);
 }
 
@@ -241,6 +273,16 @@ DEVI void wave0_exclusive_scan(int32_t* a, int n, int32_t* total) {
 //     highest MFMA intensity per staged byte); otherwise cfg 2.
 // The rule reproduces the fastest measured configuration on the benchmarked
 // layer shapes; a fitted cost model over these statistics can replace it.
+DEVI int config_rule(int mx, int active, int rows, int tiles32, int I, int num_cfgs, int cus) {
+  if (num_cfgs <= 1) return 0;
+  const long items32 = (long)tiles32 * (I / 128);
+  if (items32 < cus) return 0;
+  if (mx <= 32) return 1;
+  if (mx <= 64 || num_cfgs < 4) return num_cfgs < 3 ? 1 : 2;
+  return (active > 0 && rows >= 64 * active && rows >= CFG3_MIN_ROWS) ? 3 : 2;
+}
+
+// The histogram statistics by one wave over the counts in LDS, then the rule.
 DEVI int choose_config(const int32_t* cnt, int G, int I, int num_cfgs, int cus, int lane,
                       int* max_out) {
   int mx = 0, active = 0, rows = 0, tiles32 = 0;
@@ -260,12 +302,7 @@ DEVI int choose_config(const int32_t* cnt, int G, int I, int num_cfgs, int cus, 
     tiles32 += __shfl_xor(tiles32, o, 64);
   }
   *max_out = mx;
-  if (num_cfgs <= 1) return 0;
-  const long items32 = (long)tiles32 * (I / 128);
-  if (items32 < cus) return 0;
-  if (mx <= 32) return 1;
-  if (mx <= 64 || num_cfgs < 4) return num_cfgs < 3 ? 1 : 2;
-  return (active > 0 && rows >= 64 * active && rows >= CFG3_MIN_ROWS) ? 3 : 2;
+  return config_rule(mx, active, rows, tiles32, I, num_cfgs, cus);
 }
 
 // Shared tail of both dispatch paths.  cnt (LDS, G entries) holds the
@@ -425,15 +462,14 @@ __global__ void __launch_bounds__(1024) k_dispatch_small(DispatchArgs d) {
 DEVI void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // One wave does everything for decode-sized batches (S <= 1024 slots, at
-// most 64 groups): thread-per-token routing (scores staged in LDS by
-// coalesced loads when they fit), stable ranks over 64-slot chunks (one
-// ballot per distinct id present in the chunk; group g's running count
+// most 64 groups): thread-per-token routing on scores staged in LDS,
+// stable ranks over 64-slot chunks from ballots (group g's running count
 // lives in lane g), the group scan, the active list, the configuration and
 // its block table -- with no workgroup barrier.  The other waves of the
 // grid quantise the activation rows meanwhile.
 __global__ void __launch_bounds__(256) k_dispatch_tiny(DispatchArgs d) {
   __shared__ int32_t ids_l[TINY_DISPATCH_SLOTS];
-  __shared__ int32_t cnt_l[64];
+  __shared__ int32_t rk_l[TINY_DISPATCH_SLOTS];
   __shared__ float sc_l[TINY_SCORE_LDS];
   const int lane = threadIdx.x & 63;
   if (blockIdx.x != 0 || threadIdx.x >= 64) {
@@ -447,7 +483,15 @@ __global__ void __launch_bounds__(256) k_dispatch_tiny(DispatchArgs d) {
     const int n = d.T * d.E;
     const float* src = d.scores;
     if (n <= TINY_SCORE_LDS) {
-      for (int i = lane; i < n; i += 64) sc_l[i] = d.scores[i];
+      // four loads in flight per lane and pass
+      for (int i = lane; i < n; i += 256) {
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = i + 64 * u < n ? d.scores[i + 64 * u] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (i + 64 * u < n) sc_l[i + 64 * u] = v[u];
+      }
       wave_lds_sync();
       src = sc_l;
     }
@@ -458,28 +502,29 @@ __global__ void __launch_bounds__(256) k_dispatch_tiny(DispatchArgs d) {
     for (int p = lane; p < S; p += 64) ids_l[p] = d.ids_in[p];
   }
   wave_lds_sync();
-  // ranks, chunk by chunk in slot order
-  constexpr int MAXC = TINY_DISPATCH_SLOTS / 64;
-  int rk[MAXC];
+  // Stable ranks, chunk by chunk in slot order.  Ids are below 64, so the
+  // lanes holding id x are the intersection over the six id bits b of
+  // ballot(bit b set) or its complement: M(x).  A lane's rank in its chunk
+  // is the number of lower lanes in M(id); lane g adds |M(g)| to its
+  // running count of group g.
+  const uint64_t below = (1ull << lane) - 1ull;
   int run = 0;                               // lane g: rows of group g so far
   const int nch = (S + 63) / 64;
-#pragma unroll
-  for (int c = 0; c < MAXC; ++c) {
-    rk[c] = 0;
-    if (c >= nch) continue;
+  for (int c = 0; c < nch; ++c) {
     const int p = c * 64 + lane;
     const bool valid = p < S;
-    const int e = valid ? ids_l[p] : -1;
-    uint64_t todo = __ballot(valid);
-    while (todo) {
-      const int leader = __ffsll((unsigned long long)todo) - 1;
-      const int le = __shfl(e, leader, 64);
-      const uint64_t m = __ballot(e == le);
-      const int base = __shfl(run, le, 64);
-      if (e == le) rk[c] = base + __popcll(m & ((1ull << lane) - 1ull));
-      if (lane == le) run += __popcll(m);
-      todo &= ~m;
+    const int e = valid ? ids_l[p] : 0;
+    const uint64_t vm = __ballot(valid);
+    uint64_t me = vm, mg = vm;                // lanes with my id / with id == lane
+#pragma unroll
+    for (int bt = 0; bt < 6; ++bt) {
+      const uint64_t bb = __ballot(valid && ((e >> bt) & 1));
+      me &= ((e >> bt) & 1) ? bb : ~bb;
+      mg &= ((lane >> bt) & 1) ? bb : ~bb;
     }
+    const int base = __shfl(run, e, 64);
+    if (valid) rk_l[p] = base + __popcll(me & below);
+    run += __popcll(mg);
   }
   const int cnt = lane < d.E ? run : (lane < G ? d.T : 0);   // group E is the shared expert
   // exclusive scan of the counts
@@ -494,15 +539,20 @@ __global__ void __launch_bounds__(256) k_dispatch_tiny(DispatchArgs d) {
   if (lane < G) {
     d.counts[lane] = cnt;
     d.indptr[lane] = excl;
-    cnt_l[lane] = cnt;
   }
   if (lane == 0) d.indptr[G] = total;
   // active list
   const uint64_t act = __ballot(lane < G && cnt > 0);
-  if (lane < G && cnt > 0) d.active[__popcll(act & ((1ull << lane) - 1ull))] = lane;
-  wave_lds_sync();
-  int mx = 0;
-  int cfg = choose_config(cnt_l, G, d.I, d.num_cfgs, d.cus, lane, &mx);
+  if (lane < G && cnt > 0) d.active[__popcll(act & below)] = lane;
+  // configuration from the histogram statistics (lane g holds group g)
+  int mx = cnt, t32 = (cnt + 31) / 32;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const int v = __shfl_xor(mx, o, 64);
+    mx = v > mx ? v : mx;
+    t32 += __shfl_xor(t32, o, 64);
+  }
+  int cfg = config_rule(mx, __popcll(act), total, t32, d.I, d.num_cfgs, d.cus);
   if (d.force_cfg >= 0) cfg = d.force_cfg;
   // block table for the chosen row-block height
   const int bm = cfg_rows(cfg);
@@ -527,14 +577,12 @@ __global__ void __launch_bounds__(256) k_dispatch_tiny(DispatchArgs d) {
     d.meta[META_BM] = bm;
     d.meta[META_ERROR] = 0;
   }
-  // gather / inverse slots
-#pragma unroll
-  for (int c = 0; c < MAXC; ++c) {
-    if (c >= nch) continue;
+  // gather / inverse slots (a lane reads back only its own rank entries)
+  for (int c = 0; c < nch; ++c) {
     const int p = c * 64 + lane;
     const bool valid = p < S;
     const int e = valid ? ids_l[p] : 0;
-    const int slot = __shfl(excl, e, 64) + rk[c];
+    const int slot = __shfl(excl, e, 64) + (valid ? rk_l[p] : 0);
     if (valid) {
       d.gather[slot] = p;
       d.inv[p] = slot;
