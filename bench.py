@@ -3,20 +3,25 @@
 Default workload: the Mixtral-8x7B-shaped layer (H 4096, I 14336, 8 experts,
 top-2, SwiGLU) in FP8 e4m3 W8A8 (per-output-channel weight scales, dynamic
 per-token activation scales) at T = 128 tokens, the largest decode batch
-the layer is quoted at; T = 32 is timed in the same run as a second point.
-A step is one moe_layer_forward call: routing, dispatch, input
-quantisation, fused gate/up + SwiGLU grouped GEMM, requantisation, down
-grouped GEMM and combine, on inputs already resident in HBM (replayed as a
-hipGraph, the decode launch path).
+the layer is quoted at; T = 32 and the Qwen3.5-35B-A3B-shaped layer at
+T = 8192 (128x128 weight blocks, 1x128 activation groups) are timed in the
+same run as further points of the metric.  A step is one moe_layer_forward
+call: routing, dispatch, input quantisation, fused gate/up + SwiGLU grouped
+GEMM, requantisation, down grouped GEMM and combine, on inputs already
+resident in HBM.  The K timed calls are captured in one hipGraph and
+replayed once, as a model step holds its layers in one graph; the same K
+calls issued one launch per call (a graph each at decode sizes) are
+reported beside it ("layer_us_one_launch_per_call").
 
 Printed: one JSON line.  `value` is the algorithmic HBM throughput of the
 layer (GB/s): bytes the method must move (weights and scales of the experts
 that receive tokens, x read once, y written once, the FP8 intermediate
 written and read once) over the measured time per step.  Also reported:
-layer microseconds and active TFLOP/s (6*H*I*rows), the roofline of the
-dominant kernel (its duration measured with HIP events recorded around it
-on the launch stream, eager path, right after the timed steps), and the CPU
-oracle timed on a bounded sample of the same batch.
+layer microseconds, active TFLOP/s (6*H*I*rows) and their fraction of the
+FP8 MFMA peak, the roofline of the dominant kernel (its duration measured
+with HIP events recorded around it on the launch stream, eager path, right
+after the timed steps), and the CPU oracle timed on a bounded sample of the
+same batch.
 """
 from __future__ import annotations
 
@@ -50,6 +55,7 @@ def kernel_src_sha() -> str:
     data = b"".join(open(os.path.join(ROOT, f), "rb").read() for f in KERNEL_SRC)
     return hashlib.sha256(data).hexdigest()[:16]
 HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
 STAGES = ["route+dispatch", "quant_x", "gemm_gateup_swiglu", "quant_h", "gemm_down", "combine"]
 
 
@@ -115,17 +121,39 @@ def time_point(name, T, steps, warmup, force_cfg=-1):
     if force_cfg >= 0:
         ws.force_config(force_cfg)
     stream = torch.cuda.Stream()
+    # warm-up: at least `warmup` calls and 0.2 s of them, so clocks and
+    # caches settle before the first timed point
     with torch.cuda.stream(stream):
-        for _ in range(warmup):
+        n, t_w = 0, time.perf_counter()
+        while n < warmup or time.perf_counter() - t_w < 0.2:
             g.layer_forward(ws, dW, x, s, y, stream=stream)
+            n += 1
+            if n % 16 == 0:
+                stream.synchronize()
     torch.cuda.synchronize()
+    # (a) one launch per layer call (a graph of its own at decode sizes)
     t0 = time.perf_counter()
     with torch.cuda.stream(stream):
         for _ in range(steps):
             g.layer_forward(ws, dW, x, s, y, stream=stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    ms_call = (t1 - t0) * 1e3 / steps
+    # (b) the K layer calls captured in one graph and replayed once, as a
+    # model step holds its layers in one graph: the host/command-processor
+    # cost of launching a graph is paid once, not per layer
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for _ in range(steps):
+            g.layer_forward(ws, dW, x, s, y, stream=stream)
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    graph.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / steps
+    del graph
     cfg = ws.last_config(stream)
     # per-stage durations, eager path, events on the launch stream
     evs = []
@@ -148,7 +176,8 @@ def time_point(name, T, steps, warmup, force_cfg=-1):
     total_b, g1_b, rows = layer_bytes(sh, T, n_active)
     flops = 6.0 * sh.hidden * sh.inter * rows
     us = ms_step * 1e3
-    return dict(sh=sh, B=B, W=W, T=T, us=us, ms=ms_step, gbs=total_b / (us * 1e-6) / 1e9,
+    return dict(sh=sh, B=B, W=W, T=T, us=us, ms=ms_step, us_call=ms_call * 1e3,
+                gbs=total_b / (us * 1e-6) / 1e9,
                 tflops=flops / (us * 1e-6) / 1e12, bytes=total_b, g1_bytes=g1_b, flops=flops,
                 stage_ms=stage_ms, cfg=cfg, n_active=n_active, rows=rows)
 
@@ -183,6 +212,8 @@ def main():
     ap.add_argument("--tokens", type=int, default=0)
     ap.add_argument("--cpu-tokens", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the 8192-token Qwen-shaped point of the default run")
     ap.add_argument("--force-config", type=int, default=-1,
                     help="tile configuration (default: chosen on the device)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -222,6 +253,13 @@ def main():
     points.append(main_pt)
     log(f"[bench] T={T_main}: {main_pt['us']:.1f} us, {main_pt['gbs']:.0f} GB/s, "
         f"{main_pt['tflops']:.2f} TFLOP/s, stages(ms)={[round(v, 4) for v in main_pt['stage_ms']]}")
+    if args.workload == "mixtral" and not args.tokens and not args.no_prefill:
+        # the metric's 8192-token point: the Qwen3.5-35B-A3B-shaped layer
+        qp = time_point("qwen", 8192, args.steps, args.warmup)
+        points.append(qp)
+        log(f"[bench] qwen T=8192: {qp['us']:.1f} us, {qp['gbs']:.0f} GB/s, "
+            f"{qp['tflops']:.2f} TFLOP/s ({qp['tflops'] / FP8_PEAK_TFLOPS:.3f} of FP8 peak), "
+            f"stages(ms)={[round(v, 4) for v in qp['stage_ms']]}")
     dom = int(np.argmax(main_pt["stage_ms"]))
     dom_ms = main_pt["stage_ms"][dom]
     if dom == 2:
@@ -255,9 +293,11 @@ def main():
                    "tokens": T_main, "hidden": sh.hidden, "inter": sh.inter,
                    "experts": sh.experts, "top_k": sh.top_k, "w_format": sh.w_format,
                    "a_format": sh.a_format, "tile_config": main_pt["cfg"]},
-        "points": [{"tokens": p["T"], "layer_us": round(p["us"], 2),
+        "points": [{"workload": p["sh"].name, "tokens": p["T"], "layer_us": round(p["us"], 2),
+                    "layer_us_one_launch_per_call": round(p["us_call"], 2),
                     "active_tflops": round(p["tflops"], 3), "hbm_gbs": round(p["gbs"], 1),
                     "hbm_frac": round(p["gbs"] / HBM_PEAK_GBS, 4),
+                    "fp8_mfma_frac": round(p["tflops"] / FP8_PEAK_TFLOPS, 4),
                     "stage_ms": {STAGES[i]: round(v, 5) for i, v in enumerate(p["stage_ms"])}}
                    for p in points],
         "roofline": roof,

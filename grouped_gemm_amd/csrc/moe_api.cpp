@@ -552,7 +552,12 @@ int moe_layer_forward(moe_ws* ws, const moe_weights* w, const uint16_t* x, const
   int rc = check_weights(ws, w);
   if (rc) return rc;
   hipStream_t st = (hipStream_t)stream;
-  const bool use_graph = ws->graphs && st != nullptr && T <= 128 && !ws->any_stage_events();
+  // inside a caller's stream capture the launches become part of the
+  // caller's graph; otherwise decode-sized calls replay a graph of their own
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (st != nullptr) HIP_TRY(hipStreamIsCapturing(st, &cap), "capture query");
+  const bool use_graph = ws->graphs && st != nullptr && T <= 128 && !ws->any_stage_events() &&
+                         cap == hipStreamCaptureStatusNone;
   if (!use_graph) return enqueue_layer(ws, w, x, scores, T, y, st);
   GraphKey key{};
   key.T = T;

@@ -208,7 +208,11 @@ MOE_API int moe_config_rows(int cfg_id);
 
 /* Enable (1, default) or disable (0) hipGraph capture of moe_layer_forward
  * for decode token counts (T <= 128): the first call at each T captures
- * and instantiates a graph, later calls with the same pointers replay it. */
+ * and instantiates a graph, later calls with the same pointers replay it.
+ * A call made while `stream` is being captured by the caller (for example
+ * a whole model step in one graph) enqueues its kernels into the caller's
+ * capture instead; no library call on the path allocates or sets memory,
+ * so the captured launches replay like the eager ones. */
 MOE_API int moe_workspace_set_graphs(moe_ws* ws, int enable);
 
 /* Profiling: record the caller's HIP events (hipEvent_t, created with

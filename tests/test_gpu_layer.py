@@ -77,6 +77,48 @@ def test_layer_is_deterministic_and_graph_replay_matches_eager():
         np.testing.assert_array_equal(y.cpu().numpy().view(np.uint16), y0)
 
 
+@pytest.mark.parametrize("idx", [1, 2, 4], ids=["fp8_channel", "fp8_block", "mxfp4"])
+def test_layer_calls_in_a_caller_captured_graph(idx):
+    """Three layer calls captured in one caller graph (as a model step would
+    hold many layers) replay to the eager outputs, several times, with eager
+    work between the replays."""
+    import grouped_gemm_amd as g
+    _, sh, T = SMALL[idx]
+    W = ms.gen_weights(sh)
+    dW = dev_weights(W)
+    ws = workspace(sh, T)
+    batches = [ms.gen_batch(sh, T) for _ in range(1)]
+    B = batches[0]
+    x = torch.from_numpy(B.x_bits.view(np.int16)).cuda()
+    s = torch.from_numpy(B.scores).cuda()
+    s2 = (s * 0.5).contiguous()                 # a second routing for the middle call
+    ws.set_graphs(False)
+    ref = []
+    for sc in (s, s2, s):
+        yy = torch.empty(T, sh.hidden, dtype=torch.int16, device="cuda")
+        g.layer_forward(ws, dW, x, sc, yy)
+        torch.cuda.synchronize()
+        ref.append(yy.cpu().numpy().copy())
+    ws.set_graphs(True)
+    ys = [torch.zeros(T, sh.hidden, dtype=torch.int16, device="cuda") for _ in range(3)]
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):                 # warm the library outside the capture
+        g.layer_forward(ws, dW, x, s, ys[0], stream=st)
+    st.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=st):
+        for yy, sc in zip(ys, (s, s2, s)):
+            g.layer_forward(ws, dW, x, sc, yy, stream=st)
+    for rep in range(3):
+        for yy in ys:
+            yy.zero_()                          # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for yy, r in zip(ys, ref):
+            np.testing.assert_array_equal(yy.cpu().numpy(), r)
+
+
 def test_zero_token_experts_with_nan_weights_are_inert():
     sh = SMALL[1][1]
     T = 20
