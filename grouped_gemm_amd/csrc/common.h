@@ -93,6 +93,49 @@ DEVI float wave_sum(float v) {
   return v;
 }
 
+// Reductions over a row of 16 lanes by DPP moves (no LDS round trip): xor 1
+// and xor 2 inside quads, then the half-row and row mirrors, after which
+// every lane of the row holds the row's result.
+template <int CTRL>
+DEVI uint32_t dpp_mov(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+DEVI uint32_t row16_max(uint32_t v) {
+  uint32_t o = dpp_mov<0xB1>(v);
+  v = o > v ? o : v;
+  o = dpp_mov<0x4E>(v);
+  v = o > v ? o : v;
+  o = dpp_mov<0x141>(v);
+  v = o > v ? o : v;
+  o = dpp_mov<0x140>(v);
+  return o > v ? o : v;
+}
+// max over the 4 lanes of a quad
+DEVI uint32_t quad_max(uint32_t v) {
+  uint32_t o = dpp_mov<0xB1>(v);
+  v = o > v ? o : v;
+  o = dpp_mov<0x4E>(v);
+  return o > v ? o : v;
+}
+DEVI uint32_t row16_min(uint32_t v) {
+  uint32_t o = dpp_mov<0xB1>(v);
+  v = o < v ? o : v;
+  o = dpp_mov<0x4E>(v);
+  v = o < v ? o : v;
+  o = dpp_mov<0x141>(v);
+  v = o < v ? o : v;
+  o = dpp_mov<0x140>(v);
+  return o < v ? o : v;
+}
+// (each pairing adds the same two partial sums, so all lanes agree bitwise)
+DEVI float row16_sum(float v) {
+  v += __uint_as_float(dpp_mov<0xB1>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_mov<0x4E>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_mov<0x141>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_mov<0x140>(__float_as_uint(v)));
+  return v;
+}
+
 // ---------------------------------------------------------------- MFMA
 DEVI f32x4 mfma_f8(const i32x8& a, const i32x8& b, f32x4 c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);

@@ -4,7 +4,7 @@
 // before the gate/up projection and requantisation of the intermediate;
 // Alpha-MoE news page, "The MoE bottleneck": FP8 W8A8).  Per group of a
 // row: a = max|v|; FP8 groups use the fp32 scale s = a/448 (1 when a = 0)
-// and q = e4m3_rne(clamp(v/s, +-448)) with IEEE division; MX groups (OCP MX
+// and q = e4m3_rne(clamp(v/s, +-448)) with the correctly rounded fp32 quotient; MX groups (OCP MX
 // v1.0) use X = 2^(floor(log2 a) - 8) stored as e8m0, and q = e4m3_rne_sat(v/X).
 //
 // Combine (LightMoE README, "MoE inference": routing-weight application and
@@ -91,8 +91,9 @@ __global__ void __launch_bounds__(256) k_quant(QuantArgs qa) {
       if ((c & 3) == 0) ((uint8_t*)qa.scale)[(size_t)row * (n / 32) + c / 4] = (uint8_t)(ex + 127);
     } else {
       float s = a > 0.f ? a / 448.0f : 1.0f;
-      lo = cvt4_e4m3(v[j][0] / s, v[j][1] / s, v[j][2] / s, v[j][3] / s);
-      hi = cvt4_e4m3(v[j][4] / s, v[j][5] / s, v[j][6] / s, v[j][7] / s);
+      const uint2 qc = qr_codes_div(v[j], s);
+      lo = qc.x;
+      hi = qc.y;
       if (AF == MOE_A_FP8_TOKEN) {
         if (c == 0) ((float*)qa.scale)[row] = s;
       } else if ((c & 15) == 0) {
@@ -120,7 +121,11 @@ static int elementwise_grid(int rows) {
 template <int AF, bool IN_BF16>
 static hipError_t quant_dispatch_j(const QuantArgs& q, hipStream_t st) {
   int nch = q.n / 8, j = (nch + 255) / 256;
-  dim3 grid(elementwise_grid(q.R)), block(256);
+  // a launch that runs only for one configuration (its rows are then few)
+  // keeps a small grid, so skipping it costs little
+  int blocks = elementwise_grid(q.R);
+  if (q.meta && blocks > 256) blocks = 256;
+  dim3 grid(blocks), block(256);
   if (j <= 1) hipLaunchKernelGGL((k_quant<AF, IN_BF16, 1>), grid, block, 0, st, q);
   else if (j <= 2) hipLaunchKernelGGL((k_quant<AF, IN_BF16, 2>), grid, block, 0, st, q);
   else if (j <= 4) hipLaunchKernelGGL((k_quant<AF, IN_BF16, 4>), grid, block, 0, st, q);
@@ -148,16 +153,17 @@ hipError_t launch_quant(const QuantArgs& q, hipStream_t st) {
 
 // bf16 rows, one wave per row: the same device code the routing launches
 // run on their spare waves
+template <int QF>
 __global__ void __launch_bounds__(256) k_quant_rows(QuantArgs q) {
-  quant_rows_waves(q, (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6), (int)gridDim.x * 4,
-                   threadIdx.x & 63);
+  quant_rows_waves<QF>(q, (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6), (int)gridDim.x * 4,
+                       threadIdx.x & 63);
 }
 
 hipError_t launch_quant_rows(const QuantArgs& q, hipStream_t st) {
   if (q.R == 0) return hipSuccess;
   if (!q.in_bf16) return hipErrorInvalidValue;
   const int blocks = (q.R + 3) / 4;
-  hipLaunchKernelGGL(k_quant_rows, dim3(blocks < 2048 ? blocks : 2048), dim3(256), 0, st, q);
+  LAUNCH_QF(quant_format(q), k_quant_rows, dim3(blocks < 2048 ? blocks : 2048), dim3(256), 0, st, q);
   return hipGetLastError();
 }
 

@@ -16,18 +16,16 @@
 #define META_ERROR 6     // nonzero: the device rejected the group offsets
 #define META_WORDS 16
 
-// Slots up to which one 1024-thread block does the whole dispatch; it also
-// routes (scores staged in LDS) when everything fits in DISPATCH_LDS_MAX.
-#define SMALL_DISPATCH_SLOTS 8192
+// Slots up to which one 1024-thread block does the whole dispatch (it also
+// routes, when the batch routes in one or two passes); larger batches take
+// the two-launch chunked path.
+#define SMALL_DISPATCH_SLOTS 2048
 // Slots up to which one wave does the whole dispatch (at most 64 groups)
 #define TINY_DISPATCH_SLOTS 1024
 // Router scores (floats) the one-wave path stages in LDS before routing
 #define TINY_SCORE_LDS 4096
-#define DISPATCH_LDS_MAX (64 * 1024)
-// Expert counts up to which one thread routes a token (above: one wave)
+// Expert counts up to which one thread routes a token (above: a 16-lane row)
 #define SMALL_E_THREAD_ROUTE 32
-// LDS ints the multi-block scan stages per pass of chunk counts
-#define SCAN_STAGE_INTS 12288
 
 // Tile configurations: 0 streams weights (decode-sized groups); the others
 // are LDS-tiled with the given row-block height.
@@ -68,7 +66,7 @@ struct DispatchArgs {
   int32_t* active;        // [G]
   int32_t* tiles;         // [2 * max tiles]
   int32_t* meta;          // [META_WORDS]
-  int32_t* chunk;         // [ceil(S/1024) * E]
+  int32_t* chunk;         // [chunks * E], chunks = ceil(T / floor(1024 / k))
   int force_cfg;          // -1: choose from the histogram
   int H, I, wbits, xbits; // for the cost model
   int num_cfgs;           // configurations the library has kernels for
@@ -137,7 +135,7 @@ struct CombineArgs {
 hipError_t launch_route(const float* scores, int T, int E, int k, int score_fn, int32_t* ids,
                         float* w, const QuantArgs& fq, hipStream_t st);
 hipError_t launch_dispatch(const DispatchArgs& d, hipStream_t st);
-size_t dispatch_small_lds(int T, int k, int G, int E, bool route);
+size_t dispatch_small_lds(int S, int G);
 hipError_t launch_quant(const QuantArgs& q, hipStream_t st);
 // bf16 activation rows, one wave per row (the routing launches' quantiser)
 hipError_t launch_quant_rows(const QuantArgs& q, hipStream_t st);

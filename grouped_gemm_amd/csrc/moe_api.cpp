@@ -98,7 +98,7 @@ Layout make_layout(const moe_layer_desc& d) {
   L.S = T * k;
   L.S_tot = L.S + (d.shared_experts ? T : 0);
   L.max_tiles = L.S_tot / 16 + L.G + 1;
-  L.nchunks = (L.S + 1023) / 1024;
+  L.nchunks = (T + 1024 / k - 1) / (1024 / k);   // whole-token chunks of <= 1024 slots
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;

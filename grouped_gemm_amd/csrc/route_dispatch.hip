@@ -30,58 +30,74 @@ DEVI uint64_t shfl_xor_u64(uint64_t v, int m) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// One wave routes one token.  Each lane keeps up to four candidate experts
-// (e = lane + 64*i) as 64-bit keys (score key, 0xFFFF - e): the maximum key
-// is the highest score with the lowest index among equals.
-DEVI void route_one_token(const float* row, int E, int k, int score_fn, int lane, int32_t* ids_out,
-                          float* w_out, int32_t* ids_lds) {
-  uint64_t key[4];
+// Inverse of score_key (a -0 score comes back as +0, which weighs the same).
+DEVI float key_score(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+// One row of 16 lanes routes one token (E <= 256): lane l of the row holds
+// the keys of experts e = 4l + j + 64q (j, q < 4).  Pass j takes the row
+// maximum of the keys, then the lowest expert index holding it (the key
+// order: score, then lowest index), and the owning lane drops that key.
+// Lane j < k keeps the j-th choice; the weights are renormalised over the
+// k.  Every lane of the row must run this (rows with tv = false compute on
+// zero keys and write nothing).
+DEVI void route_row16(const float* row, bool tv, int E, int k, int score_fn, int l16,
+                      int32_t* ids_out, float* w_out, int32_t* ids_lds) {
+  uint32_t key[16];
+  if (((E & 3) | ((uintptr_t)row & 15)) == 0) {   // 16-byte aligned rows: four experts per load
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int e = lane + 64 * i;
-    key[i] = (e < E) ? (((uint64_t)score_key(row[e]) << 32) | (uint32_t)(0xFFFF - e)) : 0ull;
+    for (int q = 0; q < 4; ++q) {
+      const int e0 = 4 * l16 + 64 * q;
+      float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+      const bool ok = tv && e0 < E;
+      if (ok) f = *(const float4*)(row + e0);
+      key[4 * q + 0] = ok ? score_key(f.x) : 0u;
+      key[4 * q + 1] = ok ? score_key(f.y) : 0u;
+      key[4 * q + 2] = ok ? score_key(f.z) : 0u;
+      key[4 * q + 3] = ok ? score_key(f.w) : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e = 4 * l16 + (i & 3) + 64 * (i >> 2);
+      key[i] = (tv && e < E) ? score_key(row[e]) : 0u;
+    }
   }
-  int my_id = 0;
+  // finite scores have keys >= 0x00800000, so 0 marks an absent or taken expert
+  uint32_t my_id = 0, my_key = 0, top_key = 0;
   for (int j = 0; j < k; ++j) {
-    uint64_t best = key[0];
+    uint32_t m = 0;
 #pragma unroll
-    for (int i = 1; i < 4; ++i) best = key[i] > best ? key[i] : best;
+    for (int i = 0; i < 16; ++i) m = key[i] > m ? key[i] : m;
+    m = row16_max(m);
+    uint32_t be = 0xFFFFu;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      uint64_t other = shfl_xor_u64(best, o);
-      best = other > best ? other : best;
-    }
-    int be = 0xFFFF - (int)(best & 0xFFFFu);
-    if (lane == (be & 63)) {
+    for (int i = 15; i >= 0; --i)   // indices grow with i: the lowest match wins
+      be = key[i] == m ? (uint32_t)(4 * l16 + (i & 3) + 64 * (i >> 2)) : be;
+    be = row16_min(be);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (i == (be >> 6)) key[i] = 0ull;
-    }
-    if (lane == j) my_id = be;
+    for (int i = 0; i < 16; ++i)
+      key[i] = (uint32_t)(4 * l16 + (i & 3) + 64 * (i >> 2)) == be ? 0u : key[i];
+    top_key = j == 0 ? m : top_key;
+    my_id = l16 == j ? be : my_id;
+    my_key = l16 == j ? m : my_key;
   }
-  // gate weights over the chosen k, renormalised
-  float l = (lane < k) ? row[my_id] : 0.f;
-  float top = __shfl(l, 0, 64);
-  float v = 0.f;
-  if (lane < k) {
-    if (score_fn == MOE_SCORE_SOFTMAX)
-      v = expf(l - top);
-    else if (score_fn == MOE_SCORE_SIGMOID)
-      v = 1.0f / (1.0f + expf(-l));
-    else
-      v = l;
-  }
-  float sum = wave_sum(v);
-  if (lane < k) {
-    ids_out[lane] = my_id;
-    w_out[lane] = v / sum;
-    if (ids_lds) ids_lds[lane] = my_id;
+  const float lv = key_score(my_key), top = key_score(top_key);
+  float v = score_fn == MOE_SCORE_SOFTMAX ? expf(lv - top)
+            : score_fn == MOE_SCORE_SIGMOID ? 1.0f / (1.0f + expf(-lv)) : lv;
+  v = l16 < k ? v : 0.f;
+  const float sum = row16_sum(v);
+  if (tv && l16 < k) {
+    ids_out[l16] = (int32_t)my_id;
+    w_out[l16] = v / sum;
+    if (ids_lds) ids_lds[l16] = (int32_t)my_id;
   }
 }
 
 // One thread routes one token (small expert counts, E <= 32): k passes over
 // the E scores, each taking the largest remaining key (score, then lowest
-// index) -- exactly the order route_one_token produces.  Compact rolled
+// index) -- exactly the order route_row16 produces.  Compact rolled
 // loops, for scores staged in LDS.
 DEVI void route_token_thread(const float* row, int E, int k, int score_fn, int32_t* ids_out,
                              float* w_out, int32_t* ids_lds) {
@@ -148,12 +164,13 @@ DEVI void route_token_regs(const float* row, int E, int k, int score_fn, int32_t
   for (int j = 0; j < k; ++j) w_out[j] = w_out[j] / sum;
 }
 
+template <int QF>
 __global__ void __launch_bounds__(256) k_route_thread(const float* __restrict__ scores, int T, int E,
                                                       int k, int score_fn, int32_t* __restrict__ ids,
                                                       float* __restrict__ w, QuantArgs fq) {
   const int rb = (T + 255) / 256;
   if ((int)blockIdx.x >= rb) {
-    quant_rows_waves(fq, ((int)blockIdx.x - rb) * 4 + (threadIdx.x >> 6), ((int)gridDim.x - rb) * 4,
+    quant_rows_waves<QF>(fq, ((int)blockIdx.x - rb) * 4 + (threadIdx.x >> 6), ((int)gridDim.x - rb) * 4,
                      threadIdx.x & 63);
     return;
   }
@@ -163,43 +180,42 @@ __global__ void __launch_bounds__(256) k_route_thread(const float* __restrict__ 
                      nullptr);
 }
 
-__global__ void __launch_bounds__(256) k_route(const float* __restrict__ scores, int T, int E, int k,
-                                               int score_fn, int32_t* __restrict__ ids,
-                                               float* __restrict__ w, QuantArgs fq) {
+// Sixteen tokens per 256-thread block, one DPP row each.
+template <int QF>
+__global__ void __launch_bounds__(256) k_route16(const float* __restrict__ scores, int T, int E,
+                                                 int k, int score_fn, int32_t* __restrict__ ids,
+                                                 float* __restrict__ w, QuantArgs fq) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int rb = (T + 3) / 4;
+  const int rb = (T + 15) / 16;
   if ((int)blockIdx.x >= rb) {
-    quant_rows_waves(fq, ((int)blockIdx.x - rb) * 4 + wave, ((int)gridDim.x - rb) * 4, lane);
+    quant_rows_waves<QF>(fq, ((int)blockIdx.x - rb) * 4 + wave, ((int)gridDim.x - rb) * 4, lane);
     return;
   }
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= T) return;
-  route_one_token(scores + (size_t)t * E, E, k, score_fn, lane, ids + (size_t)t * k,
-                  w + (size_t)t * k, nullptr);
+  const int t = (int)blockIdx.x * 16 + (int)(threadIdx.x >> 4);
+  const bool tv = t < T;
+  const size_t tt = tv ? (size_t)t : 0;
+  route_row16(scores + tt * E, tv, E, k, score_fn, threadIdx.x & 15, ids + tt * k, w + tt * k,
+              nullptr);
 }
 
 // ------------------------------------------------------------------ ranks
-// For lanes holding key e (valid), the number of lower lanes with the same
-// key, the number of lanes with that key, and whether this lane is the
-// highest one of its key.
-DEVI void wave_match(int e, bool valid, int lane, int& rank, int& cnt, bool& last) {
-  uint64_t todo = __ballot(valid);
-  rank = 0;
-  cnt = 0;
-  last = false;
-  while (todo) {
-    int leader = __ffsll((unsigned long long)todo) - 1;
-    int le = __shfl(e, leader, 64);
-    bool mine = valid && e == le;
-    uint64_t m = __ballot(mine);
-    if (mine) {
-      rank = __popcll(m & ((1ull << lane) - 1ull));
-      cnt = __popcll(m);
-      last = lane == (63 - __clzll(m));
-    }
-    todo &= ~m;
+// For lanes holding key e (valid, 0 <= e < 2^nbits), the number of lower
+// lanes with the same key, the number of lanes with that key, and whether
+// this lane is the highest one of its key.  The lanes holding my key are the
+// intersection over the key bits b of ballot(bit b set) or its complement.
+DEVI void wave_match(int e, bool valid, int lane, int nbits, int& rank, int& cnt, bool& last) {
+  uint64_t m = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t bb = __ballot(valid && bit);
+    m &= bit ? bb : ~bb;
   }
+  rank = __popcll(m & ((1ull << lane) - 1ull));
+  cnt = __popcll(m);
+  last = (m >> lane) == 1ull;
 }
+
+DEVI int key_bits(int n) { return n <= 1 ? 0 : 32 - __clz(n - 1); }
 
 // Stable ranks of up to 1024 keys held one per thread of a 1024-thread
 // block (thread order = slot order).  wcnt is LDS [16][G] and must be zero
@@ -210,7 +226,7 @@ DEVI int block_stable_rank(int e, bool valid, int32_t* wcnt, int G, int32_t* tot
   int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int rank, cnt;
   bool last;
-  wave_match(e, valid, lane, rank, cnt, last);
+  wave_match(e, valid, lane, key_bits(G), rank, cnt, last);
   if (valid && last) wcnt[wave * G + e] = cnt;
   __syncthreads();
   int pre = 0;
@@ -382,9 +398,31 @@ DEVI void finalize_dispatch(const DispatchArgs& d, int32_t* cnt, int32_t* scan_b
 }
 
 // ---------------------------------------------------------------- small path
+// Routing of tokens [t0, t0 + nt) by a 1024-thread block, ids also to
+// ids_l[(t - t0) * k + j]: one thread per token for small expert counts,
+// else one 16-lane row per token (64 tokens per pass).
+DEVI void block_route(const DispatchArgs& d, int t0, int nt, int32_t* ids_l) {
+  const int tid = threadIdx.x, k = d.k, E = d.E;
+  if (E <= SMALL_E_THREAD_ROUTE) {
+    for (int t = tid; t < nt; t += blockDim.x)
+      route_token_regs(d.scores + (size_t)(t0 + t) * E, E, k, d.score_fn,
+                       d.ids + (size_t)(t0 + t) * k, d.w + (size_t)(t0 + t) * k, ids_l + t * k);
+  } else {
+    for (int tb = 0; tb < nt; tb += 64) {
+      const int t = tb + (tid >> 4);
+      const bool tv = t < nt;
+      const int tt = tv ? t : 0;
+      route_row16(d.scores + (size_t)(t0 + tt) * E, tv, E, k, d.score_fn, tid & 15,
+                  d.ids + (size_t)(t0 + tt) * k, d.w + (size_t)(t0 + tt) * k, ids_l + tt * k);
+    }
+  }
+}
+
 // One 1024-thread block: (optionally) routing, then counts, scan, stable
-// scatter, active list, configuration and block table.  For S = T*k <= 8192.
-// Blocks past the first quantise the activation rows.
+// scatter, active list, configuration and block table, for batches that
+// route in one or two passes.  Blocks past the first quantise the
+// activation rows.
+template <int QF>
 __global__ void __launch_bounds__(1024) k_dispatch_small(DispatchArgs d) {
   extern __shared__ int32_t smem[];
   const int G = d.E + d.shared;
@@ -396,27 +434,13 @@ __global__ void __launch_bounds__(1024) k_dispatch_small(DispatchArgs d) {
   int32_t* scan_buf = wcnt + 16 * G;           // [G]
   int32_t* flag_buf = scan_buf + G;            // [G]
   int32_t* tiles_buf = flag_buf + G;           // [G]
-  float* sc_l = (float*)(tiles_buf + G);       // [T*E] router scores (routing fused)
   int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (blockIdx.x != 0) {   // blocks past the first quantise the activation rows
-    quant_rows_waves(d.fq, ((int)blockIdx.x - 1) * 16 + wave, ((int)gridDim.x - 1) * 16, lane);
+    quant_rows_waves<QF>(d.fq, ((int)blockIdx.x - 1) * 16 + wave, ((int)gridDim.x - 1) * 16, lane);
     return;
   }
-
   if (d.scores) {
-    // all scores into LDS with coalesced loads, then one wave per token
-    const int n = d.T * d.E;
-    for (int i = tid; i < n; i += blockDim.x) sc_l[i] = d.scores[i];
-    __syncthreads();
-    if (d.E <= SMALL_E_THREAD_ROUTE) {
-      for (int t = tid; t < d.T; t += blockDim.x)
-        route_token_thread(sc_l + t * d.E, d.E, d.k, d.score_fn, d.ids + (size_t)t * d.k,
-                           d.w + (size_t)t * d.k, ids_l + t * d.k);
-    } else {
-      for (int t = wave; t < d.T; t += 16)
-        route_one_token(sc_l + t * d.E, d.E, d.k, d.score_fn, lane, d.ids + (size_t)t * d.k,
-                        d.w + (size_t)t * d.k, ids_l + t * d.k);
-    }
+    block_route(d, 0, d.T, ids_l);
   } else {
     for (int p = tid; p < S; p += blockDim.x) ids_l[p] = d.ids_in[p];
   }
@@ -426,7 +450,10 @@ __global__ void __launch_bounds__(1024) k_dispatch_small(DispatchArgs d) {
   }
   for (int i = tid; i < 16 * G; i += blockDim.x) wcnt[i] = 0;
   __syncthreads();
-  for (int p = tid; p < S; p += blockDim.x) atomicAdd(&cnt[ids_l[p]], 1);
+  for (int p = tid; p < S; p += blockDim.x) {
+    const int e = ids_l[p];
+    if ((unsigned)e < (unsigned)d.E) atomicAdd(&cnt[e], 1);   // an id out of range is dropped
+  }
   __syncthreads();
   if (tid == 0 && d.shared) cnt[d.E] = d.T;
   __syncthreads();
@@ -436,8 +463,10 @@ __global__ void __launch_bounds__(1024) k_dispatch_small(DispatchArgs d) {
   // slot of group g; `run` collects this round's per-group totals.
   for (int base = 0; base < S; base += 1024) {
     int p = base + tid;
-    bool valid = p < S;
-    int e = valid ? ids_l[p] : 0;
+    int e = p < S ? ids_l[p] : 0;
+    const bool valid = p < S && (unsigned)e < (unsigned)d.E;
+    if (p < S && !valid) d.inv[p] = -1;
+    e = valid ? e : 0;
     int r = block_stable_rank(e, valid, wcnt, G, run);
     if (valid) {
       int slot = scan_buf[e] + r;
@@ -467,13 +496,14 @@ DEVI void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 // lives in lane g), the group scan, the active list, the configuration and
 // its block table -- with no workgroup barrier.  The other waves of the
 // grid quantise the activation rows meanwhile.
+template <int QF>
 __global__ void __launch_bounds__(256) k_dispatch_tiny(DispatchArgs d) {
   __shared__ int32_t ids_l[TINY_DISPATCH_SLOTS];
   __shared__ int32_t rk_l[TINY_DISPATCH_SLOTS];
   __shared__ float sc_l[TINY_SCORE_LDS];
   const int lane = threadIdx.x & 63;
   if (blockIdx.x != 0 || threadIdx.x >= 64) {
-    quant_rows_waves(d.fq, (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6) - 1, (int)gridDim.x * 4 - 1,
+    quant_rows_waves<QF>(d.fq, (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6) - 1, (int)gridDim.x * 4 - 1,
                      lane);
     return;
   }
@@ -512,8 +542,9 @@ __global__ void __launch_bounds__(256) k_dispatch_tiny(DispatchArgs d) {
   const int nch = (S + 63) / 64;
   for (int c = 0; c < nch; ++c) {
     const int p = c * 64 + lane;
-    const bool valid = p < S;
-    const int e = valid ? ids_l[p] : 0;
+    const int e0 = p < S ? ids_l[p] : 0;
+    const bool valid = p < S && (unsigned)e0 < (unsigned)d.E;   // an id out of range is dropped
+    const int e = valid ? e0 : 0;
     const uint64_t vm = __ballot(valid);
     uint64_t me = vm, mg = vm;                // lanes with my id / with id == lane
 #pragma unroll
@@ -580,89 +611,152 @@ __global__ void __launch_bounds__(256) k_dispatch_tiny(DispatchArgs d) {
   // gather / inverse slots (a lane reads back only its own rank entries)
   for (int c = 0; c < nch; ++c) {
     const int p = c * 64 + lane;
-    const bool valid = p < S;
-    const int e = valid ? ids_l[p] : 0;
+    const int e0 = p < S ? ids_l[p] : 0;
+    const bool valid = p < S && (unsigned)e0 < (unsigned)d.E;
+    const int e = valid ? e0 : 0;
     const int slot = __shfl(excl, e, 64) + (valid ? rk_l[p] : 0);
     if (valid) {
       d.gather[slot] = p;
       d.inv[p] = slot;
+    } else if (p < S) {
+      d.inv[p] = -1;
     }
   }
   if (d.shared)
     for (int t = lane; t < d.T; t += 64) d.gather[S + t] = t * d.k;
 }
 
-// ---------------------------------------------------------------- large path
-// 1) per-chunk histograms (1024 slots per chunk)
-__global__ void __launch_bounds__(1024) k_dispatch_hist(DispatchArgs d) {
+// ---------------------------------------------------------------- chunked path
+// Two launches for large batches.  Chunk c holds the tokens
+// [c*TC, c*TC + TC), TC = floor(1024 / k): whole tokens, at most 1024 slots.
+DEVI int chunk_tokens(int k) { return 1024 / k; }
+
+// Pass 1, block c: route the chunk's tokens (or read their ids), rank each
+// slot among the chunk's slots of the same expert (slot order, so stable)
+// and write the chunk's expert histogram.  The rank is parked in inv[];
+// pass 2 replaces it by the slot.  Blocks past the chunks quantise the
+// activation rows.
+template <int QF>
+__global__ void __launch_bounds__(1024) k_dispatch_chunk(DispatchArgs d) {
   extern __shared__ int32_t smem[];
-  int32_t* cnt = smem;   // [E]
-  int S = d.T * d.k, c = blockIdx.x, tid = threadIdx.x;
-  for (int e = tid; e < d.E; e += blockDim.x) cnt[e] = 0;
+  int32_t* ids_l = smem;             // [1024]
+  int32_t* wcnt = smem + 1024;       // [16][E]
+  const int E = d.E, k = d.k, TC = chunk_tokens(k);
+  const int nch = (d.T + TC - 1) / TC;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if ((int)blockIdx.x >= nch) {
+    quant_rows_waves<QF>(d.fq, ((int)blockIdx.x - nch) * 16 + wave, ((int)gridDim.x - nch) * 16, lane);
+    return;
+  }
+  const int c = blockIdx.x, t0 = c * TC, nt = min(TC, d.T - t0), ns = nt * k, p0 = t0 * k;
+  for (int i = tid; i < 16 * E; i += blockDim.x) wcnt[i] = 0;
+  if (d.scores) block_route(d, t0, nt, ids_l);
+  else
+    for (int i = tid; i < ns; i += blockDim.x) ids_l[i] = d.ids_in[p0 + i];
   __syncthreads();
-  int p = c * 1024 + tid;
-  if (p < S) atomicAdd(&cnt[d.ids_in[p]], 1);
+  const int e0 = tid < ns ? ids_l[tid] : 0;
+  const bool valid = tid < ns && (unsigned)e0 < (unsigned)E;   // an id out of range is dropped
+  const int e = valid ? e0 : 0;
+  int rank, cnt;
+  bool last;
+  wave_match(e, valid, lane, key_bits(E), rank, cnt, last);
+  if (valid && last) wcnt[wave * E + e] = cnt;
   __syncthreads();
-  for (int e = tid; e < d.E; e += blockDim.x) d.chunk[(size_t)c * d.E + e] = cnt[e];
+  if (valid) {
+    int pre = 0;
+    for (int w = 0; w < wave; ++w) pre += wcnt[w * E + e];
+    d.inv[p0 + tid] = pre + rank;
+  }
+  for (int g = tid; g < E; g += blockDim.x) {
+    int s = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) s += wcnt[w * E + g];
+    d.chunk[(size_t)c * E + g] = s;
+  }
 }
 
-// 2) one block: chunk bases, group counts, scan, active list, config, table.
-// The per-chunk counts are staged through LDS in coalesced passes of CG
-// chunks, so no thread walks a chain of dependent global loads.
-__global__ void __launch_bounds__(1024) k_dispatch_scan(DispatchArgs d) {
+// Pass 2, block c: from the chunk histograms, each group's total and its
+// rows in the chunks before c (P = 1024/E threads per group split the
+// chunks); the exclusive scan of the totals gives the group starts, and the
+// chunk's slots land at start + earlier rows + rank.  Block 0 also writes
+// counts, m_indptr, the active list, the configuration and its block table.
+// ids_in holds the routed ids.
+__global__ void __launch_bounds__(1024) k_dispatch_place(DispatchArgs d) {
   extern __shared__ int32_t smem[];
-  const int G = d.E + d.shared;
-  int32_t* cnt = smem;
-  int32_t* scan_buf = cnt + G;
-  int32_t* flag_buf = scan_buf + G;
-  int32_t* tiles_buf = flag_buf + G;
-  int32_t* stage = tiles_buf + G;                 // [CG][E]
-  const int CG = SCAN_STAGE_INTS / d.E;
-  int S = d.T * d.k, nchunks = (S + 1023) / 1024, tid = threadIdx.x;
-  int run = 0;
-  for (int c0 = 0; c0 < nchunks; c0 += CG) {
-    const int n = min(CG, nchunks - c0);
-    for (int i = tid; i < n * d.E; i += blockDim.x) stage[i] = d.chunk[(size_t)c0 * d.E + i];
-    __syncthreads();
-    if (tid < d.E) {
-      for (int c = 0; c < n; ++c) {
-        const int v = stage[c * d.E + tid];
-        d.chunk[(size_t)(c0 + c) * d.E + tid] = run;
-        run += v;
+  const int E = d.E, G = E + d.shared, k = d.k, TC = chunk_tokens(k);
+  const int S = d.T * k, nch = (d.T + TC - 1) / TC;
+  int32_t* cnt = smem;                 // [G]
+  int32_t* pre_l = cnt + G;            // [G]
+  int32_t* scan_buf = pre_l + G;       // [G]
+  int32_t* flag_buf = scan_buf + G;    // [G]
+  int32_t* tiles_buf = flag_buf + G;   // [G]
+  int32_t* part = tiles_buf + G;       // [2][1024]
+  const int c = blockIdx.x, tid = threadIdx.x;
+  const int P = 1024 / E, g = tid % E, q = tid / E;
+  int tot = 0, pre = 0;
+  if (q < P) {
+    for (int c0 = q; c0 < nch; c0 += 8 * P) {   // eight loads in flight
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int cc = c0 + u * P;
+        v[u] = cc < nch ? d.chunk[(size_t)cc * E + g] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        tot += v[u];
+        pre += c0 + u * P < c ? v[u] : 0;
       }
     }
+  }
+  part[tid] = tot;
+  part[1024 + tid] = pre;
+  __syncthreads();
+  if (tid < E) {
+    int a = 0, b = 0;
+    for (int qq = 0; qq < P; ++qq) {
+      a += part[qq * E + tid];
+      b += part[1024 + qq * E + tid];
+    }
+    cnt[tid] = a;
+    pre_l[tid] = b;
+  }
+  if (tid == 0 && d.shared) cnt[E] = d.T;
+  __syncthreads();
+  if (c == 0) {
+    finalize_dispatch(d, cnt, scan_buf, flag_buf, tiles_buf, G, S + (d.shared ? d.T : 0));
+  } else {
+    for (int i = tid; i < G; i += blockDim.x) scan_buf[i] = cnt[i];
     __syncthreads();
+    wave0_exclusive_scan(scan_buf, G, nullptr);
   }
-  if (tid < d.E) cnt[tid] = run;
-  if (tid == 0 && d.shared) cnt[d.E] = d.T;
   __syncthreads();
-  finalize_dispatch(d, cnt, scan_buf, flag_buf, tiles_buf, G, S + (d.shared ? d.T : 0));
+  const int t0 = c * TC, ns = min(TC, d.T - t0) * k, p = t0 * k + tid;
+  if (tid < ns) {
+    const int e = d.ids_in[p];
+    if ((unsigned)e < (unsigned)E) {
+      const int slot = scan_buf[e] + pre_l[e] + d.inv[p];
+      d.gather[slot] = p;
+      d.inv[p] = slot;
+    } else {
+      d.inv[p] = -1;
+    }
+  }
   if (d.shared)
-    for (int t = tid; t < d.T; t += blockDim.x) d.gather[S + t] = t * d.k;
-}
-
-// 3) stable scatter of each chunk
-__global__ void __launch_bounds__(1024) k_dispatch_scatter(DispatchArgs d) {
-  extern __shared__ int32_t smem[];
-  const int G = d.E;
-  int32_t* wcnt = smem;  // [16*E]
-  int S = d.T * d.k, c = blockIdx.x, tid = threadIdx.x;
-  for (int i = tid; i < 16 * G; i += blockDim.x) wcnt[i] = 0;
-  __syncthreads();
-  int p = c * 1024 + tid;
-  bool valid = p < S;
-  int e = valid ? d.ids_in[p] : 0;
-  int r = block_stable_rank(e, valid, wcnt, G, nullptr);
-  if (valid) {
-    int slot = d.indptr[e] + d.chunk[(size_t)c * d.E + e] + r;
-    d.gather[slot] = p;
-    d.inv[p] = slot;
-  }
+    for (int t = c * 1024 + tid; t < d.T; t += nch * 1024) d.gather[S + t] = t * k;
 }
 
 // ---------------------------------------------------------------- host launchers
-size_t dispatch_small_lds(int T, int k, int G, int E, bool route) {
-  return sizeof(int32_t) * ((size_t)T * k + 2 * G + 16 * G + 3 * G + (route ? (size_t)T * E : 0));
+size_t dispatch_small_lds(int S, int G) {
+  return sizeof(int32_t) * ((size_t)S + 2 * G + 16 * G + 3 * G);
+}
+
+// The one-block path routes in at most two passes (thread per token for
+// small expert counts, else 64 tokens per pass) and scatters at most two
+// rounds of 1024 slots.
+static bool small_path(const DispatchArgs& d) {
+  const int S = d.T * d.k;
+  return S <= SMALL_DISPATCH_SLOTS && (d.E <= SMALL_E_THREAD_ROUTE || d.T <= 128);
 }
 
 // Blocks (of `wpb` waves) to add to a launch so its spare waves quantise
@@ -680,12 +774,12 @@ hipError_t launch_route(const float* scores, int T, int E, int k, int score_fn, 
   if (T == 0) return hipSuccess;
   if (E <= SMALL_E_THREAD_ROUTE) {
     const int rb = (T + 255) / 256;
-    hipLaunchKernelGGL(k_route_thread, dim3(rb + quant_blocks(fq, 4, 0)), dim3(256), 0, st, scores,
-                       T, E, k, score_fn, ids, w, fq);
+    LAUNCH_QF(quant_format(fq), k_route_thread, dim3(rb + quant_blocks(fq, 4, 0)), dim3(256), 0, st,
+              scores, T, E, k, score_fn, ids, w, fq);
   } else {
-    const int rb = (T + 3) / 4;
-    hipLaunchKernelGGL(k_route, dim3(rb + quant_blocks(fq, 4, 0)), dim3(256), 0, st, scores, T, E, k,
-                       score_fn, ids, w, fq);
+    const int rb = (T + 15) / 16;
+    LAUNCH_QF(quant_format(fq), k_route16, dim3(rb + quant_blocks(fq, 4, 0)), dim3(256), 0, st,
+              scores, T, E, k, score_fn, ids, w, fq);
   }
   return hipGetLastError();
 }
@@ -695,45 +789,25 @@ hipError_t launch_dispatch(const DispatchArgs& d, hipStream_t st) {
   const int S = d.T * d.k;
   if (S <= TINY_DISPATCH_SLOTS && G <= 64 && (!d.scores || d.E <= SMALL_E_THREAD_ROUTE)) {
     const int grid = 1 + quant_blocks(d.fq, 4, 3);
-    hipLaunchKernelGGL(k_dispatch_tiny, dim3(grid), dim3(256), 0, st, d);
+    LAUNCH_QF(quant_format(d.fq), k_dispatch_tiny, dim3(grid), dim3(256), 0, st, d);
     return hipGetLastError();
   }
-  if (S <= SMALL_DISPATCH_SLOTS) {
-    // routing is fused into the block when the scores fit in its LDS
-    if (d.scores && dispatch_small_lds(d.T, d.k, G, d.E, true) > DISPATCH_LDS_MAX) {
-      hipError_t e = launch_route(d.scores, d.T, d.E, d.k, d.score_fn, d.ids, d.w, d.fq, st);
-      if (e != hipSuccess) return e;
-      DispatchArgs d2 = d;
-      d2.scores = nullptr;
-      d2.ids_in = d.ids;
-      d2.fq.R = 0;
-      hipLaunchKernelGGL(k_dispatch_small, dim3(1), dim3(1024),
-                         dispatch_small_lds(d.T, d.k, G, d.E, false), st, d2);
-      return hipGetLastError();
-    }
+  if (small_path(d)) {
     const int grid = 1 + quant_blocks(d.fq, 16, 0);
-    hipLaunchKernelGGL(k_dispatch_small, dim3(grid), dim3(1024),
-                       dispatch_small_lds(d.T, d.k, G, d.E, d.scores != nullptr), st, d);
+    LAUNCH_QF(quant_format(d.fq), k_dispatch_small, dim3(grid), dim3(1024), dispatch_small_lds(S, G),
+              st, d);
     return hipGetLastError();
   }
-  // large path: routing (if requested, with the input quantisation) runs as
-  // its own grid first
+  // chunked path: routing (if requested) and the input quantisation ride
+  // the first launch
+  const int TC = 1024 / d.k, nch = (d.T + TC - 1) / TC;
+  LAUNCH_QF(quant_format(d.fq), k_dispatch_chunk, dim3(nch + quant_blocks(d.fq, 16, 0)), dim3(1024),
+            sizeof(int32_t) * (1024 + 16 * d.E), st, d);
   DispatchArgs d2 = d;
   d2.fq.R = 0;
-  if (d.scores) {
-    hipError_t e = launch_route(d.scores, d.T, d.E, d.k, d.score_fn, d.ids, d.w, d.fq, st);
-    if (e != hipSuccess) return e;
-    d2.scores = nullptr;
-    d2.ids_in = d.ids;
-  } else if (d.fq.R > 0) {
-    hipError_t e = launch_quant(d.fq, st);
-    if (e != hipSuccess) return e;
-  }
-  int nchunks = (S + 1023) / 1024;
-  hipLaunchKernelGGL(k_dispatch_hist, dim3(nchunks), dim3(1024), sizeof(int32_t) * d.E, st, d2);
-  hipLaunchKernelGGL(k_dispatch_scan, dim3(1), dim3(1024),
-                     sizeof(int32_t) * (4 * G + SCAN_STAGE_INTS), st, d2);
-  hipLaunchKernelGGL(k_dispatch_scatter, dim3(nchunks), dim3(1024), sizeof(int32_t) * 16 * d.E, st,
+  d2.ids_in = d.scores ? d.ids : d.ids_in;
+  d2.scores = nullptr;
+  hipLaunchKernelGGL(k_dispatch_place, dim3(nch), dim3(1024), sizeof(int32_t) * (5 * G + 2048), st,
                      d2);
   return hipGetLastError();
 }

@@ -132,9 +132,11 @@ MOE_API int moe_route_topk(const float* scores, int T, int E, int k, int score_f
  *   m_indptr  [E+1] int32 out: exclusive prefix sum of counts
  *   gather    [T*k] int32 out: slot -> t*k+j
  *   inv       [T*k] int32 out: t*k+j -> slot
- * E must equal the workspace's num_experts and T <= max_tokens.  The
- * workspace supplies scratch (per-chunk histograms).  Errors: EINVAL,
- * ECAPACITY. */
+ * E must equal the workspace's num_experts and T <= max_tokens.  An id
+ * outside [0, E) takes no slot: it is not counted, its inv entry is -1 and
+ * m_indptr[E] falls short of T*k by the number of such ids.  The workspace
+ * supplies scratch (per-chunk histograms); inv also holds per-chunk ranks
+ * between the two launches of large batches.  Errors: EINVAL, ECAPACITY. */
 MOE_API int moe_dispatch(moe_ws* ws, const int32_t* topk_ids, int T, int k, int E, int32_t* counts,
                  int32_t* m_indptr, int32_t* gather, int32_t* inv, void* stream);
 

@@ -26,10 +26,12 @@ SMALL = [
     ("mxfp4", ms.small_shape("imbalance", hidden=384, inter=512, experts=10, top_k=3), 41),
     ("tiny_cfg", ms.CONFIGS["tiny"], 32),
     # more slots than the one-wave dispatch takes: one-block dispatch with
-    # routing fused (700), and the multi-block path with thread routing (4200);
-    # both quantise x on the routing launch's spare waves
+    # routing fused (700), the chunked path with thread routing (4200) and
+    # with 16-lane-row routing (40 experts, 600); all quantise x on the
+    # routing launch's spare waves
     ("fp8_channel_700", ms.small_shape("mixtral", hidden=256, inter=256, experts=8, top_k=2), 700),
     ("fp8_channel_4200", ms.small_shape("mixtral", hidden=256, inter=256, experts=8, top_k=2), 4200),
+    ("fp8_block_600", ms.small_shape("qwen", hidden=256, inter=256, experts=40, top_k=4), 600),
 ]
 
 

@@ -135,3 +135,37 @@ def test_quantize_act_bit_exact(name):
     else:
         np.testing.assert_array_equal(sc.cpu().numpy().astype(np.float64).reshape(s_ref.shape),
                                       s_ref)
+
+
+@pytest.mark.parametrize("E,k,T", [(8, 2, 20), (256, 8, 50), (256, 8, 1000), (63, 5, 700)])
+def test_dispatch_drops_out_of_range_ids(E, k, T):
+    """Ids outside [0, E) take no slot (inv = -1); the other slots keep the
+    expert-major, flat-index order, on the one-wave, one-block and chunked
+    paths."""
+    say("dispatch bad ids", E, k, T)
+    rng = np.random.default_rng(7 * T + E)
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    flat = ids.reshape(-1).copy()
+    bad = rng.random(flat.size) < 0.05
+    flat[bad] = np.where(rng.random(bad.sum()) < 0.5, -1, E + 3)
+    ids = flat.reshape(T, k)
+    ok = (flat >= 0) & (flat < E)
+    counts = np.bincount(flat[ok], minlength=E).astype(np.int32)
+    indptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    p_ok = np.nonzero(ok)[0]
+    gather = p_ok[np.argsort(flat[p_ok], kind="stable")].astype(np.int32)
+    inv = np.full(flat.size, -1, np.int32)
+    inv[gather] = np.arange(gather.size, dtype=np.int32)
+    sh = ms.small_shape("qwen", hidden=256, inter=256, experts=E, top_k=k)
+    ws = workspace(sh, T)
+    S = T * k
+    d_c = torch.empty(E, dtype=torch.int32, device="cuda")
+    d_i = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    d_g = torch.full((S,), -7, dtype=torch.int32, device="cuda")
+    d_v = torch.empty(S, dtype=torch.int32, device="cuda")
+    g.dispatch(ws, dev(ids), E, d_c, d_i, d_g, d_v)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(d_c.cpu().numpy(), counts)
+    np.testing.assert_array_equal(d_i.cpu().numpy(), indptr)
+    np.testing.assert_array_equal(d_g.cpu().numpy()[: gather.size], gather)
+    np.testing.assert_array_equal(d_v.cpu().numpy(), inv)
