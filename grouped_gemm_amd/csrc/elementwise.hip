@@ -29,34 +29,20 @@ __global__ void __launch_bounds__(256) k_quant(QuantArgs qa) {
   const int n = qa.n, nch = n / 8;
   const int tid = threadIdx.x;
   for (int row = blockIdx.x; row < nrows; row += gridDim.x) {
+  // all chunk loads of the row first (indices clamped into the row), so
+  // they are in flight together
+  QrChunk<IN_BF16> raw[MAXJ];
+#pragma unroll
+  for (int j = 0; j < MAXJ; ++j) {
+    const int c = tid + 256 * j;
+    raw[j] = qr_fetch<IN_BF16>(qa.in, row, n, c < nch ? c : nch - 1);
+  }
   float v[MAXJ][8];
   float gmax[MAXJ];
 #pragma unroll
   for (int j = 0; j < MAXJ; ++j) {
-    int c = tid + 256 * j;
-    gmax[j] = 0.f;
-    if (c < nch) {
-      if (IN_BF16) {
-        const uint16_t* src = (const uint16_t*)qa.in + (size_t)row * n + 8 * c;
-        uint4 raw = *(const uint4*)src;
-        uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[j][2 * i] = bf16_to_f32((uint16_t)(w4[i] & 0xFFFF));
-          v[j][2 * i + 1] = bf16_to_f32((uint16_t)(w4[i] >> 16));
-        }
-      } else {
-        const float* src = (const float*)qa.in + (size_t)row * n + 8 * c;
-        float4 a = *(const float4*)src, b = *(const float4*)(src + 4);
-        v[j][0] = a.x; v[j][1] = a.y; v[j][2] = a.z; v[j][3] = a.w;
-        v[j][4] = b.x; v[j][5] = b.y; v[j][6] = b.z; v[j][7] = b.w;
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) gmax[j] = fmaxf(gmax[j], fabsf(v[j][i]));
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[j][i] = 0.f;
-    }
+    qr_unpack<IN_BF16>(raw[j], v[j]);
+    gmax[j] = tid + 256 * j < nch ? qr_amax8(v[j]) : 0.f;
   }
   if (AF == MOE_A_FP8_TOKEN) {
     __shared__ float red[4];
@@ -90,7 +76,7 @@ __global__ void __launch_bounds__(256) k_quant(QuantArgs qa) {
       hi = cvt4_e4m3(v[j][4] * inv, v[j][5] * inv, v[j][6] * inv, v[j][7] * inv);
       if ((c & 3) == 0) ((uint8_t*)qa.scale)[(size_t)row * (n / 32) + c / 4] = (uint8_t)(ex + 127);
     } else {
-      float s = a > 0.f ? a / 448.0f : 1.0f;
+      float s = qr_scale(a);
       const uint2 qc = qr_codes_div(v[j], s);
       lo = qc.x;
       hi = qc.y;
@@ -124,7 +110,7 @@ static hipError_t quant_dispatch_j(const QuantArgs& q, hipStream_t st) {
   // a launch that runs only for one configuration (its rows are then few)
   // keeps a small grid, so skipping it costs little
   int blocks = elementwise_grid(q.R);
-  if (q.meta && blocks > 256) blocks = 256;
+  if (q.meta && blocks > 64) blocks = 64;
   dim3 grid(blocks), block(256);
   if (j <= 1) hipLaunchKernelGGL((k_quant<AF, IN_BF16, 1>), grid, block, 0, st, q);
   else if (j <= 2) hipLaunchKernelGGL((k_quant<AF, IN_BF16, 2>), grid, block, 0, st, q);
@@ -173,56 +159,42 @@ hipError_t launch_quant_rows(const QuantArgs& q, hipStream_t st) {
 // routing weight in the down projection's epilogue; either way the k rows
 // (then the shared expert's) are added in a fixed order in fp32 and the sum
 // is rounded to bf16 once.
-DEVI void load8(const void* base, size_t row, int H, int ch, bool bf16, float (&v)[8]) {
-  if (bf16) {
-    const uint4 r = *(const uint4*)((const uint16_t*)base + row * H + 8 * ch);
-    const uint32_t w4[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = bf16_to_f32((uint16_t)(w4[i] & 0xFFFF));
-      v[2 * i + 1] = bf16_to_f32((uint16_t)(w4[i] >> 16));
-    }
-  } else {
-    const float* o = (const float*)base + row * H + 8 * ch;
-    const float4 a = *(const float4*)o, b = *(const float4*)(o + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  }
-}
-
 // Blocks stride over the tokens.  The k slot rows of a chunk are loaded in
-// groups of up to CK (all loads of a group in flight together) and added in
-// ascending j.
-template <int CK>
+// groups of CK, all loads of a group issued before any is used (slots past
+// k re-read the first row and are not added); rows are added in ascending
+// j, then the shared expert's.  WB: bf16 slot rows carrying their weights.
+template <int CK, bool WB>
 __global__ void __launch_bounds__(256) k_combine(CombineArgs c) {
   const int H = c.H, nch = H / 8, k = c.k;
   const int S = c.T * k;
-  const bool wb = c.weighted_bf16 != 0;
   for (int t = blockIdx.x; t < c.T; t += gridDim.x) {
     for (int ch = threadIdx.x; ch < nch; ch += 256) {
       float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       for (int j0 = 0; j0 < k; j0 += CK) {
-        float v[CK][8];
+        int slot[CK];
         float wj[CK];
 #pragma unroll
         for (int u = 0; u < CK; ++u) {
-          if (j0 + u < k) {
-            const int slot = ldu(c.inv + (size_t)t * k + j0 + u);
-            wj[u] = wb ? 1.0f : ldu(c.w + (size_t)t * k + j0 + u);
-            load8(c.out_slot, (size_t)slot, H, ch, wb, v[u]);
-          }
+          const int j = j0 + u < k ? j0 + u : j0;
+          slot[u] = ldu(c.inv + (size_t)t * k + j);
+          wj[u] = WB ? 1.0f : ldu(c.w + (size_t)t * k + j);
         }
+        QrChunk<WB> raw[CK];
+#pragma unroll
+        for (int u = 0; u < CK; ++u) raw[u] = qr_fetch<WB>(c.out_slot, (size_t)slot[u], H, ch);
 #pragma unroll
         for (int u = 0; u < CK; ++u) {
           if (j0 + u < k) {
+            float v[8];
+            qr_unpack<WB>(raw[u], v);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] += wj[u] * v[u][i];
+            for (int i = 0; i < 8; ++i) acc[i] += wj[u] * v[i];
           }
         }
       }
       if (c.shared) {
         float v[8];
-        load8(c.out_slot, (size_t)(S + t), H, ch, wb, v);
+        qr_unpack<WB>(qr_fetch<WB>(c.out_slot, (size_t)(S + t), H, ch), v);
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] += v[i];
       }
@@ -238,8 +210,14 @@ __global__ void __launch_bounds__(256) k_combine(CombineArgs c) {
 hipError_t launch_combine(const CombineArgs& c, hipStream_t st) {
   if (c.T == 0) return hipSuccess;
   const dim3 grid(elementwise_grid(c.T)), block(256);
-  if (c.k <= 2) hipLaunchKernelGGL(k_combine<2>, grid, block, 0, st, c);
-  else if (c.k <= 4) hipLaunchKernelGGL(k_combine<4>, grid, block, 0, st, c);
-  else hipLaunchKernelGGL(k_combine<8>, grid, block, 0, st, c);
+  if (c.weighted_bf16) {
+    if (c.k <= 2) hipLaunchKernelGGL((k_combine<2, true>), grid, block, 0, st, c);
+    else if (c.k <= 4) hipLaunchKernelGGL((k_combine<4, true>), grid, block, 0, st, c);
+    else hipLaunchKernelGGL((k_combine<8, true>), grid, block, 0, st, c);
+  } else {
+    if (c.k <= 2) hipLaunchKernelGGL((k_combine<2, false>), grid, block, 0, st, c);
+    else if (c.k <= 4) hipLaunchKernelGGL((k_combine<4, false>), grid, block, 0, st, c);
+    else hipLaunchKernelGGL((k_combine<8, false>), grid, block, 0, st, c);
+  }
   return hipGetLastError();
 }

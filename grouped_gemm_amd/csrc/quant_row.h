@@ -11,21 +11,42 @@
 #pragma once
 #include "layer.h"
 
+// Raw bytes of one 8-element chunk (bf16: 16 B, fp32: 32 B).  Callers
+// fetch all chunks of a pass first (indices clamped into the row, so no
+// load sits behind a branch) and unpack afterwards, keeping the loads in
+// flight together.
 template <bool IN_BF16>
-DEVI void qr_load8(const void* in, size_t row, int n, int c, float (&v)[8]) {
-  if (IN_BF16) {
-    const uint4 raw = *(const uint4*)((const uint16_t*)in + row * n + 8 * c);
-    const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+struct QrChunk {
+  uint4 w[IN_BF16 ? 1 : 2];
+};
+
+template <bool IN_BF16>
+DEVI QrChunk<IN_BF16> qr_fetch(const void* in, size_t row, int n, int c) {
+  QrChunk<IN_BF16> r;
+  if constexpr (IN_BF16) {
+    r.w[0] = *(const uint4*)((const uint16_t*)in + row * n + 8 * c);
+  } else {
+    const uint4* p = (const uint4*)((const float*)in + row * n + 8 * c);
+    r.w[0] = p[0];
+    r.w[1] = p[1];
+  }
+  return r;
+}
+
+template <bool IN_BF16>
+DEVI void qr_unpack(const QrChunk<IN_BF16>& r, float (&v)[8]) {
+  if constexpr (IN_BF16) {
+    const uint32_t w4[4] = {r.w[0].x, r.w[0].y, r.w[0].z, r.w[0].w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      v[2 * i] = bf16_to_f32((uint16_t)(w4[i] & 0xFFFF));
-      v[2 * i + 1] = bf16_to_f32((uint16_t)(w4[i] >> 16));
+      v[2 * i] = __uint_as_float(w4[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w4[i] & 0xFFFF0000u);
     }
   } else {
-    const float* src = (const float*)in + row * n + 8 * c;
-    const float4 a = *(const float4*)src, b = *(const float4*)(src + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    v[0] = __uint_as_float(r.w[0].x); v[1] = __uint_as_float(r.w[0].y);
+    v[2] = __uint_as_float(r.w[0].z); v[3] = __uint_as_float(r.w[0].w);
+    v[4] = __uint_as_float(r.w[1].x); v[5] = __uint_as_float(r.w[1].y);
+    v[6] = __uint_as_float(r.w[1].z); v[7] = __uint_as_float(r.w[1].w);
   }
 }
 
@@ -36,39 +57,57 @@ DEVI float qr_amax8(const float (&v)[8]) {
   return m;
 }
 
-// a / s rounded to nearest, from r = RN(1/s) and one residual step:
-// q0 = RN(a*r) is within an ulp of a/s, the residual e = a - q0*s is exact
-// and RN(q0 + e*r) = RN(a/s) (Markstein's theorem on FMA-based division),
-// provided no intermediate underflows or overflows -- which holds for
-// s in [2^-60, 2^60] and |a| >= 2^-60.  e = 0 means q0 is exact (this also
-// keeps the sign of a zero a).
-DEVI float qr_div_fast(float a, float s, float r) {
-  const float q0 = a * r;
-  const float e = __builtin_fmaf(-q0, s, a);
-  return e == 0.f ? q0 : __builtin_fmaf(e, r, q0);
+// FP8 scale of a group maximum m > 0: s = RN(m / 448), by one residual
+// step from the constant RN(1/448) (Markstein's theorem on FMA-based
+// division: q0 = RN(m*y) is within an ulp of m/448, the residual
+// e = m - 448*q0 is exact and RN(q0 + e*y) = RN(m/448) while nothing
+// underflows or overflows, which holds for m in [2^-40, 2^68]).
+DEVI float qr_scale448(float m) {
+  constexpr float y = 1.0f / 448.0f;
+  const float q0 = m * y;
+  const float e = __builtin_fmaf(-q0, 448.0f, m);
+  return __builtin_fmaf(e, y, q0);
 }
 
-// the IEEE quotients of a chunk (outside the residual step's domain; kept
-// out of line so the common path stays short)
+// The codes of one chunk need e4m3_rne(RN(v/s)).  For s in [2^-49, 2^60]
+// the same residual step from r = RN(1/s) gives RN(v/s) exactly for every
+// |v| >= 2^-60 (and v = 0, whose sign copysign restores); for smaller
+// nonzero |v| the quotient is below 2^-11, which rounds to an e4m3 zero of
+// v's sign whichever way its last bits fall.  Groups outside that range of
+// s divide.
+DEVI bool qr_fast_scale(float s) { return s >= 0x1p-49f && s <= 0x1p60f; }
+
+DEVI uint2 qr_codes_fast(const float (&v)[8], float s) {
+  const float r = 1.0f / s;
+  float o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float q0 = v[i] * r;
+    const float e = __builtin_fmaf(-q0, s, v[i]);
+    o[i] = __builtin_copysignf(__builtin_fmaf(e, r, q0), v[i]);
+  }
+  return make_uint2(cvt4_e4m3(o[0], o[1], o[2], o[3]), cvt4_e4m3(o[4], o[5], o[6], o[7]));
+}
+
+// the IEEE quotients of a chunk (out of line: rare)
 __device__ __attribute__((noinline)) uint2 qr_codes_ieee(float4 a, float4 b, float s) {
   return make_uint2(cvt4_e4m3(a.x / s, a.y / s, a.z / s, a.w / s),
                     cvt4_e4m3(b.x / s, b.y / s, b.z / s, b.w / s));
 }
 
-// codes of one chunk with the FP8 scale s: v/s rounded to nearest (the
-// IEEE quotient), by the residual step where its domain holds, else by the
-// division itself
+__device__ __attribute__((noinline)) float qr_div448_ieee(float m) { return m / 448.0f; }
+
+// scale of group maximum m (1 when m = 0)
+DEVI float qr_scale(float m) {
+  if (m <= 0.f) return 1.0f;
+  if (m >= 0x1p-40f && m <= 0x1p68f) return qr_scale448(m);
+  return qr_div448_ieee(m);
+}
+
+// codes of one chunk with the FP8 scale s: e4m3_rne(clamp(v/s))
 DEVI uint2 qr_codes_div(const float (&v)[8], float s) {
-  bool fast = s >= 0x1p-60f && s <= 0x1p60f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) fast = fast && (fabsf(v[i]) >= 0x1p-60f || v[i] == 0.f);
-  if (!fast)
-    return qr_codes_ieee(make_float4(v[0], v[1], v[2], v[3]), make_float4(v[4], v[5], v[6], v[7]), s);
-  const float r = 1.0f / s;
-  float o[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = qr_div_fast(v[i], s, r);
-  return make_uint2(cvt4_e4m3(o[0], o[1], o[2], o[3]), cvt4_e4m3(o[4], o[5], o[6], o[7]));
+  if (qr_fast_scale(s)) return qr_codes_fast(v, s);
+  return qr_codes_ieee(make_float4(v[0], v[1], v[2], v[3]), make_float4(v[4], v[5], v[6], v[7]), s);
 }
 
 // Per-token scale: the whole row shares one amax.  Rows of up to 4096
@@ -78,18 +117,21 @@ DEVI void quant_row_wave_token(const QuantArgs& q, int row, int lane) {
   const int n = q.n, nch = n / 8;
   uint8_t* qrow = q.q + (size_t)row * n;
   if (nch <= 8 * 64) {
+    QrChunk<IN_BF16> raw[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = lane + 64 * j;
+      raw[j] = qr_fetch<IN_BF16>(q.in, row, n, c < nch ? c : nch - 1);
+    }
     float v[8][8];
     float m = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int c = lane + 64 * j;
-      if (c < nch) {
-        qr_load8<IN_BF16>(q.in, row, n, c, v[j]);
-        m = fmaxf(m, qr_amax8(v[j]));
-      }
+      qr_unpack<IN_BF16>(raw[j], v[j]);
+      if (lane + 64 * j < nch) m = fmaxf(m, qr_amax8(v[j]));
     }
     m = wave_max(m);
-    const float s = m > 0.f ? m / 448.0f : 1.0f;
+    const float s = qr_scale(m);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int c = lane + 64 * j;
@@ -101,14 +143,14 @@ DEVI void quant_row_wave_token(const QuantArgs& q, int row, int lane) {
   float m = 0.f;
   for (int c = lane; c < nch; c += 64) {
     float v[8];
-    qr_load8<IN_BF16>(q.in, row, n, c, v);
+    qr_unpack<IN_BF16>(qr_fetch<IN_BF16>(q.in, row, n, c), v);
     m = fmaxf(m, qr_amax8(v));
   }
   m = wave_max(m);
-  const float s = m > 0.f ? m / 448.0f : 1.0f;
+  const float s = qr_scale(m);
   for (int c = lane; c < nch; c += 64) {
     float v[8];
-    qr_load8<IN_BF16>(q.in, row, n, c, v);
+    qr_unpack<IN_BF16>(qr_fetch<IN_BF16>(q.in, row, n, c), v);
     *(uint2*)(qrow + 8 * c) = qr_codes_div(v, s);
   }
   if (lane == 0) ((float*)q.scale)[row] = s;
@@ -124,16 +166,18 @@ DEVI void quant_row_wave_group(const QuantArgs& q, int row, int lane) {
   const int n = q.n, nch = n / 8;
   uint8_t* qrow = q.q + (size_t)row * n;
   for (int c0 = 0; c0 < nch; c0 += 64 * QP) {
+    QrChunk<IN_BF16> raw[QP];
+#pragma unroll
+    for (int u = 0; u < QP; ++u) {
+      const int c = c0 + 64 * u + lane;
+      raw[u] = qr_fetch<IN_BF16>(q.in, row, n, c < nch ? c : nch - 1);
+    }
     float v[QP][8];
     float m[QP];
 #pragma unroll
     for (int u = 0; u < QP; ++u) {
-      const int c = c0 + 64 * u + lane;
-      m[u] = 0.f;
-      if (c < nch) {
-        qr_load8<IN_BF16>(q.in, row, n, c, v[u]);
-        m[u] = qr_amax8(v[u]);
-      }
+      qr_unpack<IN_BF16>(raw[u], v[u]);
+      m[u] = c0 + 64 * u + lane < nch ? qr_amax8(v[u]) : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < QP; ++u) {
@@ -154,7 +198,7 @@ DEVI void quant_row_wave_group(const QuantArgs& q, int row, int lane) {
             cvt4_e4m3(v[u][4] * inv, v[u][5] * inv, v[u][6] * inv, v[u][7] * inv));
         if ((c & 3) == 0) ((uint8_t*)q.scale)[(size_t)row * (n / 32) + c / 4] = (uint8_t)(ex + 127);
       } else {
-        const float s = m[u] > 0.f ? m[u] / 448.0f : 1.0f;
+        const float s = qr_scale(m[u]);
         *(uint2*)(qrow + 8 * c) = qr_codes_div(v[u], s);
         if ((c & 15) == 0) ((float*)q.scale)[(size_t)row * (n / 128) + c / 16] = s;
       }

@@ -675,12 +675,13 @@ __global__ void __launch_bounds__(1024) k_dispatch_chunk(DispatchArgs d) {
   }
 }
 
-// Pass 2, block c: from the chunk histograms, each group's total and its
-// rows in the chunks before c (P = 1024/E threads per group split the
+// Pass 2.  Block c < nch: from the chunk histograms, each group's total and
+// its rows in the chunks before c (P = 1024/E threads per group split the
 // chunks); the exclusive scan of the totals gives the group starts, and the
-// chunk's slots land at start + earlier rows + rank.  Block 0 also writes
-// counts, m_indptr, the active list, the configuration and its block table.
-// ids_in holds the routed ids.
+// chunk's slots land at start + earlier rows + rank.  Block nch writes
+// counts, m_indptr, the active list, the configuration and its block table
+// (and the shared group's gather entries), so no placing block waits for
+// it.  ids_in holds the routed ids.
 __global__ void __launch_bounds__(1024) k_dispatch_place(DispatchArgs d) {
   extern __shared__ int32_t smem[];
   const int E = d.E, G = E + d.shared, k = d.k, TC = chunk_tokens(k);
@@ -692,6 +693,12 @@ __global__ void __launch_bounds__(1024) k_dispatch_place(DispatchArgs d) {
   int32_t* tiles_buf = flag_buf + G;   // [G]
   int32_t* part = tiles_buf + G;       // [2][1024]
   const int c = blockIdx.x, tid = threadIdx.x;
+  const bool table = c == nch;
+  // this thread's slot: its id and rank load first, in flight meanwhile
+  const int t0 = c * TC, ns = table ? 0 : min(TC, d.T - t0) * k, p = t0 * k + tid;
+  const bool mine = tid < ns;
+  const int e = mine ? d.ids_in[p] : -1;
+  const int rank = mine ? d.inv[p] : 0;
   const int P = 1024 / E, g = tid % E, q = tid / E;
   int tot = 0, pre = 0;
   if (q < P) {
@@ -723,27 +730,25 @@ __global__ void __launch_bounds__(1024) k_dispatch_place(DispatchArgs d) {
   }
   if (tid == 0 && d.shared) cnt[E] = d.T;
   __syncthreads();
-  if (c == 0) {
+  if (table) {
     finalize_dispatch(d, cnt, scan_buf, flag_buf, tiles_buf, G, S + (d.shared ? d.T : 0));
-  } else {
-    for (int i = tid; i < G; i += blockDim.x) scan_buf[i] = cnt[i];
-    __syncthreads();
-    wave0_exclusive_scan(scan_buf, G, nullptr);
+    if (d.shared)
+      for (int t = tid; t < d.T; t += blockDim.x) d.gather[S + t] = t * k;
+    return;
   }
+  for (int i = tid; i < G; i += blockDim.x) scan_buf[i] = cnt[i];
   __syncthreads();
-  const int t0 = c * TC, ns = min(TC, d.T - t0) * k, p = t0 * k + tid;
-  if (tid < ns) {
-    const int e = d.ids_in[p];
+  wave0_exclusive_scan(scan_buf, G, nullptr);
+  __syncthreads();
+  if (mine) {
     if ((unsigned)e < (unsigned)E) {
-      const int slot = scan_buf[e] + pre_l[e] + d.inv[p];
+      const int slot = scan_buf[e] + pre_l[e] + rank;
       d.gather[slot] = p;
       d.inv[p] = slot;
     } else {
       d.inv[p] = -1;
     }
   }
-  if (d.shared)
-    for (int t = c * 1024 + tid; t < d.T; t += nch * 1024) d.gather[S + t] = t * k;
 }
 
 // ---------------------------------------------------------------- host launchers
@@ -807,8 +812,8 @@ hipError_t launch_dispatch(const DispatchArgs& d, hipStream_t st) {
   d2.fq.R = 0;
   d2.ids_in = d.scores ? d.ids : d.ids_in;
   d2.scores = nullptr;
-  hipLaunchKernelGGL(k_dispatch_place, dim3(nch), dim3(1024), sizeof(int32_t) * (5 * G + 2048), st,
-                     d2);
+  hipLaunchKernelGGL(k_dispatch_place, dim3(nch + 1), dim3(1024), sizeof(int32_t) * (5 * G + 2048),
+                     st, d2);
   return hipGetLastError();
 }
 

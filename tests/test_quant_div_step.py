@@ -1,6 +1,7 @@
-"""Host check of the division step the GPU quantiser takes: a correctly
-rounded reciprocal and one FMA residual step give the IEEE quotient bit for
-bit on the domain where the kernel uses them (it divides elsewhere)."""
+"""Host check of the division steps the GPU quantiser takes: the scale
+m/448 and the quotients v/s from a correctly rounded reciprocal and one FMA
+residual step equal the IEEE results wherever the kernel uses them (it
+divides elsewhere), up to the sign-correct e4m3 zeros of tiny quotients."""
 import os
 import shutil
 import subprocess
@@ -17,5 +18,5 @@ def test_residual_step_division_is_exact(tmp_path):
                     os.path.join(HERE, "cpu_checks", "div_step.c"), "-lm"], check=True)
     out = subprocess.run([exe, "6000000"], check=True, capture_output=True, text=True).stdout
     checked, bad = map(int, out.split())
-    assert checked > 1_000_000
+    assert checked > 2_000_000
     assert bad == 0
