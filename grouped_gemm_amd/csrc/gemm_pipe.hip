@@ -370,32 +370,47 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
     lds_dma4(cs_src, cs_dst);
   };
 
-  // one stage into ring slot `slot`, then advance the bases by one K step
-  auto issue = [&](int slot) {
+  // One stage into ring slot `slot` is NP DMA instructions per wave (token
+  // rows, weight rows, then the step's scales); part k issues the k-th.
+  // The main loop spreads the parts between its MFMA groups, so the
+  // address unit streams the next stage while the matrix cores work;
+  // advance() then moves the bases by one K step.
+  constexpr int NSC = F == F_FP8_BLK ? 1 : (F == F_MX ? 2 : 0);
+  constexpr int NP = NTOK + NWT + NSC;
+  constexpr bool SPREAD = F != F_MX;   // parts spread over the MFMA groups
+  auto issue_part = [&](int slot, int k) {
     uint8_t* st = lds + slot * PC::STAGE;
-#pragma unroll
-    for (int i = 0; i < NTOK; ++i) lds_dma16(ib_tok + toff[i], st + (wave * NTOK + i) * 1024);
-    // the offset is re-materialised as a 32-bit value in the loop, so the
-    // loads take the scalar base + 32-bit lane offset form
-    uint32_t wo = woff;
-    asm volatile("" : "+v"(wo));
-#pragma unroll
-    for (int jj = 0; jj < NWT; ++jj)
+    if (k < NTOK) {
+      lds_dma16(ib_tok + toff[k], st + (wave * NTOK + k) * 1024);
+    } else if (k < NTOK + NWT) {
+      const int jj = k - NTOK;
+      // the offset is re-materialised as a 32-bit value, so the loads take
+      // the scalar base + 32-bit lane offset form
+      uint32_t wo = woff;
+      asm volatile("" : "+v"(wo));
       lds_dma16(ib_w + (size_t)jj * RPI * wrow + wo, st + PC::TOKB + (wave * NWT + jj) * 1024);
-    if constexpr (F == F_FP8_BLK) {
+    } else if constexpr (F == F_FP8_BLK) {
       if (wave == NW - 1)   // the step's weight block scales (lanes 0 and 1)
         lds_dma4(ib_ws, st + PC::TOKB + PC::WTB + (NW - 1) * 256);
       else
         lds_dma4(ib_a + aoff, st + PC::TOKB + PC::WTB + wave * 256);
+    } else if constexpr (F == F_MX) {
+      if (k == NTOK + NWT)
+        lds_dma4(ib_a + aoff, st + PC::TOKB + PC::WTB + wave * 256);
+      else
+        lds_dma4(ib_ws + wsoff, st + PC::TOKB + PC::WTB + PC::ASB + wave * 256);
     }
-    if constexpr (F == F_MX) {
-      lds_dma4(ib_a + aoff, st + PC::TOKB + PC::WTB + wave * 256);
-      lds_dma4(ib_ws + wsoff, st + PC::TOKB + PC::WTB + PC::ASB + wave * 256);
-    }
+  };
+  auto advance = [&]() {
     ib_tok += 128;
     ib_w += PC::WROWB;
     ib_a += 4;
     ib_ws += 4;
+  };
+  auto issue = [&](int slot) {
+#pragma unroll
+    for (int k = 0; k < NP; ++k) issue_part(slot, k);
+    advance();
   };
 
   // ---- start: row indices of the first item, then the first D stages
@@ -438,16 +453,24 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
       else wait_vm_ab<LOADS, 0, NSTAGE - 3>(ahead, false);
     }
     raw_barrier();
-    if (ji < nit) {
+    // the stage this step issues (into the slot every wave has finished
+    // reading: the barrier above), spread over the MFMA groups below
+    const bool iss = ji < nit;
+    const int islot = is_;
+    if (iss) {
       if (si == 0) {
         begin_item(ji);
         meta_rows(ji + 1);
       }
-      issue(is_);
       is_ = is_ + 1 == NSTAGE ? 0 : is_ + 1;
       if (++si == ns) {
         si = 0;
         ++ji;
+      }
+      // MX weights (half the bytes per row) measure faster issued at once
+      if constexpr (!SPREAD) {
+#pragma unroll
+        for (int k = 0; k < NP; ++k) issue_part(islot, k);
       }
     }
     const uint8_t* st = lds + cs * PC::STAGE;
@@ -496,12 +519,19 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
       }
       constexpr int NC = NM * RT;
       f32x4 d[2][TT];
+      constexpr int PPC = (NP + NC - 1) / NC;   // DMA parts per MFMA group
 #pragma unroll
       for (int c = 0; c <= NC; ++c) {
         if (c < NC) {
+          if (iss) {
+#pragma unroll
+            for (int k = c * PPC; k < (c + 1) * PPC && k < NP; ++k) issue_part(islot, k);
+          }
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int t = 0; t < TT; ++t)
             d[c & 1][t] = mfma_f8(afr[c / RT][c % RT], bfr[t], (f32x4){0.f, 0.f, 0.f, 0.f});
+          __builtin_amdgcn_sched_barrier(0);
         }
         if (c > 0) {
           const int pc = c - 1, pm = pc / RT, prt = pc % RT;
@@ -515,10 +545,18 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
 #pragma unroll
         for (int t = 0; t < TT; ++t) sbx[t] = (st + PC::TOKB + PC::WTB)[(trow0 + t * 16 + r16) * 4 + lg];
       }
+      constexpr int NC = NM * RT;
+      constexpr int PPC = (NP + NC - 1) / NC;   // DMA parts per MFMA group
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+        for (int rt = 0; rt < RT; ++rt) {
+          const int c = m * RT + rt;
+          if (SPREAD && iss) {
+#pragma unroll
+            for (int k = c * PPC; k < (c + 1) * PPC && k < NP; ++k) issue_part(islot, k);
+          }
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int t = 0; t < TT; ++t) {
             if constexpr (F == F_MX)
@@ -526,7 +564,10 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
             else
               acc[m][rt][t] = mfma_f8(afr[m][rt], bfr[t], acc[m][rt][t]);
           }
+          __builtin_amdgcn_sched_barrier(0);
+        }
     }
+    if (iss) advance();
     if (++s < ns) continue;
 
     // ------------------------------------------------------------ epilogue
