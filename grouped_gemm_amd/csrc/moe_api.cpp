@@ -324,7 +324,9 @@ int enqueue_layer(moe_ws* ws, const moe_weights* w, const uint16_t* x, const flo
                    fused_requant ? ws->at<void>(L.hs) : nullptr, S_tot, st),
           "gate/up grouped GEMM launch");
   HIP_TRY(mark(2, 1), "event record");
-  if (quant) {
+  // with the fused requantisation only the streaming configuration leaves
+  // fp32 h behind; skip the launch when that configuration cannot occur
+  if (quant && (!fused_requant || candidates(ws, S_tot).stream)) {
     QuantArgs q{ws->at<void>(L.h), 0, S_tot, d.inter, nullptr, ws->at<uint8_t>(L.hq),
                 ws->at<void>(L.hs), d.a_format};
     if (fused_requant) {   // only the streaming configuration left fp32 h behind
