@@ -172,6 +172,7 @@ struct PipeCfg {
   static_assert(F != F_MX || !GATEUP || NR == 256, "MX gate/up scale rows: one matrix per wave pair");
   static_assert((NSTAGE - 2) * (LOADS + NMETA) <= 63, "vmcnt range");
   static_assert(NM_ * NBC <= NW * 64 && NBC % 64 == 0, "channel scales: one per lane of the waves");
+  static_assert(RT % 2 == 0 || BM < 128 || (GATEUP && F != F_FP8_BLK), "regrouped stores pair 16-channel tiles");
 };
 
 // byte offset of (row, 16-byte chunk) in a swizzled [rows][128 B] block
@@ -591,7 +592,45 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
           }
       }
     }
+    // Prefill tiles regroup their outputs for wider stores (decode tiles,
+    // whose rows are few, measured faster with the direct stores).
+    constexpr bool REGROUP = BM >= 128;
     if constexpr (!GATEUP) {
+      if (REGROUP && p.row_w) {
+        // Weighted bf16 slot rows.  The MFMA layout gives a lane 4 channels
+        // of each 16-channel tile (16 rows x 32 B per store); four shuffles
+        // per dword regroup them so lane lg holds channels 8lg..8lg+7 of
+        // each 32-channel half, and each 16-byte store covers 16 rows x 64 B.
+        const int sA = r16 + 32 * (lg & 1), sB = sA + 16;   // lanes holding its channels
+        const bool hiq = lg >= 2;                            // second 16-channel tile of the half
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+          const int r = trow0 + t * 16 + r16;
+          const int slot = m0 + r;
+          const float w = (r < M && slot < p.row_w_n) ? rwj[r] : 1.0f;
+          uint32_t pk[RT][2];
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            const f32x4 vw = acc[0][rt][t] * w;
+            pk[rt][0] = (uint32_t)f32_to_bf16(vw[0]) | ((uint32_t)f32_to_bf16(vw[1]) << 16);
+            pk[rt][1] = (uint32_t)f32_to_bf16(vw[2]) | ((uint32_t)f32_to_bf16(vw[3]) << 16);
+          }
+#pragma unroll
+          for (int h = 0; h < RT / 2; ++h) {
+            uint32_t o[4];
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+              const uint32_t a0 = __shfl(pk[2 * h][x], sA, 64), a1 = __shfl(pk[2 * h + 1][x], sA, 64);
+              const uint32_t b0 = __shfl(pk[2 * h][x], sB, 64), b1 = __shfl(pk[2 * h + 1][x], sB, 64);
+              o[x] = hiq ? a1 : a0;
+              o[2 + x] = hiq ? b1 : b0;
+            }
+            if (r < M)
+              *(uint4*)((uint16_t*)p.out + (size_t)slot * N + c0 + 32 * h + 8 * lg) =
+                  make_uint4(o[0], o[1], o[2], o[3]);
+          }
+        }
+      } else {
 #pragma unroll
       for (int t = 0; t < TT; ++t) {
         const int r = trow0 + t * 16 + r16;
@@ -612,6 +651,7 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
           }
         }
       }
+      }
     } else {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
@@ -628,7 +668,7 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) *(f32x4*)(orow + c0 + rt * 16 + 4 * lg) = acc[0][rt][t];
         }
-      } else if constexpr (F == F_FP8_BLK) {
+      } else if constexpr (F == F_FP8_BLK && REGROUP) {
         // 1x128 group = the item's 128 channels, spread over the WN waves
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
@@ -644,7 +684,50 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
         // LDS-only exchange: the stage loads in flight must not be waited for
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         raw_barrier();
-          const int nb = cur.cbase / 128;
+        const int nb = cur.cbase / 128;
+        // codes regrouped as in the down projection's store: lane lg writes
+        // channels 8lg..8lg+7 of each 32-channel half (16 rows x 32 B per
+        // store instead of 16 rows x 16 B)
+        const int sA = r16 + 32 * (lg & 1), sB = sA + 16;
+        const bool hiq = lg >= 2;
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+          const int r = trow0 + t * 16 + r16;
+          float a = 0.f;
+#pragma unroll
+          for (int w = 0; w < WN; ++w) a = fmaxf(a, amax_l[w * BM + r]);
+          const float sc = a > 0.f ? a / 448.0f : 1.0f;
+          const float isc = 1.0f / sc;
+          uint32_t cd[RT];
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            const f32x4 h = acc[0][rt][t];
+            cd[rt] = cvt4_e4m3(h[0] * isc, h[1] * isc, h[2] * isc, h[3] * isc);
+          }
+          uint8_t* orow = (uint8_t*)p.out + (size_t)(m0 + r) * N;
+#pragma unroll
+          for (int hh = 0; hh < RT / 2; ++hh) {
+            const uint32_t a0 = __shfl(cd[2 * hh], sA, 64), a1 = __shfl(cd[2 * hh + 1], sA, 64);
+            const uint32_t b0 = __shfl(cd[2 * hh], sB, 64), b1 = __shfl(cd[2 * hh + 1], sB, 64);
+            if (r < M) *(uint2*)(orow + c0 + 32 * hh + 8 * lg) = make_uint2(hiq ? a1 : a0, hiq ? b1 : b0);
+          }
+          if (r < M && wn == 0 && lg == 0) ((float*)p.out_scale)[(size_t)(m0 + r) * (N / 128) + nb] = sc;
+        }
+      } else if constexpr (F == F_FP8_BLK) {
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+          float mx = 0.f;
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(acc[0][rt][t][i]));
+          mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+          if (lg == 0) amax_l[wn * BM + trow0 + t * 16 + r16] = mx;
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        raw_barrier();
+        const int nb = cur.cbase / 128;
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
           const int r = trow0 + t * 16 + r16;
