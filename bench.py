@@ -44,7 +44,7 @@ METRIC = ("MoE layer µs + active TFLOP/s / HBM GB/s (FP8 W8A8) at 32, 128, 8192
 # figure is only reported while the kernel sources still hash to the value
 # they had when the counters were taken.
 TRAFFIC = {
-    ("mixtral", 128, 2): {"bytes": 962548567, "src_sha": "743efb5c33e287c2"},
+    ("mixtral", 128, 2): {"bytes": 962553351, "src_sha": "6ee7d8f65d5e47fa"},
 }
 KERNEL_SRC = ["grouped_gemm_amd/csrc/gemm_pipe.hip", "grouped_gemm_amd/csrc/common.h",
               "grouped_gemm_amd/csrc/layer.h"]
