@@ -10,6 +10,8 @@ import numpy as np
 import pytest
 import torch
 
+import grouped_gemm_amd as g
+
 import moe_synth as ms
 import oracle
 from gpu_util import (bf16_to_f64, check_routing, dev_weights, relerr, run_layer, say, tol_for,
@@ -216,3 +218,23 @@ def test_layer_every_config_matches_oracle(name, sh, T):
         assert err <= tol_for(sh), (cfg, err)
         outs.append(y)
     ws.force_config(-1)
+
+
+def test_layer_with_no_tokens_is_a_no_op():
+    """An empty batch is a valid call that launches nothing; the workspace
+    serves a real batch right after it."""
+    sh = SMALL[2][1]
+    ws = workspace(sh, 16)
+    W = ms.gen_weights(sh)
+    dW = dev_weights(W)
+    x = torch.zeros(0, sh.hidden, dtype=torch.int16, device="cuda")
+    s = torch.zeros(0, sh.experts, dtype=torch.float32, device="cuda")
+    y = torch.zeros(0, sh.hidden, dtype=torch.int16, device="cuda")
+    g.layer_forward(ws, dW, x, s, y)
+    torch.cuda.synchronize()
+    B = ms.gen_batch(sh, 4)
+    yy = run_layer(ws, dW, B.x_bits, B.scores)
+    ids, w = oracle.route(B.scores, sh.top_k, sh.score_fn)
+    ref = oracle.layer_forward(W, B.x_bits, ids, w)
+    err = np.linalg.norm(bf16_to_f64(yy) - ref) / np.linalg.norm(ref)
+    assert err < tol_for(sh)

@@ -169,3 +169,44 @@ def test_dispatch_drops_out_of_range_ids(E, k, T):
     np.testing.assert_array_equal(d_i.cpu().numpy(), indptr)
     np.testing.assert_array_equal(d_g.cpu().numpy()[: gather.size], gather)
     np.testing.assert_array_equal(d_v.cpu().numpy(), inv)
+
+
+@pytest.mark.parametrize("E,k,T", [(256, 16, 70), (40, 16, 33), (256, 8, 513)])
+def test_route_topk_at_the_k_limit(E, k, T):
+    """k up to 16 (every lane of a 16-lane routing row holds a choice), with
+    exact ties; ids bit-exact, weights within 1e-6."""
+    say("route k-limit", E, k, T)
+    rng = np.random.default_rng(E * 7 + k * 131 + T)
+    s = rng.standard_normal((T, E)).astype(np.float32)
+    s[: T // 3, : 2 * k] = np.round(s[: T // 3, : 2 * k])   # many exact ties
+    ids_ref, w_ref = oracle.route(s, k, ms.SCORE_SOFTMAX)
+    ids = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    g.route_topk(dev(s), k, ms.SCORE_SOFTMAX, ids, w)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ids.cpu().numpy(), ids_ref)
+    np.testing.assert_allclose(w.cpu().numpy().astype(np.float64), w_ref, rtol=0, atol=1e-6)
+
+
+@pytest.mark.parametrize("E,k,T", [(256, 8, 129), (256, 8, 256), (64, 5, 409), (48, 16, 65),
+                                   (256, 8, 4096)])
+def test_dispatch_chunk_boundaries(E, k, T):
+    """The chunked path (chunks of floor(1024/k) whole tokens) at and just
+    past chunk boundaries, including a last chunk of one token."""
+    say("dispatch chunks", E, k, T)
+    rng = np.random.default_rng(E + 3 * k + 5 * T)
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    counts, indptr, gather, inv = oracle.dispatch(ids, E)
+    sh = ms.small_shape("qwen", hidden=256, inter=256, experts=E, top_k=k)
+    ws = workspace(sh, T)
+    S = T * k
+    d_c = torch.empty(E, dtype=torch.int32, device="cuda")
+    d_i = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    d_g = torch.empty(S, dtype=torch.int32, device="cuda")
+    d_v = torch.empty(S, dtype=torch.int32, device="cuda")
+    g.dispatch(ws, dev(ids), E, d_c, d_i, d_g, d_v)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(d_c.cpu().numpy(), counts)
+    np.testing.assert_array_equal(d_i.cpu().numpy(), indptr)
+    np.testing.assert_array_equal(d_g.cpu().numpy(), gather)
+    np.testing.assert_array_equal(d_v.cpu().numpy(), inv)
