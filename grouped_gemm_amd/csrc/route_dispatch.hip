@@ -97,8 +97,9 @@ DEVI void route_row16(const float* row, bool tv, int E, int k, int score_fn, int
 
 // One thread routes one token (small expert counts, E <= 32): k passes over
 // the E scores, each taking the largest remaining key (score, then lowest
-// index) -- exactly the order route_row16 produces.  Compact rolled
-// loops, for scores staged in LDS.
+// index) -- exactly the order route_row16 produces.  Compact rolled loops,
+// for scores staged in LDS; the choices go to ids_lds, from which a second
+// pass forms the renormalised weights (no read-back of global memory).
 DEVI void route_token_thread(const float* row, int E, int k, int score_fn, int32_t* ids_out,
                              float* w_out, int32_t* ids_lds) {
   uint32_t taken = 0;
@@ -115,20 +116,27 @@ DEVI void route_token_thread(const float* row, int E, int k, int score_fn, int32
       }
     }
     taken |= 1u << best;
-    ids_out[j] = best;
-    if (ids_lds) ids_lds[j] = best;
+    ids_lds[j] = best;
     const float l = row[best];
     if (j == 0) top = l;
+    sum += score_fn == MOE_SCORE_SOFTMAX ? expf(l - top)
+           : score_fn == MOE_SCORE_SIGMOID ? 1.0f / (1.0f + expf(-l)) : l;
+  }
+  for (int j = 0; j < k; ++j) {
+    const int id = ids_lds[j];
+    const float l = row[id];
     const float x = score_fn == MOE_SCORE_SOFTMAX ? expf(l - top)
                     : score_fn == MOE_SCORE_SIGMOID ? 1.0f / (1.0f + expf(-l)) : l;
-    w_out[j] = x;
-    sum += x;
+    ids_out[j] = id;
+    w_out[j] = x / sum;
   }
-  for (int j = 0; j < k; ++j) w_out[j] = w_out[j] / sum;
 }
 
 // The same selection with the token's scores held in registers (all loads
-// issued at once), for scores read from global memory.
+// issued at once), for scores read from global memory.  The pass loop stays
+// rolled (short code); the selection runs twice -- once for the weights'
+// sum, once to write ids and renormalised weights -- rather than reading
+// the unnormalised weights back from global memory.
 DEVI void route_token_regs(const float* row, int E, int k, int score_fn, int32_t* ids_out,
                            float* w_out, int32_t* ids_lds) {
   float v[SMALL_E_THREAD_ROUTE];
@@ -137,32 +145,35 @@ DEVI void route_token_regs(const float* row, int E, int k, int score_fn, int32_t
   uint32_t key[SMALL_E_THREAD_ROUTE];
 #pragma unroll
   for (int e = 0; e < SMALL_E_THREAD_ROUTE; ++e) key[e] = score_key(v[e]);
-  uint32_t taken = 0;
   float top = 0.f, sum = 0.f;
-  // the pass loop stays rolled (short code); unnormalised weights go to
-  // w_out and are divided by their sum once all k are known
-  for (int j = 0; j < k; ++j) {
-    int best = -1;
-    uint32_t bk = 0;
-    float bv = 0.f;
+  for (int pass = 0; pass < 2; ++pass) {
+    uint32_t taken = 0;
+    for (int j = 0; j < k; ++j) {
+      int best = -1;
+      uint32_t bk = 0;
+      float bv = 0.f;
 #pragma unroll
-    for (int e = 0; e < SMALL_E_THREAD_ROUTE; ++e) {
-      const bool ok = e < E && !((taken >> e) & 1u) && (best < 0 || key[e] > bk);
-      best = ok ? e : best;
-      bk = ok ? key[e] : bk;
-      bv = ok ? v[e] : bv;
+      for (int e = 0; e < SMALL_E_THREAD_ROUTE; ++e) {
+        const bool ok = e < E && !((taken >> e) & 1u) && (best < 0 || key[e] > bk);
+        best = ok ? e : best;
+        bk = ok ? key[e] : bk;
+        bv = ok ? v[e] : bv;
+      }
+      taken |= 1u << best;
+      if (j == 0) top = bv;
+      const float x = score_fn == MOE_SCORE_SOFTMAX ? expf(bv - top)
+                      : score_fn == MOE_SCORE_SIGMOID ? 1.0f / (1.0f + expf(-bv)) : bv;
+      if (pass == 0) {
+        sum += x;
+      } else {
+        ids_out[j] = best;
+        w_out[j] = x / sum;
+        if (ids_lds) ids_lds[j] = best;
+      }
     }
-    taken |= 1u << best;
-    ids_out[j] = best;
-    if (ids_lds) ids_lds[j] = best;
-    if (j == 0) top = bv;
-    const float x = score_fn == MOE_SCORE_SOFTMAX ? expf(bv - top)
-                    : score_fn == MOE_SCORE_SIGMOID ? 1.0f / (1.0f + expf(-bv)) : bv;
-    w_out[j] = x;
-    sum += x;
   }
-  for (int j = 0; j < k; ++j) w_out[j] = w_out[j] / sum;
 }
+
 
 template <int QF>
 __global__ void __launch_bounds__(256) k_route_thread(const float* __restrict__ scores, int T, int E,
@@ -513,13 +524,14 @@ __global__ void __launch_bounds__(256) k_dispatch_tiny(DispatchArgs d) {
     const int n = d.T * d.E;
     const float* src = d.scores;
     if (n <= TINY_SCORE_LDS) {
-      // four loads in flight per lane and pass
-      for (int i = lane; i < n; i += 256) {
-        float v[4];
+      // sixteen loads in flight per lane and pass (indices clamped into
+      // the array, so no load waits behind a branch)
+      for (int i = lane; i < n; i += 1024) {
+        float v[16];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = i + 64 * u < n ? d.scores[i + 64 * u] : 0.f;
+        for (int u = 0; u < 16; ++u) v[u] = d.scores[min(i + 64 * u, n - 1)];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 16; ++u)
           if (i + 64 * u < n) sc_l[i + 64 * u] = v[u];
       }
       wave_lds_sync();
