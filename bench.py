@@ -11,7 +11,10 @@ GEMM, requantisation, down grouped GEMM and combine, on inputs already
 resident in HBM.  The K timed calls are captured in one hipGraph and
 replayed once, as a model step holds its layers in one graph; the same K
 calls issued one launch per call (a graph each at decode sizes) are
-reported beside it ("layer_us_one_launch_per_call").
+reported beside it ("layer_us_one_launch_per_call"), and so are the calls
+timed one at a time with HIP events, a 512 MiB buffer read between them so
+the weights start from HBM rather than the 256 MB last-level cache
+("layer_us_single_cold_llc": median, p10, p90).
 
 Printed: one JSON line.  `value` is the algorithmic HBM throughput of the
 layer (GB/s): bytes the method must move (weights and scales of the experts
@@ -155,6 +158,26 @@ def time_point(name, T, steps, warmup, force_cfg=-1):
     ms_step = (t1 - t0) * 1e3 / steps
     del graph
     cfg = ws.last_config(stream)
+    # (c) the same calls timed one by one with events on the launch stream,
+    # a 512 MiB scratch buffer read between them (outside the timed region;
+    # read, not written, so no dirty lines are left to write back during
+    # the call) so the weights do not sit in the 256 MB last-level cache:
+    # median, p10 and p90
+    flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    flush_sum = torch.empty((), dtype=torch.float32, device="cuda")
+    single = []
+    with torch.cuda.stream(stream):
+        for i in range(steps):
+            torch.sum(flush, dim=0, out=flush_sum)
+            b = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            b.record(stream)
+            g.layer_forward(ws, dW, x, s, y, stream=stream)
+            e.record(stream)
+            single.append((b, e))
+    torch.cuda.synchronize()
+    single_us = np.array([b.elapsed_time(e) * 1e3 for b, e in single])
+    del flush, flush_sum
     # per-stage durations, eager path, events on the launch stream
     evs = []
     with torch.cuda.stream(stream):
@@ -177,6 +200,7 @@ def time_point(name, T, steps, warmup, force_cfg=-1):
     flops = 6.0 * sh.hidden * sh.inter * rows
     us = ms_step * 1e3
     return dict(sh=sh, B=B, W=W, T=T, us=us, ms=ms_step, us_call=ms_call * 1e3,
+                us_flushed=[float(np.percentile(single_us, q)) for q in (50, 10, 90)],
                 gbs=total_b / (us * 1e-6) / 1e9,
                 tflops=flops / (us * 1e-6) / 1e12, bytes=total_b, g1_bytes=g1_b, flops=flops,
                 stage_ms=stage_ms, cfg=cfg, n_active=n_active, rows=rows)
@@ -295,6 +319,9 @@ def main():
                    "a_format": sh.a_format, "tile_config": main_pt["cfg"]},
         "points": [{"workload": p["sh"].name, "tokens": p["T"], "layer_us": round(p["us"], 2),
                     "layer_us_one_launch_per_call": round(p["us_call"], 2),
+                    "layer_us_single_cold_llc": {"median": round(p["us_flushed"][0], 2),
+                                                 "p10": round(p["us_flushed"][1], 2),
+                                                 "p90": round(p["us_flushed"][2], 2)},
                     "active_tflops": round(p["tflops"], 3), "hbm_gbs": round(p["gbs"], 1),
                     "hbm_frac": round(p["gbs"] / HBM_PEAK_GBS, 4),
                     "fp8_mfma_frac": round(p["tflops"] / FP8_PEAK_TFLOPS, 4),
