@@ -815,15 +815,23 @@ hipError_t launch_dispatch(const DispatchArgs& d, hipStream_t st) {
               st, d);
     return hipGetLastError();
   }
-  // chunked path: routing (if requested) and the input quantisation ride
-  // the first launch
+  // chunked path: routing (with the input quantisation on spare blocks) as
+  // a grid of its own over every CU -- concentrated on the chunk blocks it
+  // would be bound by their vector ALUs -- then ranks and histograms per
+  // chunk, then placement
+  DispatchArgs d1 = d;
+  if (d.scores) {
+    hipError_t e = launch_route(d.scores, d.T, d.E, d.k, d.score_fn, d.ids, d.w, d.fq, st);
+    if (e != hipSuccess) return e;
+    d1.scores = nullptr;
+    d1.ids_in = d.ids;
+    d1.fq.R = 0;
+  }
   const int TC = 1024 / d.k, nch = (d.T + TC - 1) / TC;
-  LAUNCH_QF(quant_format(d.fq), k_dispatch_chunk, dim3(nch + quant_blocks(d.fq, 16, 0)), dim3(1024),
-            sizeof(int32_t) * (1024 + 16 * d.E), st, d);
-  DispatchArgs d2 = d;
+  LAUNCH_QF(quant_format(d1.fq), k_dispatch_chunk, dim3(nch + quant_blocks(d1.fq, 16, 0)), dim3(1024),
+            sizeof(int32_t) * (1024 + 16 * d.E), st, d1);
+  DispatchArgs d2 = d1;
   d2.fq.R = 0;
-  d2.ids_in = d.scores ? d.ids : d.ids_in;
-  d2.scores = nullptr;
   hipLaunchKernelGGL(k_dispatch_place, dim3(nch + 1), dim3(1024), sizeof(int32_t) * (5 * G + 2048),
                      st, d2);
   return hipGetLastError();
