@@ -256,33 +256,36 @@ DEVI int block_stable_rank(int e, bool valid, int32_t* wcnt, int G, int32_t* tot
   return pre + rank;
 }
 
-// Exclusive prefix sum of n <= 1024 ints in LDS, in place, by one wave
-// (wave 0); returns nothing, result visible after the caller's barrier.
-DEVI void wave0_exclusive_scan(int32_t* a, int n, int32_t* total) {
-  int tid = threadIdx.x;
-  if (tid >= 64) return;
-  constexpr int PER = 16;
-  int base = tid * PER;
-  int loc[PER];
-  int s = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    loc[i] = (base + i < n) ? a[base + i] : 0;
-    s += loc[i];
-  }
-  int inc = s;
+// Exclusive prefix sum of a[0..n) (n <= 1024) in LDS, in place, by all
+// threads of a 1024-thread block: one element per thread (conflict-free LDS
+// access), shuffle scans inside each wave, the 16 wave totals scanned by
+// wave 0.  wsum is LDS [16]; *total (LDS) receives the sum.  Every thread
+// must call it; a[] and *total are ready when it returns.
+DEVI void block_exclusive_scan(int32_t* a, int n, int32_t* wsum, int32_t* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int v = tid < n ? a[tid] : 0;
+  int inc = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    int v = __shfl_up(inc, o, 64);
-    if (tid >= o) inc += v;
+    const int u = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += u;
   }
-  int run = inc - s;
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  if (wave == 0) {
+    const int w = lane < 16 ? wsum[lane] : 0;
+    int winc = w;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    if (base + i < n) a[base + i] = run;
-    run += loc[i];
+    for (int o = 1; o < 16; o <<= 1) {
+      const int u = __shfl_up(winc, o, 64);
+      if (lane >= o) winc += u;
+    }
+    if (lane < 16) wsum[lane] = winc - w;
+    if (lane == 15) *total = winc;
   }
-  if (tid == 63 && total) *total = inc;
+  __syncthreads();
+  if (tid < n) a[tid] = inc - v + wsum[wave];
+  __syncthreads();
 }
 
 // ---------------------------------------------------------------- config choice
@@ -338,64 +341,47 @@ DEVI int choose_config(const int32_t* cnt, int G, int I, int num_cfgs, int cus, 
 // block must call it.
 DEVI void finalize_dispatch(const DispatchArgs& d, int32_t* cnt, int32_t* scan_buf,
                             int32_t* flag_buf, int32_t* tiles_buf, int G, int S_total) {
-  int tid = threadIdx.x;
+  const int tid = threadIdx.x;
   __shared__ int32_t s_total, s_active, s_cfg, s_max, s_ntiles;
+  __shared__ int32_t wsum[16];
   for (int g = tid; g < G; g += blockDim.x) {
     scan_buf[g] = cnt[g];
     flag_buf[g] = cnt[g] > 0 ? 1 : 0;
     d.counts[g] = cnt[g];
   }
   __syncthreads();
-  wave0_exclusive_scan(scan_buf, G, &s_total);
-  __syncthreads();
-  if (tid >= 64 && tid < 128) {
-    // a second wave scans the active flags concurrently
-    int l = tid - 64;
-    constexpr int PER = 16;
-    int base = l * PER, loc[PER], s = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      loc[i] = (base + i < G) ? flag_buf[base + i] : 0;
-      s += loc[i];
-    }
-    int inc = s;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      int v = __shfl_up(inc, o, 64);
-      if (l >= o) inc += v;
-    }
-    int run = inc - s;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      if (base + i < G && loc[i]) d.active[run] = base + i;
-      run += loc[i];
-    }
-    if (l == 63) s_active = inc;
-  }
-  if (tid >= 128 && tid < 192) {
+  if (tid < 64) {
     // one wave derives the configuration from the histogram
-    int l = tid - 128, mx = 0;
-    int cfg = choose_config(cnt, G, d.I, d.num_cfgs, d.cus, l, &mx);
+    int mx = 0;
+    int cfg = choose_config(cnt, G, d.I, d.num_cfgs, d.cus, tid, &mx);
     if (d.force_cfg >= 0) cfg = d.force_cfg;
-    if (l == 0) {
+    if (tid == 0) {
       s_max = mx;
       s_cfg = cfg;
     }
   }
-  __syncthreads();
+  block_exclusive_scan(scan_buf, G, wsum, &s_total);   // group offsets
+  block_exclusive_scan(flag_buf, G, wsum, &s_active);  // positions in the active list
+  for (int g = tid; g < G; g += blockDim.x)
+    if (cnt[g] > 0) d.active[flag_buf[g]] = g;
   for (int g = tid; g <= G; g += blockDim.x) d.indptr[g] = (g < G) ? scan_buf[g] : s_total;
-  // block table for the chosen row-block height
-  int bm = cfg_rows(s_cfg);
+  // block table for the chosen row-block height: one entry per thread, its
+  // group found by binary search over the groups' first table entries
+  const int bm = cfg_rows(s_cfg);
   for (int g = tid; g < G; g += blockDim.x) tiles_buf[g] = (cnt[g] + bm - 1) / bm;
   __syncthreads();
-  wave0_exclusive_scan(tiles_buf, G, &s_ntiles);
-  __syncthreads();
-  for (int g = tid; g < G; g += blockDim.x) {
-    int n = (cnt[g] + bm - 1) / bm, base = tiles_buf[g];
-    for (int r = 0; r < n; ++r) {
-      d.tiles[2 * (base + r)] = g;
-      d.tiles[2 * (base + r) + 1] = r * bm;
+  block_exclusive_scan(tiles_buf, G, wsum, &s_ntiles);
+  for (int i = tid; i < s_ntiles; i += blockDim.x) {
+    // the last group whose first entry is <= i owns entry i (groups without
+    // rows share their first entry with the next group)
+    int lo = 0, hi = G - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tiles_buf[mid] <= i) lo = mid;
+      else hi = mid - 1;
     }
+    d.tiles[2 * i] = lo;
+    d.tiles[2 * i + 1] = (i - tiles_buf[lo]) * bm;
   }
   if (tid == 0) {
     d.meta[META_NACTIVE] = s_active;
@@ -714,15 +700,16 @@ __global__ void __launch_bounds__(1024) k_dispatch_place(DispatchArgs d) {
   const int P = 1024 / E, g = tid % E, q = tid / E;
   int tot = 0, pre = 0;
   if (q < P) {
-    for (int c0 = q; c0 < nch; c0 += 8 * P) {   // eight loads in flight
-      int v[8];
+    for (int c0 = q; c0 < nch; c0 += 16 * P) {   // sixteen loads in flight
+      int v[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 16; ++u) {
         const int cc = c0 + u * P;
-        v[u] = cc < nch ? d.chunk[(size_t)cc * E + g] : 0;
+        v[u] = d.chunk[(size_t)min(cc, nch - 1) * E + g];
+        v[u] = cc < nch ? v[u] : 0;
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 16; ++u) {
         tot += v[u];
         pre += c0 + u * P < c ? v[u] : 0;
       }
@@ -750,8 +737,8 @@ __global__ void __launch_bounds__(1024) k_dispatch_place(DispatchArgs d) {
   }
   for (int i = tid; i < G; i += blockDim.x) scan_buf[i] = cnt[i];
   __syncthreads();
-  wave0_exclusive_scan(scan_buf, G, nullptr);
-  __syncthreads();
+  __shared__ int32_t wsum_p[16], total_p;
+  block_exclusive_scan(scan_buf, G, wsum_p, &total_p);
   if (mine) {
     if ((unsigned)e < (unsigned)E) {
       const int slot = scan_buf[e] + pre_l[e] + rank;
