@@ -68,6 +68,8 @@ class LayerShape:
     a_format: int = A_BF16
     tokens: tuple = (32,)
     score_recipe: str = "normal"   # normal | zipf_bias | dirichlet2
+    activation: int = 0      # 0 SwiGLU, 1 bounded SwiGLU, 2 SwiGLU-OAI, 3 GeGLU, 4 ReGLU, 5 ReLU^2
+    act_limit: float = 0.0   # clamp of bounded SwiGLU / SwiGLU-OAI (0: 10 / 7)
 
     def with_(self, **kw) -> "LayerShape":
         return dataclasses.replace(self, **kw)
@@ -270,11 +272,11 @@ def _popularity(shape: LayerShape) -> np.ndarray:
     return rng.dirichlet(np.full(shape.experts, 0.1))
 
 
-def gen_batch(shape: LayerShape, T: int, seed_extra: int = 0) -> Batch:
+def gen_batch(shape: LayerShape, T: int, seed_extra: int = 0, x_std: float = ACT_STD) -> Batch:
     kx, ks = np.random.SeedSequence([0, shape.cfg_id, T, seed_extra]).spawn(2) if seed_extra \
         else np.random.SeedSequence([0, shape.cfg_id, T]).spawn(2)
     rx = np.random.Generator(np.random.PCG64(kx))
-    x = rx.standard_normal((T, shape.hidden), dtype=np.float32) * np.float32(ACT_STD)
+    x = rx.standard_normal((T, shape.hidden), dtype=np.float32) * np.float32(x_std)
     x_bits = _bf16_bits(x)
     rs = np.random.Generator(np.random.PCG64(ks))
     E = shape.experts

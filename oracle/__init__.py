@@ -65,10 +65,13 @@ def lib():
         L.oracle_tile_table.restype = i
         L.oracle_tile_table.argtypes = [P, i, i, P, i]
         L.oracle_layer_forward.restype = None
-        L.oracle_layer_forward.argtypes = [i, i, i, i, i, i, P, P, P, P, P, P, i, i,
+        L.oracle_layer_forward.argtypes = [i, i, i, i, i, i, i, C.c_double, P, P, P, P, P, P, i, i,
                                            P, P, P, P, P, P, P, P, P, P, i, P]
         L.oracle_grouped_gemm.restype = None
-        L.oracle_grouped_gemm.argtypes = [i, i, i, P, P, P, i, P, i, i, i, P, P, P, P, P]
+        L.oracle_grouped_gemm.argtypes = [i, i, i, i, C.c_double, P, P, P, i, P, i, i, i, P, P,
+                                          P, P, P]
+        L.oracle_activation.restype = C.c_double
+        L.oracle_activation.argtypes = [i, C.c_double, C.c_double, C.c_double]
         _lib = L
     return _lib
 
@@ -161,6 +164,23 @@ def tile_table(counts, bm: int) -> np.ndarray:
     return tab[:n]
 
 
+# ------------------------------------------------------------- activations
+ACT_SWIGLU, ACT_SWIGLU_BOUNDED, ACT_SWIGLU_OAI, ACT_GEGLU, ACT_REGLU, ACT_RELU2 = range(6)
+
+
+def act_limit(act: int, limit: float) -> float:
+    """The clamp L in use: the given one, else 10 (bounded SwiGLU) or 7
+    (SwiGLU-OAI) when limit <= 0."""
+    if limit > 0:
+        return float(limit)
+    return {ACT_SWIGLU_BOUNDED: 10.0, ACT_SWIGLU_OAI: 7.0}.get(int(act), 0.0)
+
+
+def activation(act: int, limit: float, g: float, u: float) -> float:
+    """The expert activation of one gate value g and up value u (fp64)."""
+    return lib().oracle_activation(int(act), float(act_limit(act, limit)), float(g), float(u))
+
+
 # ------------------------------------------------------------------ layer
 def layer_forward(weights, x_bits, ids, w, tokens=None) -> np.ndarray:
     """fp64 layer output rows for ``tokens`` (default: all), given routing."""
@@ -173,6 +193,7 @@ def layer_forward(weights, x_bits, ids, w, tokens=None) -> np.ndarray:
     y = np.zeros((len(toks), sh.hidden), dtype=np.float64)
     lib().oracle_layer_forward(
         sh.hidden, sh.inter, sh.experts, sh.top_k, sh.w_format, sh.a_format,
+        int(sh.activation), float(act_limit(sh.activation, sh.act_limit)),
         _p(weights.w_gate), _p(weights.s_gate), _p(weights.w_up), _p(weights.s_up),
         _p(weights.w_down), _p(weights.s_down),
         int(sh.shared), int(sh.shared_inter),
@@ -183,17 +204,18 @@ def layer_forward(weights, x_bits, ids, w, tokens=None) -> np.ndarray:
 
 
 def grouped_gemm(w_format, a_format, op, a, a_scale, a_gather, gather_div, m_indptr, N, K,
-                 b0, b0s, b1=None, b1s=None) -> np.ndarray:
-    """fp64 grouped projection (op 0 plain, op 1 SwiGLU of gate/up)."""
+                 b0, b0s, b1=None, b1s=None, act=0, limit=0.0) -> np.ndarray:
+    """fp64 grouped projection (op 0 plain, op 1 gated activation of gate/up)."""
     m_indptr = _c(m_indptr, np.int32)
     E = len(m_indptr) - 1
     R = int(m_indptr[-1])
     out = np.zeros((R, N), dtype=np.float64)
     ag = None if a_gather is None else _c(a_gather, np.int32)
-    lib().oracle_grouped_gemm(w_format, a_format, op, _p(np.ascontiguousarray(a)),
+    lib().oracle_grouped_gemm(w_format, a_format, op, int(act), float(act_limit(act, limit)),
+                              _p(np.ascontiguousarray(a)),
                               None if a_scale is None else _p(np.ascontiguousarray(a_scale)),
                               _p(ag), int(gather_div), _p(m_indptr), E, N, K,
-                              _p(np.ascontiguousarray(b0)),
+                              None if b0 is None else _p(np.ascontiguousarray(b0)),
                               None if b0s is None else _p(np.ascontiguousarray(b0s)),
                               None if b1 is None else _p(np.ascontiguousarray(b1)),
                               None if b1s is None else _p(np.ascontiguousarray(b1s)), _p(out))

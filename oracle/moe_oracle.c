@@ -53,6 +53,12 @@
 #define A_FP8_TOKEN 1
 #define A_FP8_G128 2
 #define A_MXFP8_G32 3
+#define ACT_SWIGLU 0
+#define ACT_SWIGLU_BOUNDED 1
+#define ACT_SWIGLU_OAI 2
+#define ACT_GEGLU 3
+#define ACT_REGLU 4
+#define ACT_RELU2 5
 
 /* ------------------------------------------------------------------ codecs */
 
@@ -325,16 +331,54 @@ static void matvec(const oracle_mat* m, const double* a, double* out) {
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
-/* One expert on one (already dequantised) token row: SwiGLU MLP with the
- * intermediate requantised under the activation format.  o has H entries. */
+static double clampd(double v, double lo, double hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+/*
+ * The expert's activation of its gate value g and up value u (LightMoE
+ * README, "Compatibility" and "MoE inference": SwiGLU, bounded SwiGLU with
+ * an activation clamp, SwiGLU-OAI, GeGLU, ReGLU, and ReLU^2 in the
+ * two-weight form).  The pages name these without formulas; the readings:
+ *   SwiGLU          SiLU(g) * u
+ *   bounded SwiGLU  SiLU(min(g, L)) * clamp(u, -L, L)         (L = limit)
+ *   SwiGLU-OAI      g' sigma(1.702 g') (clamp(u, -L, L) + 1), g' = min(g, L)
+ *   GeGLU           GELU(g) * u, GELU(z) = z (1 + erf(z / sqrt 2)) / 2
+ *   ReGLU           max(g, 0) * u
+ *   ReLU^2          max(u, 0)^2 (no gate projection; g is unused)
+ */
+double oracle_activation(int act, double limit, double g, double u) {
+  switch (act) {
+    case ACT_SWIGLU_BOUNDED:
+      return silu(g < limit ? g : limit) * clampd(u, -limit, limit);
+    case ACT_SWIGLU_OAI: {
+      double gc = g < limit ? g : limit;
+      return gc / (1.0 + exp(-1.702 * gc)) * (clampd(u, -limit, limit) + 1.0);
+    }
+    case ACT_GEGLU:
+      return 0.5 * g * (1.0 + erf(g / sqrt(2.0))) * u;
+    case ACT_REGLU:
+      return (g > 0.0 ? g : 0.0) * u;
+    case ACT_RELU2:
+      return u > 0.0 ? u * u : 0.0;
+    default:
+      return silu(g) * u;
+  }
+}
+
+/* One expert on one (already dequantised) token row: gated MLP with the
+ * intermediate requantised under the activation format.  o has H entries.
+ * g is NULL for the two-weight ReLU^2 form. */
 static void expert_forward(const oracle_mat* g, const oracle_mat* u, const oracle_mat* d,
-                           const double* xq, int a_format, double* o) {
-  int I = g->N;
+                           const double* xq, int a_format, int act, double limit, double* o) {
+  int I = u->N;
   double* gv = (double*)malloc(sizeof(double) * (size_t)I);
   double* uv = (double*)malloc(sizeof(double) * (size_t)I);
-  matvec(g, xq, gv);
+  if (act == ACT_RELU2) {
+    for (int n = 0; n < I; ++n) gv[n] = 0.0;
+  } else {
+    matvec(g, xq, gv);
+  }
   matvec(u, xq, uv);
-  for (int n = 0; n < I; ++n) gv[n] = silu(gv[n]) * uv[n];
+  for (int n = 0; n < I; ++n) gv[n] = oracle_activation(act, limit, gv[n], uv[n]);
   quant_dequant_row(gv, I, a_format);
   matvec(d, gv, o);
   free(gv);
@@ -375,8 +419,8 @@ static oracle_mat expert_mat(int w_format, const void* codes, const void* scales
  *   tokens  which rows of y to compute; y is [ntok, H] (fp64)
  * y_t = sum_j w[t,j] * expert_{ids[t,j]}(x_t) (+ shared(x_t)), j ascending.
  */
-void oracle_layer_forward(int H, int I, int E, int k, int w_format, int a_format,
-                          const void* wg, const void* sg, const void* wu, const void* su,
+void oracle_layer_forward(int H, int I, int E, int k, int w_format, int a_format, int act,
+                          double limit, const void* wg, const void* sg, const void* wu, const void* su,
                           const void* wd, const void* sd, int has_shared, int Is,
                           const void* shg, const void* shsg, const void* shu, const void* shsu,
                           const void* shd, const void* shsd, const uint16_t* x_bits,
@@ -395,7 +439,7 @@ void oracle_layer_forward(int H, int I, int E, int k, int w_format, int a_format
       oracle_mat g = expert_mat(w_format, wg, sg, e, I, H);
       oracle_mat u = expert_mat(w_format, wu, su, e, I, H);
       oracle_mat d = expert_mat(w_format, wd, sd, e, H, I);
-      expert_forward(&g, &u, &d, xq, a_format, o);
+      expert_forward(&g, &u, &d, xq, a_format, act, limit, o);
       double wj = w[(size_t)t * k + j];
       for (int h = 0; h < H; ++h) yt[h] += wj * o[h];
     }
@@ -403,7 +447,7 @@ void oracle_layer_forward(int H, int I, int E, int k, int w_format, int a_format
       oracle_mat g = expert_mat(w_format, shg, shsg, 0, Is, H);
       oracle_mat u = expert_mat(w_format, shu, shsu, 0, Is, H);
       oracle_mat d = expert_mat(w_format, shd, shsd, 0, H, Is);
-      expert_forward(&g, &u, &d, xq, a_format, o);
+      expert_forward(&g, &u, &d, xq, a_format, act, limit, o);
       for (int h = 0; h < H; ++h) yt[h] += o[h];
     }
   }
@@ -418,9 +462,11 @@ void oracle_layer_forward(int H, int I, int E, int k, int w_format, int a_format
  * activation row a_gather ? a_gather[r] / gather_div : r, dequantised under
  * a_format (codes times the row's, group's or block's scale).
  *   op 0: out[r, n] = sum_k a[r, k] * B0[e, n, k]
- *   op 1: out[r, n] = SiLU(sum_k a B0) * (sum_k a B1), not requantised.
+ *   op 1: out[r, n] = act(sum_k a B0, sum_k a B1) (oracle_activation), not
+ *         requantised; ReLU^2 reads only B1 (B0 may be NULL).
  * out is fp64 [m_indptr[E], N]. */
-void oracle_grouped_gemm(int w_format, int a_format, int op, const void* a, const void* a_scale,
+void oracle_grouped_gemm(int w_format, int a_format, int op, int act, double limit,
+                         const void* a, const void* a_scale,
                          const int32_t* a_gather, int gather_div, const int32_t* m_indptr, int E,
                          int N, int K, const void* b0, const void* b0s, const void* b1,
                          const void* b1s, double* out) {
@@ -428,7 +474,8 @@ void oracle_grouped_gemm(int w_format, int a_format, int op, const void* a, cons
   double* g = (double*)malloc(sizeof(double) * (size_t)N);
   double* u = (double*)malloc(sizeof(double) * (size_t)N);
   for (int e = 0; e < E; ++e) {
-    oracle_mat B0 = expert_mat(w_format, b0, b0s, e, N, K);
+    const int relu2 = op == 1 && act == ACT_RELU2;
+    oracle_mat B0 = expert_mat(w_format, relu2 ? b1 : b0, relu2 ? b1s : b0s, e, N, K);
     oracle_mat B1 = expert_mat(w_format, b1 ? b1 : b0, b1 ? b1s : b0s, e, N, K);
     for (int r = m_indptr[e]; r < m_indptr[e + 1]; ++r) {
       long src = a_gather ? a_gather[r] / gather_div : r;
@@ -447,10 +494,14 @@ void oracle_grouped_gemm(int w_format, int a_format, int op, const void* a, cons
           s = oracle_e8m0_decode(((const uint8_t*)a_scale)[src * (K / 32) + k / 32]);
         arow[k] = q * s;
       }
-      matvec(&B0, arow, g);
+      if (op == 1 && relu2) {
+        for (int n = 0; n < N; ++n) g[n] = 0.0;
+      } else {
+        matvec(&B0, arow, g);
+      }
       if (op == 1) {
         matvec(&B1, arow, u);
-        for (int n = 0; n < N; ++n) out[(size_t)r * N + n] = silu(g[n]) * u[n];
+        for (int n = 0; n < N; ++n) out[(size_t)r * N + n] = oracle_activation(act, limit, g[n], u[n]);
       } else {
         for (int n = 0; n < N; ++n) out[(size_t)r * N + n] = g[n];
       }
