@@ -60,6 +60,10 @@ def kernel_src_sha() -> str:
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 STAGES = ["route+dispatch", "quant_x", "gemm_gateup_swiglu", "quant_h", "gemm_down", "combine"]
+# expert activations (include/moe.h MOE_ACT_*)
+ACTIVATIONS = {"swiglu": 0, "swiglu_bounded": 1, "swiglu_oai": 2, "geglu": 3, "reglu": 4,
+               "relu2": 5}
+ACT_RELU2 = 5
 
 
 def log(*a):
@@ -81,7 +85,8 @@ def layer_bytes(sh, T, n_active):
 
     groups = n_active + sh.shared
     rows = T * sh.top_k + (T if sh.shared else 0)
-    gateup = groups * 2 * (H * I * wbits / 8 + mat_scales(I, H))
+    nmat = 1 if sh.activation == ACT_RELU2 else 2      # ReLU^2: no gate projection
+    gateup = groups * nmat * (H * I * wbits / 8 + mat_scales(I, H))
     down = groups * (H * I * wbits / 8 + mat_scales(H, I))
     x_in = T * H * 2                                   # bf16 x read once
     y_out = T * H * 2                                  # bf16 y written once
@@ -91,11 +96,11 @@ def layer_bytes(sh, T, n_active):
     return total, g1, rows
 
 
-def setup(name, T, seed_dev="cuda"):
+def setup(name, T, seed_dev="cuda", act=0):
     import torch
     import grouped_gemm_amd as g
     import moe_synth as ms
-    sh = ms.CONFIGS[name]
+    sh = ms.CONFIGS[name].with_(activation=act)
     B = ms.gen_batch(sh, T)
     # experts that receive tokens (stable argsort of the scores, top k)
     order = np.argsort(-B.scores.astype(np.float64), axis=1, kind="stable")[:, :sh.top_k]
@@ -108,19 +113,22 @@ def setup(name, T, seed_dev="cuda"):
               if getattr(W, n) is not None else None)
           for n in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
                     "sh_gate", "sh_up", "sh_down", "ss_gate", "ss_up", "ss_down")}
+    if act == ACT_RELU2:    # two-weight form: the gate weights are not passed
+        for n in ("w_gate", "s_gate", "sh_gate", "ss_gate"):
+            dW[n] = None
     ws = g.Workspace(sh.hidden, sh.inter, sh.experts, sh.top_k, T, shared_experts=sh.shared,
                      shared_inter=sh.shared_inter, score_fn=sh.score_fn, w_format=sh.w_format,
-                     a_format=sh.a_format)
+                     a_format=sh.a_format, activation=sh.activation, act_limit=sh.act_limit)
     x = torch.from_numpy(B.x_bits.view(np.int16)).to(seed_dev)
     s = torch.from_numpy(B.scores).to(seed_dev)
     y = torch.empty(T, sh.hidden, dtype=torch.int16, device=seed_dev)
     return sh, B, W, dW, ws, x, s, y, len(active)
 
 
-def time_point(name, T, steps, warmup, force_cfg=-1):
+def time_point(name, T, steps, warmup, force_cfg=-1, act=0):
     import torch
     import grouped_gemm_amd as g
-    sh, B, W, dW, ws, x, s, y, n_active = setup(name, T)
+    sh, B, W, dW, ws, x, s, y, n_active = setup(name, T, act=act)
     if force_cfg >= 0:
         ws.force_config(force_cfg)
     stream = torch.cuda.Stream()
@@ -197,7 +205,7 @@ def time_point(name, T, steps, warmup, force_cfg=-1):
         ws.set_stage_events(st, None, None)
     stage_ms = [float(np.mean([p[st][0].elapsed_time(p[st][1]) for p in evs])) for st in range(6)]
     total_b, g1_b, rows = layer_bytes(sh, T, n_active)
-    flops = 6.0 * sh.hidden * sh.inter * rows
+    flops = (4.0 if sh.activation == ACT_RELU2 else 6.0) * sh.hidden * sh.inter * rows
     us = ms_step * 1e3
     return dict(sh=sh, B=B, W=W, T=T, us=us, ms=ms_step, us_call=ms_call * 1e3,
                 us_flushed=[float(np.percentile(single_us, q)) for q in (50, 10, 90)],
@@ -240,6 +248,8 @@ def main():
                     help="skip the 8192-token Qwen-shaped point of the default run")
     ap.add_argument("--force-config", type=int, default=-1,
                     help="tile configuration (default: chosen on the device)")
+    ap.add_argument("--activation", default="swiglu", choices=list(ACTIVATIONS),
+                    help="expert activation of every timed point (default SwiGLU)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain elementwise copy of 256 MiB (fp32 in, fp32 out), "
                          "whose known byte counts calibrate hardware traffic counters")
@@ -265,21 +275,22 @@ def main():
         log(f"[bench] copy calibration: 3 x elementwise copy, {4 * n} bytes read and "
             f"{4 * n} bytes written per launch")
         del a, b
+    act = ACTIVATIONS[args.activation]
     sh0 = ms.CONFIGS[args.workload]
     T_main = args.tokens or max(sh0.tokens)
     points = []
     extra_T = [t for t in sh0.tokens if t != T_main and t >= 16] if not args.tokens else []
     for T in extra_T:
-        p = time_point(args.workload, T, args.steps, args.warmup, args.force_config)
+        p = time_point(args.workload, T, args.steps, args.warmup, args.force_config, act)
         points.append(p)
         log(f"[bench] T={T}: {p['us']:.1f} us, {p['gbs']:.0f} GB/s, {p['tflops']:.2f} TFLOP/s")
-    main_pt = time_point(args.workload, T_main, args.steps, args.warmup, args.force_config)
+    main_pt = time_point(args.workload, T_main, args.steps, args.warmup, args.force_config, act)
     points.append(main_pt)
     log(f"[bench] T={T_main}: {main_pt['us']:.1f} us, {main_pt['gbs']:.0f} GB/s, "
         f"{main_pt['tflops']:.2f} TFLOP/s, stages(ms)={[round(v, 4) for v in main_pt['stage_ms']]}")
     if args.workload == "mixtral" and not args.tokens and not args.no_prefill:
         # the metric's 8192-token point: the Qwen3.5-35B-A3B-shaped layer
-        qp = time_point("qwen", 8192, args.steps, args.warmup)
+        qp = time_point("qwen", 8192, args.steps, args.warmup, act=act)
         points.append(qp)
         log(f"[bench] qwen T=8192: {qp['us']:.1f} us, {qp['gbs']:.0f} GB/s, "
             f"{qp['tflops']:.2f} TFLOP/s ({qp['tflops'] / FP8_PEAK_TFLOPS:.3f} of FP8 peak), "
@@ -293,13 +304,13 @@ def main():
     roof = None
     if dom_bytes is not None:
         ach = dom_bytes / (dom_ms * 1e-3) / 1e9
-        tr = TRAFFIC.get((args.workload, T_main, main_pt["cfg"]))
+        tr = TRAFFIC.get((args.workload, T_main, main_pt["cfg"])) if act == 0 else None
         traffic = tr["bytes"] if tr and tr["src_sha"] == kernel_src_sha() else None
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": ("k_gemm_stream (gate/up + SwiGLU)" if main_pt["cfg"] == 0 else
-                           "k_gemm_pipe (gate/up + SwiGLU, %d-row blocks)"
-                           % {1: 32, 2: 64, 3: 128}.get(main_pt["cfg"], 0)),
+                "kernel": ("k_gemm_stream (gate/up + %s)" % args.activation if main_pt["cfg"] == 0
+                           else "k_gemm_pipe (gate/up + %s, %d-row blocks)"
+                           % (args.activation, {1: 32, 2: 64, 3: 128}.get(main_pt["cfg"], 0))),
                 "avg_ms": round(dom_ms, 5),
                 "bytes_per_launch": int(dom_bytes)}
     cpu = None
@@ -316,7 +327,8 @@ def main():
                                f"E{sh.experts} top{sh.top_k}, T={T_main}",
                    "tokens": T_main, "hidden": sh.hidden, "inter": sh.inter,
                    "experts": sh.experts, "top_k": sh.top_k, "w_format": sh.w_format,
-                   "a_format": sh.a_format, "tile_config": main_pt["cfg"]},
+                   "a_format": sh.a_format, "activation": args.activation,
+                   "tile_config": main_pt["cfg"]},
         "points": [{"workload": p["sh"].name, "tokens": p["T"], "layer_us": round(p["us"], 2),
                     "layer_us_one_launch_per_call": round(p["us_call"], 2),
                     "layer_us_single_cold_llc": {"median": round(p["us_flushed"][0], 2),

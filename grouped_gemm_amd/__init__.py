@@ -11,7 +11,9 @@ import ctypes as C
 import os
 
 from ._binding import (  # noqa: F401
-    A_BF16, A_FP8_G128, A_FP8_TOKEN, A_MXFP8_G32, OP_GATEUP_SWIGLU, OP_PLAIN, SCORE_PROBS,
+    ACT_GEGLU, ACT_REGLU, ACT_RELU2, ACT_SWIGLU, ACT_SWIGLU_BOUNDED, ACT_SWIGLU_OAI,
+    A_BF16, A_FP8_G128, A_FP8_TOKEN, A_MXFP8_G32, OP_GATEUP_ACT, OP_GATEUP_SWIGLU, OP_PLAIN,
+    SCORE_PROBS,
     SCORE_SIGMOID, SCORE_SOFTMAX, W_BF16, W_FP8_BLOCK128, W_FP8_CHANNEL, W_MXFP4, MoeError,
     LayerDesc, Workspace, combine, config_rows, dispatch, grouped_gemm, layer_forward,
     library_path, quantize_act, route_topk, symbols)

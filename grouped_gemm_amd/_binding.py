@@ -10,7 +10,10 @@ _SO = os.path.join(_HERE, "libmoe.so")
 SCORE_SOFTMAX, SCORE_SIGMOID, SCORE_PROBS = 0, 1, 2
 W_BF16, W_FP8_CHANNEL, W_FP8_BLOCK128, W_MXFP4 = 0, 1, 2, 3
 A_BF16, A_FP8_TOKEN, A_FP8_G128, A_MXFP8_G32 = 0, 1, 2, 3
-OP_PLAIN, OP_GATEUP_SWIGLU = 0, 1
+OP_PLAIN, OP_GATEUP_ACT = 0, 1
+OP_GATEUP_SWIGLU = OP_GATEUP_ACT
+(ACT_SWIGLU, ACT_SWIGLU_BOUNDED, ACT_SWIGLU_OAI, ACT_GEGLU, ACT_REGLU,
+ ACT_RELU2) = range(6)
 
 SYMBOLS = (
     "moe_status_string", "moe_last_error", "moe_workspace_size", "moe_workspace_create",
@@ -28,7 +31,8 @@ class MoeError(RuntimeError):
 class LayerDesc(C.Structure):
     _fields_ = [(n, C.c_int) for n in (
         "hidden", "inter", "num_experts", "top_k", "shared_experts", "shared_inter", "score_fn",
-        "renormalize", "w_format", "a_format", "max_tokens")]
+        "renormalize", "w_format", "a_format", "max_tokens", "activation")] + \
+        [("act_limit", C.c_float)]
 
 
 class _Weights(C.Structure):
@@ -112,11 +116,12 @@ class Workspace:
 
     def __init__(self, hidden, inter, num_experts, top_k, max_tokens, *, shared_experts=0,
                  shared_inter=0, score_fn=SCORE_SOFTMAX, w_format=W_BF16, a_format=A_BF16,
-                 device="cuda"):
+                 activation=ACT_SWIGLU, act_limit=0.0, device="cuda"):
         import torch
         L = _load()
         self.desc = LayerDesc(hidden, inter, num_experts, top_k, shared_experts, shared_inter,
-                              score_fn, 1, w_format, a_format, max_tokens)
+                              score_fn, 1, w_format, a_format, max_tokens, activation,
+                              act_limit)
         n = C.c_size_t(0)
         _check(L.moe_workspace_size(C.byref(self.desc), C.byref(n)))
         self.nbytes = n.value

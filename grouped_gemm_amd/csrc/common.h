@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -69,6 +71,46 @@ DEVI uint32_t cvt4_e4m3(float a, float b, float c, float d) {
 // z * sigmoid(z); the reciprocal is the hardware one (1 ulp), far inside the
 // rounding of the bf16 / e4m3 values the result is stored as.
 DEVI float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+
+// Expert activations of a gate value g and an up value u (LightMoE README,
+// "Compatibility": SwiGLU, bounded SwiGLU, SwiGLU-OAI, GeGLU, ReGLU and the
+// two-weight ReLU^2, whose kernels receive the up projection as both
+// operands).  L clamps the bounded forms.  Kernels take the activation as a
+// template argument, so each instantiation inlines exactly one formula.
+enum { ACT_SWIGLU = 0, ACT_SWIGLU_BOUNDED, ACT_SWIGLU_OAI, ACT_GEGLU, ACT_REGLU, ACT_RELU2 };
+template <int ACT>
+DEVI float gated_act(float L, float g, float u) {
+  if constexpr (ACT == ACT_SWIGLU_BOUNDED) {
+    return silu(fminf(g, L)) * fminf(fmaxf(u, -L), L);
+  } else if constexpr (ACT == ACT_SWIGLU_OAI) {
+    const float gc = fminf(g, L);
+    return gc * __builtin_amdgcn_rcpf(1.0f + __expf(-1.702f * gc)) * (fminf(fmaxf(u, -L), L) + 1.0f);
+  } else if constexpr (ACT == ACT_GEGLU) {
+    return 0.5f * g * (1.0f + erff(g * 0.70710678118654752f)) * u;
+  } else if constexpr (ACT == ACT_REGLU) {
+    return fmaxf(g, 0.0f) * u;
+  } else if constexpr (ACT == ACT_RELU2) {
+    const float r = fmaxf(u, 0.0f);
+    return r * r;
+  } else {
+    return silu(g) * u;
+  }
+}
+
+// Calls f(std::integral_constant<int, ACT>{}) for the runtime activation id
+// (SwiGLU for ids outside the table, which the API rejects earlier).
+template <class Fn>
+inline auto with_act(int act, Fn&& f) {
+  switch (act) {
+    case ACT_SWIGLU_BOUNDED: return f(std::integral_constant<int, ACT_SWIGLU_BOUNDED>{});
+    case ACT_SWIGLU_OAI: return f(std::integral_constant<int, ACT_SWIGLU_OAI>{});
+    case ACT_GEGLU: return f(std::integral_constant<int, ACT_GEGLU>{});
+    case ACT_REGLU: return f(std::integral_constant<int, ACT_REGLU>{});
+    case ACT_RELU2: return f(std::integral_constant<int, ACT_RELU2>{});
+    default: return f(std::integral_constant<int, ACT_SWIGLU>{});
+  }
+}
+
 
 // floor(log2(a)) for a finite a > 0 (exact, from the exponent field).
 DEVI int ilog2_floor(float a) {

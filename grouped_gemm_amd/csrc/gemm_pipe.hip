@@ -201,7 +201,9 @@ constexpr int pipe_lds_bytes() {
 //
 // All DMA sources are a wave-uniform base (advanced per step in scalar
 // registers) plus a fixed 32-bit per-lane offset.
-template <int F, bool GATEUP, int BM, int NR, int WM, int NW>
+// ACT: the gate/up epilogue's activation (ACT_*; the down projection
+// ignores it).
+template <int F, bool GATEUP, int BM, int NR, int WM, int NW, int ACT>
 DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
   using PC = PipeCfg<F, GATEUP, BM, NR, WM, NW>;
   constexpr int WB = PC::WB, WN = PC::WN, NSTAGE = PC::NSTAGE;
@@ -657,12 +659,23 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
       }
       }
     } else {
+      if constexpr (ACT == ACT_SWIGLU) {
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int t = 0; t < TT; ++t)
+          for (int t = 0; t < TT; ++t)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[0][rt][t][i] = silu(acc[0][rt][t][i]) * acc[1][rt][t][i];
+            for (int i = 0; i < 4; ++i) acc[0][rt][t][i] = silu(acc[0][rt][t][i]) * acc[1][rt][t][i];
+      } else {
+        const float L = p.act_limit;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[0][rt][t][i] = gated_act<ACT>(L, acc[0][rt][t][i], acc[1][rt][t][i]);
+      }
       if constexpr (F == F_FP8_CH) {
   #pragma unroll
         for (int t = 0; t < TT; ++t) {
@@ -829,26 +842,26 @@ struct PipeShapes {
 
 // The device's configuration choice (meta) selects the tile shape: this
 // kernel serves configurations 1 and 2 and returns at once for the others.
-template <int F, bool GATEUP>
+template <int F, bool GATEUP, int ACT>
 __global__ void __launch_bounds__(256) k_gemm_pipe(GemmArgs p) {
   using SH = PipeShapes<F, GATEUP>;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[SH::LDS4];
   const int cfg = p.meta[META_CFG];
   if (p.cfg_self >= 0 && cfg != p.cfg_self) return;
-  if (cfg == 1) pipe_body<F, GATEUP, 32, SH::NR_SMALL, 1, 4>(p, lds);
-  else if (cfg == 2) pipe_body<F, GATEUP, 64, SH::NR_SMALL, 1, 4>(p, lds);
+  if (cfg == 1) pipe_body<F, GATEUP, 32, SH::NR_SMALL, 1, 4, ACT>(p, lds);
+  else if (cfg == 2) pipe_body<F, GATEUP, 64, SH::NR_SMALL, 1, 4, ACT>(p, lds);
 }
 
 // Configuration 3 (128-row blocks).
-template <int F, bool GATEUP>
+template <int F, bool GATEUP, int ACT>
 __global__ void __launch_bounds__(Pipe8Waves<F>::NW * 64) k_gemm_pipe8(GemmArgs p) {
   using SH = PipeShapes<F, GATEUP>;
   constexpr int WM = Pipe8Waves<F>::WM, NW = Pipe8Waves<F>::NW;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[SH::LDS8];
   const int cfg = p.meta[META_CFG];
   if (cfg != 3 || (p.cfg_self >= 0 && cfg != p.cfg_self)) return;
-  if (GATEUP || p.N % 256 == 0) pipe_body<F, GATEUP, 128, 256, WM, NW>(p, lds);
-  else if constexpr (!GATEUP) pipe_body<F, GATEUP, 128, 128, WM, NW>(p, lds);
+  if (GATEUP || p.N % 256 == 0) pipe_body<F, GATEUP, 128, 256, WM, NW, ACT>(p, lds);
+  else if constexpr (!GATEUP) pipe_body<F, GATEUP, 128, 128, WM, NW, ACT>(p, lds);
 }
 
 namespace {
@@ -871,9 +884,19 @@ hipError_t launch_pipe_t(int family, const GemmArgs& g, hipStream_t st) {
   // persistent grid: one workgroup per CU (the stage ring fills the LDS),
   // a multiple of the 8 XCDs
   const unsigned grid = (unsigned)pipe_cus();
-  if (family == 0) hipLaunchKernelGGL((k_gemm_pipe<F, GATEUP>), dim3(grid), dim3(256), 0, st, g);
-  else hipLaunchKernelGGL((k_gemm_pipe8<F, GATEUP>), dim3(grid), dim3(Pipe8Waves<F>::NW * 64), 0, st, g);
-  return hipGetLastError();
+  const dim3 b8(Pipe8Waves<F>::NW * 64);
+  if constexpr (GATEUP) {
+    return with_act(g.act, [&](auto a) {
+      constexpr int ACT = decltype(a)::value;
+      if (family == 0) hipLaunchKernelGGL((k_gemm_pipe<F, true, ACT>), dim3(grid), dim3(256), 0, st, g);
+      else hipLaunchKernelGGL((k_gemm_pipe8<F, true, ACT>), dim3(grid), b8, 0, st, g);
+      return hipGetLastError();
+    });
+  } else {
+    if (family == 0) hipLaunchKernelGGL((k_gemm_pipe<F, false, ACT_SWIGLU>), dim3(grid), dim3(256), 0, st, g);
+    else hipLaunchKernelGGL((k_gemm_pipe8<F, false, ACT_SWIGLU>), dim3(grid), b8, 0, st, g);
+    return hipGetLastError();
+  }
 }
 
 }  // namespace

@@ -21,7 +21,8 @@ struct WScale {
   }
 };
 
-template <int F, bool GATEUP, int WAVES, int MT>
+// ACT: the gate/up epilogue's activation (ACT_*).
+template <int F, bool GATEUP, int WAVES, int MT, int ACT>
 __global__ void __launch_bounds__(WAVES * 64) k_gemm_stream(GemmArgs p) {
   constexpr int WB = FmtBits<F>::W, XB = FmtBits<F>::X;
   constexpr int NW = GATEUP ? 2 : 1;
@@ -172,7 +173,8 @@ __global__ void __launch_bounds__(WAVES * 64) k_gemm_stream(GemmArgs p) {
         if (GATEUP) {
           f32x4 h;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) h[i] = silu(v0[i]) * v1[i];
+          for (int i = 0; i < 4; ++i)
+            h[i] = gated_act<ACT>(p.act_limit, v0[i], v1[i]);
           if (F == F_BF16) {
             uint32_t lo = (uint32_t)f32_to_bf16(h[0]) | ((uint32_t)f32_to_bf16(h[1]) << 16);
             uint32_t hi = (uint32_t)f32_to_bf16(h[2]) | ((uint32_t)f32_to_bf16(h[3]) << 16);
@@ -189,18 +191,27 @@ __global__ void __launch_bounds__(WAVES * 64) k_gemm_stream(GemmArgs p) {
   }
 }
 
-template <int F, bool GATEUP>
-static hipError_t stream_waves(const GemmArgs& g, hipStream_t st) {
+template <int F, bool GATEUP, int ACT>
+static hipError_t stream_waves_x(const GemmArgs& g, hipStream_t st) {
   const int steps = g.K / 128;
   dim3 grid((unsigned)g.max_groups * (unsigned)(g.N / 16));
   if (grid.x == 0) return hipSuccess;
   if (steps % 4 == 0)
-    hipLaunchKernelGGL((k_gemm_stream<F, GATEUP, 4, 4>), grid, dim3(256), 0, st, g);
+    hipLaunchKernelGGL((k_gemm_stream<F, GATEUP, 4, 4, ACT>), grid, dim3(256), 0, st, g);
   else if (steps % 2 == 0)
-    hipLaunchKernelGGL((k_gemm_stream<F, GATEUP, 2, 4>), grid, dim3(128), 0, st, g);
+    hipLaunchKernelGGL((k_gemm_stream<F, GATEUP, 2, 4, ACT>), grid, dim3(128), 0, st, g);
   else
-    hipLaunchKernelGGL((k_gemm_stream<F, GATEUP, 1, 4>), grid, dim3(64), 0, st, g);
+    hipLaunchKernelGGL((k_gemm_stream<F, GATEUP, 1, 4, ACT>), grid, dim3(64), 0, st, g);
   return hipGetLastError();
+}
+
+template <int F, bool GATEUP>
+static hipError_t stream_waves(const GemmArgs& g, hipStream_t st) {
+  if constexpr (GATEUP) {
+    return with_act(g.act, [&](auto a) { return stream_waves_x<F, true, decltype(a)::value>(g, st); });
+  } else {
+    return stream_waves_x<F, false, ACT_SWIGLU>(g, st);
+  }
 }
 
 hipError_t launch_gemm_stream(int fmt, bool gateup, const GemmArgs& g, hipStream_t st) {

@@ -45,7 +45,8 @@ struct Lds {
 
 }  // namespace
 
-template <int F, bool GATEUP, int BM, int RTW>
+// ACT: the gate/up epilogue's activation (ACT_*).
+template <int F, bool GATEUP, int BM, int RTW, int ACT>
 __global__ void __launch_bounds__(THREADS) k_gemm_tiled(GemmArgs p) {
   using TF = TileFmt<F>;
   constexpr int XB = TF::XB, WB = TF::WB;
@@ -273,13 +274,24 @@ __global__ void __launch_bounds__(THREADS) k_gemm_tiled(GemmArgs p) {
         for (int rt = 0; rt < RTW; ++rt) store_down(p, m0 + r, nw0 + rt * 16 + 4 * lg, acc[0][rt][t]);
       }
     } else {
-      // h = SiLU(gate) * up, in place in acc[0]
+      // h = act(gate, up), in place in acc[0]
+      if constexpr (ACT == ACT_SWIGLU) {
 #pragma unroll
-      for (int rt = 0; rt < RTW; ++rt)
+        for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
-        for (int t = 0; t < TT; ++t)
+          for (int t = 0; t < TT; ++t)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[0][rt][t][i] = silu(acc[0][rt][t][i]) * acc[1][rt][t][i];
+            for (int i = 0; i < 4; ++i) acc[0][rt][t][i] = silu(acc[0][rt][t][i]) * acc[1][rt][t][i];
+      } else {
+        const float L = p.act_limit;
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+          for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[0][rt][t][i] = gated_act<ACT>(L, acc[0][rt][t][i], acc[1][rt][t][i]);
+      }
       if constexpr (F == F_BF16) {
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
@@ -406,7 +418,15 @@ hipError_t launch_one(const GemmArgs& g, hipStream_t st) {
   long grid = (long)cu_count() * 2;
   if (grid > items) grid = items;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL((k_gemm_tiled<F, GATEUP, BM, RTW>), dim3((unsigned)grid), dim3(THREADS), 0, st, g);
+  if constexpr (GATEUP) {
+    with_act(g.act, [&](auto a) {
+      hipLaunchKernelGGL((k_gemm_tiled<F, true, BM, RTW, decltype(a)::value>), dim3((unsigned)grid),
+                         dim3(THREADS), 0, st, g);
+      return 0;
+    });
+  } else {
+    hipLaunchKernelGGL((k_gemm_tiled<F, false, BM, RTW, ACT_SWIGLU>), dim3((unsigned)grid), dim3(THREADS), 0, st, g);
+  }
   return hipGetLastError();
 }
 

@@ -107,6 +107,9 @@ struct GemmArgs {
   const float* row_w;
   const int32_t* row_w_idx;
   int row_w_n;
+  // gate/up op: expert activation (ACT_*) and its clamp
+  int act;
+  float act_limit;
 };
 
 // Store four consecutive down-projection outputs of one row.

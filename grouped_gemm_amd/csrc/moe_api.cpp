@@ -77,6 +77,9 @@ int validate_desc(const moe_layer_desc* d) {
   if (fmt_of(*d) < 0)
     return fail(MOE_EUNSUPPORTED, "unsupported weight/activation format pair (%d, %d)", d->w_format,
                 d->a_format);
+  if (d->activation < MOE_ACT_SWIGLU || d->activation > MOE_ACT_RELU2)
+    return fail(MOE_EINVAL, "unknown activation %d", d->activation);
+  if (!(d->act_limit == d->act_limit)) return fail(MOE_EINVAL, "act_limit is NaN");
   if (d->max_tokens < 1) return fail(MOE_EINVAL, "max_tokens must be >= 1");
   if ((long)d->max_tokens * d->top_k > (1L << 20))
     return fail(MOE_EUNSUPPORTED, "max_tokens * top_k must not exceed 1048576");
@@ -200,9 +203,18 @@ DispatchArgs dispatch_args(const moe_ws* ws, int T) {
   return a;
 }
 
+// The clamp of the bounded activations (the desc's, else 10 for bounded
+// SwiGLU and 7 for SwiGLU-OAI).
+float act_limit(const moe_layer_desc& d) {
+  if (d.act_limit > 0.0f) return d.act_limit;
+  return d.activation == MOE_ACT_SWIGLU_BOUNDED ? 10.0f : (d.activation == MOE_ACT_SWIGLU_OAI ? 7.0f : 0.0f);
+}
+
 GemmArgs gemm_args(const moe_ws* ws) {
   GemmArgs g{};
   g.E = ws->d.num_experts;
+  g.act = ws->d.activation;
+  g.act_limit = act_limit(ws->d);
   g.counts = ws->at<int32_t>(ws->L.counts);
   g.indptr = ws->at<int32_t>(ws->L.indptr);
   g.active = ws->at<int32_t>(ws->L.active);
@@ -300,13 +312,15 @@ int enqueue_layer(moe_ws* ws, const moe_weights* w, const uint16_t* x, const flo
   max_groups += d.shared_experts;
   if (max_groups > G) max_groups = G;
   GemmArgs g1 = gemm_args(ws);
-  g1.w0 = (const uint8_t*)w->w_gate;
+  // ReLU^2 has no gate projection: the up weights serve as both operands
+  const bool relu2 = d.activation == MOE_ACT_RELU2;
+  g1.w0 = (const uint8_t*)(relu2 ? w->w_up : w->w_gate);
   g1.w1 = (const uint8_t*)w->w_up;
-  g1.w0s = w->s_gate;
+  g1.w0s = relu2 ? w->s_up : w->s_gate;
   g1.w1s = w->s_up;
-  g1.sh_w0 = (const uint8_t*)w->sh_gate;
+  g1.sh_w0 = (const uint8_t*)(relu2 ? w->sh_up : w->sh_gate);
   g1.sh_w1 = (const uint8_t*)w->sh_up;
-  g1.sh_w0s = w->ss_gate;
+  g1.sh_w0s = relu2 ? w->ss_up : w->ss_gate;
   g1.sh_w1s = w->ss_up;
   g1.N = d.inter;
   g1.K = d.hidden;
@@ -367,13 +381,16 @@ int enqueue_layer(moe_ws* ws, const moe_weights* w, const uint16_t* x, const flo
 
 int check_weights(const moe_ws* ws, const moe_weights* w) {
   if (!w) return fail(MOE_EINVAL, "weights is NULL");
-  if (!w->w_gate || !w->w_up || !w->w_down) return fail(MOE_EINVAL, "null routed weight pointer");
-  if (ws->fmt != F_BF16 && (!w->s_gate || !w->s_up || !w->s_down))
+  // the two-weight ReLU^2 form reads no gate weights
+  const bool gate = ws->d.activation != MOE_ACT_RELU2;
+  if ((gate && !w->w_gate) || !w->w_up || !w->w_down)
+    return fail(MOE_EINVAL, "null routed weight pointer");
+  if (ws->fmt != F_BF16 && ((gate && !w->s_gate) || !w->s_up || !w->s_down))
     return fail(MOE_EINVAL, "null weight scale pointer");
   if (ws->d.shared_experts) {
-    if (!w->sh_gate || !w->sh_up || !w->sh_down)
+    if ((gate && !w->sh_gate) || !w->sh_up || !w->sh_down)
       return fail(MOE_EINVAL, "null shared-expert weight pointer");
-    if (ws->fmt != F_BF16 && (!w->ss_gate || !w->ss_up || !w->ss_down))
+    if (ws->fmt != F_BF16 && ((gate && !w->ss_gate) || !w->ss_up || !w->ss_down))
       return fail(MOE_EINVAL, "null shared-expert scale pointer");
   }
   return MOE_OK;
@@ -470,14 +487,19 @@ int moe_grouped_gemm(moe_ws* ws, int op, const void* a, const void* a_scale,
                      int K, const void* b0, const void* b0_scale, const void* b1,
                      const void* b1_scale, void* out, void* out_scale, void* stream) {
   if (!ws) return fail(MOE_EINVAL, "workspace is NULL");
-  if (op != MOE_OP_PLAIN && op != MOE_OP_GATEUP_SWIGLU) return fail(MOE_EINVAL, "unknown op");
+  if (op != MOE_OP_PLAIN && op != MOE_OP_GATEUP_ACT) return fail(MOE_EINVAL, "unknown op");
   if (E < 1 || E > ws->d.num_experts + ws->d.shared_experts)
     return fail(MOE_EINVAL, "E must be in [1, %d]", ws->d.num_experts + ws->d.shared_experts);
   if (N <= 0 || K <= 0 || N % 128 || K % 128)
     return fail(MOE_EUNSUPPORTED, "N and K must be positive multiples of 128");
   if (N > 16384 || K > 16384) return fail(MOE_EUNSUPPORTED, "N and K are limited to 16384");
-  const bool gateup = op == MOE_OP_GATEUP_SWIGLU;
+  const bool gateup = op == MOE_OP_GATEUP_ACT;
   const bool quant = ws->fmt != F_BF16;
+  // ReLU^2 has no gate projection: B1 (up) serves as both operands
+  if (gateup && ws->d.activation == MOE_ACT_RELU2) {
+    b0 = b1;
+    b0_scale = b1_scale;
+  }
   if (!a || !m_indptr || !b0 || !out || (gateup && !b1)) return fail(MOE_EINVAL, "null pointer");
   if (quant && (!a_scale || !b0_scale || (gateup && (!b1_scale || !out_scale))))
     return fail(MOE_EINVAL, "null scale pointer");

@@ -66,7 +66,21 @@ extern "C" {
 
 /* Grouped GEMM operations. */
 #define MOE_OP_PLAIN 0          /* out[r, n] = sum_k A[r,k] * B0[e,n,k], fp32 out */
-#define MOE_OP_GATEUP_SWIGLU 1  /* out[r, n] = SiLU(A*B0^T) * (A*B1^T), activation format */
+#define MOE_OP_GATEUP_ACT 1     /* out[r, n] = act(A*B0^T, A*B1^T), activation format */
+#define MOE_OP_GATEUP_SWIGLU MOE_OP_GATEUP_ACT  /* the default activation is SwiGLU */
+
+/* Expert activations, act(g, u) of the gate value g and the up value u
+ * (LightMoE README, "Compatibility" and "MoE inference": SwiGLU, bounded
+ * SwiGLU with an activation clamp, SwiGLU-OAI, GeGLU, ReGLU, ReLU^2 in the
+ * two-weight form).  The pages name them without formulas; L is the desc's
+ * act_limit (<= 0 selects 10 for bounded SwiGLU, 7 for SwiGLU-OAI). */
+#define MOE_ACT_SWIGLU 0          /* SiLU(g) * u */
+#define MOE_ACT_SWIGLU_BOUNDED 1  /* SiLU(min(g, L)) * clamp(u, -L, L) */
+#define MOE_ACT_SWIGLU_OAI 2      /* g' sigmoid(1.702 g') (clamp(u, -L, L) + 1), g' = min(g, L) */
+#define MOE_ACT_GEGLU 3           /* g (1 + erf(g / sqrt 2)) / 2 * u */
+#define MOE_ACT_REGLU 4           /* max(g, 0) * u */
+#define MOE_ACT_RELU2 5           /* max(u, 0)^2: no gate projection (w_gate unused, may be
+                                     NULL; the GEMM's B0 may be NULL) */
 
 typedef struct moe_ws moe_ws; /* opaque host handle */
 
@@ -84,6 +98,8 @@ typedef struct moe_layer_desc {
   int a_format;        /* MOE_A_*; pairs: BF16/BF16, FP8_CHANNEL/FP8_TOKEN,
                           FP8_BLOCK128/FP8_G128, MXFP4/MXFP8_G32 */
   int max_tokens;      /* T capacity; T*top_k must not exceed 1,048,576 */
+  int activation;      /* MOE_ACT_* (0 = SwiGLU) */
+  float act_limit;     /* clamp L of the bounded activations; <= 0: their default */
 } moe_layer_desc;
 
 /* Caller-owned expert weights, layout [E, N, K] K-contiguous (see formats). */
@@ -143,7 +159,7 @@ MOE_API int moe_dispatch(moe_ws* ws, const int32_t* topk_ids, int T, int k, int 
 /* Grouped GEMM over expert-major rows, one launch for all experts and no
  * padding (pure-Triton MoE commentary, second paragraph: block-id ->
  * (expert, offset) map; LightMoE README, "Grouped GEMM").
- *   op        MOE_OP_PLAIN or MOE_OP_GATEUP_SWIGLU
+ *   op        MOE_OP_PLAIN or MOE_OP_GATEUP_ACT (the workspace's activation)
  *   a         activation rows in the workspace's activation format:
  *             bf16 [rows, K] for A_BF16, else e4m3 codes [rows, K]
  *   a_scale   activation scales: fp32 [rows] (FP8_TOKEN), fp32 [rows, K/128]
@@ -154,8 +170,9 @@ MOE_API int moe_dispatch(moe_ws* ws, const int32_t* topk_ids, int T, int k, int 
  *   m_indptr  [E+1] int32, m_indptr[E] = total rows R (<= workspace capacity)
  *   N, K      output columns and contraction length; b0/b1 are [E, N, K]
  *             in the workspace's weight format with scales b0_scale/b1_scale
- *             (b1 only for GATEUP_SWIGLU)
- *   out       PLAIN: fp32 [R, N].  GATEUP_SWIGLU: h in the activation
+ *             (b1 only for GATEUP_ACT; b0 unused and may be NULL for
+ *             MOE_ACT_RELU2)
+ *   out       PLAIN: fp32 [R, N].  GATEUP_ACT: h in the activation
  *             format (bf16 [R, N], or e4m3 codes [R, N] + out_scale as for
  *             a_scale with K replaced by N)
  * Errors: EINVAL, EUNSUPPORTED (N or K not a multiple of 128), ECAPACITY. */
@@ -182,8 +199,8 @@ MOE_API int moe_combine(moe_ws* ws, const float* out_slot, const float* topk_w, 
                 uint16_t* y_bf16, void* stream);
 
 /* The whole layer: x bf16 [T, H] and router scores [T, E] -> y bf16 [T, H].
- * Runs routing, dispatch, activation quantisation, the fused gate/up SwiGLU
- * grouped GEMM, intermediate requantisation, the down grouped GEMM and the
+ * Runs routing, dispatch, activation quantisation, the fused gate/up
+ * grouped GEMM with the desc's activation in its epilogue, intermediate requantisation, the down grouped GEMM and the
  * combine.  The tile configuration is chosen on the device from the expert
  * histogram (RaMP abstract: configuration from the runtime routing
  * distribution, not batch size alone).  T = 0 is a no-op.

@@ -44,7 +44,8 @@ def workspace(shape, max_tokens) -> g.Workspace:
     return g.Workspace(shape.hidden, shape.inter, shape.experts, shape.top_k, max_tokens,
                        shared_experts=shape.shared, shared_inter=shape.shared_inter,
                        score_fn=shape.score_fn, w_format=shape.w_format,
-                       a_format=shape.a_format)
+                       a_format=shape.a_format, activation=shape.activation,
+                       act_limit=shape.act_limit)
 
 
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:

@@ -33,7 +33,7 @@ def test_library_exports_every_header_symbol():
 def _desc(**kw):
     base = dict(hidden=4096, inter=14336, num_experts=8, top_k=2, shared_experts=0,
                 shared_inter=0, score_fn=0, renormalize=1, w_format=1, a_format=1,
-                max_tokens=128)
+                max_tokens=128, activation=0, act_limit=0.0)
     base.update(kw)
     return g.LayerDesc(*[base[n] for n, _ in g.LayerDesc._fields_])
 
@@ -43,6 +43,7 @@ def _desc(**kw):
     (dict(hidden=4000), 2), (dict(inter=100), 2), (dict(w_format=1, a_format=2), 2),
     (dict(renormalize=0), 2), (dict(shared_experts=1, shared_inter=1024), 2),
     (dict(score_fn=7), 1), (dict(max_tokens=0), 1), (dict(max_tokens=1 << 20, top_k=2), 2),
+    (dict(activation=6), 1), (dict(activation=-1), 1), (dict(act_limit=float("nan")), 1),
 ])
 def test_workspace_size_validation(kw, code):
     lib = C.CDLL(g.library_path())
