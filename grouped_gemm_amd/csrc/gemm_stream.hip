@@ -21,12 +21,16 @@ struct WScale {
   }
 };
 
-// ACT: the gate/up epilogue's activation (ACT_*).
-template <int F, bool GATEUP, int WAVES, int MT, int ACT>
+// ACT: the gate/up epilogue's activation (ACT_*).  MT: 16-row token tiles
+// per pass; U: K steps whose loads are issued together.  Groups of at most
+// 16 rows (decode) run MT = 1, U = 2: the registers of the unused tiles and
+// of deep load batches would cut the waves per SIMD, and at decode sizes
+// more waves in flight move more bytes (Mixtral-shaped T=1 layer 97 ->
+// 84 us) than deeper batches per wave.
+template <int F, bool GATEUP, int WAVES, int MT, int ACT, int U>
 __global__ void __launch_bounds__(WAVES * 64) k_gemm_stream(GemmArgs p) {
   constexpr int WB = FmtBits<F>::W, XB = FmtBits<F>::X;
   constexpr int NW = GATEUP ? 2 : 1;
-  constexpr int U = 4;   // K steps whose loads are issued together
   const int nblk = p.N >> 4;
   const int gi = blockIdx.x / nblk, nb = blockIdx.x - gi * nblk;
   if (p.cfg_self >= 0 && p.meta[META_CFG] != p.cfg_self) return;
@@ -196,12 +200,14 @@ static hipError_t stream_waves_x(const GemmArgs& g, hipStream_t st) {
   const int steps = g.K / 128;
   dim3 grid((unsigned)g.max_groups * (unsigned)(g.N / 16));
   if (grid.x == 0) return hipSuccess;
-  if (steps % 4 == 0)
-    hipLaunchKernelGGL((k_gemm_stream<F, GATEUP, 4, 4, ACT>), grid, dim3(256), 0, st, g);
+  if (g.max_group_rows <= 16 && steps % 4 == 0)
+    hipLaunchKernelGGL((k_gemm_stream<F, GATEUP, 4, 1, ACT, 2>), grid, dim3(256), 0, st, g);
+  else if (steps % 4 == 0)
+    hipLaunchKernelGGL((k_gemm_stream<F, GATEUP, 4, 4, ACT, 4>), grid, dim3(256), 0, st, g);
   else if (steps % 2 == 0)
-    hipLaunchKernelGGL((k_gemm_stream<F, GATEUP, 2, 4, ACT>), grid, dim3(128), 0, st, g);
+    hipLaunchKernelGGL((k_gemm_stream<F, GATEUP, 2, 4, ACT, 4>), grid, dim3(128), 0, st, g);
   else
-    hipLaunchKernelGGL((k_gemm_stream<F, GATEUP, 1, 4, ACT>), grid, dim3(64), 0, st, g);
+    hipLaunchKernelGGL((k_gemm_stream<F, GATEUP, 1, 4, ACT, 4>), grid, dim3(64), 0, st, g);
   return hipGetLastError();
 }
 

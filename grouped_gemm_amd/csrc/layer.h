@@ -101,6 +101,7 @@ struct GemmArgs {
   void* out_scale;        // gate/up with in-kernel requantisation: h scales
   int max_groups;         // grid bound on active groups
   int max_rows;           // grid bound on rows (all groups)
+  int max_group_rows;     // bound on the rows of any one group
   // down projection of the layer: when row_w is set, row `slot` is scaled by
   // its routing weight row_w[row_w_idx[slot]] (1 for slot >= row_w_n, the
   // shared expert) and stored as bf16; otherwise stored as fp32

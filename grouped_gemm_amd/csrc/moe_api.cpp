@@ -221,6 +221,7 @@ GemmArgs gemm_args(const moe_ws* ws) {
   g.tiles = ws->at<int32_t>(ws->L.tiles);
   g.meta = ws->at<int32_t>(ws->L.meta);
   g.cfg_self = -1;
+  g.max_group_rows = 1 << 30;
   return g;
 }
 
@@ -229,7 +230,8 @@ GemmArgs gemm_args(const moe_ws* ws) {
 // most min(G, rows_tot) groups.  The device rule picks the streaming kernel
 // exactly when a 32-row tiled grid would have fewer items than CUs, with
 // items = (sum over groups of ceil(rows/32)) * (I/128), and that sum lies in
-// [ceil(rows_tot/32), ceil(rows_tot/32) + groups].  A forced configuration
+// [ceil(rows_tot/32), floor((rows_tot + 31 * groups) / 32)] (each group
+// adds at most 31/32 of a tile to its exact share).  A forced configuration
 // is known outright.
 struct Candidates {
   bool stream, small, big;   // streaming kernel; tiled configurations 1-2; configuration 3
@@ -240,7 +242,7 @@ Candidates candidates(const moe_ws* ws, long rows_tot) {
   const long cus = device_cus(), cb = ws->d.inter / 128;
   const long G = ws->L.G;
   const long groups = rows_tot < G ? rows_tot : G;
-  const long lo = (rows_tot + 31) / 32, hi = lo + groups;
+  const long lo = (rows_tot + 31) / 32, hi = (rows_tot + 31 * groups) / 32;
   const bool tiled = hi * cb >= cus;
   // configuration 3 needs a group above 64 rows, at least 64 rows per
   // active group and CFG3_MIN_ROWS rows; it is certain when every group
@@ -331,6 +333,7 @@ int enqueue_layer(moe_ws* ws, const moe_weights* w, const uint16_t* x, const flo
   g1.out = ws->at<void>(L.h);
   g1.max_groups = max_groups;
   g1.max_rows = S_tot;
+  g1.max_group_rows = T;   // a token takes at most one slot per group
   // the tiled kernels requantise 1x128 and MX intermediates themselves
   const bool fused_requant = ws->fmt == F_FP8_BLK || ws->fmt == F_MX;
   HIP_TRY(mark(2, 0), "event record");
@@ -365,6 +368,7 @@ int enqueue_layer(moe_ws* ws, const moe_weights* w, const uint16_t* x, const flo
   g2.out = ws->at<void>(L.out_slot);
   g2.max_groups = max_groups;
   g2.max_rows = S_tot;
+  g2.max_group_rows = T;
   g2.row_w = ws->at<float>(L.w);          // weight of slot = w[gather[slot]]
   g2.row_w_idx = ws->at<int32_t>(L.gather);
   g2.row_w_n = S;
@@ -527,6 +531,7 @@ int moe_grouped_gemm(moe_ws* ws, int op, const void* a, const void* a_scale,
   g.gather_div = a_gather ? gather_div : 1;
   g.max_groups = E;
   g.max_rows = (int)cap;
+  g.max_group_rows = (int)cap;
   g.cfg_self = -1;
   if (gateup && quant) {
     g.out = ws->at<void>(ws->L.h);

@@ -220,6 +220,29 @@ def test_layer_every_config_matches_oracle(name, sh, T):
     ws.force_config(-1)
 
 
+DECODE = [(n, sh) for n, sh, _ in SMALL[:5]]
+
+
+@pytest.mark.parametrize("T", [1, 7, 16])
+@pytest.mark.parametrize("name,sh", DECODE, ids=[c[0] for c in DECODE])
+def test_layer_decode_streaming_matches_oracle(name, sh, T):
+    """Streaming configuration at decode sizes (every group holds at most 16
+    rows: the single-tile streaming kernels), every format."""
+    say("layer decode", name, T)
+    W = ms.gen_weights(sh)
+    B = ms.gen_batch(sh, T)
+    ws = workspace(sh, T)
+    ws.force_config(0)
+    y = run_layer(ws, dev_weights(W), B.x_bits, B.scores)
+    assert ws.last_config() == 0
+    ids, w = check_routing(sh, T, ws_routing(ws, sh, T), B.scores)
+    ref = oracle.layer_forward(W, B.x_bits, ids, w)
+    err = relerr(bf16_to_f64(y), ref)
+    say("  relerr", err)
+    assert np.all(np.isfinite(bf16_to_f64(y)))
+    assert err <= tol_for(sh)
+
+
 def test_layer_with_no_tokens_is_a_no_op():
     """An empty batch is a valid call that launches nothing; the workspace
     serves a real batch right after it."""
