@@ -163,53 +163,64 @@ hipError_t launch_quant_rows(const QuantArgs& q, hipStream_t st) {
 // groups of CK, all loads of a group issued before any is used (slots past
 // k re-read the first row and are not added); rows are added in ascending
 // j, then the shared expert's.  WB: bf16 slot rows carrying their weights.
+// One item = one token's channel range of 256 eight-channel chunks (one
+// pass of the block), so a small batch still spreads over many blocks; the
+// item's slots and weights are read before its rows, and every row of the
+// item (the k routed rows, then the shared expert's) is fetched before any
+// is added.
 template <int CK, bool WB>
 __global__ void __launch_bounds__(256) k_combine(CombineArgs c) {
   const int H = c.H, nch = H / 8, k = c.k;
   const int S = c.T * k;
-  for (int t = blockIdx.x; t < c.T; t += gridDim.x) {
-    for (int ch = threadIdx.x; ch < nch; ch += 256) {
-      float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int j0 = 0; j0 < k; j0 += CK) {
-        int slot[CK];
-        float wj[CK];
+  const int nsplit = (nch + 255) / 256;
+  for (int item = blockIdx.x; item < c.T * nsplit; item += gridDim.x) {
+    const int t = item / nsplit;
+    const int ch = (item - t * nsplit) * 256 + threadIdx.x;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j0 = 0; j0 < k; j0 += CK) {
+      int slot[CK];
+      float wj[CK];
 #pragma unroll
-        for (int u = 0; u < CK; ++u) {
-          const int j = j0 + u < k ? j0 + u : j0;
-          slot[u] = ldu(c.inv + (size_t)t * k + j);
-          wj[u] = WB ? 1.0f : ldu(c.w + (size_t)t * k + j);
-        }
-        QrChunk<WB> raw[CK];
+      for (int u = 0; u < CK; ++u) {
+        const int j = j0 + u < k ? j0 + u : j0;
+        slot[u] = ldu(c.inv + (size_t)t * k + j);
+        wj[u] = WB ? 1.0f : ldu(c.w + (size_t)t * k + j);
+      }
+      if (ch >= nch) continue;
+      QrChunk<WB> raw[CK + 1];
 #pragma unroll
-        for (int u = 0; u < CK; ++u) raw[u] = qr_fetch<WB>(c.out_slot, (size_t)slot[u], H, ch);
+      for (int u = 0; u < CK; ++u) raw[u] = qr_fetch<WB>(c.out_slot, (size_t)slot[u], H, ch);
+      const bool sh = c.shared && j0 + CK >= k;   // the last pass also takes the shared row
+      if (sh) raw[CK] = qr_fetch<WB>(c.out_slot, (size_t)(S + t), H, ch);
 #pragma unroll
-        for (int u = 0; u < CK; ++u) {
-          if (j0 + u < k) {
-            float v[8];
-            qr_unpack<WB>(raw[u], v);
+      for (int u = 0; u < CK; ++u) {
+        if (j0 + u < k) {
+          float v[8];
+          qr_unpack<WB>(raw[u], v);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] += wj[u] * v[i];
-          }
+          for (int i = 0; i < 8; ++i) acc[i] += wj[u] * v[i];
         }
       }
-      if (c.shared) {
+      if (sh) {
         float v[8];
-        qr_unpack<WB>(qr_fetch<WB>(c.out_slot, (size_t)(S + t), H, ch), v);
+        qr_unpack<WB>(raw[CK], v);
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] += v[i];
       }
-      uint32_t p[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        p[i] = (uint32_t)f32_to_bf16(acc[2 * i]) | ((uint32_t)f32_to_bf16(acc[2 * i + 1]) << 16);
-      *(uint4*)(c.y + (size_t)t * H + 8 * ch) = make_uint4(p[0], p[1], p[2], p[3]);
     }
+    if (ch >= nch) continue;
+    uint32_t p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      p[i] = (uint32_t)f32_to_bf16(acc[2 * i]) | ((uint32_t)f32_to_bf16(acc[2 * i + 1]) << 16);
+    *(uint4*)(c.y + (size_t)t * H + 8 * ch) = make_uint4(p[0], p[1], p[2], p[3]);
   }
 }
 
 hipError_t launch_combine(const CombineArgs& c, hipStream_t st) {
   if (c.T == 0) return hipSuccess;
-  const dim3 grid(elementwise_grid(c.T)), block(256);
+  const int nsplit = (c.H / 8 + 255) / 256;
+  const dim3 grid(elementwise_grid(c.T * nsplit)), block(256);
   if (c.weighted_bf16) {
     if (c.k <= 2) hipLaunchKernelGGL((k_combine<2, true>), grid, block, 0, st, c);
     else if (c.k <= 4) hipLaunchKernelGGL((k_combine<4, true>), grid, block, 0, st, c);
