@@ -235,6 +235,52 @@ def cpu_baseline(pt, n_tokens):
                       f"({full:.1f}s per layer call)"}
 
 
+def config_sweep(name, T, act=0, rounds=3, calls=30):
+    """Median µs per layer call (eager, one launch sequence per call) for the
+    device's own configuration choice and for every forced configuration,
+    interleaved over `rounds` rounds after at least one second of warm-up
+    (the best median of each is kept; the first calls after the weights are
+    placed run several percent slower)."""
+    import torch
+    import grouped_gemm_amd as g
+    sh, B, W, dW, ws, x, s, y, n_active = setup(name, T, act=act)
+    ws.set_graphs(False)
+    ncfg = 3 if sh.w_format == 0 else 4
+    st = torch.cuda.Stream()
+
+    def median_us(n):
+        with torch.cuda.stream(st):
+            ts = []
+            for _ in range(n):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(st)
+                g.layer_forward(ws, dW, x, s, y, stream=st)
+                e1.record(st)
+                e1.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3)
+        return float(np.median(ts))
+
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 1.0:  # clocks and caches settle first
+        median_us(10)
+    best, chosen = {}, None
+    for r in range(rounds):
+        order = [-1] + list(range(ncfg))
+        for c in (order if r % 2 == 0 else order[::-1]):
+            ws.force_config(c)
+            median_us(3)
+            us = median_us(calls)
+            best[c] = min(best.get(c, 1e30), us)
+            if c < 0:
+                chosen = ws.last_config()
+    ws.force_config(-1)
+    fastest = min(range(ncfg), key=lambda c: best[c])
+    return {"workload": name, "tokens": T, "auto_config": chosen, "auto_us": round(best[-1], 1),
+            "forced_us": {str(c): round(best[c], 1) for c in range(ncfg)},
+            "fastest_config": fastest, "auto_over_fastest": round(best[-1] / best[fastest] - 1, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -250,6 +296,10 @@ def main():
                     help="tile configuration (default: chosen on the device)")
     ap.add_argument("--activation", default="swiglu", choices=list(ACTIVATIONS),
                     help="expert activation of every timed point (default SwiGLU)")
+    ap.add_argument("--config-sweep", action="store_true",
+                    help="time the device's configuration choice against every forced "
+                         "configuration at each token count of the workload (or --tokens) "
+                         "and print one JSON line per point instead of the benchmark line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain elementwise copy of 256 MiB (fp32 in, fp32 out), "
                          "whose known byte counts calibrate hardware traffic counters")
@@ -277,6 +327,10 @@ def main():
         del a, b
     act = ACTIVATIONS[args.activation]
     sh0 = ms.CONFIGS[args.workload]
+    if args.config_sweep:
+        for T in ([args.tokens] if args.tokens else list(sh0.tokens)):
+            print(json.dumps(config_sweep(args.workload, T, act)), flush=True)
+        return
     T_main = args.tokens or max(sh0.tokens)
     points = []
     extra_T = [t for t in sh0.tokens if t != T_main and t >= 16] if not args.tokens else []

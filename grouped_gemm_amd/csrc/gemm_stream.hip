@@ -200,7 +200,7 @@ static hipError_t stream_waves_x(const GemmArgs& g, hipStream_t st) {
   const int steps = g.K / 128;
   dim3 grid((unsigned)g.max_groups * (unsigned)(g.N / 16));
   if (grid.x == 0) return hipSuccess;
-  if (g.max_group_rows <= 16 && steps % 4 == 0)
+  if (g.max_group_rows <= DECODE_STREAM_TOKENS && steps % 4 == 0)
     hipLaunchKernelGGL((k_gemm_stream<F, GATEUP, 4, 1, ACT, 2>), grid, dim3(256), 0, st, g);
   else if (steps % 4 == 0)
     hipLaunchKernelGGL((k_gemm_stream<F, GATEUP, 4, 4, ACT, 4>), grid, dim3(256), 0, st, g);

@@ -76,6 +76,10 @@ struct DispatchArgs {
 };
 
 // Grouped GEMM over expert-major row groups.
+// Batches of at most this many tokens take the streaming configuration (every
+// group then holds at most this many rows: one 16-row token tile).
+constexpr int DECODE_STREAM_TOKENS = 16;
+
 struct GemmArgs {
   const uint8_t* w0;      // routed weights [E, N, K] (gate or down)
   const uint8_t* w1;      // routed up weights (gate/up op)

@@ -236,9 +236,11 @@ GemmArgs gemm_args(const moe_ws* ws) {
 struct Candidates {
   bool stream, small, big;   // streaming kernel; tiled configurations 1-2; configuration 3
 };
-Candidates candidates(const moe_ws* ws, long rows_tot) {
+Candidates candidates(const moe_ws* ws, long rows_tot, int T) {
   if (ws->force_cfg >= 0)
     return {ws->force_cfg == 0, ws->force_cfg == 1 || ws->force_cfg == 2, ws->force_cfg == 3};
+  // the device rule streams every batch of at most DECODE_STREAM_TOKENS tokens
+  if (T <= DECODE_STREAM_TOKENS || num_cfgs(ws->fmt) <= 1) return {true, false, false};
   const long cus = device_cus(), cb = ws->d.inter / 128;
   const long G = ws->L.G;
   const long groups = rows_tot < G ? rows_tot : G;
@@ -258,8 +260,8 @@ Candidates candidates(const moe_ws* ws, long rows_tot) {
 // tiled kernels, which requantise the intermediate in their epilogue for the
 // 1x128 and MX formats.
 hipError_t run_gemm(const moe_ws* ws, bool gateup, GemmArgs g, void* tiled_out, void* tiled_scale,
-                    long rows_tot, hipStream_t st) {
-  const Candidates cand = candidates(ws, rows_tot);
+                    long rows_tot, int T, hipStream_t st) {
+  const Candidates cand = candidates(ws, rows_tot, T);
   if (cand.stream) {
     g.cfg_self = 0;
     hipError_t e = launch_gemm_stream(ws->fmt, gateup, g, st);
@@ -338,12 +340,12 @@ int enqueue_layer(moe_ws* ws, const moe_weights* w, const uint16_t* x, const flo
   const bool fused_requant = ws->fmt == F_FP8_BLK || ws->fmt == F_MX;
   HIP_TRY(mark(2, 0), "event record");
   HIP_TRY(run_gemm(ws, true, g1, fused_requant ? ws->at<void>(L.hq) : nullptr,
-                   fused_requant ? ws->at<void>(L.hs) : nullptr, S_tot, st),
+                   fused_requant ? ws->at<void>(L.hs) : nullptr, S_tot, T, st),
           "gate/up grouped GEMM launch");
   HIP_TRY(mark(2, 1), "event record");
   // with the fused requantisation only the streaming configuration leaves
   // fp32 h behind; skip the launch when that configuration cannot occur
-  if (quant && (!fused_requant || candidates(ws, S_tot).stream)) {
+  if (quant && (!fused_requant || candidates(ws, S_tot, T).stream)) {
     QuantArgs q{ws->at<void>(L.h), 0, S_tot, d.inter, nullptr, ws->at<uint8_t>(L.hq),
                 ws->at<void>(L.hs), d.a_format};
     if (fused_requant) {   // only the streaming configuration left fp32 h behind
@@ -373,7 +375,7 @@ int enqueue_layer(moe_ws* ws, const moe_weights* w, const uint16_t* x, const flo
   g2.row_w_idx = ws->at<int32_t>(L.gather);
   g2.row_w_n = S;
   HIP_TRY(mark(4, 0), "event record");
-  HIP_TRY(run_gemm(ws, false, g2, nullptr, nullptr, S_tot, st), "down grouped GEMM launch");
+  HIP_TRY(run_gemm(ws, false, g2, nullptr, nullptr, S_tot, T, st), "down grouped GEMM launch");
   HIP_TRY(mark(4, 1), "event record");
   CombineArgs c{ws->at<void>(L.out_slot), ws->at<float>(L.w), ws->at<int32_t>(L.inv), T,
                 d.top_k, d.hidden, d.shared_experts, y, 1};

@@ -293,6 +293,9 @@ DEVI void block_exclusive_scan(int32_t* a, int n, int32_t* wsum, int32_t* total)
 // kernel configuration depends on the routing distribution, not on the batch
 // size alone).  Statistics of the histogram: the active groups A, the largest
 // group m, the mean group r = rows / A.  The rule, in order:
+//  0. a batch of at most 16 tokens (every group then holds at most 16 rows)
+//     -> cfg 0: the single-tile streaming kernel measured as fast as or
+//     faster than 32-row tiles there (Mixtral-shaped T=8/16: 3-5% faster);
 //  1. the work items a 32-row tiled grid would have (row blocks times output
 //     channel blocks of the first projection) cannot fill the CUs -> cfg 0,
 //     the streaming kernel, which splits K across waves instead;
@@ -303,8 +306,8 @@ DEVI void block_exclusive_scan(int32_t* a, int n, int32_t* wsum, int32_t* total)
 //     highest MFMA intensity per staged byte); otherwise cfg 2.
 // The rule reproduces the fastest measured configuration on the benchmarked
 // layer shapes; a fitted cost model over these statistics can replace it.
-DEVI int config_rule(int mx, int active, int rows, int tiles32, int I, int num_cfgs, int cus) {
-  if (num_cfgs <= 1) return 0;
+DEVI int config_rule(int mx, int active, int rows, int tiles32, int I, int num_cfgs, int cus, int T) {
+  if (num_cfgs <= 1 || T <= DECODE_STREAM_TOKENS) return 0;
   const long items32 = (long)tiles32 * (I / 128);
   if (items32 < cus) return 0;
   if (mx <= 32) return 1;
@@ -313,7 +316,7 @@ DEVI int config_rule(int mx, int active, int rows, int tiles32, int I, int num_c
 }
 
 // The histogram statistics by one wave over the counts in LDS, then the rule.
-DEVI int choose_config(const int32_t* cnt, int G, int I, int num_cfgs, int cus, int lane,
+DEVI int choose_config(const int32_t* cnt, int G, int I, int num_cfgs, int cus, int T, int lane,
                       int* max_out) {
   int mx = 0, active = 0, rows = 0, tiles32 = 0;
   for (int g = lane; g < G; g += 64) {
@@ -332,7 +335,7 @@ DEVI int choose_config(const int32_t* cnt, int G, int I, int num_cfgs, int cus, 
     tiles32 += __shfl_xor(tiles32, o, 64);
   }
   *max_out = mx;
-  return config_rule(mx, active, rows, tiles32, I, num_cfgs, cus);
+  return config_rule(mx, active, rows, tiles32, I, num_cfgs, cus, T);
 }
 
 // Shared tail of both dispatch paths.  cnt (LDS, G entries) holds the
@@ -353,7 +356,7 @@ DEVI void finalize_dispatch(const DispatchArgs& d, int32_t* cnt, int32_t* scan_b
   if (tid < 64) {
     // one wave derives the configuration from the histogram
     int mx = 0;
-    int cfg = choose_config(cnt, G, d.I, d.num_cfgs, d.cus, tid, &mx);
+    int cfg = choose_config(cnt, G, d.I, d.num_cfgs, d.cus, d.T, tid, &mx);
     if (d.force_cfg >= 0) cfg = d.force_cfg;
     if (tid == 0) {
       s_max = mx;
@@ -581,7 +584,7 @@ __global__ void __launch_bounds__(256) k_dispatch_tiny(DispatchArgs d) {
     mx = v > mx ? v : mx;
     t32 += __shfl_xor(t32, o, 64);
   }
-  int cfg = config_rule(mx, __popcll(act), total, t32, d.I, d.num_cfgs, d.cus);
+  int cfg = config_rule(mx, __popcll(act), total, t32, d.I, d.num_cfgs, d.cus, d.T);
   if (d.force_cfg >= 0) cfg = d.force_cfg;
   // block table for the chosen row-block height
   const int bm = cfg_rows(cfg);
