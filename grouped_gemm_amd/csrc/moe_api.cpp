@@ -228,7 +228,8 @@ GemmArgs gemm_args(const moe_ws* ws) {
 // Which kernel families the device's choice can land on, from bounds the
 // host knows without reading the histogram: rows_tot rows spread over at
 // most min(G, rows_tot) groups.  The device rule picks the streaming kernel
-// exactly when a 32-row tiled grid would have fewer items than CUs, with
+// for batches of at most DECODE_STREAM_TOKENS tokens, and otherwise exactly
+// when a 32-row tiled grid would have fewer items than half the CUs, with
 // items = (sum over groups of ceil(rows/32)) * (I/128), and that sum lies in
 // [ceil(rows_tot/32), floor((rows_tot + 31 * groups) / 32)] (each group
 // adds at most 31/32 of a tile to its exact share).  A forced configuration
@@ -245,13 +246,13 @@ Candidates candidates(const moe_ws* ws, long rows_tot, int T) {
   const long G = ws->L.G;
   const long groups = rows_tot < G ? rows_tot : G;
   const long lo = (rows_tot + 31) / 32, hi = (rows_tot + 31 * groups) / 32;
-  const bool tiled = hi * cb >= cus;
+  const bool tiled = 2 * hi * cb >= cus;
   // configuration 3 needs a group above 64 rows, at least 64 rows per
   // active group and CFG3_MIN_ROWS rows; it is certain when every group
   // count bound forces it (mean over all groups above 64, enough items)
   const bool big = tiled && num_cfgs(ws->fmt) > 3 && rows_tot >= CFG3_MIN_ROWS && rows_tot > 64;
-  const bool big_certain = big && lo * cb >= cus && rows_tot > 64 * G;
-  return {lo * cb < cus, tiled && !big_certain, big};
+  const bool big_certain = big && 2 * lo * cb >= cus && rows_tot > 64 * G;
+  return {2 * lo * cb < cus, tiled && !big_certain, big};
 }
 
 // Run a projection with the kernel families the configuration can land on;

@@ -297,8 +297,10 @@ DEVI void block_exclusive_scan(int32_t* a, int n, int32_t* wsum, int32_t* total)
 //     -> cfg 0: the single-tile streaming kernel measured as fast as or
 //     faster than 32-row tiles there (Mixtral-shaped T=8/16: 3-5% faster);
 //  1. the work items a 32-row tiled grid would have (row blocks times output
-//     channel blocks of the first projection) cannot fill the CUs -> cfg 0,
-//     the streaming kernel, which splits K across waves instead;
+//     channel blocks of the first projection) cannot fill half the CUs ->
+//     cfg 0, the streaming kernel, which splits K across waves instead (with
+//     rule 0 in place, larger batches leave it candidate only for layers
+//     this small, so its launch rarely runs for nothing);
 //  2. every group fits one 32-row block -> cfg 1 (each weight byte read
 //     once, least MFMA padding);
 //  3. every group fits one 64-row block -> cfg 2;
@@ -309,7 +311,7 @@ DEVI void block_exclusive_scan(int32_t* a, int n, int32_t* wsum, int32_t* total)
 DEVI int config_rule(int mx, int active, int rows, int tiles32, int I, int num_cfgs, int cus, int T) {
   if (num_cfgs <= 1 || T <= DECODE_STREAM_TOKENS) return 0;
   const long items32 = (long)tiles32 * (I / 128);
-  if (items32 < cus) return 0;
+  if (2 * items32 < cus) return 0;
   if (mx <= 32) return 1;
   if (mx <= 64 || num_cfgs < 4) return num_cfgs < 3 ? 1 : 2;
   return (active > 0 && rows >= 64 * active && rows >= CFG3_MIN_ROWS) ? 3 : 2;
