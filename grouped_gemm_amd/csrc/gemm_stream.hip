@@ -31,6 +31,8 @@ template <int F, bool GATEUP, int WAVES, int MT, int ACT, int U>
 __global__ void __launch_bounds__(WAVES * 64) k_gemm_stream(GemmArgs p) {
   constexpr int WB = FmtBits<F>::W, XB = FmtBits<F>::X;
   constexpr int NW = GATEUP ? 2 : 1;
+  // ReLU^2 has no gate projection: its loads and products are skipped
+  constexpr bool GATE = !(GATEUP && ACT == ACT_RELU2);
   const int nblk = p.N >> 4;
   const int gi = blockIdx.x / nblk, nb = blockIdx.x - gi * nblk;
   if (p.cfg_self >= 0 && p.meta[META_CFG] != p.cfg_self) return;
@@ -90,7 +92,8 @@ __global__ void __launch_bounds__(WAVES * 64) k_gemm_stream(GemmArgs p) {
       for (int u = 0; u < U; ++u) {
         int ks = ks0 + 128 * u;
         if (ks < kend) {
-          a0[u].load(W0, ks, lg);
+          if (GATE) a0[u].load(W0, ks, lg);
+          else a0[u].zero();
           if (GATEUP) a1[u].load(W1, ks, lg);
         } else {
           a0[u].zero();
@@ -115,9 +118,11 @@ __global__ void __launch_bounds__(WAVES * 64) k_gemm_stream(GemmArgs p) {
             const int kb = ks >> 7;
             float sx = tv[t] ? ((const float*)p.a_scale)[(size_t)tok[t] * (K / 128) + kb] : 0.f;
             f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            f32x4 d0 = mfma_f8(a0[u].v, b[u].v, z);
-            float s0 = sx * WScale<F>::blk(S0, N, K, nb * 16, kb);
-            acc[t][0] += d0 * s0;
+            if constexpr (GATE) {
+              f32x4 d0 = mfma_f8(a0[u].v, b[u].v, z);
+              float s0 = sx * WScale<F>::blk(S0, N, K, nb * 16, kb);
+              acc[t][0] += d0 * s0;
+            }
             if (GATEUP) {
               f32x4 d1 = mfma_f8(a1[u].v, b[u].v, z);
               float s1 = sx * WScale<F>::blk(S1, N, K, nb * 16, kb);
@@ -126,14 +131,16 @@ __global__ void __launch_bounds__(WAVES * 64) k_gemm_stream(GemmArgs p) {
           } else if constexpr (F == F_MX) {
             const int kq = (ks >> 5) + lg;
             int sb = tv[t] ? ((const uint8_t*)p.a_scale)[(size_t)tok[t] * (K / 32) + kq] : 127;
-            int sa0 = ((const uint8_t*)S0)[(size_t)n_ld * (K / 32) + kq];
-            acc[t][0] = mfma_f4f8_scaled(a0[u].v, b[u].v, acc[t][0], sa0, sb);
+            if constexpr (GATE) {
+              int sa0 = ((const uint8_t*)S0)[(size_t)n_ld * (K / 32) + kq];
+              acc[t][0] = mfma_f4f8_scaled(a0[u].v, b[u].v, acc[t][0], sa0, sb);
+            }
             if (GATEUP) {
               int sa1 = ((const uint8_t*)S1)[(size_t)n_ld * (K / 32) + kq];
               acc[t][NW - 1] = mfma_f4f8_scaled(a1[u].v, b[u].v, acc[t][NW - 1], sa1, sb);
             }
           } else {
-            acc[t][0] = mma_step(a0[u], b[u], acc[t][0]);
+            if constexpr (GATE) acc[t][0] = mma_step(a0[u], b[u], acc[t][0]);
             if (GATEUP) acc[t][NW - 1] = mma_step(a1[u], b[u], acc[t][NW - 1]);
           }
         }
