@@ -210,3 +210,37 @@ def test_dispatch_chunk_boundaries(E, k, T):
     np.testing.assert_array_equal(d_i.cpu().numpy(), indptr)
     np.testing.assert_array_equal(d_g.cpu().numpy(), gather)
     np.testing.assert_array_equal(d_v.cpu().numpy(), inv)
+
+
+def test_route_and_dispatch_at_the_slot_limit():
+    """The largest batch the workspace accepts: T*k = 1,048,576 slots
+    (T = 131072 tokens, 256 experts, top-8), Zipf-like expert bias so some
+    experts stay empty; routing and the permutation bit-exact."""
+    E, k, T = 256, 8, 131072
+    say("slot limit", E, k, T)
+    rng = np.random.default_rng(1 << 20)
+    bias = -1.1 * np.log1p(rng.permutation(E)).astype(np.float64)
+    scores = (rng.standard_normal((T, E)) + bias[None, :]).astype(np.float32)
+    ids_ref, w_ref = oracle.route(scores, k, ms.SCORE_SOFTMAX)
+    counts, indptr, gather, inv = oracle.dispatch(ids_ref, E)
+    assert counts.min() == 0 and counts.sum() == T * k
+    ds = dev(scores)
+    ids = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    g.route_topk(ds, k, ms.SCORE_SOFTMAX, ids, w)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ids.cpu().numpy(), ids_ref)
+    np.testing.assert_allclose(w.cpu().numpy().astype(np.float64), w_ref, rtol=0, atol=1e-6)
+    sh = ms.small_shape("qwen", hidden=256, inter=256, experts=E, top_k=k)
+    ws = workspace(sh, T)
+    S = T * k
+    d_c = torch.empty(E, dtype=torch.int32, device="cuda")
+    d_i = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    d_g = torch.empty(S, dtype=torch.int32, device="cuda")
+    d_v = torch.empty(S, dtype=torch.int32, device="cuda")
+    g.dispatch(ws, ids, E, d_c, d_i, d_g, d_v)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(d_c.cpu().numpy(), counts)
+    np.testing.assert_array_equal(d_i.cpu().numpy(), indptr)
+    np.testing.assert_array_equal(d_g.cpu().numpy(), gather)
+    np.testing.assert_array_equal(d_v.cpu().numpy(), inv)
