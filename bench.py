@@ -59,6 +59,7 @@ def kernel_src_sha() -> str:
     return hashlib.sha256(data).hexdigest()[:16]
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
+BF16_PEAK_TFLOPS = 2500.0
 STAGES = ["route+dispatch", "quant_x", "gemm_gateup_swiglu", "quant_h", "gemm_down", "combine"]
 # expert activations (include/moe.h MOE_ACT_*)
 ACTIVATIONS = {"swiglu": 0, "swiglu_bounded": 1, "swiglu_oai": 2, "geglu": 3, "reglu": 4,
@@ -96,11 +97,13 @@ def layer_bytes(sh, T, n_active):
     return total, g1, rows
 
 
-def setup(name, T, seed_dev="cuda", act=0):
+def setup(name, T, seed_dev="cuda", act=0, bf16=False):
     import torch
     import grouped_gemm_amd as g
     import moe_synth as ms
     sh = ms.CONFIGS[name].with_(activation=act)
+    if bf16:   # the same shape with bf16 weights and activations
+        sh = sh.with_(w_format=ms.W_BF16, a_format=ms.A_BF16)
     B = ms.gen_batch(sh, T)
     # experts that receive tokens (stable argsort of the scores, top k)
     order = np.argsort(-B.scores.astype(np.float64), axis=1, kind="stable")[:, :sh.top_k]
@@ -125,10 +128,10 @@ def setup(name, T, seed_dev="cuda", act=0):
     return sh, B, W, dW, ws, x, s, y, len(active)
 
 
-def time_point(name, T, steps, warmup, force_cfg=-1, act=0):
+def time_point(name, T, steps, warmup, force_cfg=-1, act=0, bf16=False):
     import torch
     import grouped_gemm_amd as g
-    sh, B, W, dW, ws, x, s, y, n_active = setup(name, T, act=act)
+    sh, B, W, dW, ws, x, s, y, n_active = setup(name, T, act=act, bf16=bf16)
     if force_cfg >= 0:
         ws.force_config(force_cfg)
     stream = torch.cuda.Stream()
@@ -296,6 +299,8 @@ def main():
                     help="tile configuration (default: chosen on the device)")
     ap.add_argument("--activation", default="swiglu", choices=list(ACTIVATIONS),
                     help="expert activation of every timed point (default SwiGLU)")
+    ap.add_argument("--bf16", action="store_true",
+                    help="run the workload's shape with bf16 weights and activations")
     ap.add_argument("--config-sweep", action="store_true",
                     help="time the device's configuration choice against every forced "
                          "configuration at each token count of the workload (or --tokens) "
@@ -335,16 +340,18 @@ def main():
     points = []
     extra_T = [t for t in sh0.tokens if t != T_main and t >= 16] if not args.tokens else []
     for T in extra_T:
-        p = time_point(args.workload, T, args.steps, args.warmup, args.force_config, act)
+        p = time_point(args.workload, T, args.steps, args.warmup, args.force_config, act,
+                       args.bf16)
         points.append(p)
         log(f"[bench] T={T}: {p['us']:.1f} us, {p['gbs']:.0f} GB/s, {p['tflops']:.2f} TFLOP/s")
-    main_pt = time_point(args.workload, T_main, args.steps, args.warmup, args.force_config, act)
+    main_pt = time_point(args.workload, T_main, args.steps, args.warmup, args.force_config, act,
+                         args.bf16)
     points.append(main_pt)
     log(f"[bench] T={T_main}: {main_pt['us']:.1f} us, {main_pt['gbs']:.0f} GB/s, "
         f"{main_pt['tflops']:.2f} TFLOP/s, stages(ms)={[round(v, 4) for v in main_pt['stage_ms']]}")
     if args.workload == "mixtral" and not args.tokens and not args.no_prefill:
         # the metric's 8192-token point: the Qwen3.5-35B-A3B-shaped layer
-        qp = time_point("qwen", 8192, args.steps, args.warmup, act=act)
+        qp = time_point("qwen", 8192, args.steps, args.warmup, act=act, bf16=args.bf16)
         points.append(qp)
         log(f"[bench] qwen T=8192: {qp['us']:.1f} us, {qp['gbs']:.0f} GB/s, "
             f"{qp['tflops']:.2f} TFLOP/s ({qp['tflops'] / FP8_PEAK_TFLOPS:.3f} of FP8 peak), "
@@ -375,7 +382,8 @@ def main():
     out = {
         "metric": METRIC, "value": round(main_pt["gbs"], 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(main_pt["ms"], 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if args.bf16 else "fp8",
         "data": "synthetic",
         "config": {"workload": f"{sh.name}-shaped MoE layer H{sh.hidden} I{sh.inter} "
                                f"E{sh.experts} top{sh.top_k}, T={T_main}",
@@ -391,6 +399,7 @@ def main():
                     "active_tflops": round(p["tflops"], 3), "hbm_gbs": round(p["gbs"], 1),
                     "hbm_frac": round(p["gbs"] / HBM_PEAK_GBS, 4),
                     "fp8_mfma_frac": round(p["tflops"] / FP8_PEAK_TFLOPS, 4),
+                    "bf16_mfma_frac": round(p["tflops"] / BF16_PEAK_TFLOPS, 4),
                     "stage_ms": {STAGES[i]: round(v, 5) for i, v in enumerate(p["stage_ms"])}}
                    for p in points],
         "roofline": roof,
