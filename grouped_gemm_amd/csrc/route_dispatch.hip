@@ -411,6 +411,10 @@ DEVI void block_route(const DispatchArgs& d, int t0, int nt, int32_t* ids_l) {
                        d.ids + (size_t)(t0 + t) * k, d.w + (size_t)(t0 + t) * k, ids_l + t * k);
   } else {
     for (int tb = 0; tb < nt; tb += 64) {
+      // a wave whose four rows all lie past the batch skips the routine (its
+      // cross-lane steps stay inside 16-lane rows), so at small batches the
+      // idle waves do not compete with the working row for the SIMDs
+      if (tb + 4 * (tid >> 6) >= nt) continue;
       const int t = tb + (tid >> 4);
       const bool tv = t < nt;
       const int tt = tv ? t : 0;
