@@ -53,8 +53,7 @@ def _load():
     if _lib is not None:
         return _lib
     if not os.path.exists(_SO):
-        raise MoeError(f"{_SO} is not built; run __graft_entry__.build() or "
-                       "python grouped_gemm_amd/build.py")
+        raise MoeError(f"{_SO} is not built; run python grouped_gemm_amd/build.py")
     L = C.CDLL(_SO)
     P, i = C.c_void_p, C.c_int
     L.moe_status_string.restype = C.c_char_p
