@@ -13,6 +13,8 @@
 #include "layer.h"
 #include "quant_row.h"
 
+#include <type_traits>
+
 template <int AF>
 struct QGroup {
   static constexpr int CHUNKS = AF == MOE_A_FP8_G128 ? 16 : AF == MOE_A_MXFP8_G32 ? 4 : 0;
@@ -168,7 +170,7 @@ hipError_t launch_quant_rows(const QuantArgs& q, hipStream_t st) {
 // item's slots and weights are read before its rows, and every row of the
 // item (the k routed rows, then the shared expert's) is fetched before any
 // is added.
-template <int CK, bool WB>
+template <int CK, bool WB, bool SH>
 __global__ void __launch_bounds__(256) k_combine(CombineArgs c) {
   const int H = c.H, nch = H / 8, k = c.k;
   const int S = c.T * k;
@@ -187,11 +189,13 @@ __global__ void __launch_bounds__(256) k_combine(CombineArgs c) {
         wj[u] = WB ? 1.0f : ldu(c.w + (size_t)t * k + j);
       }
       if (ch >= nch) continue;
-      QrChunk<WB> raw[CK + 1];
+      QrChunk<WB> raw[SH ? CK + 1 : CK];
 #pragma unroll
       for (int u = 0; u < CK; ++u) raw[u] = qr_fetch<WB>(c.out_slot, (size_t)slot[u], H, ch);
-      const bool sh = c.shared && j0 + CK >= k;   // the last pass also takes the shared row
-      if (sh) raw[CK] = qr_fetch<WB>(c.out_slot, (size_t)(S + t), H, ch);
+      const bool sh = SH && j0 + CK >= k;   // the last pass also takes the shared row
+      if constexpr (SH) {
+        if (sh) raw[CK] = qr_fetch<WB>(c.out_slot, (size_t)(S + t), H, ch);
+      }
 #pragma unroll
       for (int u = 0; u < CK; ++u) {
         if (j0 + u < k) {
@@ -201,7 +205,8 @@ __global__ void __launch_bounds__(256) k_combine(CombineArgs c) {
           for (int i = 0; i < 8; ++i) acc[i] += wj[u] * v[i];
         }
       }
-      if (sh) {
+      if constexpr (SH) {
+        if (!sh) continue;
         float v[8];
         qr_unpack<WB>(raw[CK], v);
 #pragma unroll
@@ -221,14 +226,22 @@ hipError_t launch_combine(const CombineArgs& c, hipStream_t st) {
   if (c.T == 0) return hipSuccess;
   const int nsplit = (c.H / 8 + 255) / 256;
   const dim3 grid(elementwise_grid(c.T * nsplit)), block(256);
+  // the shared expert's row is a template choice, so layers without one
+  // carry no code or registers for it
+  auto go = [&](auto wb, auto sh) {
+    constexpr bool WB = decltype(wb)::value, SH = decltype(sh)::value;
+    if (c.k <= 2) hipLaunchKernelGGL((k_combine<2, WB, SH>), grid, block, 0, st, c);
+    else if (c.k <= 4) hipLaunchKernelGGL((k_combine<4, WB, SH>), grid, block, 0, st, c);
+    else hipLaunchKernelGGL((k_combine<8, WB, SH>), grid, block, 0, st, c);
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
   if (c.weighted_bf16) {
-    if (c.k <= 2) hipLaunchKernelGGL((k_combine<2, true>), grid, block, 0, st, c);
-    else if (c.k <= 4) hipLaunchKernelGGL((k_combine<4, true>), grid, block, 0, st, c);
-    else hipLaunchKernelGGL((k_combine<8, true>), grid, block, 0, st, c);
+    if (c.shared) go(T_{}, T_{});
+    else go(T_{}, F_{});
   } else {
-    if (c.k <= 2) hipLaunchKernelGGL((k_combine<2, false>), grid, block, 0, st, c);
-    else if (c.k <= 4) hipLaunchKernelGGL((k_combine<4, false>), grid, block, 0, st, c);
-    else hipLaunchKernelGGL((k_combine<8, false>), grid, block, 0, st, c);
+    if (c.shared) go(F_{}, T_{});
+    else go(F_{}, F_{});
   }
   return hipGetLastError();
 }
