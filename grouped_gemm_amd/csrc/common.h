@@ -178,6 +178,29 @@ DEVI float row16_sum(float v) {
   return v;
 }
 
+// Inclusive prefix over the 64 lanes of a wave by DPP (GFX9 row shifts and
+// row broadcasts; no LDS-crossbar round trip per step): shifts by 1, 2, 4
+// and 8 inside each 16-lane row (lanes shifted in from before the row read
+// 0), then lane 15 is added into row 1, lane 47 into row 3, and lane 31 into
+// rows 2 and 3.  The operation is + or max over non-negative ints (0 is the
+// identity of both).  Every lane of the wave must be active.
+template <bool MAX>
+DEVI int wave_incl_scan(int v) {
+  auto op = [](int a, int b) { return MAX ? (a > b ? a : b) : a + b; };
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false));   // row_shr:1
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false));   // row_shr:2
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false));   // row_shr:4
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false));   // row_shr:8
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false));   // row_bcast:15
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false));   // row_bcast:31
+  return v;
+}
+// The wave's sum or maximum (lane 63 of the inclusive scan), as a scalar.
+template <bool MAX>
+DEVI int wave_total(int v) {
+  return __builtin_amdgcn_readlane(wave_incl_scan<MAX>(v), 63);
+}
+
 // ---------------------------------------------------------------- MFMA
 DEVI f32x4 mfma_f8(const i32x8& a, const i32x8& b, f32x4 c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);

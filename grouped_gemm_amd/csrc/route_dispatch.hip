@@ -264,22 +264,12 @@ DEVI int block_stable_rank(int e, bool valid, int32_t* wcnt, int G, int32_t* tot
 DEVI void block_exclusive_scan(int32_t* a, int n, int32_t* wsum, int32_t* total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int v = tid < n ? a[tid] : 0;
-  int inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(inc, o, 64);
-    if (lane >= o) inc += u;
-  }
+  const int inc = wave_incl_scan<false>(v);
   if (lane == 63) wsum[wave] = inc;
   __syncthreads();
   if (wave == 0) {
     const int w = lane < 16 ? wsum[lane] : 0;
-    int winc = w;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const int u = __shfl_up(winc, o, 64);
-      if (lane >= o) winc += u;
-    }
+    const int winc = wave_incl_scan<false>(w);
     if (lane < 16) wsum[lane] = winc - w;
     if (lane == 15) *total = winc;
   }
@@ -328,14 +318,10 @@ DEVI int choose_config(const int32_t* cnt, int G, int I, int num_cfgs, int cus, 
     rows += c;
     tiles32 += (c + 31) / 32;
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const int v = __shfl_xor(mx, o, 64);
-    mx = v > mx ? v : mx;
-    active += __shfl_xor(active, o, 64);
-    rows += __shfl_xor(rows, o, 64);
-    tiles32 += __shfl_xor(tiles32, o, 64);
-  }
+  mx = wave_total<true>(mx);
+  active = wave_total<false>(active);
+  rows = wave_total<false>(rows);
+  tiles32 = wave_total<false>(tiles32);
   *max_out = mx;
   return config_rule(mx, active, rows, tiles32, I, num_cfgs, cus, T);
 }
@@ -566,14 +552,9 @@ __global__ void __launch_bounds__(256) k_dispatch_tiny(DispatchArgs d) {
   }
   const int cnt = lane < d.E ? run : (lane < G ? d.T : 0);   // group E is the shared expert
   // exclusive scan of the counts
-  int inc = cnt;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_up(inc, o, 64);
-    if (lane >= o) inc += v;
-  }
+  const int inc = wave_incl_scan<false>(cnt);
   const int excl = inc - cnt;
-  const int total = __shfl(inc, 63, 64);
+  const int total = __builtin_amdgcn_readlane(inc, 63);
   if (lane < G) {
     d.counts[lane] = cnt;
     d.indptr[lane] = excl;
@@ -583,29 +564,18 @@ __global__ void __launch_bounds__(256) k_dispatch_tiny(DispatchArgs d) {
   const uint64_t act = __ballot(lane < G && cnt > 0);
   if (lane < G && cnt > 0) d.active[__popcll(act & below)] = lane;
   // configuration from the histogram statistics (lane g holds group g)
-  int mx = cnt, t32 = (cnt + 31) / 32;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const int v = __shfl_xor(mx, o, 64);
-    mx = v > mx ? v : mx;
-    t32 += __shfl_xor(t32, o, 64);
-  }
+  const int mx = wave_total<true>(cnt), t32 = wave_total<false>((cnt + 31) / 32);
   int cfg = config_rule(mx, __popcll(act), total, t32, d.I, d.num_cfgs, d.cus, d.T);
   if (d.force_cfg >= 0) cfg = d.force_cfg;
   // block table for the chosen row-block height
   const int bm = cfg_rows(cfg);
   const int nt = lane < G ? (cnt + bm - 1) / bm : 0;
-  int tinc = nt;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_up(tinc, o, 64);
-    if (lane >= o) tinc += v;
-  }
+  const int tinc = wave_incl_scan<false>(nt);
   for (int r = 0, b = tinc - nt; r < nt; ++r) {
     d.tiles[2 * (b + r)] = lane;
     d.tiles[2 * (b + r) + 1] = r * bm;
   }
-  const int ntiles = __shfl(tinc, 63, 64);   // every lane takes part in the shuffle
+  const int ntiles = __builtin_amdgcn_readlane(tinc, 63);
   if (lane == 0) {
     d.meta[META_NACTIVE] = __popcll(act);
     d.meta[META_NTILES] = ntiles;
