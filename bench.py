@@ -47,7 +47,7 @@ METRIC = ("MoE layer µs + active TFLOP/s / HBM GB/s (FP8 W8A8) at 32, 128, 8192
 # figure is only reported while the kernel sources still hash to the value
 # they had when the counters were taken.
 TRAFFIC = {
-    ("mixtral", 128, 2): {"bytes": 962559733, "src_sha": "7bc2b530531c4414"},
+    ("mixtral", 128, 2): {"bytes": 962554355, "src_sha": "88cae23baf526f90"},
 }
 KERNEL_SRC = ["grouped_gemm_amd/csrc/gemm_pipe.hip", "grouped_gemm_amd/csrc/common.h",
               "grouped_gemm_amd/csrc/layer.h"]
