@@ -20,12 +20,13 @@ struct QGroup {
   static constexpr int CHUNKS = AF == MOE_A_FP8_G128 ? 16 : AF == MOE_A_MXFP8_G32 ? 4 : 0;
 };
 
-// A 256-thread block quantises one row at a time and strides over the rows
-// (the grid is bounded, so a launch whose rows are absent or that the chosen
-// configuration skips costs a few blocks); thread owns 8-element chunks
-// c = tid + 256*j.
-template <int AF, bool IN_BF16, int MAXJ>
-__global__ void __launch_bounds__(256) k_quant(QuantArgs qa) {
+// A block of NT threads quantises one row at a time and strides over the
+// rows (the grid is bounded, so a launch whose rows are absent or that the
+// chosen configuration skips costs a few blocks); thread owns 8-element
+// chunks c = tid + NT*j.  Per-token scales take 1024-thread blocks: the whole
+// row is one block's, and more threads per row divide its quotient work.
+template <int AF, bool IN_BF16, int MAXJ, int NT>
+__global__ void __launch_bounds__(NT) k_quant(QuantArgs qa) {
   if (qa.meta && qa.meta[META_CFG] != qa.only_cfg) return;
   const int nrows = qa.nrows ? min(*qa.nrows, qa.R) : qa.R;
   const int n = qa.n, nch = n / 8;
@@ -36,7 +37,7 @@ __global__ void __launch_bounds__(256) k_quant(QuantArgs qa) {
   QrChunk<IN_BF16> raw[MAXJ];
 #pragma unroll
   for (int j = 0; j < MAXJ; ++j) {
-    const int c = tid + 256 * j;
+    const int c = tid + NT * j;
     raw[j] = qr_fetch<IN_BF16>(qa.in, row, n, c < nch ? c : nch - 1);
   }
   float v[MAXJ][8];
@@ -44,17 +45,19 @@ __global__ void __launch_bounds__(256) k_quant(QuantArgs qa) {
 #pragma unroll
   for (int j = 0; j < MAXJ; ++j) {
     qr_unpack<IN_BF16>(raw[j], v[j]);
-    gmax[j] = tid + 256 * j < nch ? qr_amax8(v[j]) : 0.f;
+    gmax[j] = tid + NT * j < nch ? qr_amax8(v[j]) : 0.f;
   }
   if (AF == MOE_A_FP8_TOKEN) {
-    __shared__ float red[4];
+    __shared__ float red[NT / 64];
     float m = 0.f;
 #pragma unroll
     for (int j = 0; j < MAXJ; ++j) m = fmaxf(m, gmax[j]);
     m = wave_max(m);
     if ((tid & 63) == 0) red[tid >> 6] = m;
     __syncthreads();
-    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    m = red[0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) m = fmaxf(m, red[w]);
 #pragma unroll
     for (int j = 0; j < MAXJ; ++j) gmax[j] = m;
   } else {
@@ -66,7 +69,7 @@ __global__ void __launch_bounds__(256) k_quant(QuantArgs qa) {
   }
 #pragma unroll
   for (int j = 0; j < MAXJ; ++j) {
-    int c = tid + 256 * j;
+    int c = tid + NT * j;
     if (c >= nch) continue;
     float a = gmax[j];
     uint32_t lo, hi;
@@ -108,16 +111,17 @@ static int elementwise_grid(int rows) {
 
 template <int AF, bool IN_BF16>
 static hipError_t quant_dispatch_j(const QuantArgs& q, hipStream_t st) {
-  int nch = q.n / 8, j = (nch + 255) / 256;
+  constexpr int NT = AF == MOE_A_FP8_TOKEN ? 1024 : 256;
+  int nch = q.n / 8, j = (nch + NT - 1) / NT;
   // a launch that runs only for one configuration (its rows are then few)
   // keeps a small grid, so skipping it costs little
   int blocks = elementwise_grid(q.R);
   if (q.meta && blocks > 64) blocks = 64;
-  dim3 grid(blocks), block(256);
-  if (j <= 1) hipLaunchKernelGGL((k_quant<AF, IN_BF16, 1>), grid, block, 0, st, q);
-  else if (j <= 2) hipLaunchKernelGGL((k_quant<AF, IN_BF16, 2>), grid, block, 0, st, q);
-  else if (j <= 4) hipLaunchKernelGGL((k_quant<AF, IN_BF16, 4>), grid, block, 0, st, q);
-  else if (j <= 8) hipLaunchKernelGGL((k_quant<AF, IN_BF16, 8>), grid, block, 0, st, q);
+  dim3 grid(blocks), block(NT);
+  if (j <= 1) hipLaunchKernelGGL((k_quant<AF, IN_BF16, 1, NT>), grid, block, 0, st, q);
+  else if (j <= 2) hipLaunchKernelGGL((k_quant<AF, IN_BF16, 2, NT>), grid, block, 0, st, q);
+  else if (j <= 4) hipLaunchKernelGGL((k_quant<AF, IN_BF16, 4, NT>), grid, block, 0, st, q);
+  else if (j <= 8) hipLaunchKernelGGL((k_quant<AF, IN_BF16, 8, NT>), grid, block, 0, st, q);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
