@@ -20,7 +20,8 @@ SYMBOLS = (
     "moe_workspace_destroy", "moe_route_topk", "moe_dispatch", "moe_grouped_gemm",
     "moe_quantize_act", "moe_combine", "moe_layer_forward", "moe_workspace_routing",
     "moe_workspace_force_config", "moe_workspace_last_config", "moe_config_rows",
-    "moe_workspace_set_graphs", "moe_workspace_set_stage_events",
+    "moe_workspace_set_graphs", "moe_workspace_set_stage_events", "moe_workspace_tiles",
+    "moe_workspace_check", "moe_workspace_graph_count",
 )
 
 
@@ -63,7 +64,7 @@ def _load():
     L.moe_workspace_size.argtypes = [C.POINTER(LayerDesc), C.POINTER(C.c_size_t)]
     L.moe_workspace_create.argtypes = [C.POINTER(LayerDesc), P, C.c_size_t, C.POINTER(P)]
     L.moe_workspace_destroy.argtypes = [P]
-    L.moe_route_topk.argtypes = [P, i, i, i, i, P, P, P]
+    L.moe_route_topk.argtypes = [P, i, i, i, i, i, P, P, P]
     L.moe_dispatch.argtypes = [P, P, i, i, i, P, P, P, P, P]
     L.moe_grouped_gemm.argtypes = [P, i, P, P, P, i, P, i, i, i, P, P, P, P, P, P, P]
     L.moe_quantize_act.argtypes = [P, P, i, P, P, P]
@@ -75,6 +76,9 @@ def _load():
     L.moe_config_rows.argtypes = [i]
     L.moe_workspace_set_graphs.argtypes = [P, i]
     L.moe_workspace_set_stage_events.argtypes = [P, i, P, P]
+    L.moe_workspace_tiles.argtypes = [P, C.POINTER(P), C.POINTER(P)]
+    L.moe_workspace_check.argtypes = [P, C.POINTER(i), P]
+    L.moe_workspace_graph_count.argtypes = [P, C.POINTER(i)]
     for n in SYMBOLS:
         if n not in ("moe_status_string", "moe_last_error"):
             getattr(L, n).restype = i
@@ -165,16 +169,31 @@ class Workspace:
         _check(_load().moe_workspace_last_config(self.handle, C.byref(v), _stream(stream)))
         return v.value
 
+    def tile_pointers(self):
+        ps = [C.c_void_p() for _ in range(2)]
+        _check(_load().moe_workspace_tiles(self.handle, *[C.byref(p) for p in ps]))
+        return [p.value for p in ps]
+
+    def check(self, stream=None) -> int:
+        v = C.c_int(-1)
+        _check(_load().moe_workspace_check(self.handle, C.byref(v), _stream(stream)))
+        return v.value
+
+    def graph_count(self) -> int:
+        v = C.c_int(-1)
+        _check(_load().moe_workspace_graph_count(self.handle, C.byref(v)))
+        return v.value
+
     def routing_pointers(self):
         ps = [C.c_void_p() for _ in range(6)]
         _check(_load().moe_workspace_routing(self.handle, *[C.byref(p) for p in ps]))
         return [p.value for p in ps]
 
 
-def route_topk(scores, k, score_fn, topk_ids, topk_w, stream=None):
+def route_topk(scores, k, score_fn, topk_ids, topk_w, stream=None, renorm=1):
     T, E = scores.shape
-    _check(_load().moe_route_topk(_ptr(scores), T, E, k, score_fn, _ptr(topk_ids), _ptr(topk_w),
-                                  _stream(stream)))
+    _check(_load().moe_route_topk(_ptr(scores), T, E, k, score_fn, renorm, _ptr(topk_ids),
+                                  _ptr(topk_w), _stream(stream)))
 
 
 def dispatch(ws: Workspace, topk_ids, E, counts, m_indptr, gather, inv, stream=None):

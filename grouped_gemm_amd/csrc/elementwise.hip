@@ -194,15 +194,17 @@ __global__ void __launch_bounds__(256) k_combine(CombineArgs c) {
       }
       if (ch >= nch) continue;
       QrChunk<WB> raw[SH ? CK + 1 : CK];
+      // a negative slot (an id the dispatch dropped) has no row: it adds
+      // nothing and its row is not read
 #pragma unroll
-      for (int u = 0; u < CK; ++u) raw[u] = qr_fetch<WB>(c.out_slot, (size_t)slot[u], H, ch);
+      for (int u = 0; u < CK; ++u) raw[u] = qr_fetch<WB>(c.out_slot, (size_t)(slot[u] < 0 ? 0 : slot[u]), H, ch);
       const bool sh = SH && j0 + CK >= k;   // the last pass also takes the shared row
       if constexpr (SH) {
         if (sh) raw[CK] = qr_fetch<WB>(c.out_slot, (size_t)(S + t), H, ch);
       }
 #pragma unroll
       for (int u = 0; u < CK; ++u) {
-        if (j0 + u < k) {
+        if (j0 + u < k && slot[u] >= 0) {
           float v[8];
           qr_unpack<WB>(raw[u], v);
 #pragma unroll

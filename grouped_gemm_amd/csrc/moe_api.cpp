@@ -128,15 +128,25 @@ Layout make_layout(const moe_layer_desc& d) {
   return L;
 }
 
+// One instantiated decode graph per (token count, stream).  The pointers it
+// was captured with are kept: a call with other buffers re-captures and
+// updates the instance in place (hipGraphExecUpdate), so the number of
+// instances never grows with the buffers a caller rotates through.
 struct GraphKey {
   int T;
-  const void *x, *scores, *y, *st;
+  const void* st;
+  bool operator<(const GraphKey& o) const { return std::tie(T, st) < std::tie(o.T, o.st); }
+};
+struct GraphPtrs {
+  const void *x, *scores, *y;
   const void* wp[12];
-  bool operator<(const GraphKey& o) const {
-    return std::tie(T, x, scores, y, st) < std::tie(o.T, o.x, o.scores, o.y, o.st) ||
-           (std::tie(T, x, scores, y, st) == std::tie(o.T, o.x, o.scores, o.y, o.st) &&
-            memcmp(wp, o.wp, sizeof wp) < 0);
+  bool operator==(const GraphPtrs& o) const {
+    return x == o.x && scores == o.scores && y == o.y && memcmp(wp, o.wp, sizeof wp) == 0;
   }
+};
+struct GraphEntry {
+  hipGraphExec_t exec;
+  GraphPtrs ptrs;
 };
 
 }  // namespace
@@ -149,7 +159,7 @@ struct moe_ws {
   int force_cfg = -1;
   int graphs = 1;
   int device = 0;
-  std::map<GraphKey, hipGraphExec_t> execs;
+  std::map<GraphKey, GraphEntry> execs;
   hipEvent_t stage_ev[6][2] = {};
   bool any_stage_events() const {
     for (auto& p : stage_ev)
@@ -260,9 +270,8 @@ Candidates candidates(const moe_ws* ws, long rows_tot, int T) {
 // `tiled_out` and `tiled_scale` redirect the fused gate/up output of the
 // tiled kernels, which requantise the intermediate in their epilogue for the
 // 1x128 and MX formats.
-hipError_t run_gemm(const moe_ws* ws, bool gateup, GemmArgs g, void* tiled_out, void* tiled_scale,
-                    long rows_tot, int T, hipStream_t st) {
-  const Candidates cand = candidates(ws, rows_tot, T);
+hipError_t run_gemm_c(const moe_ws* ws, bool gateup, GemmArgs g, void* tiled_out, void* tiled_scale,
+                      const Candidates& cand, hipStream_t st) {
   if (cand.stream) {
     g.cfg_self = 0;
     hipError_t e = launch_gemm_stream(ws->fmt, gateup, g, st);
@@ -283,11 +292,17 @@ hipError_t run_gemm(const moe_ws* ws, bool gateup, GemmArgs g, void* tiled_out, 
     return hipSuccess;
   }
   for (int c = 1; c < num_cfgs(ws->fmt); ++c) {
+    if (ws->force_cfg > 0 && c != ws->force_cfg) continue;
     g.cfg_self = c;
     hipError_t e = launch_gemm_tiled(ws->fmt, gateup, c, g, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+hipError_t run_gemm(const moe_ws* ws, bool gateup, GemmArgs g, void* tiled_out, void* tiled_scale,
+                    long rows_tot, int T, hipStream_t st) {
+  return run_gemm_c(ws, gateup, g, tiled_out, tiled_scale, candidates(ws, rows_tot, T), st);
 }
 
 int enqueue_layer(moe_ws* ws, const moe_weights* w, const uint16_t* x, const float* scores, int T,
@@ -450,18 +465,19 @@ int moe_workspace_create(const moe_layer_desc* desc, void* dev_buf, size_t bytes
 
 int moe_workspace_destroy(moe_ws* ws) {
   if (!ws) return MOE_OK;
-  for (auto& kv : ws->execs) (void)hipGraphExecDestroy(kv.second);
+  for (auto& kv : ws->execs) (void)hipGraphExecDestroy(kv.second.exec);
   delete ws;
   return MOE_OK;
 }
 
-int moe_route_topk(const float* scores, int T, int E, int k, int score_fn, int32_t* ids, float* w,
-                   void* stream) {
+int moe_route_topk(const float* scores, int T, int E, int k, int score_fn, int renorm, int32_t* ids,
+                   float* w, void* stream) {
   if (T < 0) return fail(MOE_EINVAL, "T must be >= 0");
   if (E < 1 || E > 256) return fail(MOE_EINVAL, "E must be in [1, 256]");
   int kmax = E < 16 ? E : 16;
   if (k < 1 || k > kmax) return fail(MOE_EINVAL, "k must be in [1, %d]", kmax);
   if (score_fn < 0 || score_fn > 2) return fail(MOE_EINVAL, "unknown score_fn");
+  if (renorm != 1) return fail(MOE_EUNSUPPORTED, "only renorm = 1 is supported");
   if (T == 0) return MOE_OK;
   if (!scores || !ids || !w) return fail(MOE_EINVAL, "null pointer");
   HIP_TRY(launch_route(scores, T, E, k, score_fn, ids, w, QuantArgs{}, (hipStream_t)stream),
@@ -515,10 +531,12 @@ int moe_grouped_gemm(moe_ws* ws, int op, const void* a, const void* a_scale,
   if (gateup && (long)N > ws->d.inter && quant)
     return fail(MOE_ECAPACITY, "N exceeds the workspace's intermediate staging width");
   hipStream_t st = (hipStream_t)stream;
-  DispatchArgs da = dispatch_args(ws, 0);
+  // the group table and the tile configuration come from m_indptr on the
+  // device, as in the layer (largest group in place of the token count)
+  DispatchArgs da = dispatch_args(ws, -1);
   da.E = E;
   da.shared = 0;
-  da.force_cfg = 0;
+  da.I = N;
   HIP_TRY(launch_indptr_table(m_indptr, (int)cap, da, st), "group table launch");
   GemmArgs g = gemm_args(ws);
   g.E = E;   // every group is a routed group here
@@ -536,17 +554,34 @@ int moe_grouped_gemm(moe_ws* ws, int op, const void* a, const void* a_scale,
   g.max_rows = (int)cap;
   g.max_group_rows = (int)cap;
   g.cfg_self = -1;
+  // the host does not know the histogram: every kernel family the device
+  // may choose is launched, and those it did not choose return at once
+  Candidates cand{true, num_cfgs(ws->fmt) > 1, num_cfgs(ws->fmt) > 3 && cap >= CFG3_MIN_ROWS};
+  if (ws->force_cfg >= 0)
+    cand = {ws->force_cfg == 0, ws->force_cfg == 1 || ws->force_cfg == 2, ws->force_cfg == 3};
   if (gateup && quant) {
+    // fp32 staging, requantised by a separate pass, except where the tiled
+    // 1x128 and MX epilogues requantise in place
+    const bool fused_requant = ws->fmt == F_FP8_BLK || ws->fmt == F_MX;
     g.out = ws->at<void>(ws->L.h);
-    HIP_TRY(launch_gemm_stream(ws->fmt, true, g, st), "grouped GEMM launch");
-    // the grid covers the capacity; rows at or beyond m_indptr[E] (read on
-    // the device) return at once, so only the R rows of `out` are written
-    QuantArgs q{ws->at<void>(ws->L.h), 0, (int)cap, N, m_indptr + E, (uint8_t*)out, out_scale,
-                ws->d.a_format};
-    HIP_TRY(launch_quant(q, st), "intermediate quantisation launch");
+    HIP_TRY(run_gemm_c(ws, true, g, fused_requant ? out : nullptr, fused_requant ? out_scale : nullptr,
+                       cand, st),
+            "grouped GEMM launch");
+    if (!fused_requant || cand.stream) {
+      // the grid covers the capacity; rows at or beyond m_indptr[E] (read
+      // on the device) return at once, so only the R rows of `out` are
+      // written
+      QuantArgs q{ws->at<void>(ws->L.h), 0, (int)cap, N, m_indptr + E, (uint8_t*)out, out_scale,
+                  ws->d.a_format};
+      if (fused_requant) {   // only the streaming configuration left fp32 h behind
+        q.meta = ws->at<int32_t>(ws->L.meta);
+        q.only_cfg = 0;
+      }
+      HIP_TRY(launch_quant(q, st), "intermediate quantisation launch");
+    }
   } else {
     g.out = out;
-    HIP_TRY(launch_gemm_stream(ws->fmt, gateup, g, st), "grouped GEMM launch");
+    HIP_TRY(run_gemm_c(ws, gateup, g, nullptr, nullptr, cand, st), "grouped GEMM launch");
   }
   return MOE_OK;
 }
@@ -591,17 +626,11 @@ int moe_layer_forward(moe_ws* ws, const moe_weights* w, const uint16_t* x, const
   const bool use_graph = ws->graphs && st != nullptr && T <= 128 && !ws->any_stage_events() &&
                          cap == hipStreamCaptureStatusNone;
   if (!use_graph) return enqueue_layer(ws, w, x, scores, T, y, st);
-  GraphKey key{};
-  key.T = T;
-  key.x = x;
-  key.scores = scores;
-  key.y = y;
-  key.st = st;
-  const void* wp[12] = {w->w_gate, w->w_up, w->w_down, w->s_gate, w->s_up, w->s_down,
-                        w->sh_gate, w->sh_up, w->sh_down, w->ss_gate, w->ss_up, w->ss_down};
-  memcpy(key.wp, wp, sizeof wp);
+  const GraphKey key{T, st};
+  GraphPtrs ptrs{x, scores, y, {w->w_gate, w->w_up, w->w_down, w->s_gate, w->s_up, w->s_down,
+                                w->sh_gate, w->sh_up, w->sh_down, w->ss_gate, w->ss_up, w->ss_down}};
   auto it = ws->execs.find(key);
-  if (it == ws->execs.end()) {
+  if (it == ws->execs.end() || !(it->second.ptrs == ptrs)) {
     hipGraph_t graph;
     HIP_TRY(hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal), "begin capture");
     rc = enqueue_layer(ws, w, x, scores, T, y, st);
@@ -611,13 +640,28 @@ int moe_layer_forward(moe_ws* ws, const moe_weights* w, const uint16_t* x, const
       return rc;
     }
     if (e != hipSuccess) return hip_fail(e, "end capture");
+    if (it != ws->execs.end()) {
+      // same launch sequence, other buffers: update the instance in place
+      hipGraphExecUpdateResult res = hipGraphExecUpdateError;
+      hipGraphNode_t err_node = nullptr;
+      e = hipGraphExecUpdate(it->second.exec, graph, &err_node, &res);
+      if (e == hipSuccess && res == hipGraphExecUpdateSuccess) {
+        (void)hipGraphDestroy(graph);
+        it->second.ptrs = ptrs;
+        HIP_TRY(hipGraphLaunch(it->second.exec, st), "graph launch");
+        return MOE_OK;
+      }
+      (void)hipGetLastError();
+      (void)hipGraphExecDestroy(it->second.exec);
+      ws->execs.erase(it);
+    }
     hipGraphExec_t exec;
     e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
     (void)hipGraphDestroy(graph);
     if (e != hipSuccess) return hip_fail(e, "graph instantiate");
-    it = ws->execs.emplace(key, exec).first;
+    it = ws->execs.emplace(key, GraphEntry{exec, ptrs}).first;
   }
-  HIP_TRY(hipGraphLaunch(it->second, st), "graph launch");
+  HIP_TRY(hipGraphLaunch(it->second.exec, st), "graph launch");
   return MOE_OK;
 }
 
@@ -639,7 +683,7 @@ int moe_workspace_force_config(moe_ws* ws, int cfg) {
   if (cfg < -1 || cfg >= num_cfgs(ws->fmt))
     return fail(MOE_EINVAL, "cfg must be in [-1, %d)", num_cfgs(ws->fmt));
   ws->force_cfg = cfg;
-  for (auto& kv : ws->execs) (void)hipGraphExecDestroy(kv.second);
+  for (auto& kv : ws->execs) (void)hipGraphExecDestroy(kv.second.exec);
   ws->execs.clear();
   return MOE_OK;
 }
@@ -652,13 +696,38 @@ int moe_workspace_last_config(const moe_ws* ws, int* cfg, void* stream) {
   return MOE_OK;
 }
 
+int moe_workspace_tiles(const moe_ws* ws, const int32_t** tiles, const int32_t** meta) {
+  if (!ws) return fail(MOE_EINVAL, "workspace is NULL");
+  if (tiles) *tiles = ws->at<int32_t>(ws->L.tiles);
+  if (meta) *meta = ws->at<int32_t>(ws->L.meta);
+  return MOE_OK;
+}
+
+int moe_workspace_check(const moe_ws* ws, int* device_status, void* stream) {
+  if (!ws || !device_status) return fail(MOE_EINVAL, "null pointer");
+  HIP_TRY(hipStreamSynchronize((hipStream_t)stream), "stream synchronise");
+  int32_t err = 0;
+  HIP_TRY(hipMemcpy(&err, ws->at<int32_t>(ws->L.meta) + META_ERROR, 4, hipMemcpyDeviceToHost),
+          "read device status");
+  *device_status = err ? MOE_EINVAL : MOE_OK;
+  if (err) fail(MOE_EINVAL, "the device rejected the last m_indptr (not non-decreasing from 0, "
+                            "or more rows than the workspace holds); no rows were computed");
+  return MOE_OK;
+}
+
+int moe_workspace_graph_count(const moe_ws* ws, int* host_n) {
+  if (!ws || !host_n) return fail(MOE_EINVAL, "null pointer");
+  *host_n = (int)ws->execs.size();
+  return MOE_OK;
+}
+
 int moe_config_rows(int cfg) { return (cfg >= 0 && cfg < kNumCfgs) ? cfg_rows(cfg) : -1; }
 
 int moe_workspace_set_graphs(moe_ws* ws, int enable) {
   if (!ws) return fail(MOE_EINVAL, "workspace is NULL");
   ws->graphs = enable ? 1 : 0;
   if (!enable) {
-    for (auto& kv : ws->execs) (void)hipGraphExecDestroy(kv.second);
+    for (auto& kv : ws->execs) (void)hipGraphExecDestroy(kv.second.exec);
     ws->execs.clear();
   }
   return MOE_OK;

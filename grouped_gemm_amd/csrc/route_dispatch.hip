@@ -299,7 +299,9 @@ DEVI void block_exclusive_scan(int32_t* a, int n, int32_t* wsum, int32_t* total)
 // The rule reproduces the fastest measured configuration on the benchmarked
 // layer shapes; a fitted cost model over these statistics can replace it.
 DEVI int config_rule(int mx, int active, int rows, int tiles32, int I, int num_cfgs, int cus, int T) {
-  if (num_cfgs <= 1 || T <= DECODE_STREAM_TOKENS) return 0;
+  // T < 0 (a caller-supplied grouping, no token count): the largest group
+  // bounds the rows of every group instead
+  if (num_cfgs <= 1 || (T >= 0 ? T : mx) <= DECODE_STREAM_TOKENS) return 0;
   const long items32 = (long)tiles32 * (I / 128);
   if (2 * items32 < cus) return 0;
   if (mx <= 32) return 1;

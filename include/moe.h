@@ -14,8 +14,8 @@
  *    caller's next synchronisation.
  *  - The caller owns every buffer: inputs, outputs, weights and the
  *    workspace memory.  No entry point allocates device memory, except
- *    moe_layer_forward's one-time graph instantiation per token count
- *    (decode sizes only; see moe_workspace_set_graphs).
+ *    moe_layer_forward's graph instantiation, once per (token count,
+ *    stream) at decode sizes (see moe_workspace_set_graphs).
  *  - A workspace serves one stream at a time (LightMoE README, "MoE
  *    inference": one plan per concurrent stream because workspaces are
  *    reused).  Calls that share a workspace on different streams race.
@@ -134,10 +134,13 @@ MOE_API int moe_workspace_destroy(moe_ws* ws);
  *   scores     [T, E] fp32: logits (SOFTMAX/SIGMOID) or probabilities (PROBS)
  *   topk_ids   [T, k] int32 out: the k largest scores in descending order,
  *              ties broken towards the lower expert index (+0 == -0)
+ *   renorm     must be 1: the weights are renormalised over the k chosen
+ *              (the only form the layer computes; 0 gives EUNSUPPORTED)
  *   topk_w     [T, k] fp32 out: gate weights renormalised over the k
- * T = 0 is a no-op.  Errors: EINVAL (nulls, k < 1, k > min(E,16), E > 256). */
-MOE_API int moe_route_topk(const float* scores, int T, int E, int k, int score_fn, int32_t* topk_ids,
-                   float* topk_w, void* stream);
+ * T = 0 is a no-op.  Errors: EINVAL (nulls, k < 1, k > min(E,16), E > 256),
+ * EUNSUPPORTED (renorm != 1). */
+MOE_API int moe_route_topk(const float* scores, int T, int E, int k, int score_fn, int renorm,
+                   int32_t* topk_ids, float* topk_w, void* stream);
 
 /* Deterministic expert-major dispatch (LightMoE README, API table and "MoE
  * training": gather indices, m_indptr, inverse slots; "Grouped GEMM":
@@ -175,6 +178,12 @@ MOE_API int moe_dispatch(moe_ws* ws, const int32_t* topk_ids, int T, int k, int 
  *   out       PLAIN: fp32 [R, N].  GATEUP_ACT: h in the activation
  *             format (bf16 [R, N], or e4m3 codes [R, N] + out_scale as for
  *             a_scale with K replaced by N)
+ * The tile configuration (streaming, or 32-, 64- or 128-row blocks) is
+ * chosen on the device from the group sizes in m_indptr, as in
+ * moe_layer_forward (moe_workspace_force_config pins it).  m_indptr is read
+ * on the device only: when it is not non-decreasing from 0, or its last
+ * entry exceeds the workspace's row capacity, the device computes no rows
+ * (out is left as it was) and moe_workspace_check reports EINVAL.
  * Errors: EINVAL, EUNSUPPORTED (N or K not a multiple of 128), ECAPACITY. */
 MOE_API int moe_grouped_gemm(moe_ws* ws, int op, const void* a, const void* a_scale,
                      const int32_t* a_gather, int gather_div, const int32_t* m_indptr, int E,
@@ -194,7 +203,8 @@ MOE_API int moe_quantize_act(moe_ws* ws, const uint16_t* x_bf16, int T, uint8_t*
  * application and deterministic combine):
  *   y[t] = bf16( sum_{j<k} w[t,j] * out_slot[inv[t*k+j]] (+ out_slot[T*k+t]
  *          when the layer has a shared expert) ), j ascending, fp32 sums.
- *   out_slot [T*k (+T), H] fp32; y [T, H] bf16 out. */
+ *   out_slot [T*k (+T), H] fp32; y [T, H] bf16 out.
+ * A negative inv entry (an id moe_dispatch dropped) contributes nothing. */
 MOE_API int moe_combine(moe_ws* ws, const float* out_slot, const float* topk_w, const int32_t* inv, int T,
                 uint16_t* y_bf16, void* stream);
 
@@ -216,6 +226,27 @@ MOE_API int moe_workspace_routing(const moe_ws* ws, const int32_t** topk_ids, co
                           const int32_t** counts, const int32_t** m_indptr,
                           const int32_t** gather, const int32_t** inv);
 
+/* Block table of the workspace's last dispatch (moe_layer_forward,
+ * moe_dispatch or moe_grouped_gemm), device pointers into the workspace:
+ * tiles [2 * n] int32 pairs (row group, first row of the block), groups in
+ * ascending order, ceil(rows / BM) blocks per group (pure-Triton MoE
+ * commentary, second paragraph: block-id -> (expert, offset) map); meta
+ * [16] int32 words: [0] active groups, [1] n = table entries, [2] the
+ * configuration, [3] largest group, [4] rows, [5] BM, [6] device status
+ * (nonzero: m_indptr rejected).  Any out pointer may be NULL. */
+MOE_API int moe_workspace_tiles(const moe_ws* ws, const int32_t** tiles, const int32_t** meta);
+
+/* Synchronise `stream` and report the device-side status of the
+ * workspace's last dispatch in *device_status: MOE_OK, or MOE_EINVAL when
+ * the device rejected a caller's m_indptr (moe_grouped_gemm then computed
+ * no rows; moe_last_error names the reason).  Returns EHIP if the
+ * synchronisation fails. */
+MOE_API int moe_workspace_check(const moe_ws* ws, int* device_status, void* stream);
+
+/* Number of instantiated decode graphs the workspace holds: at most one per
+ * (token count, stream), whatever buffers the calls pass. */
+MOE_API int moe_workspace_graph_count(const moe_ws* ws, int* host_n);
+
 /* Force the tile configuration (tests and cost-model fitting): -1 = choose
  * from the histogram (default); 0 = streaming decode kernels; 1.. = tiled
  * kernels with a row-block height given by moe_config_rows(cfg). */
@@ -226,8 +257,11 @@ MOE_API int moe_workspace_last_config(const moe_ws* ws, int* host_cfg_id, void* 
 MOE_API int moe_config_rows(int cfg_id);
 
 /* Enable (1, default) or disable (0) hipGraph capture of moe_layer_forward
- * for decode token counts (T <= 128): the first call at each T captures
- * and instantiates a graph, later calls with the same pointers replay it.
+ * for decode token counts (T <= 128): the first call at each (T, stream)
+ * captures and instantiates a graph, later calls with the same pointers
+ * replay it, and a call with other pointers re-captures and updates that
+ * instance in place (hipGraphExecUpdate; re-instantiated only if the update
+ * is refused), so the instances stay one per (T, stream).
  * A call made while `stream` is being captured by the caller (for example
  * a whole model step in one graph) enqueues its kernels into the caller's
  * capture instead; no library call on the path allocates or sets memory,

@@ -283,6 +283,17 @@ int oracle_tile_table(const int32_t* counts, int E, int bm, int32_t* table, int 
 }
 
 /* ------------------------------------------------------------------ experts */
+/* Decoded values of every e4m3 and e8m0 code, filled once when the library
+ * loads from oracle_e4m3_decode / oracle_e8m0_decode (a lookup in place of
+ * recomputing the same value per element). */
+static double e4m3_tab[256], e8m0_tab[256];
+__attribute__((constructor)) static void oracle_tables(void) {
+  for (int c = 0; c < 256; ++c) {
+    e4m3_tab[c] = oracle_e4m3_decode((uint8_t)c);
+    e8m0_tab[c] = oracle_e8m0_decode((uint8_t)c);
+  }
+}
+
 typedef struct {
   int w_format;
   const void* codes;   /* one expert's [N, K] matrix */
@@ -298,24 +309,27 @@ static void dequant_row(const oracle_mat* m, int n, double* out) {
   } else if (m->w_format == W_FP8_CHANNEL) {
     const uint8_t* c = (const uint8_t*)m->codes + (size_t)n * K;
     double s = ((const float*)m->scales)[n];
-    for (int i = 0; i < K; ++i) out[i] = oracle_e4m3_decode(c[i]) * s;
+    for (int i = 0; i < K; ++i) out[i] = e4m3_tab[c[i]] * s;
   } else if (m->w_format == W_FP8_BLOCK128) {
     const uint8_t* c = (const uint8_t*)m->codes + (size_t)n * K;
     const float* s = (const float*)m->scales + (size_t)(n / 128) * (K / 128);
-    for (int i = 0; i < K; ++i) out[i] = oracle_e4m3_decode(c[i]) * (double)s[i / 128];
+    for (int i = 0; i < K; ++i) out[i] = e4m3_tab[c[i]] * (double)s[i / 128];
   } else { /* W_MXFP4: two e2m1 codes per byte, element 2i in the low nibble */
     const uint8_t* c = (const uint8_t*)m->codes + (size_t)n * (K / 2);
     const uint8_t* s = (const uint8_t*)m->scales + (size_t)n * (K / 32);
     for (int i = 0; i < K; ++i) {
       uint8_t nib = (i & 1) ? (c[i / 2] >> 4) : (c[i / 2] & 0xF);
-      out[i] = oracle_e2m1_decode(nib) * oracle_e8m0_decode(s[i / 32]);
+      out[i] = oracle_e2m1_decode(nib) * e8m0_tab[s[i / 32]];
     }
   }
 }
 
-/* out[n] = sum_k a[k] * W[n, k] for every row n of an expert matrix. */
-static void matvec(const oracle_mat* m, const double* a, double* out) {
-#pragma omp parallel
+/* out[n] = sum_k a[k] * W[n, k] for every row n of an expert matrix, each
+ * sum in ascending k.  Rows are split over threads when `par` is set
+ * (callers that already run one token or row per thread pass 0); the split
+ * does not change any sum. */
+static void matvec(const oracle_mat* m, const double* a, double* out, int par) {
+#pragma omp parallel if (par)
   {
     double* row = (double*)malloc(sizeof(double) * (size_t)m->K);
 #pragma omp for schedule(static)
@@ -368,19 +382,20 @@ double oracle_activation(int act, double limit, double g, double u) {
  * intermediate requantised under the activation format.  o has H entries.
  * g is NULL for the two-weight ReLU^2 form. */
 static void expert_forward(const oracle_mat* g, const oracle_mat* u, const oracle_mat* d,
-                           const double* xq, int a_format, int act, double limit, double* o) {
+                           const double* xq, int a_format, int act, double limit, double* o,
+                           int par) {
   int I = u->N;
   double* gv = (double*)malloc(sizeof(double) * (size_t)I);
   double* uv = (double*)malloc(sizeof(double) * (size_t)I);
   if (act == ACT_RELU2) {
     for (int n = 0; n < I; ++n) gv[n] = 0.0;
   } else {
-    matvec(g, xq, gv);
+    matvec(g, xq, gv, par);
   }
-  matvec(u, xq, uv);
+  matvec(u, xq, uv, par);
   for (int n = 0; n < I; ++n) gv[n] = oracle_activation(act, limit, gv[n], uv[n]);
   quant_dequant_row(gv, I, a_format);
-  matvec(d, gv, o);
+  matvec(d, gv, o, par);
   free(gv);
   free(uv);
 }
@@ -418,6 +433,8 @@ static oracle_mat expert_mat(int w_format, const void* codes, const void* scales
  *           when has_shared != 0
  *   tokens  which rows of y to compute; y is [ntok, H] (fp64)
  * y_t = sum_j w[t,j] * expert_{ids[t,j]}(x_t) (+ shared(x_t)), j ascending.
+ * Tokens are independent: with several tokens each thread takes whole
+ * tokens (every sum is formed exactly as for one token on its own).
  */
 void oracle_layer_forward(int H, int I, int E, int k, int w_format, int a_format, int act,
                           double limit, const void* wg, const void* sg, const void* wu, const void* su,
@@ -426,8 +443,12 @@ void oracle_layer_forward(int H, int I, int E, int k, int w_format, int a_format
                           const void* shd, const void* shsd, const uint16_t* x_bits,
                           const int32_t* ids, const double* w, const int32_t* tokens, int ntok,
                           double* y) {
+  const int tok_par = ntok >= 4;
+#pragma omp parallel if (tok_par)
+  {
   double* xq = (double*)malloc(sizeof(double) * (size_t)H);
   double* o = (double*)malloc(sizeof(double) * (size_t)H);
+#pragma omp for schedule(dynamic, 1)
   for (int i = 0; i < ntok; ++i) {
     int t = tokens[i];
     for (int h = 0; h < H; ++h) xq[h] = oracle_bf16_decode(x_bits[(size_t)t * H + h]);
@@ -439,7 +460,7 @@ void oracle_layer_forward(int H, int I, int E, int k, int w_format, int a_format
       oracle_mat g = expert_mat(w_format, wg, sg, e, I, H);
       oracle_mat u = expert_mat(w_format, wu, su, e, I, H);
       oracle_mat d = expert_mat(w_format, wd, sd, e, H, I);
-      expert_forward(&g, &u, &d, xq, a_format, act, limit, o);
+      expert_forward(&g, &u, &d, xq, a_format, act, limit, o, !tok_par);
       double wj = w[(size_t)t * k + j];
       for (int h = 0; h < H; ++h) yt[h] += wj * o[h];
     }
@@ -447,12 +468,13 @@ void oracle_layer_forward(int H, int I, int E, int k, int w_format, int a_format
       oracle_mat g = expert_mat(w_format, shg, shsg, 0, Is, H);
       oracle_mat u = expert_mat(w_format, shu, shsu, 0, Is, H);
       oracle_mat d = expert_mat(w_format, shd, shsd, 0, H, Is);
-      expert_forward(&g, &u, &d, xq, a_format, act, limit, o);
+      expert_forward(&g, &u, &d, xq, a_format, act, limit, o, !tok_par);
       for (int h = 0; h < H; ++h) yt[h] += o[h];
     }
   }
   free(xq);
   free(o);
+  }
 }
 
 /* ------------------------------------------------------------ grouped GEMM
@@ -470,14 +492,21 @@ void oracle_grouped_gemm(int w_format, int a_format, int op, int act, double lim
                          const int32_t* a_gather, int gather_div, const int32_t* m_indptr, int E,
                          int N, int K, const void* b0, const void* b0s, const void* b1,
                          const void* b1s, double* out) {
+  const int R = m_indptr[E];
+#pragma omp parallel
+  {
   double* arow = (double*)malloc(sizeof(double) * (size_t)K);
   double* g = (double*)malloc(sizeof(double) * (size_t)N);
   double* u = (double*)malloc(sizeof(double) * (size_t)N);
-  for (int e = 0; e < E; ++e) {
+  /* rows are independent: each thread takes whole rows */
+#pragma omp for schedule(dynamic, 4)
+  for (int r = 0; r < R; ++r) {
+    int e = 0;
+    while (m_indptr[e + 1] <= r) ++e;
     const int relu2 = op == 1 && act == ACT_RELU2;
     oracle_mat B0 = expert_mat(w_format, relu2 ? b1 : b0, relu2 ? b1s : b0s, e, N, K);
     oracle_mat B1 = expert_mat(w_format, b1 ? b1 : b0, b1 ? b1s : b0s, e, N, K);
-    for (int r = m_indptr[e]; r < m_indptr[e + 1]; ++r) {
+    {
       long src = a_gather ? a_gather[r] / gather_div : r;
       for (int k = 0; k < K; ++k) {
         if (a_format == A_BF16) {
@@ -497,10 +526,10 @@ void oracle_grouped_gemm(int w_format, int a_format, int op, int act, double lim
       if (op == 1 && relu2) {
         for (int n = 0; n < N; ++n) g[n] = 0.0;
       } else {
-        matvec(&B0, arow, g);
+        matvec(&B0, arow, g, 0);
       }
       if (op == 1) {
-        matvec(&B1, arow, u);
+        matvec(&B1, arow, u, 0);
         for (int n = 0; n < N; ++n) out[(size_t)r * N + n] = oracle_activation(act, limit, g[n], u[n]);
       } else {
         for (int n = 0; n < N; ++n) out[(size_t)r * N + n] = g[n];
@@ -510,4 +539,5 @@ void oracle_grouped_gemm(int w_format, int a_format, int op, int act, double lim
   free(arow);
   free(g);
   free(u);
+  }
 }

@@ -76,13 +76,20 @@ def test_status_strings_and_null_checks():
     lib.moe_workspace_destroy.argtypes = [C.c_void_p]
     assert lib.moe_workspace_destroy(None) == 0
     # routing argument checks happen before any device work
-    lib.moe_route_topk.argtypes = [C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_int, C.c_void_p,
-                                   C.c_void_p, C.c_void_p]
-    assert lib.moe_route_topk(None, 4, 8, 0, 0, None, None, None) == 1
-    assert lib.moe_route_topk(None, 4, 300, 2, 0, None, None, None) == 1
-    assert lib.moe_route_topk(None, 4, 8, 2, 9, None, None, None) == 1
-    assert lib.moe_route_topk(None, 0, 8, 2, 0, None, None, None) == 0   # T = 0 no-op
-    assert lib.moe_route_topk(None, 4, 8, 2, 0, None, None, None) == 1   # null pointers
+    lib.moe_route_topk.argtypes = [C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int,
+                                   C.c_void_p, C.c_void_p, C.c_void_p]
+    assert lib.moe_route_topk(None, 4, 8, 0, 0, 1, None, None, None) == 1
+    assert lib.moe_route_topk(None, 4, 300, 2, 0, 1, None, None, None) == 1
+    assert lib.moe_route_topk(None, 4, 8, 2, 9, 1, None, None, None) == 1
+    assert lib.moe_route_topk(None, 4, 8, 2, 0, 0, None, None, None) == 2   # renorm = 0
+    assert lib.moe_route_topk(None, 0, 8, 2, 0, 1, None, None, None) == 0   # T = 0 no-op
+    assert lib.moe_route_topk(None, 4, 8, 2, 0, 1, None, None, None) == 1   # null pointers
+    lib.moe_workspace_check.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p]
+    assert lib.moe_workspace_check(None, None, None) == 1
+    lib.moe_workspace_tiles.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p]
+    assert lib.moe_workspace_tiles(None, None, None) == 1
+    lib.moe_workspace_graph_count.argtypes = [C.c_void_p, C.c_void_p]
+    assert lib.moe_workspace_graph_count(None, None) == 1
     lib.moe_layer_forward.argtypes = [C.c_void_p] * 5 + [C.c_int, C.c_void_p, C.c_void_p]
     assert lib.moe_layer_forward(None, None, None, None, None, 1, None, None) == 1
     assert lib.moe_config_rows(0) > 0 and lib.moe_config_rows(99) == -1

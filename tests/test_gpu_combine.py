@@ -48,3 +48,32 @@ def test_combine_matches_reference(H, k, T, shared):
     say("  relerr", err)
     assert np.all(np.isfinite(got))
     assert err <= 2e-3                                  # one bf16 rounding of fp32 sums
+
+
+def test_combine_skips_dropped_slots():
+    """moe_dispatch marks an id outside [0, E) with inv = -1; the combine adds
+    nothing for such an entry (and reads no row for it)."""
+    H, k, T = 1024, 4, 33
+    rng = np.random.default_rng(5)
+    S = T * k
+    out_slot = rng.standard_normal((S, H)).astype(np.float32)
+    w = rng.random((T, k)).astype(np.float32)
+    inv = rng.permutation(S).astype(np.int32)
+    drop = rng.random(S) < 0.3
+    drop[:k] = True                                     # a token with every slot dropped
+    inv[drop] = -1
+    ref = np.zeros((T, H))
+    for t in range(T):
+        for j in range(k):
+            if inv[t * k + j] >= 0:
+                ref[t] += np.float64(w[t, j]) * out_slot[inv[t * k + j]].astype(np.float64)
+    sh = ms.small_shape("qwen", hidden=H, inter=256, experts=16, top_k=k)
+    ws = workspace(sh, T)
+    y = torch.empty(T, H, dtype=torch.int16, device="cuda")
+    g.combine(ws, dev(out_slot), dev(w), dev(inv), y)
+    torch.cuda.synchronize()
+    got = bf16_to_f64(y.cpu().numpy().view(np.uint16))
+    assert np.all(got[0] == 0.0)
+    err = relerr(got, ref)
+    say("  dropped-slot combine relerr", err)
+    assert np.all(np.isfinite(got)) and err <= 2e-3

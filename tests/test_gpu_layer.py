@@ -14,8 +14,8 @@ import grouped_gemm_amd as g
 
 import moe_synth as ms
 import oracle
-from gpu_util import (bf16_to_f64, check_routing, dev_weights, relerr, run_layer, say, tol_for,
-                      workspace, ws_routing)
+from gpu_util import (bf16_to_f64, check_routing, dev, dev_weights, relerr, run_layer, say,
+                      tol_for, workspace, ws_routing, ws_view)
 
 pytestmark = pytest.mark.gpu
 
@@ -160,15 +160,43 @@ def test_all_tokens_one_expert():
     assert relerr(bf16_to_f64(y), ref) <= tol_for(sh)
 
 
-# Full-size layer shapes; tokens sampled for the oracle.
-FULL = [("mixtral", 1), ("mixtral", 32), ("mixtral", 128), ("tiny", 32), ("qwen", 8192),
-        ("dsv3", 1), ("dsv3", 16), ("dsv3", 256), ("dsv3", 4096), ("imbalance", 2048)]
+# Full-size layer shapes.  Every token is compared where the oracle takes
+# seconds (the metric's Mixtral T=32/128 and Qwen-shaped T=8192 points and
+# every point of at most 256 tokens); the larger DeepSeek-V3-shaped and
+# MXFP4 batches are compared on one token per row block of the table the
+# device ran (the block's last row, so ragged tails are covered) plus the
+# first and last token, which covers every active expert, every row block
+# and so every XCD's item range.
+FULL = [("mixtral", 1, "all"), ("mixtral", 32, "all"), ("mixtral", 128, "all"),
+        ("tiny", 32, "all"), ("qwen", 8192, "all"), ("dsv3", 1, "all"), ("dsv3", 16, "all"),
+        ("dsv3", 256, "all"), ("dsv3", 4096, "blocks"), ("imbalance", 2048, "blocks")]
 
 
-@pytest.mark.parametrize("name,T", FULL, ids=[f"{n}-T{t}" for n, t in FULL])
-def test_layer_full_size_sampled(name, T):
+def per_token_relerr(y, ref):
+    num = np.linalg.norm(y - ref, axis=1)
+    den = np.maximum(np.linalg.norm(ref, axis=1), 1e-300)
+    return num / den
+
+
+def block_tokens(ws, sh, T, got):
+    """One token per row block of the device's table (the block's last row)."""
+    tiles_p, meta_p = ws.tile_pointers()
+    meta = ws_view(ws, meta_p, 16)
+    n, bm = int(meta[1]), int(meta[5])
+    tab = ws_view(ws, tiles_p, 2 * n).reshape(n, 2)
+    S = T * sh.top_k
+    toks = [0, T - 1]
+    for grp, r0 in tab:
+        last = min(r0 + bm, int(got["counts"][grp])) - 1
+        slot = int(got["indptr"][grp]) + last
+        toks.append(int(got["gather"][slot]) // sh.top_k if slot < S else slot - S)
+    return np.unique(np.array(toks, dtype=np.int32))
+
+
+@pytest.mark.parametrize("name,T,mode", FULL, ids=[f"{n}-T{t}" for n, t, _ in FULL])
+def test_layer_full_size(name, T, mode):
     sh = ms.CONFIGS[name]
-    say("layer full", name, T)
+    say("layer full", name, T, mode)
     B = ms.gen_batch(sh, T)
     ids_ref, _ = oracle.route(B.scores, sh.top_k, sh.score_fn)
     active = sorted(set(np.unique(ids_ref).tolist()))
@@ -176,15 +204,59 @@ def test_layer_full_size_sampled(name, T):
     say("  weights ready,", len(active), "active experts")
     ws = workspace(sh, T)
     y = run_layer(ws, dev_weights(W), B.x_bits, B.scores)
-    ids, w = check_routing(sh, T, ws_routing(ws, sh, T), B.scores)
-    rng = np.random.default_rng(T)
-    n = min(T, 12)
-    toks = np.unique(np.concatenate([[0, T - 1], rng.choice(T, size=n, replace=False)]))
+    got = ws_routing(ws, sh, T)
+    ids, w = check_routing(sh, T, got, B.scores)
+    toks = np.arange(T, dtype=np.int32) if mode == "all" else block_tokens(ws, sh, T, got)
+    if mode != "all":
+        hit = set(ids[toks].ravel().tolist())
+        assert hit == set(active), "sampled tokens miss an active expert"
+    say("  oracle on", len(toks), "tokens")
     ref = oracle.layer_forward(W, B.x_bits, ids, w, tokens=toks)
-    err = relerr(bf16_to_f64(y[toks]), ref)
-    say("  sampled relerr", err, "tokens", len(toks))
+    yt = bf16_to_f64(y[toks])
+    err = relerr(yt, ref)
+    tok_err = per_token_relerr(yt, ref)
+    say("  relerr", err, "worst token", float(tok_err.max()), "tokens", len(toks))
     assert np.all(np.isfinite(bf16_to_f64(y)))
     assert err <= tol_for(sh)
+    # every token on its own: a misplaced or missing row has relative error
+    # near 1, while rounding keeps each token close to the global figure
+    assert tok_err.max() <= 2 * tol_for(sh), int(toks[np.argmax(tok_err)])
+
+
+def test_decode_graph_cache_stays_bounded_with_rotating_buffers():
+    """Decode calls whose x / scores / y buffers change from call to call
+    (as under a caching allocator) replay one graph per token count: the
+    instance is updated in place, the cache does not grow, and every output
+    equals the eager one."""
+    sh = SMALL[1][1]
+    T = 6
+    W = ms.gen_weights(sh)
+    dW = dev_weights(W)
+    ws = workspace(sh, T)
+    B = ms.gen_batch(sh, T)
+    rng = np.random.default_rng(11)
+    sets = []
+    for i in range(3):
+        sc = (B.scores + rng.standard_normal(B.scores.shape).astype(np.float32)).astype(np.float32)
+        sets.append((dev(B.x_bits.view(np.int16)), dev(sc)))
+    ws.set_graphs(False)
+    ref = []
+    for x, s in sets:
+        yy = torch.empty(T, sh.hidden, dtype=torch.int16, device="cuda")
+        g.layer_forward(ws, dW, x, s, yy)
+        torch.cuda.synchronize()
+        ref.append(yy.cpu().numpy().copy())
+    ws.set_graphs(True)
+    st = torch.cuda.Stream()
+    for call in range(9):
+        x, s = sets[call % 3]
+        with torch.cuda.stream(st):
+            yy = torch.empty(T, sh.hidden, dtype=torch.int16, device="cuda")
+            g.layer_forward(ws, dW, x, s, yy, stream=st)
+        st.synchronize()
+        np.testing.assert_array_equal(yy.cpu().numpy(), ref[call % 3])
+        assert ws.graph_count() == 1
+        del yy
 
 
 FORCED = [(n, sh, T) for n, sh, T in SMALL if n != "tiny_cfg"] + [
