@@ -21,7 +21,7 @@ SYMBOLS = (
     "moe_quantize_act", "moe_combine", "moe_layer_forward", "moe_workspace_routing",
     "moe_workspace_force_config", "moe_workspace_last_config", "moe_config_rows",
     "moe_workspace_set_graphs", "moe_workspace_set_stage_events", "moe_workspace_tiles",
-    "moe_workspace_check", "moe_workspace_graph_count",
+    "moe_workspace_check", "moe_workspace_graph_count", "moe_dispatch_noalloc",
 )
 
 
@@ -66,6 +66,7 @@ def _load():
     L.moe_workspace_destroy.argtypes = [P]
     L.moe_route_topk.argtypes = [P, i, i, i, i, i, P, P, P]
     L.moe_dispatch.argtypes = [P, P, i, i, i, P, P, P, P, P]
+    L.moe_dispatch_noalloc.argtypes = [P, i, i, i, P, P, P, P, P]
     L.moe_grouped_gemm.argtypes = [P, i, P, P, P, i, P, i, i, i, P, P, P, P, P, P, P]
     L.moe_quantize_act.argtypes = [P, P, i, P, P, P]
     L.moe_combine.argtypes = [P, P, P, P, i, P, P]
@@ -200,6 +201,12 @@ def dispatch(ws: Workspace, topk_ids, E, counts, m_indptr, gather, inv, stream=N
     T, k = topk_ids.shape
     _check(_load().moe_dispatch(ws.handle, _ptr(topk_ids), T, k, E, _ptr(counts), _ptr(m_indptr),
                                 _ptr(gather), _ptr(inv), _stream(stream)))
+
+
+def dispatch_noalloc(topk_ids, E, counts, m_indptr, gather, inv, stream=None):
+    T, k = topk_ids.shape
+    _check(_load().moe_dispatch_noalloc(_ptr(topk_ids), T, k, E, _ptr(counts), _ptr(m_indptr),
+                                        _ptr(gather), _ptr(inv), _stream(stream)))
 
 
 def grouped_gemm(ws: Workspace, op, a, a_scale, a_gather, gather_div, m_indptr, N, K, b0,

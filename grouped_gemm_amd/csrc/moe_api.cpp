@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <tuple>
 
@@ -418,9 +419,84 @@ int check_weights(const moe_ws* ws, const moe_weights* w) {
   return MOE_OK;
 }
 
+// ------------------------------------------------- no-allocation dispatch
+// Scratch of moe_dispatch_noalloc in device memory the library owns for the
+// life of the process (one copy per GPU, each at its own address): the meta
+// words, the active-group list, the block table and the per-chunk expert
+// histograms of the largest dispatch the entry point accepts (1,048,576
+// slots, 256 experts).  The host never uses the array's name as an address;
+// it takes each device's address from hipGetSymbolAddress once.
+constexpr int NA_MAX_SLOTS = 1 << 20;
+constexpr int NA_MAX_E = 256;
+constexpr int NA_MAX_TILES = NA_MAX_SLOTS / 16 + NA_MAX_E + 1;
+constexpr int NA_MAX_CHUNKS = 1100;   // ceil(T / floor(1024 / k)) <= 1035 for T*k <= 2^20
+constexpr size_t NA_META = 0, NA_ACTIVE = 64, NA_TILES = NA_ACTIVE + NA_MAX_E,
+                 NA_CHUNK = NA_TILES + 2 * (size_t)NA_MAX_TILES,
+                 NA_WORDS = NA_CHUNK + (size_t)NA_MAX_CHUNKS * NA_MAX_E;
+static __device__ __align__(256) int32_t scratch[NA_WORDS];
+
+constexpr int NA_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[NA_MAX_DEVICES] = {};
+
+// The calling device's copy of the scratch array (resolved once per device,
+// with that device current).
+int scratch_for_current_device(int32_t** out) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev), "get device");
+  if (dev < 0 || dev >= NA_MAX_DEVICES) return fail(MOE_EUNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "scratch symbol address");
+    g_scratch_ptr[dev] = (int32_t*)ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int moe_dispatch_noalloc(const int32_t* topk_ids, int T, int k, int E, int32_t* counts,
+                         int32_t* m_indptr, int32_t* gather, int32_t* inv, void* stream) {
+  if (E < 1 || E > NA_MAX_E) return fail(MOE_EINVAL, "E must be in [1, %d]", NA_MAX_E);
+  const int kmax = E < 16 ? E : 16;
+  if (k < 1 || k > kmax) return fail(MOE_EINVAL, "k must be in [1, %d]", kmax);
+  if (T < 0) return fail(MOE_EINVAL, "T must be >= 0");
+  if ((long)T * k > NA_MAX_SLOTS)
+    return fail(MOE_ECAPACITY, "T*k = %ld exceeds the %d slots of the static scratch", (long)T * k,
+                NA_MAX_SLOTS);
+  if (!counts || !m_indptr || (T > 0 && (!topk_ids || !gather || !inv)))
+    return fail(MOE_EINVAL, "null pointer");
+  const long TC = 1024 / k, nch = (T + TC - 1) / TC;
+  if (nch > NA_MAX_CHUNKS) return fail(MOE_ECAPACITY, "%ld chunks exceed the static scratch", nch);
+  int32_t* scr = nullptr;
+  int rc = scratch_for_current_device(&scr);
+  if (rc) return rc;
+  DispatchArgs a{};
+  a.T = T;
+  a.E = E;
+  a.k = k;
+  a.shared = 0;
+  a.ids_in = topk_ids;
+  a.counts = counts;
+  a.indptr = m_indptr;
+  a.gather = gather;
+  a.inv = inv;
+  a.meta = scr + NA_META;
+  a.active = scr + NA_ACTIVE;
+  a.tiles = scr + NA_TILES;
+  a.chunk = scr + NA_CHUNK;
+  a.force_cfg = 0;     // no layer shape: the table is built for the streaming height
+  a.H = a.I = 128;
+  a.wbits = a.xbits = 8;
+  a.num_cfgs = 1;
+  a.cus = device_cus();
+  HIP_TRY(launch_dispatch(a, (hipStream_t)stream), "dispatch launch");
+  return MOE_OK;
+}
 
 const char* moe_status_string(int s) {
   switch (s) {

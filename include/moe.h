@@ -159,6 +159,20 @@ MOE_API int moe_route_topk(const float* scores, int T, int E, int k, int score_f
 MOE_API int moe_dispatch(moe_ws* ws, const int32_t* topk_ids, int T, int k, int E, int32_t* counts,
                  int32_t* m_indptr, int32_t* gather, int32_t* inv, void* stream);
 
+/* moe_dispatch without a workspace, for callers that cannot allocate device
+ * memory or create a workspace (code under stream capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, outputs and
+ * rules as moe_dispatch (E is given here, not taken from a workspace).  Its
+ * scratch (group list, block table, per-chunk histograms) is a static device
+ * array of about 1.7 MB that the library holds on each GPU it runs on until
+ * the process ends; nothing is allocated or freed per call.  Every call on
+ * one GPU shares that GPU's array: calls that overlap on one GPU (on
+ * different streams, or from different threads) race.  Limits: E <= 256,
+ * k <= min(E, 16), T*k <= 1,048,576 (ECAPACITY beyond).  Errors: EINVAL,
+ * ECAPACITY, EHIP. */
+MOE_API int moe_dispatch_noalloc(const int32_t* topk_ids, int T, int k, int E, int32_t* counts,
+                                 int32_t* m_indptr, int32_t* gather, int32_t* inv, void* stream);
+
 /* Grouped GEMM over expert-major rows, one launch for all experts and no
  * padding (pure-Triton MoE commentary, second paragraph: block-id ->
  * (expert, offset) map; LightMoE README, "Grouped GEMM").
