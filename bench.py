@@ -218,9 +218,12 @@ def time_point(name, T, steps, warmup, force_cfg=-1, act=0, bf16=False):
 
 
 def cpu_baseline(pt, n_tokens):
+    """The oracle on `n_tokens` tokens of the timed batch (all of them by
+    default), wall-clock around the layer call only, scaled to the batch."""
     import oracle
     sh, B, W, T = pt["sh"], pt["B"], pt["W"], pt["T"]
     ids, w = oracle.route(B.scores, sh.top_k, sh.score_fn)
+    n_tokens = T if n_tokens <= 0 else min(n_tokens, T)
     toks = np.linspace(0, T - 1, n_tokens).astype(np.int32)
     try:
         cores = len(os.sched_getaffinity(0))
@@ -231,11 +234,12 @@ def cpu_baseline(pt, n_tokens):
     oracle.layer_forward(W, B.x_bits, ids, w, tokens=toks)
     dt = time.perf_counter() - t0
     full = dt * T / n_tokens
+    what = (f"all {T} tokens of the timed batch" if n_tokens == T else
+            f"{n_tokens} of the {T} tokens of the timed batch, scaled to the full batch")
     return {"value": round(pt["bytes"] / full / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{n_tokens} of the {T} tokens of the timed batch (same weights, "
-                      f"routing and activations), {dt:.1f}s wall, scaled to the full batch "
-                      f"({full:.1f}s per layer call)"}
+            "sample": f"{what} (same weights, routing and activations), {dt:.1f}s wall "
+                      f"({full:.2f}s per layer call)"}
 
 
 def config_sweep(name, T, act=0, rounds=3, calls=30):
@@ -291,10 +295,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--tokens", type=int, default=0)
-    ap.add_argument("--cpu-tokens", type=int, default=16)
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="tokens of the batch the CPU oracle is timed on (0: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the 8192-token Qwen-shaped point of the default run")
+    ap.add_argument("--no-decode-extra", action="store_true",
+                    help="skip the DeepSeek-V3-shaped T=1/16 points of the default run")
     ap.add_argument("--force-config", type=int, default=-1,
                     help="tile configuration (default: chosen on the device)")
     ap.add_argument("--activation", default="swiglu", choices=list(ACTIVATIONS),
@@ -338,7 +345,7 @@ def main():
         return
     T_main = args.tokens or max(sh0.tokens)
     points = []
-    extra_T = [t for t in sh0.tokens if t != T_main and t >= 16] if not args.tokens else []
+    extra_T = [t for t in sh0.tokens if t != T_main] if not args.tokens else []
     for T in extra_T:
         p = time_point(args.workload, T, args.steps, args.warmup, args.force_config, act,
                        args.bf16)
@@ -356,6 +363,15 @@ def main():
         log(f"[bench] qwen T=8192: {qp['us']:.1f} us, {qp['gbs']:.0f} GB/s, "
             f"{qp['tflops']:.2f} TFLOP/s ({qp['tflops'] / FP8_PEAK_TFLOPS:.3f} of FP8 peak), "
             f"stages(ms)={[round(v, 4) for v in qp['stage_ms']]}")
+    if args.workload == "mixtral" and not args.tokens and not args.no_decode_extra:
+        # the DeepSeek-V3-shaped decode points (one and sixteen tokens)
+        for T in (1, 16):
+            dp = time_point("dsv3", T, args.steps, args.warmup, act=act, bf16=args.bf16)
+            points.append(dp)
+            log(f"[bench] dsv3 T={T}: {dp['us']:.1f} us, {dp['gbs']:.0f} GB/s "
+                f"({dp['gbs'] / HBM_PEAK_GBS:.3f} of HBM), stages(ms)="
+                f"{[round(v, 4) for v in dp['stage_ms']]}")
+            del dp["W"], dp["B"]
     dom = int(np.argmax(main_pt["stage_ms"]))
     dom_ms = main_pt["stage_ms"][dom]
     if dom == 2:

@@ -826,10 +826,21 @@ struct Pipe8Waves {
 template <int F, bool GATEUP>
 struct PipeShapes {
   static constexpr int NR_SMALL = (GATEUP && F != F_FP8_CH) ? 256 : 128;
+  // MXFP4's 128-row blocks also run four waves, so one kernel holds all
+  // three tiled configurations (no launch that returns at once)
+  static constexpr bool ONE_KERNEL = Pipe8Waves<F>::NW == 4;
   static constexpr int LDS4 = [] {
     const int a = pipe_lds_bytes<F, GATEUP, 32, NR_SMALL, 1, 4>();
     const int b = pipe_lds_bytes<F, GATEUP, 64, NR_SMALL, 1, 4>();
-    return a > b ? a : b;
+    int m = a > b ? a : b;
+    if constexpr (ONE_KERNEL) {
+      const int c = pipe_lds_bytes<F, GATEUP, 128, 256, 1, 4>();
+      int d = 0;
+      if constexpr (!GATEUP) d = pipe_lds_bytes<F, GATEUP, 128, 128, 1, 4>();
+      m = m > c ? m : c;
+      m = m > d ? m : d;
+    }
+    return m;
   }();
   static constexpr int LDS8 = [] {
     constexpr int WM = Pipe8Waves<F>::WM, NW = Pipe8Waves<F>::NW;
@@ -841,7 +852,8 @@ struct PipeShapes {
 };
 
 // The device's configuration choice (meta) selects the tile shape: this
-// kernel serves configurations 1 and 2 and returns at once for the others.
+// kernel serves configurations 1 and 2 (and 3 when its blocks also run four
+// waves) and returns at once for the others.
 template <int F, bool GATEUP, int ACT>
 __global__ void __launch_bounds__(256) k_gemm_pipe(GemmArgs p) {
   using SH = PipeShapes<F, GATEUP>;
@@ -850,6 +862,12 @@ __global__ void __launch_bounds__(256) k_gemm_pipe(GemmArgs p) {
   if (p.cfg_self >= 0 && cfg != p.cfg_self) return;
   if (cfg == 1) pipe_body<F, GATEUP, 32, SH::NR_SMALL, 1, 4, ACT>(p, lds);
   else if (cfg == 2) pipe_body<F, GATEUP, 64, SH::NR_SMALL, 1, 4, ACT>(p, lds);
+  else if constexpr (SH::ONE_KERNEL) {
+    if (cfg == 3) {
+      if (GATEUP || p.N % 256 == 0) pipe_body<F, GATEUP, 128, 256, 1, 4, ACT>(p, lds);
+      else if constexpr (!GATEUP) pipe_body<F, GATEUP, 128, 128, 1, 4, ACT>(p, lds);
+    }
+  }
 }
 
 // Configuration 3 (128-row blocks).
@@ -857,11 +875,15 @@ template <int F, bool GATEUP, int ACT>
 __global__ void __launch_bounds__(Pipe8Waves<F>::NW * 64) k_gemm_pipe8(GemmArgs p) {
   using SH = PipeShapes<F, GATEUP>;
   constexpr int WM = Pipe8Waves<F>::WM, NW = Pipe8Waves<F>::NW;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[SH::LDS8];
-  const int cfg = p.meta[META_CFG];
-  if (cfg != 3 || (p.cfg_self >= 0 && cfg != p.cfg_self)) return;
-  if (GATEUP || p.N % 256 == 0) pipe_body<F, GATEUP, 128, 256, WM, NW, ACT>(p, lds);
-  else if constexpr (!GATEUP) pipe_body<F, GATEUP, 128, 128, WM, NW, ACT>(p, lds);
+  if constexpr (SH::ONE_KERNEL) {
+    return;   // configuration 3 runs inside k_gemm_pipe
+  } else {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[SH::LDS8];
+    const int cfg = p.meta[META_CFG];
+    if (cfg != 3 || (p.cfg_self >= 0 && cfg != p.cfg_self)) return;
+    if (GATEUP || p.N % 256 == 0) pipe_body<F, GATEUP, 128, 256, WM, NW, ACT>(p, lds);
+    else if constexpr (!GATEUP) pipe_body<F, GATEUP, 128, 128, WM, NW, ACT>(p, lds);
+  }
 }
 
 namespace {
@@ -885,6 +907,9 @@ hipError_t launch_pipe_t(int family, const GemmArgs& g, hipStream_t st) {
   // a multiple of the 8 XCDs
   const unsigned grid = (unsigned)pipe_cus();
   const dim3 b8(Pipe8Waves<F>::NW * 64);
+  // one kernel holds every tiled configuration for this format: family 1
+  // (configuration 3) is the same launch as family 0
+  if (PipeShapes<F, GATEUP>::ONE_KERNEL) family = 0;
   if constexpr (GATEUP) {
     return with_act(g.act, [&](auto a) {
       constexpr int ACT = decltype(a)::value;

@@ -285,6 +285,9 @@ hipError_t run_gemm_c(const moe_ws* ws, bool gateup, GemmArgs g, void* tiled_out
   }
   if (ws->fmt != F_BF16) {
     g.cfg_self = ws->force_cfg > 0 ? ws->force_cfg : -1;   // any tiled configuration
+    // MXFP4 runs every tiled configuration in one kernel (four-wave blocks
+    // throughout), so it takes one launch whichever of them the device picks
+    if (ws->fmt == F_MX) return launch_gemm_pipe(ws->fmt, gateup, 0, g, st);
     if (cand.small) {
       hipError_t e = launch_gemm_pipe(ws->fmt, gateup, 0, g, st);
       if (e != hipSuccess) return e;
