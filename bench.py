@@ -60,7 +60,8 @@ def kernel_src_sha() -> str:
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 BF16_PEAK_TFLOPS = 2500.0
-STAGES = ["route+dispatch", "quant_x", "gemm_gateup_swiglu", "quant_h", "gemm_down", "combine"]
+STAGES = ["route+dispatch", "quant_x", "gemm_gateup_swiglu", "quant_h", "gemm_down", "combine",
+          "fused_decode_layer"]
 # expert activations (include/moe.h MOE_ACT_*)
 ACTIVATIONS = {"swiglu": 0, "swiglu_bounded": 1, "swiglu_oai": 2, "geglu": 3, "reglu": 4,
                "relu2": 5}
@@ -97,6 +98,9 @@ def layer_bytes(sh, T, n_active):
     return total, g1, rows
 
 
+FUSED_DECODE = False   # --fused-decode: the single-launch decode layer for T <= 16
+
+
 def setup(name, T, seed_dev="cuda", act=0, bf16=False):
     import torch
     import grouped_gemm_amd as g
@@ -122,6 +126,8 @@ def setup(name, T, seed_dev="cuda", act=0, bf16=False):
     ws = g.Workspace(sh.hidden, sh.inter, sh.experts, sh.top_k, T, shared_experts=sh.shared,
                      shared_inter=sh.shared_inter, score_fn=sh.score_fn, w_format=sh.w_format,
                      a_format=sh.a_format, activation=sh.activation, act_limit=sh.act_limit)
+    if FUSED_DECODE:
+        ws.set_fused_decode(True)
     x = torch.from_numpy(B.x_bits.view(np.int16)).to(seed_dev)
     s = torch.from_numpy(B.scores).to(seed_dev)
     y = torch.empty(T, sh.hidden, dtype=torch.int16, device=seed_dev)
@@ -194,7 +200,7 @@ def time_point(name, T, steps, warmup, force_cfg=-1, act=0, bf16=False):
     with torch.cuda.stream(stream):
         for _ in range(steps):
             pair = []
-            for st in range(6):
+            for st in range(len(STAGES)):
                 b = torch.cuda.Event(enable_timing=True)
                 e = torch.cuda.Event(enable_timing=True)
                 b.record(stream)
@@ -204,9 +210,10 @@ def time_point(name, T, steps, warmup, force_cfg=-1, act=0, bf16=False):
             g.layer_forward(ws, dW, x, s, y, stream=stream)
             evs.append(pair)
     torch.cuda.synchronize()
-    for st in range(6):
+    for st in range(len(STAGES)):
         ws.set_stage_events(st, None, None)
-    stage_ms = [float(np.mean([p[st][0].elapsed_time(p[st][1]) for p in evs])) for st in range(6)]
+    stage_ms = [float(np.mean([p[st][0].elapsed_time(p[st][1]) for p in evs]))
+                for st in range(len(STAGES))]
     total_b, g1_b, rows = layer_bytes(sh, T, n_active)
     flops = (4.0 if sh.activation == ACT_RELU2 else 6.0) * sh.hidden * sh.inter * rows
     us = ms_step * 1e3
@@ -315,7 +322,11 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain elementwise copy of 256 MiB (fp32 in, fp32 out), "
                          "whose known byte counts calibrate hardware traffic counters")
+    ap.add_argument("--fused-decode", action="store_true",
+                    help="run batches of at most 16 tokens through the single-launch decode layer")
     args = ap.parse_args()
+    global FUSED_DECODE
+    FUSED_DECODE = args.fused_decode
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the layer holds every expert on one device); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)

@@ -22,6 +22,7 @@ SYMBOLS = (
     "moe_workspace_force_config", "moe_workspace_last_config", "moe_config_rows",
     "moe_workspace_set_graphs", "moe_workspace_set_stage_events", "moe_workspace_tiles",
     "moe_workspace_check", "moe_workspace_graph_count", "moe_dispatch_noalloc",
+    "moe_workspace_set_fused_decode",
 )
 
 
@@ -80,6 +81,7 @@ def _load():
     L.moe_workspace_tiles.argtypes = [P, C.POINTER(P), C.POINTER(P)]
     L.moe_workspace_check.argtypes = [P, C.POINTER(i), P]
     L.moe_workspace_graph_count.argtypes = [P, C.POINTER(i)]
+    L.moe_workspace_set_fused_decode.argtypes = [P, i]
     for n in SYMBOLS:
         if n not in ("moe_status_string", "moe_last_error"):
             getattr(L, n).restype = i
@@ -157,6 +159,9 @@ class Workspace:
 
     def set_graphs(self, enable: bool):
         _check(_load().moe_workspace_set_graphs(self.handle, int(bool(enable))))
+
+    def set_fused_decode(self, enable: bool):
+        _check(_load().moe_workspace_set_fused_decode(self.handle, int(bool(enable))))
 
     def set_stage_events(self, stage: int, ev_begin=None, ev_end=None):
         """Record torch.cuda.Event pairs (enable_timing=True, already recorded

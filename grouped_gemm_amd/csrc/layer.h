@@ -140,6 +140,41 @@ struct CombineArgs {
   int weighted_bf16;      // out_slot rows are bf16 and already carry w[t,j]
 };
 
+// The single-launch decode layer (batches of at most DECODE_STREAM_TOKENS
+// tokens).  ids .. meta receive the routing results for the caller (written
+// by workgroup 0); h, out_slot, amax and cnt are its scratch; bar holds the
+// grid barrier's arrival count and generation.
+struct DecodeArgs {
+  const float* scores;    // [T, E]
+  const uint16_t* x;      // [T, H] bf16
+  uint16_t* y;            // [T, H] bf16
+  int T, E, k, score_fn, shared, H, I;
+  const uint8_t *wg, *wu, *wd;      // routed weights [E, N, K] (format codes)
+  const void *sg, *su, *sd;         // their scales
+  const uint8_t *shg, *shu, *shd;   // shared expert [1, N, K] or NULL
+  const void *ssg, *ssu, *ssd;
+  int act;
+  float act_limit;
+  int32_t* ids;           // [T, k]
+  float* w;               // [T, k]
+  int32_t* counts;        // [G]
+  int32_t* indptr;        // [G + 1]
+  int32_t* gather;        // [S_tot]
+  int32_t* inv;           // [S]
+  int32_t* meta;          // [META_WORDS]
+  float* h;               // [S_tot, I] fp32 intermediate (bf16 for the bf16 format)
+  uint16_t* out_slot;     // [S_tot, H] weighted bf16 slot rows
+  uint32_t* amax;         // [2][amax_stride] per-row maxima of |h|, by launch parity
+  int32_t* cnt;           // [2][cnt_stride] arrivals per (token, 16-channel block), by parity
+  int32_t* bar;           // [2] grid barrier: arrival count, generation
+  int amax_stride, cnt_stride;
+  long spin_limit;        // bound on the barrier's wait (polls)
+};
+// Workgroups of the decode layer's persistent grid that are resident at
+// once on `cus` compute units (0: the kernel cannot run).
+int decode_layer_grid(int fmt, int act, int cus);
+hipError_t launch_decode_layer(int fmt, const DecodeArgs& a, int grid, hipStream_t st);
+
 hipError_t launch_route(const float* scores, int T, int E, int k, int score_fn, int32_t* ids,
                         float* w, const QuantArgs& fq, hipStream_t st);
 hipError_t launch_dispatch(const DispatchArgs& d, hipStream_t st);

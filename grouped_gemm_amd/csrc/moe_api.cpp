@@ -89,8 +89,12 @@ int validate_desc(const moe_layer_desc* d) {
 
 struct Layout {
   size_t ids, w, counts, indptr, gather, inv, active, tiles, meta, chunk;
-  size_t xq, xs, h, hq, hs, out_slot, total;
+  size_t xq, xs, h, hq, hs, out_slot, dstate, total;
   long S, S_tot, G, max_tiles, nchunks;
+  // single-launch decode layer state: barrier words, then per-parity row
+  // maxima and (token, channel-block) arrival counters
+  long amax_stride, cnt_stride;
+  size_t dstate_bytes;
 };
 
 size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -125,6 +129,10 @@ Layout make_layout(const moe_layer_desc& d) {
   L.hq = take((size_t)L.S_tot * I);
   L.hs = take((size_t)L.S_tot * (I / 32) * 4);
   L.out_slot = take((size_t)L.S_tot * H * 4);
+  L.amax_stride = (long)DECODE_STREAM_TOKENS * (k + d.shared_experts);
+  L.cnt_stride = (long)DECODE_STREAM_TOKENS * (H / 16);
+  L.dstate_bytes = 256 + 4 * 2 * (size_t)(L.amax_stride + L.cnt_stride);
+  L.dstate = take(L.dstate_bytes);
   L.total = off;
   return L;
 }
@@ -159,9 +167,11 @@ struct moe_ws {
   int fmt;
   int force_cfg = -1;
   int graphs = 1;
+  int fused_decode = 0;    // single-launch decode layer: opt-in (slower on gfx950, see the header)
+  int decode_grid = -1;   // resident workgroups of the decode layer (computed once)
   int device = 0;
   std::map<GraphKey, GraphEntry> execs;
-  hipEvent_t stage_ev[6][2] = {};
+  hipEvent_t stage_ev[7][2] = {};
   bool any_stage_events() const {
     for (auto& p : stage_ev)
       if (p[0] || p[1]) return true;
@@ -309,8 +319,76 @@ hipError_t run_gemm(const moe_ws* ws, bool gateup, GemmArgs g, void* tiled_out, 
   return run_gemm_c(ws, gateup, g, tiled_out, tiled_scale, candidates(ws, rows_tot, T), st);
 }
 
+// Whether the single-launch decode layer serves a call of T tokens: small
+// batches, the streaming configuration (or the device's choice), K of both
+// projections a multiple of four 128-wide steps, and a grid that fits.
+bool use_fused_decode(moe_ws* ws, int T) {
+  const moe_layer_desc& d = ws->d;
+  if (!ws->fused_decode || T > DECODE_STREAM_TOKENS) return false;
+  if (ws->force_cfg > 0) return false;
+  if (d.hidden % 512 || d.inter % 512) return false;
+  if (ws->decode_grid < 0) ws->decode_grid = decode_layer_grid(ws->fmt, d.activation, device_cus());
+  return ws->decode_grid > 0;
+}
+
+int enqueue_fused_decode(moe_ws* ws, const moe_weights* w, const uint16_t* x, const float* scores,
+                         int T, uint16_t* y, hipStream_t st) {
+  const moe_layer_desc& d = ws->d;
+  const Layout& L = ws->L;
+  const bool relu2 = d.activation == MOE_ACT_RELU2;
+  DecodeArgs a{};
+  a.scores = scores;
+  a.x = x;
+  a.y = y;
+  a.T = T;
+  a.E = d.num_experts;
+  a.k = d.top_k;
+  a.score_fn = d.score_fn;
+  a.shared = d.shared_experts;
+  a.H = d.hidden;
+  a.I = d.inter;
+  a.wg = (const uint8_t*)(relu2 ? w->w_up : w->w_gate);
+  a.wu = (const uint8_t*)w->w_up;
+  a.wd = (const uint8_t*)w->w_down;
+  a.sg = relu2 ? w->s_up : w->s_gate;
+  a.su = w->s_up;
+  a.sd = w->s_down;
+  a.shg = (const uint8_t*)(relu2 ? w->sh_up : w->sh_gate);
+  a.shu = (const uint8_t*)w->sh_up;
+  a.shd = (const uint8_t*)w->sh_down;
+  a.ssg = relu2 ? w->ss_up : w->ss_gate;
+  a.ssu = w->ss_up;
+  a.ssd = w->ss_down;
+  a.act = d.activation;
+  a.act_limit = act_limit(d);
+  a.ids = ws->at<int32_t>(L.ids);
+  a.w = ws->at<float>(L.w);
+  a.counts = ws->at<int32_t>(L.counts);
+  a.indptr = ws->at<int32_t>(L.indptr);
+  a.gather = ws->at<int32_t>(L.gather);
+  a.inv = ws->at<int32_t>(L.inv);
+  a.meta = ws->at<int32_t>(L.meta);
+  a.h = ws->at<float>(L.h);
+  a.out_slot = ws->at<uint16_t>(L.out_slot);
+  a.bar = ws->at<int32_t>(L.dstate);
+  a.amax = (uint32_t*)(ws->at<char>(L.dstate) + 256);
+  a.cnt = (int32_t*)(a.amax + 2 * L.amax_stride);
+  a.amax_stride = (int)L.amax_stride;
+  a.cnt_stride = (int)L.cnt_stride;
+  a.spin_limit = 1L << 21;
+  auto mark = [&](int stage, int which) -> hipError_t {
+    hipEvent_t e = ws->stage_ev[stage][which];
+    return e ? hipEventRecord(e, st) : hipSuccess;
+  };
+  HIP_TRY(mark(6, 0), "event record");
+  HIP_TRY(launch_decode_layer(ws->fmt, a, ws->decode_grid, st), "decode layer launch");
+  HIP_TRY(mark(6, 1), "event record");
+  return MOE_OK;
+}
+
 int enqueue_layer(moe_ws* ws, const moe_weights* w, const uint16_t* x, const float* scores, int T,
                   uint16_t* y, hipStream_t st) {
+  if (use_fused_decode(ws, T)) return enqueue_fused_decode(ws, w, x, scores, T, y, st);
   const moe_layer_desc& d = ws->d;
   const Layout& L = ws->L;
   const int S = T * d.top_k, S_tot = S + (d.shared_experts ? T : 0);
@@ -538,6 +616,13 @@ int moe_workspace_create(const moe_layer_desc* desc, void* dev_buf, size_t bytes
   ws->base = (char*)dev_buf;
   ws->fmt = fmt_of(*desc);
   if (hipGetDevice(&ws->device) != hipSuccess) ws->device = 0;
+  // the decode layer's barrier words and counters start cleared (they are
+  // kept cleared by the kernel from then on)
+  hipError_t e = hipMemset(ws->at<char>(L.dstate), 0, L.dstate_bytes);
+  if (e != hipSuccess) {
+    delete ws;
+    return hip_fail(e, "clear the decode-layer state");
+  }
   *out = ws;
   return MOE_OK;
 }
@@ -788,9 +873,14 @@ int moe_workspace_check(const moe_ws* ws, int* device_status, void* stream) {
   int32_t err = 0;
   HIP_TRY(hipMemcpy(&err, ws->at<int32_t>(ws->L.meta) + META_ERROR, 4, hipMemcpyDeviceToHost),
           "read device status");
-  *device_status = err ? MOE_EINVAL : MOE_OK;
-  if (err) fail(MOE_EINVAL, "the device rejected the last m_indptr (not non-decreasing from 0, "
-                            "or more rows than the workspace holds); no rows were computed");
+  *device_status = err == 0 ? MOE_OK : (err == 2 ? MOE_EHIP : MOE_EINVAL);
+  if (err == 2)
+    fail(MOE_EHIP, "the single-launch decode layer could not make its whole grid resident and "
+                   "stopped at its barrier; the output is incomplete and the workspace must be "
+                   "created again");
+  else if (err)
+    fail(MOE_EINVAL, "the device rejected the last m_indptr (not non-decreasing from 0, or more "
+                     "rows than the workspace holds); no rows were computed");
   return MOE_OK;
 }
 
@@ -812,9 +902,17 @@ int moe_workspace_set_graphs(moe_ws* ws, int enable) {
   return MOE_OK;
 }
 
+int moe_workspace_set_fused_decode(moe_ws* ws, int enable) {
+  if (!ws) return fail(MOE_EINVAL, "workspace is NULL");
+  ws->fused_decode = enable ? 1 : 0;
+  for (auto& kv : ws->execs) (void)hipGraphExecDestroy(kv.second.exec);
+  ws->execs.clear();
+  return MOE_OK;
+}
+
 int moe_workspace_set_stage_events(moe_ws* ws, int stage, void* ev_begin, void* ev_end) {
   if (!ws) return fail(MOE_EINVAL, "workspace is NULL");
-  if (stage < 0 || stage > 5) return fail(MOE_EINVAL, "stage must be in [0, 5]");
+  if (stage < 0 || stage > 6) return fail(MOE_EINVAL, "stage must be in [0, 6]");
   ws->stage_ev[stage][0] = (hipEvent_t)ev_begin;
   ws->stage_ev[stage][1] = (hipEvent_t)ev_end;
   return MOE_OK;

@@ -251,10 +251,12 @@ MOE_API int moe_workspace_routing(const moe_ws* ws, const int32_t** topk_ids, co
 MOE_API int moe_workspace_tiles(const moe_ws* ws, const int32_t** tiles, const int32_t** meta);
 
 /* Synchronise `stream` and report the device-side status of the
- * workspace's last dispatch in *device_status: MOE_OK, or MOE_EINVAL when
- * the device rejected a caller's m_indptr (moe_grouped_gemm then computed
- * no rows; moe_last_error names the reason).  Returns EHIP if the
- * synchronisation fails. */
+ * workspace's last dispatch in *device_status: MOE_OK; MOE_EINVAL when the
+ * device rejected a caller's m_indptr (moe_grouped_gemm then computed no
+ * rows); MOE_EHIP when the single-launch decode layer could not make its
+ * whole grid resident and stopped (its output is then incomplete, and the
+ * workspace must be created again).  moe_last_error names the reason.
+ * Returns EHIP if the synchronisation fails. */
 MOE_API int moe_workspace_check(const moe_ws* ws, int* device_status, void* stream);
 
 /* Number of instantiated decode graphs the workspace holds: at most one per
@@ -282,11 +284,30 @@ MOE_API int moe_config_rows(int cfg_id);
  * so the captured launches replay like the eager ones. */
 MOE_API int moe_workspace_set_graphs(moe_ws* ws, int enable);
 
+/* Enable (1) or disable (0, default) the single-launch decode layer: for
+ * batches of at most 16 tokens moe_layer_forward then runs routing,
+ * dispatch, both quantisations, both grouped GEMMs and the combine in one
+ * persistent kernel (Alpha-MoE news page, "How the megakernel works"),
+ * with one grid-wide barrier between the projections.  It applies when
+ * hidden and inter are multiples of 512 and no tiled configuration is
+ * forced; otherwise, or when disabled, the layer runs its separate kernels.
+ * Its grid holds only workgroups that can be resident at once and its
+ * barrier's wait is bounded: should the launch not get every workgroup
+ * resident (another kernel holding the GPU), it stops and sets the device
+ * status that moe_workspace_check reports, rather than waiting for ever.
+ * Results equal the separate kernels' streaming configuration bit for bit
+ * (GeGLU: within one bf16 step on a few outputs).  It is off by default
+ * because on gfx950 it is slower than the separate kernels: every
+ * workgroup's device-wide release before the barrier writes back its XCD's
+ * L2, which a kernel boundary does once. */
+MOE_API int moe_workspace_set_fused_decode(moe_ws* ws, int enable);
+
 /* Profiling: record the caller's HIP events (hipEvent_t, created with
  * timing enabled) immediately before and after the launches of one stage of
  * moe_layer_forward.  Stages: 0 routing + dispatch, 1 input quantisation,
  * 2 gate/up grouped GEMM, 3 intermediate requantisation, 4 down grouped
- * GEMM, 5 combine.  NULL events clear the stage.  While any stage has
+ * GEMM, 5 combine, 6 the single-launch decode layer (which replaces stages
+ * 0-5 when it runs).  NULL events clear the stage.  While any stage has
  * events, moe_layer_forward runs its eager path (no graph replay). */
 MOE_API int moe_workspace_set_stage_events(moe_ws* ws, int stage, void* ev_begin, void* ev_end);
 
