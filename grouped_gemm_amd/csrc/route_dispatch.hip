@@ -654,6 +654,136 @@ __global__ void __launch_bounds__(1024) k_dispatch_place(DispatchArgs d) {
   }
 }
 
+// ---------------------------------------------------------------- decode path
+// Batches of at most DECODE_STREAM_TOKENS tokens, any expert count: one
+// 256-thread block routes every token (one 16-lane row each), counts the
+// groups in LDS, scans the counts with one wave (five groups per lane),
+// places each slot by counting the earlier slots of its group (at most 255)
+// and writes the tables (with ids distinct per token a group holds at most
+// 16 rows, one block-table entry whatever the configuration).  Blocks past
+// the first quantise the activation rows.
+template <int QF>
+__global__ void __launch_bounds__(256) k_dispatch_decode(DispatchArgs d) {
+  __shared__ int32_t ids_l[DECODE_STREAM_TOKENS * 16];
+  __shared__ int32_t cnt_l[320];
+  __shared__ int32_t ind_l[321];
+  __shared__ int32_t act_l[320];
+  __shared__ int32_t tof_l[321];
+  __shared__ int32_t nact_l, mx_l, cfg_l, ntiles_l;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (blockIdx.x != 0) {
+    quant_rows_waves<QF>(d.fq, ((int)blockIdx.x - 1) * 4 + wave, ((int)gridDim.x - 1) * 4, lane);
+    return;
+  }
+  const int T = d.T, E = d.E, k = d.k, S = T * k;
+  const int G = E + d.shared;
+  if (d.scores) {
+    const int t = wave * 4 + (lane >> 4);
+    const bool tv = t < T;
+    route_row16(d.scores + (size_t)(tv ? t : 0) * E, tv, E, k, d.score_fn, lane & 15,
+                d.ids + (size_t)(tv ? t : 0) * k, d.w + (size_t)(tv ? t : 0) * k,
+                ids_l + (tv ? t : 0) * k);
+  } else {
+    for (int p = tid; p < S; p += 256) ids_l[p] = d.ids_in[p];
+  }
+  for (int g = tid; g < 320; g += 256) cnt_l[g] = 0;
+  __syncthreads();
+  for (int p = tid; p < S; p += 256) {
+    const int e = ids_l[p];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt_l[e], 1);   // an id out of range is dropped
+  }
+  __syncthreads();
+  if (tid == 0 && d.shared) cnt_l[E] = T;
+  __syncthreads();
+  if (wave == 0) {
+    int c[5], f[5], cs = 0, fs = 0, mx = 0, t32 = 0;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      c[i] = cnt_l[lane * 5 + i];   // zero past G
+      f[i] = c[i] > 0;
+      cs += c[i];
+      fs += f[i];
+      mx = c[i] > mx ? c[i] : mx;
+      t32 += (c[i] + 31) / 32;
+    }
+    int ce = wave_incl_scan<false>(cs) - cs, fe = wave_incl_scan<false>(fs) - fs;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const int gg = lane * 5 + i;
+      if (gg < G) {
+        ind_l[gg] = ce;
+        if (f[i]) act_l[fe] = gg;
+      }
+      ce += c[i];
+      fe += f[i];
+    }
+    const int tot = wave_total<false>(cs), nact = wave_total<false>(fs);
+    mx = wave_total<true>(mx);
+    t32 = wave_total<false>(t32);
+    if (lane == 0) {
+      ind_l[G] = tot;
+      nact_l = nact;
+      mx_l = mx;
+      cfg_l = d.force_cfg >= 0 ? d.force_cfg
+                               : config_rule(mx, nact, tot, t32, d.I, d.num_cfgs, d.cus, d.T);
+    }
+  }
+  __syncthreads();
+  // stable placement: slot order is expert, then flat index t*k+j
+  for (int p = tid; p < S; p += 256) {
+    const int e = ids_l[p];
+    if ((unsigned)e < (unsigned)E) {
+      int r = 0;
+      for (int q = 0; q < p; ++q) r += ids_l[q] == e;
+      const int slot = ind_l[e] + r;
+      d.gather[slot] = p;
+      d.inv[p] = slot;
+    } else {
+      d.inv[p] = -1;
+    }
+  }
+  if (d.shared)
+    for (int t = tid; t < T; t += 256) d.gather[S + t] = t * k;
+  const int nact = nact_l, bm = cfg_rows(cfg_l);
+  for (int g = tid; g < G; g += 256) d.counts[g] = cnt_l[g];
+  for (int g = tid; g <= G; g += 256) d.indptr[g] = ind_l[g];
+  for (int i = tid; i < nact; i += 256) d.active[i] = act_l[i];
+  // block table: ceil(rows / bm) entries per group, groups ascending
+  if (wave == 0) {
+    int nt[5], ns = 0;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      nt[i] = (cnt_l[lane * 5 + i] + bm - 1) / bm;
+      ns += nt[i];
+    }
+    int o = wave_incl_scan<false>(ns) - ns;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      tof_l[lane * 5 + i] = o;
+      o += nt[i];
+    }
+    const int tot = wave_total<false>(ns);
+    if (lane == 0) ntiles_l = tot;
+  }
+  __syncthreads();
+  for (int g = tid; g < G; g += 256) {
+    const int n = (cnt_l[g] + bm - 1) / bm, o = tof_l[g];
+    for (int r = 0; r < n; ++r) {
+      d.tiles[2 * (o + r)] = g;
+      d.tiles[2 * (o + r) + 1] = r * bm;
+    }
+  }
+  if (tid == 0) {
+    d.meta[META_NACTIVE] = nact;
+    d.meta[META_NTILES] = ntiles_l;
+    d.meta[META_CFG] = cfg_l;
+    d.meta[META_MAXCNT] = mx_l;
+    d.meta[META_ROWS] = S + (d.shared ? T : 0);
+    d.meta[META_BM] = cfg_rows(cfg_l);
+    d.meta[META_ERROR] = 0;
+  }
+}
+
 // ---------------------------------------------------------------- host launchers
 size_t dispatch_small_lds(int S, int G) {
   return sizeof(int32_t) * ((size_t)S + 2 * G + 16 * G + 3 * G);
@@ -695,6 +825,11 @@ hipError_t launch_route(const float* scores, int T, int E, int k, int score_fn, 
 hipError_t launch_dispatch(const DispatchArgs& d, hipStream_t st) {
   const int G = d.E + d.shared;
   const int S = d.T * d.k;
+  if (d.T >= 1 && d.T <= DECODE_STREAM_TOKENS && G <= 320) {
+    const int grid = 1 + (d.fq.R > 0 ? (d.fq.R + 3) / 4 : 0);
+    LAUNCH_QF(quant_format(d.fq), k_dispatch_decode, dim3(grid), dim3(256), 0, st, d);
+    return hipGetLastError();
+  }
   if (S <= TINY_DISPATCH_SLOTS && G <= 64 && (!d.scores || d.E <= SMALL_E_THREAD_ROUTE)) {
     const int grid = 1 + quant_blocks(d.fq, 4, 3);
     LAUNCH_QF(quant_format(d.fq), k_dispatch_tiny, dim3(grid), dim3(256), 0, st, d);
