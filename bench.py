@@ -295,6 +295,86 @@ def config_sweep(name, T, act=0, rounds=3, calls=30):
             "fastest_config": fastest, "auto_over_fastest": round(best[-1] / best[fastest] - 1, 4)}
 
 
+def config_sweep_many(name, tokens, act=0, rounds=3, calls=20):
+    """config_sweep at several token counts of one workload with one weight
+    draw (every expert), also reporting the routing histogram each point ran
+    (the data the tile-configuration cost model is fitted to)."""
+    import torch
+    import grouped_gemm_amd as g
+    import moe_synth as ms
+    import oracle
+    sh = ms.CONFIGS[name].with_(activation=act)
+    t0 = time.time()
+    W = ms.gen_weights(sh)
+    log(f"[sweep] {name}: all {sh.experts} experts drawn in {time.time() - t0:.1f}s")
+    dW = {n: (torch.from_numpy(np.ascontiguousarray(getattr(W, n))).cuda()
+              if getattr(W, n) is not None else None)
+          for n in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
+                    "sh_gate", "sh_up", "sh_down", "ss_gate", "ss_up", "ss_down")}
+    del W
+    ncfg = 3 if sh.w_format == 0 else 4
+    st = torch.cuda.Stream()
+    out = []
+    for T in tokens:
+        B = ms.gen_batch(sh, T)
+        ids, _ = oracle.route(B.scores, sh.top_k, sh.score_fn)
+        counts = np.bincount(ids.ravel(), minlength=sh.experts).tolist()
+        if sh.shared:
+            counts.append(T)
+        ws = g.Workspace(sh.hidden, sh.inter, sh.experts, sh.top_k, T, shared_experts=sh.shared,
+                         shared_inter=sh.shared_inter, score_fn=sh.score_fn,
+                         w_format=sh.w_format, a_format=sh.a_format, activation=sh.activation,
+                         act_limit=sh.act_limit)
+        ws.set_graphs(False)
+        x = torch.from_numpy(B.x_bits.view(np.int16)).cuda()
+        sc = torch.from_numpy(B.scores).cuda()
+        y = torch.empty(T, sh.hidden, dtype=torch.int16, device="cuda")
+
+        def median_us(n):
+            with torch.cuda.stream(st):
+                ts = []
+                for _ in range(n):
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(st)
+                    g.layer_forward(ws, dW, x, sc, y, stream=st)
+                    e1.record(st)
+                    e1.synchronize()
+                    ts.append(e0.elapsed_time(e1) * 1e3)
+            return float(np.median(ts))
+
+        tw = time.perf_counter()
+        while time.perf_counter() - tw < 0.3:
+            median_us(5)
+        # -1: the library's choice with the cost model (default); -2: with
+        # the fixed histogram rule; 0..: each configuration forced
+        best, chosen = {}, {}
+        for r in range(rounds):
+            order = [-1, -2] + list(range(ncfg))
+            for c in (order if r % 2 == 0 else order[::-1]):
+                ws.set_config_model(c != -2)
+                ws.force_config(max(c, -1))
+                median_us(2)
+                best[c] = min(best.get(c, 1e30), median_us(calls))
+                if c < 0:
+                    chosen[c] = ws.last_config()
+        ws.set_config_model(True)
+        ws.force_config(-1)
+        fastest = min(range(ncfg), key=lambda c: best[c])
+        rec = {"workload": name, "tokens": T, "hidden": sh.hidden, "inter": sh.inter,
+               "experts": sh.experts, "top_k": sh.top_k, "shared": sh.shared,
+               "w_format": sh.w_format, "counts": counts, "auto_config": chosen[-1],
+               "auto_us": round(best[-1], 2), "candidates": ws.candidates(T),
+               "rule_config": chosen[-2], "rule_us": round(best[-2], 2),
+               "forced_us": {str(c): round(best[c], 2) for c in range(ncfg)},
+               "fastest_config": fastest}
+        log(f"[sweep] {name} T={T}: {rec['forced_us']} model {chosen[-1]} rule {chosen[-2]}")
+        print(json.dumps(rec), flush=True)
+        out.append(rec)
+        del ws
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -319,6 +399,9 @@ def main():
                     help="time the device's configuration choice against every forced "
                          "configuration at each token count of the workload (or --tokens) "
                          "and print one JSON line per point instead of the benchmark line")
+    ap.add_argument("--sweep-tokens", default="",
+                    help="with --config-sweep: comma-separated token counts timed with one "
+                         "weight draw of every expert, printing the routing histogram of each")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain elementwise copy of 256 MiB (fp32 in, fp32 out), "
                          "whose known byte counts calibrate hardware traffic counters")
@@ -351,6 +434,9 @@ def main():
     act = ACTIVATIONS[args.activation]
     sh0 = ms.CONFIGS[args.workload]
     if args.config_sweep:
+        if args.sweep_tokens:
+            config_sweep_many(args.workload, [int(t) for t in args.sweep_tokens.split(",")], act)
+            return
         for T in ([args.tokens] if args.tokens else list(sh0.tokens)):
             print(json.dumps(config_sweep(args.workload, T, act)), flush=True)
         return

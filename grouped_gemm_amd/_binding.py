@@ -22,7 +22,8 @@ SYMBOLS = (
     "moe_workspace_force_config", "moe_workspace_last_config", "moe_config_rows",
     "moe_workspace_set_graphs", "moe_workspace_set_stage_events", "moe_workspace_tiles",
     "moe_workspace_check", "moe_workspace_graph_count", "moe_dispatch_noalloc",
-    "moe_workspace_set_fused_decode",
+    "moe_workspace_set_fused_decode", "moe_workspace_set_config_model", "moe_workspace_candidates",
+    "moe_config_model_params",
 )
 
 
@@ -82,6 +83,9 @@ def _load():
     L.moe_workspace_check.argtypes = [P, C.POINTER(i), P]
     L.moe_workspace_graph_count.argtypes = [P, C.POINTER(i)]
     L.moe_workspace_set_fused_decode.argtypes = [P, i]
+    L.moe_workspace_set_config_model.argtypes = [P, i]
+    L.moe_workspace_candidates.argtypes = [P, i, C.POINTER(i)]
+    L.moe_config_model_params.argtypes = [C.POINTER(C.c_double)]
     for n in SYMBOLS:
         if n not in ("moe_status_string", "moe_last_error"):
             getattr(L, n).restype = i
@@ -163,6 +167,15 @@ class Workspace:
     def set_fused_decode(self, enable: bool):
         _check(_load().moe_workspace_set_fused_decode(self.handle, int(bool(enable))))
 
+    def set_config_model(self, enable: bool):
+        _check(_load().moe_workspace_set_config_model(self.handle, int(bool(enable))))
+
+    def candidates(self, T: int) -> int:
+        """Configurations (bit c) whose kernels a T-token call launches."""
+        v = C.c_int(0)
+        _check(_load().moe_workspace_candidates(self.handle, T, C.byref(v)))
+        return v.value
+
     def set_stage_events(self, stage: int, ev_begin=None, ev_end=None):
         """Record torch.cuda.Event pairs (enable_timing=True, already recorded
         once so that they exist) around one stage of layer_forward."""
@@ -194,6 +207,14 @@ class Workspace:
         ps = [C.c_void_p() for _ in range(6)]
         _check(_load().moe_workspace_routing(self.handle, *[C.byref(p) for p in ps]))
         return [p.value for p in ps]
+
+
+def config_model_params():
+    """The cost model's fitted parameters compiled into the library, as a
+    list of 5 rows of 4 floats."""
+    buf = (C.c_double * 20)()
+    _check(_load().moe_config_model_params(buf))
+    return [list(buf[4 * r:4 * r + 4]) for r in range(5)]
 
 
 def route_topk(scores, k, score_fn, topk_ids, topk_w, stream=None, renorm=1):

@@ -53,6 +53,62 @@ struct QuantArgs {
   int only_cfg;
 };
 
+// Histogram statistics the configuration choice reads: largest group,
+// active groups, rows, and the row blocks of 16, 32, 64 and 128 rows the
+// groups need (sums of ceil(rows / b)).
+struct HistStats {
+  int mx, active, rows, s16, s32, s64, s128;
+};
+
+// The fitted tile-configuration cost model (RaMP abstract: a four-parameter
+// wave cost model over the runtime expert histogram, depending only on the
+// kernels' grid geometry).  Predicted time of configuration cfg for a layer
+// of shape (H, I) in weight format fmt (0 bf16, 1/2 fp8, 3 MXFP4) and T
+// tokens: th[row][0] + th[row][1] * (weight bytes streamed / HBM peak)
+//        + th[row][2] * (padded MFMA work / MFMA peak) + th[row][3] * waves,
+// row = cfg (row 4: streaming above DECODE_STREAM_TOKENS tokens).  The
+// features mirror grouped_gemm_amd/costmodel.py, which fits th.
+struct CostModel {
+  const double* th;       // th[5][4], row-major (device memory in DispatchArgs)
+  int on;                 // 0: the histogram rule instead
+  int mask;               // configurations the device may choose (bit c)
+};
+
+__host__ __device__ inline double cost_model_time(const double* th, const HistStats& h, int cfg,
+                                                  int fmt, int H, int I, int T, int cus) {
+  // no fused multiply-adds: host and device then predict the same times
+#pragma clang fp contract(off)
+  const double wbytes = fmt == 0 ? 2.0 : (fmt == 3 ? 0.5 : 1.0);
+  const double peak = fmt == 0 ? 2.5e9 : 5.0e9;          // MFMA flop per us
+  const double hbm = 8.0e6;                              // HBM bytes per us
+  const double mlp = 3.0 * H * I * wbytes, flop_row = 6.0 * H * I;
+  double wb, padded, waves;
+  int row = cfg;
+  if (cfg == 0) {
+    const bool dec = T >= 0 ? T <= 16 : h.mx <= 16;
+    row = dec ? 0 : 4;
+    wb = (dec ? h.s16 : h.s64) * mlp;
+    padded = 16.0 * h.s16;
+    waves = (double)h.active * (I / 16 + H / 16) / (cus * 8.0);
+  } else {
+    const int bm = cfg == 1 ? 32 : (cfg == 2 ? 64 : 128);
+    const int tiles = cfg == 1 ? h.s32 : (cfg == 2 ? h.s64 : h.s128);
+    int cb_gu, cb_dn;
+    if (cfg == 3) {
+      cb_gu = I / 128;
+      cb_dn = H % 256 == 0 ? H / 256 : H / 128;
+    } else {
+      cb_gu = I / (fmt == 1 ? 64 : 128);
+      cb_dn = H / 128;
+    }
+    wb = h.active * mlp;
+    padded = (double)tiles * bm;
+    waves = (double)(((long)tiles * cb_gu + cus - 1) / cus + ((long)tiles * cb_dn + cus - 1) / cus);
+  }
+  const double* t = th + 4 * row;
+  return t[0] + t[1] * (wb / hbm) + t[2] * (padded * flop_row / peak) + t[3] * waves;
+}
+
 struct DispatchArgs {
   const float* scores;    // [T,E] or NULL when ids are given
   const int32_t* ids_in;  // [T,k] when scores == NULL
@@ -73,6 +129,8 @@ struct DispatchArgs {
   int cus;                // compute units of the device (configuration rule)
   QuantArgs fq;           // activation rows the routing launch quantises on
                           // its spare waves (fq.R = 0: none)
+  int fmt;                // weight format (Fmt), for the cost model
+  CostModel cm;           // fitted configuration cost model (cm.on = 0: the rule)
 };
 
 // Grouped GEMM over expert-major row groups.
@@ -115,6 +173,7 @@ struct GemmArgs {
   // gate/up op: expert activation (ACT_*) and its clamp
   int act;
   float act_limit;
+  int grid_cap;           // streaming kernel: most workgroups (0: one per work item)
 };
 
 // Store four consecutive down-projection outputs of one row.

@@ -11,6 +11,7 @@
 #include <tuple>
 
 #include "../../include/moe.h"
+#include "costmodel_params.h"
 #include "layer.h"
 
 namespace {
@@ -89,7 +90,7 @@ int validate_desc(const moe_layer_desc* d) {
 
 struct Layout {
   size_t ids, w, counts, indptr, gather, inv, active, tiles, meta, chunk;
-  size_t xq, xs, h, hq, hs, out_slot, dstate, total;
+  size_t xq, xs, h, hq, hs, out_slot, dstate, cmth, total;
   long S, S_tot, G, max_tiles, nchunks;
   // single-launch decode layer state: barrier words, then per-parity row
   // maxima and (token, channel-block) arrival counters
@@ -133,6 +134,7 @@ Layout make_layout(const moe_layer_desc& d) {
   L.cnt_stride = (long)DECODE_STREAM_TOKENS * (H / 16);
   L.dstate_bytes = 256 + 4 * 2 * (size_t)(L.amax_stride + L.cnt_stride);
   L.dstate = take(L.dstate_bytes);
+  L.cmth = take(sizeof kCostModelTheta);   // the cost model's parameters, read by dispatch
   L.total = off;
   return L;
 }
@@ -168,6 +170,7 @@ struct moe_ws {
   int force_cfg = -1;
   int graphs = 1;
   int fused_decode = 0;    // single-launch decode layer: opt-in (slower on gfx950, see the header)
+  int config_model = 1;    // fitted cost model picks the configuration (0: the histogram rule)
   int decode_grid = -1;   // resident workgroups of the decode layer (computed once)
   int device = 0;
   std::map<GraphKey, GraphEntry> execs;
@@ -196,6 +199,110 @@ int device_cus() {
   return n;
 }
 
+// ---------------------------------------------------------------------------
+// Host side of the fitted configuration cost model.  Before the histogram
+// exists the host only knows the batch, so it evaluates the model on three
+// routings that bound what the histogram can be (T*k rows spread evenly
+// over the experts, packed into k experts of T rows, and T/2 tokens packed
+// with the rest spread; a shared expert adds a group of T rows).  Over the
+// sets of kernel launches it takes the one whose best configuration's mean
+// predicted time over those routings, plus kLaunchUs for every launch beyond
+// the first, is least (the first such set on a tie), and passes the
+// configurations those launches serve to the dispatch kernel, which picks,
+// on the real histogram, the least predicted time among them.
+// grouped_gemm_amd/costmodel.py (candidate_mask) computes the same set.
+// a set of launches per projection beyond the first (both projections): the
+// layer measured a median 5.1 us slower with two than the forced single one
+constexpr double kLaunchUs = 5.0;
+
+void add_groups(HistStats& h, long c, long m) {
+  if (c <= 0 || m <= 0) return;
+  h.mx = c > h.mx ? (int)c : h.mx;
+  h.active += (int)m;
+  h.rows += (int)(c * m);
+  h.s16 += (int)(m * ((c + 15) / 16));
+  h.s32 += (int)(m * ((c + 31) / 32));
+  h.s64 += (int)(m * ((c + 63) / 64));
+  h.s128 += (int)(m * ((c + 127) / 128));
+}
+
+
+// The configurations each kernel launch serves (bit c): the streaming
+// kernel; bf16 one launch per tiled configuration; FP8 one for 32/64-row
+// blocks and one for 128-row blocks; MXFP4 one for every tiled one.
+int launch_families(int fmt, int* fam) {
+  fam[0] = 1;
+  if (fmt == F_BF16) {
+    fam[1] = 2;
+    fam[2] = 4;
+    return 3;
+  }
+  if (fmt == F_MX) {
+    fam[1] = 14;
+    return 2;
+  }
+  fam[1] = 6;
+  fam[2] = 8;
+  return 3;
+}
+
+CostModel cost_model(const moe_ws* ws, int T) {
+  CostModel m{};
+  m.th = ws->at<double>(ws->L.cmth);
+  if (!ws->config_model || ws->force_cfg >= 0 || T < 0) return m;   // off: the rule
+  const double* th = &kCostModelTheta[0][0];
+  const moe_layer_desc& d = ws->d;
+  const long E = d.num_experts, k = d.top_k, q = (long)T * k / E, r = (long)T * k % E;
+  const long t1 = T / 2, q2 = (T - t1) * k / E, r2 = (T - t1) * k % E, kr = k < r2 ? k : r2;
+  const int nc = num_cfgs(ws->fmt), cus = device_cus();
+  HistStats h[3] = {};
+  add_groups(h[0], q + 1, r);                    // even: the first r experts one row more
+  add_groups(h[0], q, E - r);
+  add_groups(h[1], T, k);                        // packed
+  add_groups(h[2], t1 + q2 + 1, kr);             // T/2 tokens on experts 0..k-1, the rest even
+  add_groups(h[2], t1 + q2, k - kr);
+  add_groups(h[2], q2 + 1, r2 - k > 0 ? r2 - k : 0);
+  add_groups(h[2], q2, E - (k > r2 ? k : r2));
+  for (auto& x : h)
+    if (d.shared_experts) add_groups(x, T, 1);
+  double t[3][kNumCfgs];
+  for (int i = 0; i < 3; ++i)
+    for (int c = 0; c < nc; ++c) t[i][c] = cost_model_time(th, h[i], c, ws->fmt, d.hidden, d.inter, T, cus);
+  int fam[3];
+  const int nf = launch_families(ws->fmt, fam);
+  int best = 0;
+  double best_cost = 0.0;
+  for (int sel = 1; sel < (1 << nf); ++sel) {
+    // every configuration a launched kernel serves is a candidate
+    int mask = 0, nl = 0;
+    for (int i = 0; i < nf; ++i)
+      if ((sel >> i) & 1) {
+        mask |= fam[i];
+        ++nl;
+      }
+    mask &= (1 << nc) - 1;
+    double cost = 0.0;
+    for (int i = 0; i < 3; ++i) {
+      double mn = 0.0;
+      bool any = false;
+      for (int c = 0; c < nc; ++c)
+        if ((mask >> c) & 1 && (!any || t[i][c] < mn)) {
+          mn = t[i][c];
+          any = true;
+        }
+      cost += mn;
+    }
+    cost = cost / 3.0 + kLaunchUs * (nl - 1);
+    if (best == 0 || cost < best_cost) {
+      best = mask;
+      best_cost = cost;
+    }
+  }
+  m.on = 1;
+  m.mask = best;
+  return m;
+}
+
 DispatchArgs dispatch_args(const moe_ws* ws, int T) {
   DispatchArgs a{};
   const moe_layer_desc& d = ws->d;
@@ -221,6 +328,13 @@ DispatchArgs dispatch_args(const moe_ws* ws, int T) {
   a.xbits = xbits_of(ws->fmt);
   a.num_cfgs = num_cfgs(ws->fmt);
   a.cus = device_cus();
+  a.fmt = ws->fmt;
+  a.cm = cost_model(ws, T);
+  if (a.cm.on && !(a.cm.mask & (a.cm.mask - 1))) {
+    // one candidate: the dispatch kernel takes it without evaluating the model
+    a.force_cfg = __builtin_ctz(a.cm.mask);
+    a.cm.on = 0;
+  }
   return a;
 }
 
@@ -255,14 +369,23 @@ GemmArgs gemm_args(const moe_ws* ws) {
 // [ceil(rows_tot/32), floor((rows_tot + 31 * groups) / 32)] (each group
 // adds at most 31/32 of a tile to its exact share).  A forced configuration
 // is known outright.
+// With the cost model on, the candidates are the model's mask (the device
+// picks within it).
 struct Candidates {
   bool stream, small, big;   // streaming kernel; tiled configurations 1-2; configuration 3
+  int mask;                  // configurations whose kernels are launched (bit c)
 };
+Candidates from_flags(bool stream, bool small, bool big) {
+  return {stream, small, big, (stream ? 1 : 0) | (small ? 6 : 0) | (big ? 8 : 0)};
+}
+Candidates from_mask(int mask) { return {(mask & 1) != 0, (mask & 6) != 0, (mask & 8) != 0, mask}; }
+Candidates forced(int cfg) { return from_mask(1 << cfg); }
 Candidates candidates(const moe_ws* ws, long rows_tot, int T) {
-  if (ws->force_cfg >= 0)
-    return {ws->force_cfg == 0, ws->force_cfg == 1 || ws->force_cfg == 2, ws->force_cfg == 3};
+  if (ws->force_cfg >= 0) return forced(ws->force_cfg);
+  const CostModel m = cost_model(ws, T);
+  if (m.on) return from_mask(m.mask);
   // the device rule streams every batch of at most DECODE_STREAM_TOKENS tokens
-  if (T <= DECODE_STREAM_TOKENS || num_cfgs(ws->fmt) <= 1) return {true, false, false};
+  if (T <= DECODE_STREAM_TOKENS || num_cfgs(ws->fmt) <= 1) return from_flags(true, false, false);
   const long cus = device_cus(), cb = ws->d.inter / 128;
   const long G = ws->L.G;
   const long groups = rows_tot < G ? rows_tot : G;
@@ -273,7 +396,7 @@ Candidates candidates(const moe_ws* ws, long rows_tot, int T) {
   // count bound forces it (mean over all groups above 64, enough items)
   const bool big = tiled && num_cfgs(ws->fmt) > 3 && rows_tot >= CFG3_MIN_ROWS && rows_tot > 64;
   const bool big_certain = big && 2 * lo * cb >= cus && rows_tot > 64 * G;
-  return {2 * lo * cb < cus, tiled && !big_certain, big};
+  return from_flags(2 * lo * cb < cus, tiled && !big_certain, big);
 }
 
 // Run a projection with the kernel families the configuration can land on;
@@ -285,7 +408,12 @@ hipError_t run_gemm_c(const moe_ws* ws, bool gateup, GemmArgs g, void* tiled_out
                       const Candidates& cand, hipStream_t st) {
   if (cand.stream) {
     g.cfg_self = 0;
+    // a streaming launch the device may not choose gets a capped grid whose
+    // workgroups stride the work items: when it returns at once it starts
+    // a few thousand workgroups instead of one per (group, 16 channels)
+    if (cand.mask != 1) g.grid_cap = device_cus() * 8;
     hipError_t e = launch_gemm_stream(ws->fmt, gateup, g, st);
+    g.grid_cap = 0;
     if (e != hipSuccess) return e;
   }
   if (!cand.small && !cand.big) return hipSuccess;
@@ -306,7 +434,7 @@ hipError_t run_gemm_c(const moe_ws* ws, bool gateup, GemmArgs g, void* tiled_out
     return hipSuccess;
   }
   for (int c = 1; c < num_cfgs(ws->fmt); ++c) {
-    if (ws->force_cfg > 0 && c != ws->force_cfg) continue;
+    if (!((cand.mask >> c) & 1)) continue;
     g.cfg_self = c;
     hipError_t e = launch_gemm_tiled(ws->fmt, gateup, c, g, st);
     if (e != hipSuccess) return e;
@@ -623,6 +751,11 @@ int moe_workspace_create(const moe_layer_desc* desc, void* dev_buf, size_t bytes
     delete ws;
     return hip_fail(e, "clear the decode-layer state");
   }
+  e = hipMemcpy(ws->at<char>(L.cmth), kCostModelTheta, sizeof kCostModelTheta, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    delete ws;
+    return hip_fail(e, "copy the cost model's parameters");
+  }
   *out = ws;
   return MOE_OK;
 }
@@ -720,9 +853,8 @@ int moe_grouped_gemm(moe_ws* ws, int op, const void* a, const void* a_scale,
   g.cfg_self = -1;
   // the host does not know the histogram: every kernel family the device
   // may choose is launched, and those it did not choose return at once
-  Candidates cand{true, num_cfgs(ws->fmt) > 1, num_cfgs(ws->fmt) > 3 && cap >= CFG3_MIN_ROWS};
-  if (ws->force_cfg >= 0)
-    cand = {ws->force_cfg == 0, ws->force_cfg == 1 || ws->force_cfg == 2, ws->force_cfg == 3};
+  Candidates cand = from_flags(true, num_cfgs(ws->fmt) > 1, num_cfgs(ws->fmt) > 3 && cap >= CFG3_MIN_ROWS);
+  if (ws->force_cfg >= 0) cand = forced(ws->force_cfg);
   if (gateup && quant) {
     // fp32 staging, requantised by a separate pass, except where the tiled
     // 1x128 and MX epilogues requantise in place
@@ -907,6 +1039,27 @@ int moe_workspace_set_fused_decode(moe_ws* ws, int enable) {
   ws->fused_decode = enable ? 1 : 0;
   for (auto& kv : ws->execs) (void)hipGraphExecDestroy(kv.second.exec);
   ws->execs.clear();
+  return MOE_OK;
+}
+
+int moe_workspace_set_config_model(moe_ws* ws, int enable) {
+  if (!ws) return fail(MOE_EINVAL, "workspace is NULL");
+  ws->config_model = enable ? 1 : 0;
+  for (auto& kv : ws->execs) (void)hipGraphExecDestroy(kv.second.exec);
+  ws->execs.clear();
+  return MOE_OK;
+}
+
+int moe_workspace_candidates(const moe_ws* ws, int T, int* host_mask) {
+  if (!ws || !host_mask) return fail(MOE_EINVAL, "null pointer");
+  if (T < 0) return fail(MOE_EINVAL, "T must be >= 0");
+  *host_mask = candidates(ws, (long)T * ws->d.top_k + (ws->d.shared_experts ? T : 0), T).mask;
+  return MOE_OK;
+}
+
+int moe_config_model_params(double* host_theta20) {
+  if (!host_theta20) return fail(MOE_EINVAL, "null pointer");
+  memcpy(host_theta20, kCostModelTheta, sizeof kCostModelTheta);
   return MOE_OK;
 }
 

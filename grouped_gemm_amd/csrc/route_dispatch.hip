@@ -232,23 +232,61 @@ DEVI int config_rule(int mx, int active, int rows, int tiles32, int I, int num_c
   return (active > 0 && rows >= 64 * active && rows >= CFG3_MIN_ROWS) ? 3 : 2;
 }
 
-// The histogram statistics by one wave over the counts in LDS, then the rule.
-DEVI int choose_config(const int32_t* cnt, int G, int I, int num_cfgs, int cus, int T, int lane,
-                      int* max_out) {
-  int mx = 0, active = 0, rows = 0, tiles32 = 0;
-  for (int g = lane; g < G; g += 64) {
-    const int c = cnt[g];
-    mx = c > mx ? c : mx;
-    active += c > 0;
-    rows += c;
-    tiles32 += (c + 31) / 32;
+// The configuration of a histogram: the fitted cost model's least
+// predicted time among the configurations the host launched kernels for
+// (d.cm.mask; the lowest configuration on a tie), else the rule.  The loop
+// over configurations is unrolled, so each evaluation reads the statistics
+// at fixed fields (a per-lane configuration index would make the compiler
+// index them through scratch memory).
+DEVI int pick_config(const DispatchArgs& d, const HistStats& h) {
+  if (d.cm.on && d.cm.mask) {
+    int best = -1;
+    double bt = 0.0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (c < d.num_cfgs && ((d.cm.mask >> c) & 1)) {
+        const double t = cost_model_time(d.cm.th, h, c, d.fmt, d.H, d.I, d.T, d.cus);
+        if (best < 0 || t < bt) {
+          best = c;
+          bt = t;
+        }
+      }
+    }
+    if (best >= 0) return best;
   }
-  mx = wave_total<true>(mx);
-  active = wave_total<false>(active);
-  rows = wave_total<false>(rows);
-  tiles32 = wave_total<false>(tiles32);
-  *max_out = mx;
-  return config_rule(mx, active, rows, tiles32, I, num_cfgs, cus, T);
+  return config_rule(h.mx, h.active, h.rows, h.s32, d.I, d.num_cfgs, d.cus, d.T);
+}
+
+// Wave-wide histogram statistics from each lane's partial ones.
+DEVI HistStats wave_stats(HistStats h) {
+  h.mx = wave_total<true>(h.mx);
+  h.active = wave_total<false>(h.active);
+  h.rows = wave_total<false>(h.rows);
+  h.s16 = wave_total<false>(h.s16);
+  h.s32 = wave_total<false>(h.s32);
+  h.s64 = wave_total<false>(h.s64);
+  h.s128 = wave_total<false>(h.s128);
+  return h;
+}
+
+DEVI void add_group(HistStats& h, int c) {
+  h.mx = c > h.mx ? c : h.mx;
+  h.active += c > 0;
+  h.rows += c;
+  h.s16 += (c + 15) >> 4;
+  h.s32 += (c + 31) >> 5;
+  h.s64 += (c + 63) >> 6;
+  h.s128 += (c + 127) >> 7;
+}
+
+// The histogram statistics by one wave over the counts in LDS, then the
+// configuration.
+DEVI int choose_config(const DispatchArgs& d, const int32_t* cnt, int G, int lane, int* max_out) {
+  HistStats h{};
+  for (int g = lane; g < G; g += 64) add_group(h, cnt[g]);
+  h = wave_stats(h);
+  *max_out = h.mx;
+  return pick_config(d, h);
 }
 
 // Shared tail of both dispatch paths.  cnt (LDS, G entries) holds the
@@ -269,7 +307,7 @@ DEVI void finalize_dispatch(const DispatchArgs& d, int32_t* cnt, int32_t* scan_b
   if (tid < 64) {
     // one wave derives the configuration from the histogram
     int mx = 0;
-    int cfg = choose_config(cnt, G, d.I, d.num_cfgs, d.cus, d.T, tid, &mx);
+    int cfg = choose_config(d, cnt, G, tid, &mx);
     if (d.force_cfg >= 0) cfg = d.force_cfg;
     if (tid == 0) {
       s_max = mx;
@@ -489,9 +527,10 @@ __global__ void __launch_bounds__(256) k_dispatch_tiny(DispatchArgs d) {
   const uint64_t act = __ballot(lane < G && cnt > 0);
   if (lane < G && cnt > 0) d.active[__popcll(act & below)] = lane;
   // configuration from the histogram statistics (lane g holds group g)
-  const int mx = wave_total<true>(cnt), t32 = wave_total<false>((cnt + 31) / 32);
-  int cfg = config_rule(mx, __popcll(act), total, t32, d.I, d.num_cfgs, d.cus, d.T);
-  if (d.force_cfg >= 0) cfg = d.force_cfg;
+  HistStats hs{};
+  add_group(hs, cnt);
+  const int mx = wave_total<true>(cnt);
+  const int cfg = d.force_cfg >= 0 ? d.force_cfg : pick_config(d, wave_stats(hs));
   // block table for the chosen row-block height
   const int bm = cfg_rows(cfg);
   const int nt = lane < G ? (cnt + bm - 1) / bm : 0;
@@ -696,15 +735,15 @@ __global__ void __launch_bounds__(256) k_dispatch_decode(DispatchArgs d) {
   if (tid == 0 && d.shared) cnt_l[E] = T;
   __syncthreads();
   if (wave == 0) {
-    int c[5], f[5], cs = 0, fs = 0, mx = 0, t32 = 0;
+    int c[5], f[5], cs = 0, fs = 0;
+    HistStats hs{};
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
       c[i] = cnt_l[lane * 5 + i];   // zero past G
       f[i] = c[i] > 0;
       cs += c[i];
       fs += f[i];
-      mx = c[i] > mx ? c[i] : mx;
-      t32 += (c[i] + 31) / 32;
+      add_group(hs, c[i]);
     }
     int ce = wave_incl_scan<false>(cs) - cs, fe = wave_incl_scan<false>(fs) - fs;
 #pragma unroll
@@ -718,14 +757,13 @@ __global__ void __launch_bounds__(256) k_dispatch_decode(DispatchArgs d) {
       fe += f[i];
     }
     const int tot = wave_total<false>(cs), nact = wave_total<false>(fs);
-    mx = wave_total<true>(mx);
-    t32 = wave_total<false>(t32);
+    const int mx = wave_total<true>(hs.mx);
+    const int cfg = d.force_cfg >= 0 ? d.force_cfg : pick_config(d, wave_stats(hs));
     if (lane == 0) {
       ind_l[G] = tot;
       nact_l = nact;
       mx_l = mx;
-      cfg_l = d.force_cfg >= 0 ? d.force_cfg
-                               : config_rule(mx, nact, tot, t32, d.I, d.num_cfgs, d.cus, d.T);
+      cfg_l = cfg;
     }
   }
   __syncthreads();

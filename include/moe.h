@@ -267,6 +267,38 @@ MOE_API int moe_workspace_graph_count(const moe_ws* ws, int* host_n);
  * from the histogram (default); 0 = streaming decode kernels; 1.. = tiled
  * kernels with a row-block height given by moe_config_rows(cfg). */
 MOE_API int moe_workspace_force_config(moe_ws* ws, int cfg_id);
+
+/* Choose the configuration of moe_layer_forward with the fitted wave cost
+ * model (1, default) or with the fixed histogram rule (0).  RaMP abstract:
+ * a four-parameter wave cost model, fitted once from profiling, picks the
+ * fastest configuration from the runtime expert histogram and depends only
+ * on the kernels' grid geometry.  Configuration c's predicted time is
+ *   th[r][0] + th[r][1]*x1 + th[r][2]*x2 + th[r][3]*x3   (microseconds)
+ * with x1 the weight bytes it streams over the 8 TB/s HBM peak, x2 the MFMA
+ * work of its padded row blocks over the format's dense MFMA peak, and x3
+ * its grid waves (gate/up and down summed); r = c, except r = 4 for the
+ * streaming configuration above 16 tokens (another kernel variant).  The
+ * host launches the kernels of a candidate set chosen before the histogram
+ * exists (moe_workspace_candidates) and the dispatch kernel picks, on the
+ * real histogram, the least predicted time within it.  Results do not
+ * depend on the configuration beyond the format's tolerance (the K split
+ * and summation order differ between configurations).  Clears the
+ * workspace's decode graphs. */
+MOE_API int moe_workspace_set_config_model(moe_ws* ws, int enable);
+
+/* The configurations (bit c = configuration c) whose kernels
+ * moe_layer_forward launches for a batch of T tokens: the one forced, the
+ * cost model's candidate set (the set whose best member's mean predicted
+ * time over three bounding routings - T*k rows spread evenly over the
+ * experts, packed into k experts of T rows, and T/2 tokens packed with the
+ * rest spread; a shared expert adds T rows - plus 5 us for every launch
+ * beyond the first is least), or
+ * the families the histogram rule can land on.  Host only, no GPU work. */
+MOE_API int moe_workspace_candidates(const moe_ws* ws, int T, int* host_mask);
+
+/* The fitted parameters th[5][4] compiled into the library (row-major, 20
+ * doubles), as moe_workspace_set_config_model describes them. */
+MOE_API int moe_config_model_params(double* host_theta20);
 /* Configuration used by the last moe_layer_forward (synchronises `stream`). */
 MOE_API int moe_workspace_last_config(const moe_ws* ws, int* host_cfg_id, void* stream);
 /* Row-block height of a configuration, or -1 if unknown. */
