@@ -43,10 +43,13 @@ MFMA_FLOP_PER_US = {0: 2.5e9, 1: 5.0e9, 2: 5.0e9, 3: 5.0e9}   # bf16, fp8 (MXFP4
 WEIGHT_BYTES = {0: 2.0, 1: 1.0, 2: 1.0, 3: 0.5}
 CUS = 256
 DECODE_STREAM_TOKENS = 16
-# a launch per projection beyond the first, that the device may not choose:
-# the library's time with two launches per projection measured a median
-# 5.1 us above the forced configuration's single launch (0.9 us with one)
-LAUNCH_US = 5.0
+# a kernel family launched for both projections that the device may not
+# choose: a launch that returns at once still holds the stream ~4.7 us
+# (kernel trace of the default bench run: the 128-row family at T=128)
+LAUNCH_US = 9.0
+# weights of the two bounding routings (even, packed): routers trained with
+# load balancing keep histograms near even
+ROUTING_PRIOR = (0.8, 0.2)
 CFG_ROWS = {1: 32, 2: 64, 3: 128}
 
 
@@ -150,21 +153,15 @@ def choose(th: np.ndarray, rec: dict) -> int:
 
 
 def bounding_histograms(T: int, E: int, k: int, shared: int) -> list:
-    """Histograms the host evaluates the model on before it launches, knowing
-    only the batch: the T*k routed rows spread evenly over the E experts
-    (the first T*k mod E experts one row more), packed into k experts of T
-    rows (each token takes k distinct experts), and the mixture in which
-    T // 2 tokens take experts 0..k-1 and the other tokens spread evenly;
-    the shared experts add one group of T rows.  Each is a list of
-    (count, multiplicity) pairs, and each is a routing some scores produce
-    (no expert above T rows)."""
+    """The two routings the host weighs before it launches, knowing only the
+    batch: the T*k routed rows spread evenly over the E experts (the first
+    T*k mod E experts one row more), and packed into k experts of T rows
+    (every token taking the same k experts); the shared experts add one
+    group of T rows.  Each is a list of (count, multiplicity) pairs, and
+    each is a routing some scores produce (no expert above T rows)."""
     sh = [(T, 1)] if shared else []        # the shared experts form one group
     q, r = divmod(T * k, E)
-    t1 = T // 2
-    q2, r2 = divmod((T - t1) * k, E)
-    kr = min(k, r2)
-    mixed = [(t1 + q2 + 1, kr), (t1 + q2, k - kr), (q2 + 1, max(0, r2 - k)), (q2, E - max(k, r2))]
-    return [[(q + 1, r), (q, E - r)] + sh, [(T, k)] + sh, mixed + sh]
+    return [[(q + 1, r), (q, E - r)] + sh, [(T, k)] + sh]
 
 
 def families(f: int) -> list:
@@ -189,9 +186,10 @@ def candidate_mask(th: np.ndarray, T: int, E: int, k: int, shared: int, H: int, 
     """Configurations the host launches kernels for (bit c: configuration
     c), before the histogram exists: over the sets of kernel launches
     (families), the one whose best configuration's predicted time, averaged
-    over the bounding histograms, plus LAUNCH_US for each launch beyond the
-    first (a launch the device did not choose still starts and ends its
-    workgroups) is least; on a tie the first in enumeration order."""
+    over the bounding histograms with ROUTING_PRIOR's weights, plus
+    LAUNCH_US for each launch beyond the first (a launch the device did not
+    choose still starts and ends its workgroups) is least; on a tie the
+    first in enumeration order."""
     preds = []
     for hist in bounding_histograms(T, E, k, shared):
         st = hist_stats(hist)
@@ -201,7 +199,8 @@ def candidate_mask(th: np.ndarray, T: int, E: int, k: int, shared: int, H: int, 
     for sel in range(1, 1 << len(fams)):
         # every configuration a launched kernel serves is a candidate
         mask = sum(fam for i, fam in enumerate(fams) if (sel >> i) & 1) & ((1 << ncfg) - 1)
-        cost = sum(min(p[c] for c in range(ncfg) if (mask >> c) & 1) for p in preds) / len(preds)
+        cost = sum(w * min(p[c] for c in range(ncfg) if (mask >> c) & 1)
+                   for w, p in zip(ROUTING_PRIOR, preds))
         cost += LAUNCH_US * (launches(mask, f) - 1)
         if best == 0 or cost < best_cost:
             best, best_cost = mask, cost

@@ -201,19 +201,23 @@ int device_cus() {
 
 // ---------------------------------------------------------------------------
 // Host side of the fitted configuration cost model.  Before the histogram
-// exists the host only knows the batch, so it evaluates the model on three
+// exists the host only knows the batch, so it evaluates the model on the two
 // routings that bound what the histogram can be (T*k rows spread evenly
-// over the experts, packed into k experts of T rows, and T/2 tokens packed
-// with the rest spread; a shared expert adds a group of T rows).  Over the
-// sets of kernel launches it takes the one whose best configuration's mean
-// predicted time over those routings, plus kLaunchUs for every launch beyond
-// the first, is least (the first such set on a tie), and passes the
+// over the experts, and packed into k experts of T rows; a shared expert
+// adds a group of T rows).  Over the
+// sets of kernel launches it takes the one whose best configuration's
+// predicted time, averaged over those routings with kRoutingPrior's weights,
+// plus kLaunchUs for every launch beyond the first, is least (the first such
+// set on a tie), and passes the
 // configurations those launches serve to the dispatch kernel, which picks,
 // on the real histogram, the least predicted time among them.
 // grouped_gemm_amd/costmodel.py (candidate_mask) computes the same set.
-// a set of launches per projection beyond the first (both projections): the
-// layer measured a median 5.1 us slower with two than the forced single one
-constexpr double kLaunchUs = 5.0;
+// a kernel family launched for both projections that the device may not
+// choose: a launch that returns at once still holds the stream ~4.7 us
+constexpr double kLaunchUs = 9.0;
+// weights of the two bounding routings (even, packed): routers trained with
+// load balancing keep histograms near even
+constexpr double kRoutingPrior[2] = {0.8, 0.2};
 
 void add_groups(HistStats& h, long c, long m) {
   if (c <= 0 || m <= 0) return;
@@ -253,20 +257,15 @@ CostModel cost_model(const moe_ws* ws, int T) {
   const double* th = &kCostModelTheta[0][0];
   const moe_layer_desc& d = ws->d;
   const long E = d.num_experts, k = d.top_k, q = (long)T * k / E, r = (long)T * k % E;
-  const long t1 = T / 2, q2 = (T - t1) * k / E, r2 = (T - t1) * k % E, kr = k < r2 ? k : r2;
   const int nc = num_cfgs(ws->fmt), cus = device_cus();
-  HistStats h[3] = {};
+  HistStats h[2] = {};
   add_groups(h[0], q + 1, r);                    // even: the first r experts one row more
   add_groups(h[0], q, E - r);
   add_groups(h[1], T, k);                        // packed
-  add_groups(h[2], t1 + q2 + 1, kr);             // T/2 tokens on experts 0..k-1, the rest even
-  add_groups(h[2], t1 + q2, k - kr);
-  add_groups(h[2], q2 + 1, r2 - k > 0 ? r2 - k : 0);
-  add_groups(h[2], q2, E - (k > r2 ? k : r2));
   for (auto& x : h)
     if (d.shared_experts) add_groups(x, T, 1);
-  double t[3][kNumCfgs];
-  for (int i = 0; i < 3; ++i)
+  double t[2][kNumCfgs];
+  for (int i = 0; i < 2; ++i)
     for (int c = 0; c < nc; ++c) t[i][c] = cost_model_time(th, h[i], c, ws->fmt, d.hidden, d.inter, T, cus);
   int fam[3];
   const int nf = launch_families(ws->fmt, fam);
@@ -282,7 +281,7 @@ CostModel cost_model(const moe_ws* ws, int T) {
       }
     mask &= (1 << nc) - 1;
     double cost = 0.0;
-    for (int i = 0; i < 3; ++i) {
+    for (int i = 0; i < 2; ++i) {
       double mn = 0.0;
       bool any = false;
       for (int c = 0; c < nc; ++c)
@@ -290,9 +289,9 @@ CostModel cost_model(const moe_ws* ws, int T) {
           mn = t[i][c];
           any = true;
         }
-      cost += mn;
+      cost += kRoutingPrior[i] * mn;
     }
-    cost = cost / 3.0 + kLaunchUs * (nl - 1);
+    cost += kLaunchUs * (nl - 1);
     if (best == 0 || cost < best_cost) {
       best = mask;
       best_cost = cost;

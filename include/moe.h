@@ -288,11 +288,11 @@ MOE_API int moe_workspace_set_config_model(moe_ws* ws, int enable);
 
 /* The configurations (bit c = configuration c) whose kernels
  * moe_layer_forward launches for a batch of T tokens: the one forced, the
- * cost model's candidate set (the set whose best member's mean predicted
- * time over three bounding routings - T*k rows spread evenly over the
- * experts, packed into k experts of T rows, and T/2 tokens packed with the
- * rest spread; a shared expert adds T rows - plus 5 us for every launch
- * beyond the first is least), or
+ * cost model's candidate set (the set whose best member's predicted time,
+ * averaged with weights 0.8 / 0.2 over two routings - T*k rows spread
+ * evenly over the experts, and packed into k experts of T rows; a shared
+ * expert adds T rows - plus 9 us for every launch beyond the first is
+ * least), or
  * the families the histogram rule can land on.  Host only, no GPU work. */
 MOE_API int moe_workspace_candidates(const moe_ws* ws, int T, int* host_mask);
 

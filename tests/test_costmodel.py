@@ -99,7 +99,7 @@ def test_features_worked_example():
                                           (100, 128, 8, 0), (3, 4, 4, 1), (513, 257, 8, 1)])
 def test_bounding_histograms_are_routings(T, E, k, shared):
     hists = cm.bounding_histograms(T, E, k, shared)
-    assert len(hists) == 3
+    assert len(hists) == 2
     for h in hists:
         groups = [c for c, m in h for _ in range(m) if c > 0]
         st = cm.hist_stats(h)
