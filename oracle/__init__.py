@@ -1,4 +1,5 @@
-"""CPU oracle of the fused MoE layer forward (fp64, plain C + numpy glue).
+"""CPU oracle of the fused MoE layer forward and of the routed expert layer's
+backward (fp64, plain C + numpy glue).
 
 TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the
 benchmark's CPU-baseline leg are the only callers. The HIP library never
@@ -72,6 +73,13 @@ def lib():
                                           P, P, P]
         L.oracle_activation.restype = C.c_double
         L.oracle_activation.argtypes = [i, C.c_double, C.c_double, C.c_double]
+        L.oracle_activation_grad.restype = None
+        L.oracle_activation_grad.argtypes = [i, C.c_double, C.c_double, C.c_double, P, P]
+        L.oracle_expert_backward.restype = None
+        L.oracle_expert_backward.argtypes = [i, i, i, i, i, C.c_double, P, P, P, P, P, P, i, P,
+                                             i, P, P, P, P, P]
+        L.oracle_router_backward.restype = None
+        L.oracle_router_backward.argtypes = [P, P, P, P, i, i, i, i, P]
         _lib = L
     return _lib
 
@@ -219,4 +227,49 @@ def grouped_gemm(w_format, a_format, op, a, a_scale, a_gather, gather_div, m_ind
                               None if b0s is None else _p(np.ascontiguousarray(b0s)),
                               None if b1 is None else _p(np.ascontiguousarray(b1)),
                               None if b1s is None else _p(np.ascontiguousarray(b1s)), _p(out))
+    return out
+
+
+# ------------------------------------------------------------------ backward
+def activation_grad(act: int, limit: float, g: float, u: float):
+    """(d act / d g, d act / d u) at one (g, u) (fp64)."""
+    dg, du = C.c_double(), C.c_double()
+    lib().oracle_activation_grad(int(act), float(act_limit(act, limit)), float(g), float(u),
+                                 C.byref(dg), C.byref(du))
+    return dg.value, du.value
+
+
+def expert_backward(H, I, E, k, act, limit, w_gate, w_up, w_down, x_bits, ids, w, dy_bits,
+                    round_bf16=True):
+    """Gradients of the routed expert layer (bf16 weights): returns
+    (dx [T,H], dW_gate [E,I,H], dW_up [E,I,H], dW_down [E,H,I], dw [T,k]),
+    fp64.  w_gate may be None for ReLU^2 (dW_gate is then zero)."""
+    x_bits = _c(x_bits, np.uint16)
+    dy_bits = _c(dy_bits, np.uint16)
+    ids = _c(ids, np.int32)
+    w = _c(w, np.float64)
+    T = x_bits.shape[0]
+    dx = np.zeros((T, H))
+    dwg = np.zeros((E, I, H))
+    dwu = np.zeros((E, I, H))
+    dwd = np.zeros((E, H, I))
+    dw = np.zeros((T, k))
+    lib().oracle_expert_backward(
+        H, I, E, k, int(act), float(act_limit(act, limit)),
+        None if w_gate is None else _p(_c(w_gate, np.uint16)), _p(_c(w_up, np.uint16)),
+        _p(_c(w_down, np.uint16)), _p(x_bits), _p(ids), _p(w), T, _p(dy_bits),
+        int(bool(round_bf16)), _p(dx), _p(dwg), _p(dwu), _p(dwd), _p(dw))
+    return dx, dwg, dwu, dwd, dw
+
+
+def router_backward(scores, ids, w, dw, score_fn: int) -> np.ndarray:
+    """Gradient [T,E] with respect to the router scores, given the gradient
+    dw [T,k] with respect to the renormalised top-k weights w."""
+    s = _c(scores, np.float32)
+    T, E = s.shape
+    ids = _c(ids, np.int32)
+    k = ids.shape[1]
+    out = np.zeros((T, E))
+    lib().oracle_router_backward(_p(s), _p(ids), _p(_c(w, np.float64)), _p(_c(dw, np.float64)),
+                                 T, E, k, int(score_fn), _p(out))
     return out

@@ -1,5 +1,6 @@
 /*
- * moe_oracle.c -- plain, slow, fp64 reference of the fused MoE layer forward.
+ * moe_oracle.c -- plain, slow, fp64 reference of the fused MoE layer forward
+ * and of the routed expert layer's backward.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg may load this library.  The product path (the
@@ -30,7 +31,11 @@
  *    times up (pure-Triton MoE commentary, second paragraph), then the down
  *    projection;
  *  - routing-weight application and combine in a fixed order (LightMoE
- *    README, "MoE inference").
+ *    README, "MoE inference");
+ *  - the gradients of the routed expert layer with respect to its input,
+ *    its expert weights and its routing weights, and of the routing weights
+ *    with respect to the router scores (LightMoE README, "MoE training" and
+ *    "Highlights"), as the derivatives of the forward written out.
  *
  * Everything is accumulated in double over exactly dequantised operands.
  * Where the activations are quantised on the fly, the oracle applies the
@@ -539,5 +544,215 @@ void oracle_grouped_gemm(int w_format, int a_format, int op, int act, double lim
   free(arow);
   free(g);
   free(u);
+  }
+}
+
+/* ---------------------------------------------------------------- backward
+ * Gradients of the routed expert layer (LightMoE README, "MoE training" and
+ * "Highlights": deterministic dispatch, combine, input-gradient,
+ * weight-gradient and router-gradient kernels).  The pages name the
+ * gradients but give no formulas; these are the derivatives of the forward
+ * above, written out.
+ *
+ * Partial derivatives of oracle_activation with respect to g and u.  At a
+ * clamp boundary the derivative of the branch the forward takes: min(g, L)
+ * passes g only for g < L, clamp(u, -L, L) passes u for -L <= u <= L.
+ *   SwiGLU          dg = SiLU'(g) u,     du = SiLU(g)
+ *                   SiLU'(z) = s(z) (1 + z (1 - s(z))), s the logistic
+ *   GeGLU           dg = GELU'(g) u,     du = GELU(g)
+ *                   GELU'(z) = Phi(z) + z phi(z) (standard normal cdf, pdf)
+ *   ReLU^2          dg = 0,              du = 2 max(u, 0)
+ * ReGLU has no backward here (the pages' training set excludes it).
+ */
+static double sigm(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+void oracle_activation_grad(int act, double limit, double g, double u, double* dg, double* du) {
+  switch (act) {
+    case ACT_SWIGLU_BOUNDED: {
+      const int gin = g < limit, uin = u >= -limit && u <= limit;
+      const double gc = gin ? g : limit, uc = clampd(u, -limit, limit);
+      const double s = sigm(gc);
+      *dg = gin ? s * (1.0 + gc * (1.0 - s)) * uc : 0.0;
+      *du = uin ? gc * s : 0.0;
+      return;
+    }
+    case ACT_SWIGLU_OAI: {
+      const int gin = g < limit, uin = u >= -limit && u <= limit;
+      const double gc = gin ? g : limit, uc = clampd(u, -limit, limit);
+      const double s = sigm(1.702 * gc);
+      *dg = gin ? (s + 1.702 * gc * s * (1.0 - s)) * (uc + 1.0) : 0.0;
+      *du = uin ? gc * s : 0.0;
+      return;
+    }
+    case ACT_GEGLU: {
+      const double Phi = 0.5 * (1.0 + erf(g / sqrt(2.0)));
+      const double phi = exp(-0.5 * g * g) / sqrt(2.0 * acos(-1.0));
+      *dg = (Phi + g * phi) * u;
+      *du = g * Phi;
+      return;
+    }
+    case ACT_RELU2:
+      *dg = 0.0;
+      *du = u > 0.0 ? 2.0 * u : 0.0;
+      return;
+    default: {
+      const double s = sigm(g);
+      *dg = s * (1.0 + g * (1.0 - s)) * u;
+      *du = g * s;
+      return;
+    }
+  }
+}
+
+static double bf16_read(const uint16_t* p, size_t i) { return oracle_bf16_decode(p[i]); }
+
+/*
+ * Expert-layer backward for bf16 weights (gate, up [E, I, H]; down
+ * [E, H, I]), activations x and upstream gradient dy bf16 [T, H], routing
+ * ids and weights w [T, k].  Forward per slot (t, j), e = ids[t, j]:
+ *   g = Wg[e] x_t, u = Wu[e] x_t, h = act(g, u), o = Wd[e] h,
+ *   y_t = sum_j w[t, j] o.
+ * Backward:
+ *   r  = Wd[e]^T dy_t                  (gradient at h before the weight)
+ *   dw[t, j] = <r, h>                  (= <dy_t, o>: the router's input)
+ *   dWd[e] += (w dy_t) h^T
+ *   dg = w r * dact/dg, du = w r * dact/du
+ *   dWg[e] += dg x_t^T,  dWu[e] += du x_t^T
+ *   dx_t = sum_j (Wg[e]^T dg + Wu[e]^T du), j ascending
+ * With round_bf16 set, h, w dy_t, dg and du are rounded to bf16 before they
+ * multiply anything else (they are the operands of the layer's bf16
+ * products); otherwise every quantity stays fp64.  ReLU^2 ignores Wg (may
+ * be NULL; dWg is then left untouched).  Outputs fp64: dx [T, H],
+ * dwg/dwu [E, I, H], dwd [E, H, I], dw [T, k]; the dW arrays are zeroed
+ * here.  Experts are independent: each thread owns whole experts and adds
+ * their slots in ascending (t, j) order.
+ */
+void oracle_expert_backward(int H, int I, int E, int k, int act, double limit,
+                            const uint16_t* wg, const uint16_t* wu, const uint16_t* wd,
+                            const uint16_t* x_bits, const int32_t* ids, const double* w, int T,
+                            const uint16_t* dy_bits, int round_bf16, double* dx, double* dwg,
+                            double* dwu, double* dwd, double* dw) {
+  const size_t S = (size_t)T * k;
+  const int relu2 = act == ACT_RELU2;
+  double* da = (double*)calloc(S * (size_t)H, sizeof(double));   /* per-slot input gradient */
+  if (!relu2) memset(dwg, 0, sizeof(double) * (size_t)E * I * H);
+  memset(dwu, 0, sizeof(double) * (size_t)E * I * H);
+  memset(dwd, 0, sizeof(double) * (size_t)E * H * I);
+#pragma omp parallel
+  {
+  double* xt = (double*)malloc(sizeof(double) * (size_t)H);
+  double* dyt = (double*)malloc(sizeof(double) * (size_t)H);
+  double* dot = (double*)malloc(sizeof(double) * (size_t)H);
+  double* g = (double*)malloc(sizeof(double) * (size_t)I);
+  double* u = (double*)malloc(sizeof(double) * (size_t)I);
+  double* h = (double*)malloc(sizeof(double) * (size_t)I);
+  double* r = (double*)malloc(sizeof(double) * (size_t)I);
+  double* dg = (double*)malloc(sizeof(double) * (size_t)I);
+  double* du = (double*)malloc(sizeof(double) * (size_t)I);
+#pragma omp for schedule(dynamic, 1)
+  for (int e = 0; e < E; ++e) {
+    const uint16_t* Wg = relu2 ? NULL : wg + (size_t)e * I * H;
+    const uint16_t* Wu = wu + (size_t)e * I * H;
+    const uint16_t* Wd = wd + (size_t)e * H * I;
+    double* dWg = relu2 ? NULL : dwg + (size_t)e * I * H;
+    double* dWu = dwu + (size_t)e * I * H;
+    double* dWd = dwd + (size_t)e * H * I;
+    for (int t = 0; t < T; ++t)
+      for (int j = 0; j < k; ++j) {
+        if (ids[(size_t)t * k + j] != e) continue;
+        const size_t slot = (size_t)t * k + j;
+        const double wj = w[slot];
+        for (int c = 0; c < H; ++c) {
+          xt[c] = bf16_read(x_bits, (size_t)t * H + c);
+          dyt[c] = bf16_read(dy_bits, (size_t)t * H + c);
+          dot[c] = round_bf16 ? oracle_bf16_round(wj * dyt[c]) : wj * dyt[c];
+        }
+        /* forward of this slot */
+        for (int n = 0; n < I; ++n) {
+          double ag = 0.0, au = 0.0;
+          for (int c = 0; c < H; ++c) {
+            if (!relu2) ag += bf16_read(Wg, (size_t)n * H + c) * xt[c];
+            au += bf16_read(Wu, (size_t)n * H + c) * xt[c];
+          }
+          g[n] = ag;
+          u[n] = au;
+          const double hv = oracle_activation(act, limit, ag, au);
+          h[n] = round_bf16 ? oracle_bf16_round(hv) : hv;
+          r[n] = 0.0;
+        }
+        /* r = Wd^T dy_t, and dWd += (w dy_t) h^T */
+        for (int c = 0; c < H; ++c) {
+          const uint16_t* wrow = Wd + (size_t)c * I;
+          double* drow = dWd + (size_t)c * I;
+          for (int n = 0; n < I; ++n) {
+            r[n] += bf16_read(wrow, n) * dyt[c];
+            drow[n] += dot[c] * h[n];
+          }
+        }
+        double acc = 0.0;
+        for (int n = 0; n < I; ++n) acc += r[n] * h[n];
+        dw[slot] = acc;
+        for (int n = 0; n < I; ++n) {
+          double pg, pu;
+          oracle_activation_grad(act, limit, g[n], u[n], &pg, &pu);
+          const double dh = wj * r[n];
+          dg[n] = round_bf16 ? oracle_bf16_round(dh * pg) : dh * pg;
+          du[n] = round_bf16 ? oracle_bf16_round(dh * pu) : dh * pu;
+        }
+        double* dat = da + slot * (size_t)H;
+        for (int n = 0; n < I; ++n) {
+          for (int c = 0; c < H; ++c) {
+            if (!relu2) {
+              dWg[(size_t)n * H + c] += dg[n] * xt[c];
+              dat[c] += dg[n] * bf16_read(Wg, (size_t)n * H + c);
+            }
+            dWu[(size_t)n * H + c] += du[n] * xt[c];
+            dat[c] += du[n] * bf16_read(Wu, (size_t)n * H + c);
+          }
+        }
+      }
+  }
+  free(xt); free(dyt); free(dot); free(g); free(u); free(h); free(r); free(dg); free(du);
+  }
+  /* dispatch backward: each token's input gradient, j ascending */
+  for (int t = 0; t < T; ++t)
+    for (int c = 0; c < H; ++c) {
+      double acc = 0.0;
+      for (int j = 0; j < k; ++j) acc += da[((size_t)t * k + j) * H + c];
+      dx[(size_t)t * H + c] = acc;
+    }
+  free(da);
+}
+
+/*
+ * Router backward: gradient of a loss with respect to the router scores
+ * [T, E], given its gradient dw [T, k] with respect to the renormalised
+ * top-k weights (the selection itself is piecewise constant).  With
+ * m = sum_j w_j dw_j over the token's k slots, for a selected expert i:
+ *   softmax  w_i = exp(l_i) / sum_sel exp(l):  dl_i = w_i (dw_i - m)
+ *   sigmoid  w_i = s_i / S, S = sum_sel s:     dl_i = s_i (1 - s_i) (dw_i - m) / S
+ *   probs    w_i = p_i / P, P = sum_sel p:     dp_i = (dw_i - m) / P
+ * Unselected scores get 0.  w is the oracle's fp64 routing weights.
+ */
+void oracle_router_backward(const float* scores, const int32_t* ids, const double* w,
+                            const double* dw, int T, int E, int k, int score_fn, double* dscores) {
+  memset(dscores, 0, sizeof(double) * (size_t)T * E);
+  for (int t = 0; t < T; ++t) {
+    double m = 0.0, den = 0.0;
+    for (int j = 0; j < k; ++j) m += w[(size_t)t * k + j] * dw[(size_t)t * k + j];
+    for (int j = 0; j < k; ++j) {
+      const double l = scores[(size_t)t * E + ids[(size_t)t * k + j]];
+      den += score_fn == SCORE_SIGMOID ? sigm(l) : l;
+    }
+    for (int j = 0; j < k; ++j) {
+      const int e = ids[(size_t)t * k + j];
+      const double l = scores[(size_t)t * E + e];
+      const double d = dw[(size_t)t * k + j] - m;
+      double v;
+      if (score_fn == SCORE_SOFTMAX) v = w[(size_t)t * k + j] * d;
+      else if (score_fn == SCORE_SIGMOID) v = sigm(l) * (1.0 - sigm(l)) * d / den;
+      else v = d / den;
+      dscores[(size_t)t * E + e] = v;
+    }
   }
 }
