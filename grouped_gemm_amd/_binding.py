@@ -23,7 +23,8 @@ SYMBOLS = (
     "moe_workspace_set_graphs", "moe_workspace_set_stage_events", "moe_workspace_tiles",
     "moe_workspace_check", "moe_workspace_graph_count", "moe_dispatch_noalloc",
     "moe_workspace_set_fused_decode", "moe_workspace_set_config_model", "moe_workspace_candidates",
-    "moe_config_model_params",
+    "moe_config_model_params", "moe_backward_scratch_size", "moe_expert_backward",
+    "moe_router_backward",
 )
 
 
@@ -86,6 +87,10 @@ def _load():
     L.moe_workspace_set_config_model.argtypes = [P, i]
     L.moe_workspace_candidates.argtypes = [P, i, C.POINTER(i)]
     L.moe_config_model_params.argtypes = [C.POINTER(C.c_double)]
+    L.moe_backward_scratch_size.argtypes = [C.POINTER(LayerDesc), C.POINTER(C.c_size_t)]
+    L.moe_expert_backward.argtypes = [P, C.POINTER(_Weights), P, P, P, i, P, P, P, P, P, P, P,
+                                      C.c_size_t, P]
+    L.moe_router_backward.argtypes = [P, P, P, P, i, i, i, i, P, P]
     for n in SYMBOLS:
         if n not in ("moe_status_string", "moe_last_error"):
             getattr(L, n).restype = i
@@ -261,3 +266,31 @@ def layer_forward(ws: Workspace, weights: dict, x_bf16, scores, y_bf16, stream=N
                    for n, _ in _Weights._fields_])
     _check(_load().moe_layer_forward(ws.handle, C.byref(w), _ptr(x_bf16), _ptr(scores),
                                      x_bf16.shape[0], _ptr(y_bf16), _stream(stream)))
+
+
+def backward_scratch_size(ws: Workspace) -> int:
+    """Bytes of scratch expert_backward needs for this workspace."""
+    n = C.c_size_t(0)
+    _check(_load().moe_backward_scratch_size(C.byref(ws.desc), C.byref(n)))
+    return n.value
+
+
+def expert_backward(ws: Workspace, weights: dict, x_bf16, topk_ids, topk_w, dy_bf16, dx_bf16,
+                    d_w_gate, d_w_up, d_w_down, d_topk_w, scratch, stream=None):
+    """Gradients of the routed expert layer (bf16): dx, d_w_* (fp32) and
+    d_topk_w written in place; weights as for layer_forward (w_gate may be
+    absent for ReLU^2, and d_w_gate then None)."""
+    w = _Weights(*[weights[n].data_ptr() if weights.get(n) is not None else None
+                   for n, _ in _Weights._fields_])
+    _check(_load().moe_expert_backward(
+        ws.handle, C.byref(w), _ptr(x_bf16), _ptr(topk_ids), _ptr(topk_w), x_bf16.shape[0],
+        _ptr(dy_bf16), _ptr(dx_bf16), _ptr(d_w_gate), _ptr(d_w_up), _ptr(d_w_down),
+        _ptr(d_topk_w), _ptr(scratch), scratch.numel() * scratch.element_size(), _stream(stream)))
+
+
+def router_backward(scores, topk_ids, topk_w, d_topk_w, score_fn, d_scores, stream=None):
+    """d_scores [T, E] from d_topk_w [T, k] for renormalised top-k weights."""
+    T, E = scores.shape
+    _check(_load().moe_router_backward(_ptr(scores), _ptr(topk_ids), _ptr(topk_w), _ptr(d_topk_w),
+                                       T, E, topk_ids.shape[1], score_fn, _ptr(d_scores),
+                                       _stream(stream)))

@@ -255,3 +255,71 @@ hipError_t launch_gemm_tiled(int fmt, bool gateup, int cfg, const GemmArgs& g, h
 hipError_t launch_gemm_pipe(int fmt, bool gateup, int family, const GemmArgs& g, hipStream_t st);
 // Rows from which the 128-row configuration may be chosen.
 #define CFG3_MIN_ROWS 4096
+
+// ---------------------------------------------------------------- backward
+// Input-gradient GEMM over the block table's 64-row blocks:
+//   out[slot, n] = sum_src sum_k A_src[row(slot), k] * B_src[e][k, n],
+// row(slot) = a_gather ? a_gather[slot] / gather_div : slot; B_src[e] is
+// [K, N] row-major; out fp32 [rows, N].
+struct BwdNN {
+  const uint16_t* a0;
+  const uint16_t* a1;
+  const int32_t* a_gather;
+  int gather_div;
+  const uint16_t* b0;
+  const uint16_t* b1;
+  int K, N;
+  const int32_t* tiles;
+  const int32_t* meta;
+  const int32_t* counts;
+  const int32_t* indptr;
+  float* out;
+};
+// Weight-gradient GEMM: out[e][m, n] = sum over group e's rows s of
+// a[s, m] * b[brow(s), n], brow = b_gather ? b_gather[s] / gather_div : s;
+// out fp32 [E, M, N] (zeros for experts without rows).
+struct BwdTN {
+  const uint16_t* a;
+  const uint16_t* b;
+  const int32_t* b_gather;
+  int gather_div;
+  const int32_t* indptr;
+  int M, N;
+  float* out;
+};
+// Per-slot pass of the backward (see backward.hip).
+struct BwdSlot {
+  const float* G;          // [rows, I] gate pre-activations (NULL for ReLU^2)
+  const float* U;          // [rows, I]
+  const float* R;          // [rows, I] Wd^T dy
+  const uint16_t* dy;      // [T, H] bf16
+  const float* topk_w;     // [T, k]
+  const int32_t* gather;   // slot -> t * k + j
+  const int32_t* indptr;   // [E + 1]
+  int E, k, I, H, act;
+  float limit;
+  uint16_t* Hb;            // [rows, I] bf16 h
+  uint16_t* DG;            // [rows, I] bf16
+  uint16_t* DU;            // [rows, I] bf16
+  uint16_t* DO;            // [rows, H] bf16 w dy_t
+  float* dw;               // [T, k]
+};
+struct BwdDx {
+  const float* DA;         // [rows, H]
+  const int32_t* inv;      // [T * k]
+  int T, k, H;
+  uint16_t* dx;            // [T, H] bf16
+};
+struct RouterBwd {
+  const float* scores;     // [T, E]
+  const int32_t* ids;      // [T, k]
+  const float* w;          // [T, k]
+  const float* dw;         // [T, k]
+  int T, E, k, score_fn;
+  float* ds;               // [T, E]
+};
+hipError_t launch_bwd_nn(const BwdNN& a, int nsrc, int max_tiles, hipStream_t st);
+hipError_t launch_bwd_tn(const BwdTN& a, int E, hipStream_t st);
+hipError_t launch_bwd_slot(const BwdSlot& a, int max_rows, hipStream_t st);
+hipError_t launch_bwd_dx(const BwdDx& a, hipStream_t st);
+hipError_t launch_router_bwd(const RouterBwd& a, hipStream_t st);

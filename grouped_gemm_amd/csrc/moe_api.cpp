@@ -706,6 +706,210 @@ int moe_dispatch_noalloc(const int32_t* topk_ids, int T, int k, int E, int32_t* 
   return MOE_OK;
 }
 
+// ---------------------------------------------------------------- backward
+namespace {
+
+struct BwdScratch {
+  size_t G, U, R, Hb, DG, DU, DO, DA, total;
+};
+
+BwdScratch bwd_scratch(const moe_layer_desc& d) {
+  const size_t S = (size_t)d.max_tokens * d.top_k, I = d.inter, H = d.hidden;
+  BwdScratch b{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  b.G = take(S * I * 4);
+  b.U = take(S * I * 4);
+  b.R = take(S * I * 4);
+  b.Hb = take(S * I * 2);
+  b.DG = take(S * I * 2);
+  b.DU = take(S * I * 2);
+  b.DO = take(S * H * 2);
+  b.DA = take(S * H * 4);
+  b.total = off;
+  return b;
+}
+
+int bwd_check_desc(const moe_layer_desc& d) {
+  if (d.w_format != MOE_W_BF16 || d.a_format != MOE_A_BF16)
+    return fail(MOE_EUNSUPPORTED, "the backward takes bf16 weights and activations");
+  if (d.shared_experts) return fail(MOE_EUNSUPPORTED, "the backward has no shared expert");
+  if (d.activation == MOE_ACT_REGLU) return fail(MOE_EUNSUPPORTED, "no backward for ReGLU");
+  if (d.hidden % 128 || d.inter % 128)
+    return fail(MOE_EUNSUPPORTED, "the backward needs hidden and inter multiples of 128");
+  return MOE_OK;
+}
+
+}  // namespace
+
+int moe_backward_scratch_size(const moe_layer_desc* desc, size_t* bytes) {
+  if (!desc || !bytes) return fail(MOE_EINVAL, "null pointer");
+  int rc = bwd_check_desc(*desc);
+  if (rc) return rc;
+  *bytes = bwd_scratch(*desc).total;
+  return MOE_OK;
+}
+
+int moe_expert_backward(moe_ws* ws, const moe_weights* w, const void* x, const int32_t* topk_ids,
+                        const float* topk_w, int T, const void* dy, void* dx, float* d_w_gate,
+                        float* d_w_up, float* d_w_down, float* d_topk_w, void* scratch,
+                        size_t scratch_bytes, void* stream) {
+  if (!ws) return fail(MOE_EINVAL, "workspace is NULL");
+  const moe_layer_desc& d = ws->d;
+  int rc = bwd_check_desc(d);
+  if (rc) return rc;
+  if (T < 0) return fail(MOE_EINVAL, "T must be >= 0");
+  if (T > d.max_tokens) return fail(MOE_ECAPACITY, "T=%d exceeds max_tokens=%d", T, d.max_tokens);
+  if (T == 0) return MOE_OK;
+  const bool relu2 = d.activation == MOE_ACT_RELU2;
+  if (!w || !w->w_up || !w->w_down || (!relu2 && !w->w_gate))
+    return fail(MOE_EINVAL, "null weight pointer");
+  if (!x || !topk_ids || !topk_w || !dy || !dx || !d_w_up || !d_w_down || !d_topk_w ||
+      (!relu2 && !d_w_gate) || !scratch)
+    return fail(MOE_EINVAL, "null pointer");
+  const BwdScratch b = bwd_scratch(d);
+  if (scratch_bytes < b.total)
+    return fail(MOE_ECAPACITY, "scratch holds %zu bytes, the backward needs %zu", scratch_bytes,
+                b.total);
+  hipStream_t st = (hipStream_t)stream;
+  char* sc = (char*)scratch;
+  const int E = d.num_experts, k = d.top_k, H = d.hidden, I = d.inter, S = T * k;
+  // dispatch of the given routing, block table for 64-row blocks
+  DispatchArgs a = dispatch_args(ws, T);
+  a.scores = nullptr;
+  a.ids_in = topk_ids;
+  a.shared = 0;
+  a.force_cfg = 2;
+  a.cm.on = 0;
+  a.fq = QuantArgs{};
+  HIP_TRY(launch_dispatch(a, st), "dispatch launch");
+  const int32_t* gather = ws->at<int32_t>(ws->L.gather);
+  const int32_t* inv = ws->at<int32_t>(ws->L.inv);
+  const int32_t* counts = ws->at<int32_t>(ws->L.counts);
+  const int32_t* indptr = ws->at<int32_t>(ws->L.indptr);
+  const int32_t* tiles = ws->at<int32_t>(ws->L.tiles);
+  const int32_t* meta = ws->at<int32_t>(ws->L.meta);
+  float* G = (float*)(sc + b.G);
+  float* U = (float*)(sc + b.U);
+  float* R = (float*)(sc + b.R);
+  uint16_t* Hb = (uint16_t*)(sc + b.Hb);
+  uint16_t* DG = (uint16_t*)(sc + b.DG);
+  uint16_t* DU = (uint16_t*)(sc + b.DU);
+  uint16_t* DO = (uint16_t*)(sc + b.DO);
+  float* DA = (float*)(sc + b.DA);
+  // g and u recomputed by the forward's tiled bf16 grouped GEMM (64-row blocks)
+  GemmArgs g = gemm_args(ws);
+  g.E = E;
+  g.N = I;
+  g.K = H;
+  g.a = (const uint8_t*)x;
+  g.gather = gather;
+  g.gather_div = k;
+  g.max_groups = E < S ? E : S;
+  g.max_rows = S;
+  g.max_group_rows = T;
+  g.cfg_self = 2;
+  if (!relu2) {
+    g.w0 = (const uint8_t*)w->w_gate;
+    g.out = G;
+    HIP_TRY(launch_gemm_tiled(F_BF16, false, 2, g, st), "gate recompute launch");
+  }
+  g.w0 = (const uint8_t*)w->w_up;
+  g.out = U;
+  HIP_TRY(launch_gemm_tiled(F_BF16, false, 2, g, st), "up recompute launch");
+  const int max_tiles = S / 64 + E + 1;
+  // r = W_down^T dy (rows of dy gathered by token)
+  BwdNN nn{};
+  nn.a0 = (const uint16_t*)dy;
+  nn.a_gather = gather;
+  nn.gather_div = k;
+  nn.b0 = (const uint16_t*)w->w_down;
+  nn.K = H;
+  nn.N = I;
+  nn.tiles = tiles;
+  nn.meta = meta;
+  nn.counts = counts;
+  nn.indptr = indptr;
+  nn.out = R;
+  HIP_TRY(launch_bwd_nn(nn, 1, max_tiles, st), "down input-gradient launch");
+  BwdSlot sl{};
+  sl.G = relu2 ? nullptr : G;
+  sl.U = U;
+  sl.R = R;
+  sl.dy = (const uint16_t*)dy;
+  sl.topk_w = topk_w;
+  sl.gather = gather;
+  sl.indptr = indptr;
+  sl.E = E;
+  sl.k = k;
+  sl.I = I;
+  sl.H = H;
+  sl.act = d.activation;
+  sl.limit = act_limit(d);
+  sl.Hb = Hb;
+  sl.DG = DG;
+  sl.DU = DU;
+  sl.DO = DO;
+  sl.dw = d_topk_w;
+  HIP_TRY(launch_bwd_slot(sl, S, st), "activation backward launch");
+  // da = W_gate^T dg + W_up^T du
+  BwdNN nn2 = nn;
+  nn2.a_gather = nullptr;
+  nn2.gather_div = 1;
+  nn2.a0 = relu2 ? DU : DG;
+  nn2.b0 = (const uint16_t*)(relu2 ? w->w_up : w->w_gate);
+  nn2.a1 = DU;
+  nn2.b1 = (const uint16_t*)w->w_up;
+  nn2.K = I;
+  nn2.N = H;
+  nn2.out = DA;
+  HIP_TRY(launch_bwd_nn(nn2, relu2 ? 1 : 2, max_tiles, st), "gate/up input-gradient launch");
+  BwdDx bx{DA, inv, T, k, H, (uint16_t*)dx};
+  HIP_TRY(launch_bwd_dx(bx, st), "input-gradient combine launch");
+  // weight gradients over each expert's rows
+  BwdTN tn{};
+  tn.indptr = indptr;
+  tn.a = DO;
+  tn.b = Hb;
+  tn.M = H;
+  tn.N = I;
+  tn.out = d_w_down;
+  HIP_TRY(launch_bwd_tn(tn, E, st), "down weight-gradient launch");
+  tn.b = (const uint16_t*)x;
+  tn.b_gather = gather;
+  tn.gather_div = k;
+  tn.M = I;
+  tn.N = H;
+  if (!relu2) {
+    tn.a = DG;
+    tn.out = d_w_gate;
+    HIP_TRY(launch_bwd_tn(tn, E, st), "gate weight-gradient launch");
+  }
+  tn.a = DU;
+  tn.out = d_w_up;
+  HIP_TRY(launch_bwd_tn(tn, E, st), "up weight-gradient launch");
+  return MOE_OK;
+}
+
+int moe_router_backward(const float* scores, const int32_t* topk_ids, const float* topk_w,
+                        const float* d_topk_w, int T, int E, int k, int score_fn, float* d_scores,
+                        void* stream) {
+  if (T < 0) return fail(MOE_EINVAL, "T must be >= 0");
+  if (E < 1) return fail(MOE_EINVAL, "E must be >= 1");
+  const int kmax = E < 16 ? E : 16;
+  if (k < 1 || k > kmax) return fail(MOE_EINVAL, "k must be in [1, %d]", kmax);
+  if (score_fn < 0 || score_fn > 2) return fail(MOE_EINVAL, "unknown score_fn");
+  if (T == 0) return MOE_OK;
+  if (!scores || !topk_ids || !topk_w || !d_topk_w || !d_scores) return fail(MOE_EINVAL, "null pointer");
+  RouterBwd r{scores, topk_ids, topk_w, d_topk_w, T, E, k, score_fn, d_scores};
+  HIP_TRY(launch_router_bwd(r, (hipStream_t)stream), "router backward launch");
+  return MOE_OK;
+}
+
 const char* moe_status_string(int s) {
   switch (s) {
     case MOE_OK: return "ok";

@@ -343,6 +343,61 @@ MOE_API int moe_workspace_set_fused_decode(moe_ws* ws, int enable);
  * events, moe_layer_forward runs its eager path (no graph replay). */
 MOE_API int moe_workspace_set_stage_events(moe_ws* ws, int stage, void* ev_begin, void* ev_end);
 
+/* ------------------------------------------------------------------ backward
+ * Training-side gradients of the routed expert layer (LightMoE README, "MoE
+ * training" and "Highlights": deterministic dispatch, combine, input-,
+ * weight- and router-gradient kernels).  bf16 weights and activations only
+ * (w_format MOE_W_BF16, a_format MOE_A_BF16), no shared expert, and every
+ * activation but ReGLU (the pages' training set excludes it).
+ *
+ * Bytes of the caller-owned scratch buffer moe_expert_backward needs for a
+ * workspace of this description (max_tokens * top_k slots). */
+MOE_API int moe_backward_scratch_size(const moe_layer_desc* desc, size_t* bytes);
+
+/* Gradients of a loss L with respect to the layer input, the expert weights
+ * and the routing weights, given dy = dL/dy for
+ *   y_t = sum_j topk_w[t, j] * W_down[e] act(W_gate[e] x_t, W_up[e] x_t),
+ *   e = topk_ids[t, j].
+ * Per slot, r = W_down[e]^T dy_t (fp32 accumulation of bf16 operands):
+ *   d_topk_w[t, j] = <r, h>,  h = bf16(act(g, u)) recomputed from x
+ *   dg = bf16(w r dact/dg), du = bf16(w r dact/du)
+ *   dx_t = bf16(sum_j (W_gate[e]^T dg + W_up[e]^T du)), j ascending
+ *   d_w_down[e]  = sum over e's slots of bf16(w dy_t) h^T     [E, H, I]
+ *   d_w_gate[e]  = sum over e's slots of dg x_t^T             [E, I, H]
+ *   d_w_up[e]    = sum over e's slots of du x_t^T             [E, I, H]
+ * (expert slots in ascending (t, j) order; experts without tokens get
+ * zeros).  Every sum has a fixed order, so results are reproducible bit for
+ * bit.  Inputs (device): w->w_gate/w_up/w_down bf16 [E, I, H] / [E, I, H] /
+ * [E, H, I] (w_gate unused and may be NULL for ReLU^2); x, dy bf16 [T, H];
+ * topk_ids int32 [T, k] (distinct per token, < E), topk_w fp32 [T, k].
+ * Outputs (device, caller-owned, fully written): dx bf16 [T, H]; d_w_gate
+ * (not written for ReLU^2, may be NULL), d_w_up, d_w_down fp32; d_topk_w
+ * fp32 [T, k].  scratch: device memory of at least
+ * moe_backward_scratch_size bytes (scratch_bytes); the call allocates
+ * nothing.  The workspace's routing buffers are overwritten (dispatch of
+ * topk_ids).  T = 0 writes nothing.  Errors: MOE_EUNSUPPORTED for formats,
+ * shapes (hidden and inter multiples of 128) or activations outside the
+ * list above; MOE_ECAPACITY for T > max_tokens or a short scratch buffer;
+ * MOE_EINVAL for NULL pointers. */
+MOE_API int moe_expert_backward(moe_ws* ws, const moe_weights* w, const void* x,
+                                const int32_t* topk_ids, const float* topk_w, int T, const void* dy,
+                                void* dx, float* d_w_gate, float* d_w_up, float* d_w_down,
+                                float* d_topk_w, void* scratch, size_t scratch_bytes, void* stream);
+
+/* Router gradient: dL/dscores [T, E] fp32 from d_topk_w = dL/dtopk_w [T, k],
+ * for weights renormalised over the k selected experts (the selection is
+ * piecewise constant).  With m = sum_j topk_w[t, j] d_topk_w[t, j], a
+ * selected expert i gets
+ *   MOE_SCORE_SOFTMAX  w_i (dw_i - m)
+ *   MOE_SCORE_SIGMOID  s_i (1 - s_i) (dw_i - m) / sum_sel s,  s = sigmoid(score)
+ *   MOE_SCORE_PROBS    (dw_i - m) / sum_sel p
+ * and every other expert 0 (the whole [T, E] output is written).  All
+ * pointers are device pointers; topk_ids/topk_w as moe_route_topk returns
+ * them.  Errors: MOE_EINVAL for a bad T, E, k or score_fn or NULL pointers. */
+MOE_API int moe_router_backward(const float* scores, const int32_t* topk_ids, const float* topk_w,
+                                const float* d_topk_w, int T, int E, int k, int score_fn,
+                                float* d_scores, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

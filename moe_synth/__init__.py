@@ -296,6 +296,13 @@ def gen_batch(shape: LayerShape, T: int, seed_extra: int = 0, x_std: float = ACT
     return Batch(x_bits, np.ascontiguousarray(scores, dtype=np.float32))
 
 
+def gen_grad(shape: LayerShape, T: int, seed_extra: int = 0) -> np.ndarray:
+    """Seeded upstream gradient dL/dy for the backward: bf16 bits [T, H],
+    standard normal (its own stream: SeedSequence([1, cfg, T, seed_extra]))."""
+    rg = np.random.Generator(np.random.PCG64(np.random.SeedSequence([1, shape.cfg_id, T, seed_extra])))
+    return _bf16_bits(rg.standard_normal((T, shape.hidden), dtype=np.float32))
+
+
 def small_shape(base: str, **kw) -> LayerShape:
     """A reduced copy of a named recipe (same formats and score rule)."""
     return CONFIGS[base].with_(**kw)
