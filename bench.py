@@ -375,6 +375,97 @@ def config_sweep_many(name, tokens, act=0, rounds=3, calls=20):
     return out
 
 
+BWD_STAGES = {7: "transpose_w_recompute_gate_up", 8: "input_grad_down", 9: "slot_pass",
+              10: "input_grad_gate_up", 11: "input_grad_combine", 12: "weight_grad_down",
+              13: "weight_grad_gate_up"}
+
+
+def bench_backward(name="qwen", T=8192, steps=20, warmup=5):
+    """Backward of the routed expert layer in bf16 (moe_expert_backward) on
+    the named layer shape: whole-call time with HIP events, then each stage
+    between events on the launch stream.  Useful FLOPs: 12 H I per slot (the
+    input and weight gradients of three projections; the gate/up
+    recomputation, another 4 H I per slot, is not counted)."""
+    import torch
+    import grouped_gemm_amd as g
+    import moe_synth as ms
+    import oracle
+    sh = ms.CONFIGS[name].with_(w_format=ms.W_BF16, a_format=ms.A_BF16)
+    B = ms.gen_batch(sh, T)
+    ids, w = oracle.route(B.scores, sh.top_k, sh.score_fn)
+    act_e = sorted(set(np.unique(ids).tolist()))
+    t0 = time.time()
+    W = ms.gen_weights(sh, experts=act_e)
+    log(f"[bench] backward {name} T={T}: {len(act_e)} active experts, weights drawn in "
+        f"{time.time() - t0:.1f}s")
+    dW = {n: torch.from_numpy(np.ascontiguousarray(getattr(W, n)).view(np.int16)).cuda()
+          for n in ("w_gate", "w_up", "w_down")}
+    del W
+    ws = g.Workspace(sh.hidden, sh.inter, sh.experts, sh.top_k, T, score_fn=sh.score_fn,
+                     w_format=sh.w_format, a_format=sh.a_format)
+    E, I, H, k = sh.experts, sh.inter, sh.hidden, sh.top_k
+    x = torch.from_numpy(B.x_bits.view(np.int16)).cuda()
+    dy = torch.from_numpy(ms.gen_grad(sh, T).view(np.int16)).cuda()
+    tid = torch.from_numpy(ids.astype(np.int32)).cuda()
+    tw = torch.from_numpy(w.astype(np.float32)).cuda()
+    dx = torch.empty(T, H, dtype=torch.int16, device="cuda")
+    dwg = torch.empty(E, I, H, device="cuda")
+    dwu = torch.empty(E, I, H, device="cuda")
+    dwd = torch.empty(E, H, I, device="cuda")
+    dtw = torch.empty(T, k, device="cuda")
+    scratch = torch.empty(g.backward_scratch_size(ws), dtype=torch.uint8, device="cuda")
+    st = torch.cuda.Stream()
+
+    def call():
+        g.expert_backward(ws, dW, x, tid, tw, dy, dx, dwg, dwu, dwd, dtw, scratch, stream=st)
+
+    with torch.cuda.stream(st):
+        for _ in range(warmup):
+            call()
+        st.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(steps):
+            call()
+        e1.record(st)
+        e1.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        evs = {sid: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for sid in BWD_STAGES}
+        for a, b in evs.values():   # the events must exist before the library records them
+            a.record(st)
+            b.record(st)
+        for sid, (a, b) in evs.items():
+            ws.set_stage_events(sid, a, b)
+        stage = {sid: 0.0 for sid in BWD_STAGES}
+        for _ in range(steps):
+            call()
+            st.synchronize()
+            for sid, (a, b) in evs.items():
+                stage[sid] += a.elapsed_time(b) / steps
+        for sid in BWD_STAGES:
+            ws.set_stage_events(sid, None, None)
+    S = T * k
+    flops = 12.0 * H * I * S
+    # FLOPs of the stages that are one kernel launch each
+    per = {8: 2.0 * H * I * S, 10: 4.0 * H * I * S}
+    dom = max(per, key=lambda sid: stage[sid])
+    ach = per[dom] / (stage[dom] * 1e-3) / 1e12
+    out = {"workload": f"{name}-shaped MoE expert layer backward, bf16, H{H} I{I} E{E} top{k}, T={T}",
+           "us": round(us, 2), "tflops": round(flops / (us * 1e-6) / 1e12, 2),
+           "bf16_mfma_frac": round(flops / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+           "stage_ms": {BWD_STAGES[sid]: round(v, 5) for sid, v in stage.items()},
+           "roofline": {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+                        "traffic": None, "kernel": BWD_STAGES[dom],
+                        "avg_ms": round(stage[dom], 5), "flops_per_launch": per[dom]}}
+    log(f"[bench] backward {name} T={T}: {us:.1f} us, {out['tflops']:.1f} TFLOP/s "
+        f"({out['bf16_mfma_frac']:.3f} of bf16 peak), stages(ms)="
+        f"{[round(v, 4) for v in stage.values()]}")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -405,6 +496,10 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain elementwise copy of 256 MiB (fp32 in, fp32 out), "
                          "whose known byte counts calibrate hardware traffic counters")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward point (Qwen-shaped bf16 expert layer, T=8192)")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time only the backward point and print its JSON object")
     ap.add_argument("--fused-decode", action="store_true",
                     help="run batches of at most 16 tokens through the single-launch decode layer")
     args = ap.parse_args()
@@ -440,6 +535,10 @@ def main():
         for T in ([args.tokens] if args.tokens else list(sh0.tokens)):
             print(json.dumps(config_sweep(args.workload, T, act)), flush=True)
         return
+    if args.backward_only:
+        print(json.dumps(bench_backward("qwen", args.tokens or 8192, args.steps, args.warmup)),
+              flush=True)
+        return
     T_main = args.tokens or max(sh0.tokens)
     points = []
     extra_T = [t for t in sh0.tokens if t != T_main] if not args.tokens else []
@@ -469,6 +568,9 @@ def main():
                 f"({dp['gbs'] / HBM_PEAK_GBS:.3f} of HBM), stages(ms)="
                 f"{[round(v, 4) for v in dp['stage_ms']]}")
             del dp["W"], dp["B"]
+    bwd = None
+    if args.workload == "mixtral" and not args.tokens and not args.no_backward:
+        bwd = bench_backward("qwen", 8192, args.steps, args.warmup)
     dom = int(np.argmax(main_pt["stage_ms"]))
     dom_ms = main_pt["stage_ms"][dom]
     if dom == 2:
@@ -517,6 +619,7 @@ def main():
                    for p in points],
         "roofline": roof,
         "cpu_baseline": cpu,
+        "backward": bwd,
     }
     print(json.dumps(out), flush=True)
 

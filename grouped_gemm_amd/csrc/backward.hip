@@ -3,30 +3,32 @@
 // weight- and router-gradient kernels).  Per slot (t, j) of expert e, with
 // the forward g = Wg x_t, u = Wu x_t, h = act(g, u), o = Wd h and
 // y_t = sum_j w[t, j] o:
-//   r  = Wd^T dy_t                    (grouped GEMM, B not transposed)
+//   r  = Wd^T dy_t                    (input-gradient GEMM)
 //   dw = <r, h>,  dg = w r dact/dg,  du = w r dact/du   (per-slot pass)
-//   da = Wg^T dg + Wu^T du            (grouped GEMM, B not transposed)
+//   da = Wg^T dg + Wu^T du            (input-gradient GEMM, K = 2 I)
 //   dx_t = sum_j da, j ascending      (dispatch backward)
 //   dWd[e] = sum_slots (w dy_t) h^T, dWg[e] = sum dg x^T, dWu[e] = sum du x^T
 //                                     (weight-gradient GEMMs over each group's rows)
-// g and u are recomputed by the forward's tiled bf16 grouped GEMM.  Every
-// sum has a fixed order (no atomics), so the gradients are bit-for-bit
-// reproducible.
+// Every sum has a fixed order (no atomics), so the gradients are
+// bit-for-bit reproducible.
 //
-// MFMA operand layout (16x16x32 bf16): lane l feeds row (or column) l % 16
-// with K elements [8 (l/16), 8 (l/16) + 8); the result lane l holds rows
-// 4 (l/16) .. +3 of column l % 16.  The two new GEMM shapes need some
-// operand with K strided in memory (B row-major [K, N] for the input
-// gradients; both operands for the weight gradients, whose K runs over a
-// group's rows): those tiles are transposed on their way into LDS, so
-// every fragment read is one 16-byte LDS read.
+// Layout.  A 16x16x32 bf16 MFMA takes, per lane, 8 consecutive elements of
+// the contraction (K) dimension: lane l feeds row (or column) l % 16 with K
+// elements [8 (l/16), 8 (l/16) + 8); the result lane l holds rows
+// 4 (l/16) .. +3 of column l % 16.  The forward's tiled grouped GEMM wants
+// its weights [N, K] with K contiguous; the input gradients contract the
+// stored weights along their other axis, so the active experts' weights are
+// transposed once per call (k_bwd_transpose) and the forward kernel runs
+// the input gradients, and the gate/up recomputation, unchanged.  The
+// weight gradients contract over a group's rows, so their operands (w dy,
+// h, dg | du, gathered x) are written feature-major (slots contiguous) by
+// the same transpose, and k_bwd_wgrad loads MFMA fragments straight from
+// memory.
 #include "layer.h"
 
 namespace {
 
 constexpr int BT = 256;            // threads per workgroup (four waves)
-constexpr int KS = 32;             // K elements per step (one MFMA deep)
-constexpr int PK = KS + 8;         // LDS pitch of a transposed row, bf16 elements
 
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 
@@ -96,159 +98,118 @@ DEVI void act_grad(int act, float L, float g, float u, float* dg, float* du) {
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// Input-gradient GEMM over expert row groups, B not transposed:
-//   out[slot, n] = sum_src sum_k A_src[row(slot), k] * B_src[e][k, n]
-// B_src[e] is [K, N] row-major (the stored [N_fwd, K_fwd] weight read along
-// its first axis).  Work item = (row block of 64 rows from the block table,
-// 128 output columns); four waves as 2 x 2, each 32 rows x 64 columns.
-template <int NSRC>
-__global__ void __launch_bounds__(BT) k_bwd_nn(BwdNN p) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[64 * PK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[128 * PK];   // [n][k]
-  const int tile = blockIdx.y;
-  if (tile >= p.meta[META_NTILES]) return;
-  const int grp = p.tiles[2 * tile], r0 = p.tiles[2 * tile + 1];
-  const int cnt = p.counts[grp], base = p.indptr[grp];
-  const int n0 = blockIdx.x * 128;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wr = wave >> 1, wc = wave & 1;   // wave's 32-row and 64-column block
-  const int K = p.K, N = p.N;
-  // staging assignment: A: one 16-byte chunk (8 k) of one row per thread;
-  // B: two 8-column chunks of one k row per thread
-  const int ar = tid >> 2, ak = (tid & 3) * 8;
-  const int rrow = r0 + ar;
-  const bool av = rrow < cnt;
-  const int slot = base + (av ? rrow : 0);
-  const long arow = p.a_gather ? p.a_gather[slot] / p.gather_div : slot;
-  f32x4 acc[2][4];
+// Tiled transpose of 64 x 64 blocks through LDS:
+//   out[z][c][out_col0 + r] = bf16(scale(r) * in[z][row(r)][c]),  r < R, c < C,
+// row(r) = gather ? gather[r] / gather_div : r; scale(r) = scale[gather[r]]
+// (or 1).  Rows r in [R, 64 * ceil(R / 64)) are written as zeros, so a
+// whole padded row of out is defined.  Matrices z with counts[z] == 0 are
+// skipped.  Used for the weights (their [N, K] storage read along N) and
+// for the per-slot operands of the weight gradients (slot-major to
+// feature-major, so that the slot dimension is contiguous).
+__global__ void __launch_bounds__(BT) k_bwd_transpose(BwdTranspose p) {
+  __shared__ uint16_t t[64][64 + 2];
+  const int z = blockIdx.z;
+  if (p.counts && p.counts[z] == 0) return;
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  const int tid = threadIdx.x;
+  const uint16_t* in = p.in + (size_t)z * p.in_zstride;
+  // load: 64 rows x 64 columns, two 8-column chunks per thread
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int q = 0; q < 2; ++q) {
+    const int i = tid + q * BT, rr = i >> 3, cc = (i & 7) * 8;
+    const int r = r0 + rr;
+    u16x8 v = (u16x8){0, 0, 0, 0, 0, 0, 0, 0};
+    if (r < p.R) {
+      const long row = p.gather ? p.gather[r] / p.gather_div : r;
+      v = *(const u16x8*)(in + row * p.in_ld + c0 + cc);
+      if (p.scale) {
+        const float sc = p.scale[p.gather[r]];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  const int steps = NSRC * (K / KS);
-  u16x8 ra, rb[2];
-  auto gload = [&](int st) {
-    const int src = st / (K / KS), k0 = (st - src * (K / KS)) * KS;
-    const uint16_t* A = src ? p.a1 : p.a0;
-    const uint16_t* B = (src ? p.b1 : p.b0) + (size_t)grp * K * N;
-    ra = av ? *(const u16x8*)(A + arow * K + k0 + ak) : (u16x8){0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int q = tid + c * BT;             // 512 chunks: 32 k rows x 16 chunks
-      const int kr = q >> 4, nc = (q & 15) * 8;
-      rb[c] = *(const u16x8*)(B + (size_t)(k0 + kr) * N + n0 + nc);
+        for (int e = 0; e < 8; ++e) v[e] = f32_to_bf16(sc * bf16_to_f32(v[e]));
+      }
     }
-  };
-  gload(0);
-  for (int st = 0; st < steps; ++st) {
-    __syncthreads();   // the previous step's fragment reads are done
-    *(u16x8*)(As + ar * PK + ak) = ra;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int q = tid + c * BT, kr = q >> 4, nc = (q & 15) * 8;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) Bs[(nc + i) * PK + kr] = rb[c][i];
-    }
-    __syncthreads();
-    if (st + 1 < steps) gload(st + 1);   // in flight while this step computes
-    const int g8 = (lane >> 4) * 8, l16 = lane & 15;
-    bf16x8 fa[2], fb[4];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) fa[i] = as_bf16x8(*(const u16x8*)(As + (wr * 32 + i * 16 + l16) * PK + g8));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) fb[j] = as_bf16x8(*(const u16x8*)(Bs + (wc * 64 + j * 16 + l16) * PK + g8));
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(fa[i], fb[j], acc[i][j]);
+    for (int e = 0; e < 8; ++e) t[rr][cc + e] = v[e];
   }
-  // lane holds rows 4 (lane/16) .. +3 of column lane % 16 of each 16x16 tile
+  __syncthreads();
+  // store: 64 output rows (columns c) x 64 r, eight r per 16-byte chunk
+  uint16_t* out = p.out + (size_t)z * p.out_zstride;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int q = 0; q < 2; ++q) {
+    const int i = tid + q * BT, cc = i >> 3, rr = (i & 7) * 8;
+    u16x8 v;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int rr = r0 + wr * 32 + i * 16 + (lane >> 4) * 4 + r;
-      if (rr >= cnt) continue;
-      float* o = p.out + (size_t)(base + rr) * N + n0 + wc * 64 + (lane & 15);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) o[j * 16] = acc[i][j][r];
-    }
+    for (int e = 0; e < 8; ++e) v[e] = t[rr + e][cc];
+    *(u16x8*)(out + (size_t)(c0 + cc) * p.out_ld + p.out_col0 + r0 + rr) = v;
+  }
 }
 
 // ---------------------------------------------------------------------------
-// Weight-gradient GEMM over expert row groups:
-//   out[e][m, n] = sum over rows s of group e of A[s, m] * B[brow(s), n]
-// A [rows, M] and B [*, N] bf16 row-major (brow = b_gather[s] / div, or s).
+// Weight-gradient GEMM with the slot dimension contiguous in both operands:
+//   out[e][m, n] = sum over s in [indptr[e], indptr[e+1]) of a[m, s] * b[n, s]
+// a [M, lda], b [N, ldb] bf16 (feature-major copies of the per-slot rows).
 // Work item = (expert, 128 x 128 output block); four waves as 2 x 2, each
-// 64 x 64.  K runs over the group's rows in ascending order, 32 per step;
-// experts without rows write zeros.
-__global__ void __launch_bounds__(BT) k_bwd_tn(BwdTN p) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[128 * PK];   // [m][s]
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[128 * PK];   // [n][s]
+// 64 x 64 from fragments loaded straight from memory (16 bytes per lane per
+// fragment, one 32-slot MFMA depth per step, the next step's fragments in
+// flight during the current step's MFMAs).  Slot chunks that straddle the
+// group's ends are masked on the a side; experts without rows write zeros.
+__global__ void __launch_bounds__(BT) k_bwd_wgrad(BwdWgrad p) {
   const int e = blockIdx.z, m0 = blockIdx.y * 128, n0 = blockIdx.x * 128;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int M = p.M, N = p.N;
-  const int base = p.indptr[e], cnt = p.indptr[e + 1] - base;
+  const int s0 = p.indptr[e], s1 = p.indptr[e + 1];
+  const int g8 = (lane >> 4) * 8, l16 = lane & 15;
+  const uint16_t* arow[4];
+  const uint16_t* brow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    arow[i] = p.a + (size_t)(m0 + wm * 64 + i * 16 + l16) * p.lda;
+    brow[i] = p.b + (size_t)(n0 + wn * 64 + i * 16 + l16) * p.ldb;
+  }
   f32x4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  // staging: 32 rows x 128 columns per operand = 512 chunks of 8 columns,
-  // two per thread
-  u16x8 ra[2], rb[2];
-  auto gload = [&](int s0) {
+  const int sb = s0 & ~31;                 // first 32-aligned step
+  const int steps = s1 > s0 ? (s1 - sb + 31) / 32 : 0;
+  u16x8 fa[4], fb[4], na[4], nb[4];
+  auto load = [&](int st, u16x8* A, u16x8* B) {
+    const int c = sb + st * 32 + g8;        // this lane's 8 slots
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int q = tid + c * BT, sr = q >> 4, cc = (q & 15) * 8;
-      const int s = s0 + sr;
-      if (s < cnt) {
-        const long arow = base + s;
-        const long brow = p.b_gather ? p.b_gather[base + s] / p.gather_div : base + s;
-        ra[c] = *(const u16x8*)(p.a + arow * M + m0 + cc);
-        rb[c] = *(const u16x8*)(p.b + brow * N + n0 + cc);
-      } else {
-        ra[c] = (u16x8){0, 0, 0, 0, 0, 0, 0, 0};
-        rb[c] = ra[c];
-      }
+    for (int i = 0; i < 4; ++i) {
+      A[i] = *(const u16x8*)(arow[i] + c);
+      B[i] = *(const u16x8*)(brow[i] + c);
+    }
+    if (c < s0 || c + 8 > s1) {            // a chunk at the group's ends
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (c + q < s0 || c + q >= s1) A[i][q] = 0;
     }
   };
-  const int steps = (cnt + KS - 1) / KS;
-  if (steps > 0) gload(0);
+  if (steps > 0) load(0, fa, fb);
   for (int st = 0; st < steps; ++st) {
-    __syncthreads();
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int q = tid + c * BT, sr = q >> 4, cc = (q & 15) * 8;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        As[(cc + i) * PK + sr] = ra[c][i];
-        Bs[(cc + i) * PK + sr] = rb[c][i];
-      }
-    }
-    __syncthreads();
-    if (st + 1 < steps) gload((st + 1) * KS);
-    const int g8 = (lane >> 4) * 8, l16 = lane & 15;
-    bf16x8 fa[4], fb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = as_bf16x8(*(const u16x8*)(As + (wm * 64 + i * 16 + l16) * PK + g8));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) fb[j] = as_bf16x8(*(const u16x8*)(Bs + (wn * 64 + j * 16 + l16) * PK + g8));
+    if (st + 1 < steps) load(st + 1, na, nb);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(fa[i], fb[j], acc[i][j]);
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(as_bf16x8(fa[i]), as_bf16x8(fb[j]), acc[i][j]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      fa[i] = na[i];
+      fb[i] = nb[i];
+    }
   }
-  float* out = p.out + (size_t)e * M * N;
+  float* out = p.out + (size_t)e * p.M * p.N;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + r;
-      float* o = out + (size_t)m * N + n0 + wn * 64 + (lane & 15);
+      float* o = out + (size_t)m * p.N + n0 + wn * 64 + l16;
 #pragma unroll
       for (int j = 0; j < 4; ++j) o[j * 16] = acc[i][j][r];
     }
@@ -256,17 +217,16 @@ __global__ void __launch_bounds__(BT) k_bwd_tn(BwdTN p) {
 
 // ---------------------------------------------------------------------------
 // Per-slot pass: h = bf16(act(g, u)), dw = <r, h> (fixed-order block
-// reduction), dg = bf16(w r dact/dg), du = bf16(w r dact/du), and the
-// weighted upstream row w dy_t in bf16.  One workgroup per slot.
+// reduction), dg = bf16(w r dact/dg) and du = bf16(w r dact/du) side by
+// side in one row of 2 I.  One workgroup per slot.
 __global__ void __launch_bounds__(BT) k_bwd_slot(BwdSlot p) {
   __shared__ float red[BT];
   const int s = blockIdx.x;
   if (s >= p.indptr[p.E]) return;
   const int tid = threadIdx.x;
   const int pos = p.gather[s];                 // t * k + j
-  const int t = pos / p.k;
   const float w = p.topk_w[pos];
-  const int I = p.I, H = p.H;
+  const int I = p.I;
   float part = 0.0f;
   for (int n = tid; n < I; n += BT) {
     const size_t o = (size_t)s * I + n;
@@ -277,11 +237,9 @@ __global__ void __launch_bounds__(BT) k_bwd_slot(BwdSlot p) {
     float pg, pu;
     act_grad(p.act, p.limit, g, u, &pg, &pu);
     const float dh = w * r;
-    p.DG[o] = f32_to_bf16(dh * pg);
-    p.DU[o] = f32_to_bf16(dh * pu);
+    p.DGU[(size_t)s * 2 * I + n] = f32_to_bf16(dh * pg);
+    p.DGU[(size_t)s * 2 * I + I + n] = f32_to_bf16(dh * pu);
   }
-  for (int c = tid; c < H; c += BT)
-    p.DO[(size_t)s * H + c] = f32_to_bf16(w * bf16_to_f32(p.dy[(size_t)t * H + c]));
   red[tid] = part;
   __syncthreads();
   for (int o = BT / 2; o > 0; o >>= 1) {
@@ -340,17 +298,15 @@ __global__ void __launch_bounds__(64) k_router_bwd(RouterBwd p) {
 }
 
 // ---------------------------------------------------------------- host launchers
-hipError_t launch_bwd_nn(const BwdNN& a, int nsrc, int max_tiles, hipStream_t st) {
-  if (a.N % 128 || a.K % KS || max_tiles <= 0) return hipErrorInvalidValue;
-  dim3 grid(a.N / 128, max_tiles);
-  if (nsrc == 2) hipLaunchKernelGGL(k_bwd_nn<2>, grid, dim3(BT), 0, st, a);
-  else hipLaunchKernelGGL(k_bwd_nn<1>, grid, dim3(BT), 0, st, a);
+hipError_t launch_bwd_transpose(const BwdTranspose& a, int nz, hipStream_t st) {
+  if (a.C % 64 || a.R <= 0 || nz <= 0) return a.R == 0 ? hipSuccess : hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_bwd_transpose, dim3(a.C / 64, (a.R + 63) / 64, nz), dim3(BT), 0, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_tn(const BwdTN& a, int E, hipStream_t st) {
-  if (a.M % 128 || a.N % 128 || E <= 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_bwd_tn, dim3(a.N / 128, a.M / 128, E), dim3(BT), 0, st, a);
+hipError_t launch_bwd_wgrad(const BwdWgrad& a, int E, hipStream_t st) {
+  if (a.M % 128 || a.N % 128 || E <= 0 || a.lda % 8 || a.ldb % 8) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_bwd_wgrad, dim3(a.N / 128, a.M / 128, E), dim3(BT), 0, st, a);
   return hipGetLastError();
 }
 

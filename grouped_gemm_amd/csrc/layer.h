@@ -257,32 +257,33 @@ hipError_t launch_gemm_pipe(int fmt, bool gateup, int family, const GemmArgs& g,
 #define CFG3_MIN_ROWS 4096
 
 // ---------------------------------------------------------------- backward
-// Input-gradient GEMM over the block table's 64-row blocks:
-//   out[slot, n] = sum_src sum_k A_src[row(slot), k] * B_src[e][k, n],
-// row(slot) = a_gather ? a_gather[slot] / gather_div : slot; B_src[e] is
-// [K, N] row-major; out fp32 [rows, N].
-struct BwdNN {
-  const uint16_t* a0;
-  const uint16_t* a1;
-  const int32_t* a_gather;
+// Tiled transpose (64 x 64 blocks): out[z][c][out_col0 + r] =
+// bf16(scale(r) * in[z][row(r)][c]) for r < R, c < C (C a multiple of 64),
+// row(r) = gather ? gather[r] / gather_div : r, scale(r) = scale[gather[r]]
+// or 1; rows r in [R, 64 ceil(R / 64)) are written as zeros; matrices z
+// with counts[z] == 0 are skipped.
+struct BwdTranspose {
+  const uint16_t* in;
+  long in_ld, in_zstride;
+  uint16_t* out;
+  long out_ld, out_zstride;
+  int out_col0;
+  int R, C;
+  const int32_t* gather;
   int gather_div;
-  const uint16_t* b0;
-  const uint16_t* b1;
-  int K, N;
-  const int32_t* tiles;
-  const int32_t* meta;
+  const float* scale;
   const int32_t* counts;
-  const int32_t* indptr;
-  float* out;
 };
-// Weight-gradient GEMM: out[e][m, n] = sum over group e's rows s of
-// a[s, m] * b[brow(s), n], brow = b_gather ? b_gather[s] / gather_div : s;
-// out fp32 [E, M, N] (zeros for experts without rows).
-struct BwdTN {
+// Weight-gradient GEMM: out[e][m, n] = sum over s in [indptr[e],
+// indptr[e+1]) of a[m * lda + s] * b[n * ldb + s]; out fp32 [E, M, N]
+// (zeros for experts without rows).  M, N multiples of 128; lda, ldb
+// multiples of 8 and at least the rows rounded up to 32, that padding
+// finite.
+struct BwdWgrad {
   const uint16_t* a;
+  long lda;
   const uint16_t* b;
-  const int32_t* b_gather;
-  int gather_div;
+  long ldb;
   const int32_t* indptr;
   int M, N;
   float* out;
@@ -292,16 +293,13 @@ struct BwdSlot {
   const float* G;          // [rows, I] gate pre-activations (NULL for ReLU^2)
   const float* U;          // [rows, I]
   const float* R;          // [rows, I] Wd^T dy
-  const uint16_t* dy;      // [T, H] bf16
   const float* topk_w;     // [T, k]
   const int32_t* gather;   // slot -> t * k + j
   const int32_t* indptr;   // [E + 1]
-  int E, k, I, H, act;
+  int E, k, I, act;
   float limit;
   uint16_t* Hb;            // [rows, I] bf16 h
-  uint16_t* DG;            // [rows, I] bf16
-  uint16_t* DU;            // [rows, I] bf16
-  uint16_t* DO;            // [rows, H] bf16 w dy_t
+  uint16_t* DGU;           // [rows, 2 I] bf16: dg, then du
   float* dw;               // [T, k]
 };
 struct BwdDx {
@@ -318,8 +316,8 @@ struct RouterBwd {
   int T, E, k, score_fn;
   float* ds;               // [T, E]
 };
-hipError_t launch_bwd_nn(const BwdNN& a, int nsrc, int max_tiles, hipStream_t st);
-hipError_t launch_bwd_tn(const BwdTN& a, int E, hipStream_t st);
+hipError_t launch_bwd_transpose(const BwdTranspose& a, int nz, hipStream_t st);
+hipError_t launch_bwd_wgrad(const BwdWgrad& a, int E, hipStream_t st);
 hipError_t launch_bwd_slot(const BwdSlot& a, int max_rows, hipStream_t st);
 hipError_t launch_bwd_dx(const BwdDx& a, hipStream_t st);
 hipError_t launch_router_bwd(const RouterBwd& a, hipStream_t st);

@@ -174,10 +174,10 @@ struct moe_ws {
   int decode_grid = -1;   // resident workgroups of the decode layer (computed once)
   int device = 0;
   std::map<GraphKey, GraphEntry> execs;
-  hipEvent_t stage_ev[7][2] = {};
+  hipEvent_t stage_ev[14][2] = {};   // 0-6 forward stages, 7-13 backward stages
   bool any_stage_events() const {
-    for (auto& p : stage_ev)
-      if (p[0] || p[1]) return true;
+    for (int i = 0; i < 7; ++i)
+      if (stage_ev[i][0] || stage_ev[i][1]) return true;
     return false;
   }
   template <class T>
@@ -710,12 +710,15 @@ int moe_dispatch_noalloc(const int32_t* topk_ids, int T, int k, int E, int32_t* 
 namespace {
 
 struct BwdScratch {
-  size_t G, U, R, Hb, DG, DU, DO, DA, total;
+  size_t G, U, R, Hb, DGU, DA, WdT, WguT, XgT, DOT, HbT, DGUT, total;
+  long ldo;   // feature-major rows: slots padded to a multiple of 64
 };
 
 BwdScratch bwd_scratch(const moe_layer_desc& d) {
-  const size_t S = (size_t)d.max_tokens * d.top_k, I = d.inter, H = d.hidden;
+  const size_t S = (size_t)d.max_tokens * d.top_k, I = d.inter, H = d.hidden, E = d.num_experts;
   BwdScratch b{};
+  b.ldo = (long)((S + 63) / 64 * 64);
+  const size_t L = (size_t)b.ldo;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -726,10 +729,14 @@ BwdScratch bwd_scratch(const moe_layer_desc& d) {
   b.U = take(S * I * 4);
   b.R = take(S * I * 4);
   b.Hb = take(S * I * 2);
-  b.DG = take(S * I * 2);
-  b.DU = take(S * I * 2);
-  b.DO = take(S * H * 2);
+  b.DGU = take(S * 2 * I * 2);
   b.DA = take(S * H * 4);
+  b.WdT = take(E * I * H * 2);        // W_down transposed: [E, I, H]
+  b.WguT = take(E * H * 2 * I * 2);   // W_gate | W_up transposed: [E, H, 2 I]
+  b.XgT = take(H * L * 2);            // gathered x, feature-major [H, ldo]
+  b.DOT = take(H * L * 2);            // w dy, feature-major [H, ldo]
+  b.HbT = take(I * L * 2);            // h, feature-major [I, ldo]
+  b.DGUT = take(2 * I * L * 2);       // dg | du, feature-major [2 I, ldo]
   b.total = off;
   return b;
 }
@@ -776,6 +783,10 @@ int moe_expert_backward(moe_ws* ws, const moe_weights* w, const void* x, const i
     return fail(MOE_ECAPACITY, "scratch holds %zu bytes, the backward needs %zu", scratch_bytes,
                 b.total);
   hipStream_t st = (hipStream_t)stream;
+  auto mark = [&](int stage, int which) -> hipError_t {
+    hipEvent_t e = ws->stage_ev[stage][which];
+    return e ? hipEventRecord(e, st) : hipSuccess;
+  };
   char* sc = (char*)scratch;
   const int E = d.num_experts, k = d.top_k, H = d.hidden, I = d.inter, S = T * k;
   // dispatch of the given routing, block table for 64-row blocks
@@ -797,10 +808,44 @@ int moe_expert_backward(moe_ws* ws, const moe_weights* w, const void* x, const i
   float* U = (float*)(sc + b.U);
   float* R = (float*)(sc + b.R);
   uint16_t* Hb = (uint16_t*)(sc + b.Hb);
-  uint16_t* DG = (uint16_t*)(sc + b.DG);
-  uint16_t* DU = (uint16_t*)(sc + b.DU);
-  uint16_t* DO = (uint16_t*)(sc + b.DO);
+  uint16_t* DGU = (uint16_t*)(sc + b.DGU);
   float* DA = (float*)(sc + b.DA);
+  uint16_t* WdT = (uint16_t*)(sc + b.WdT);
+  uint16_t* WguT = (uint16_t*)(sc + b.WguT);
+  uint16_t* XgT = (uint16_t*)(sc + b.XgT);
+  uint16_t* DOT = (uint16_t*)(sc + b.DOT);
+  uint16_t* HbT = (uint16_t*)(sc + b.HbT);
+  uint16_t* DGUT = (uint16_t*)(sc + b.DGUT);
+  // the active experts' weights, transposed so that the forward's tiled
+  // grouped GEMM (weights [N, K], K contiguous) computes the input gradients
+  HIP_TRY(mark(7, 0), "event record");
+  BwdTranspose tr{};
+  tr.counts = counts;
+  tr.gather_div = 1;
+  tr.in = (const uint16_t*)w->w_down;   // [H, I] per expert -> [I, H]
+  tr.in_ld = I;
+  tr.in_zstride = (long)H * I;
+  tr.out = WdT;
+  tr.out_ld = H;
+  tr.out_zstride = (long)I * H;
+  tr.R = H;
+  tr.C = I;
+  HIP_TRY(launch_bwd_transpose(tr, E, st), "weight transpose launch");
+  tr.in_ld = H;                         // [I, H] per expert -> [H, 2 I] halves
+  tr.in_zstride = (long)I * H;
+  tr.out = WguT;
+  tr.out_ld = 2 * I;
+  tr.out_zstride = (long)H * 2 * I;
+  tr.R = I;
+  tr.C = H;
+  // ReLU^2 has no gate: its dg is zero, and W_up fills both halves so that
+  // the gate half holds finite values
+  tr.in = (const uint16_t*)(relu2 ? w->w_up : w->w_gate);
+  tr.out_col0 = 0;
+  HIP_TRY(launch_bwd_transpose(tr, E, st), "weight transpose launch");
+  tr.in = (const uint16_t*)w->w_up;
+  tr.out_col0 = I;
+  HIP_TRY(launch_bwd_transpose(tr, E, st), "weight transpose launch");
   // g and u recomputed by the forward's tiled bf16 grouped GEMM (64-row blocks)
   GemmArgs g = gemm_args(ws);
   g.E = E;
@@ -821,77 +866,103 @@ int moe_expert_backward(moe_ws* ws, const moe_weights* w, const void* x, const i
   g.w0 = (const uint8_t*)w->w_up;
   g.out = U;
   HIP_TRY(launch_gemm_tiled(F_BF16, false, 2, g, st), "up recompute launch");
-  const int max_tiles = S / 64 + E + 1;
-  // r = W_down^T dy (rows of dy gathered by token)
-  BwdNN nn{};
-  nn.a0 = (const uint16_t*)dy;
-  nn.a_gather = gather;
-  nn.gather_div = k;
-  nn.b0 = (const uint16_t*)w->w_down;
-  nn.K = H;
-  nn.N = I;
-  nn.tiles = tiles;
-  nn.meta = meta;
-  nn.counts = counts;
-  nn.indptr = indptr;
-  nn.out = R;
-  HIP_TRY(launch_bwd_nn(nn, 1, max_tiles, st), "down input-gradient launch");
+  HIP_TRY(mark(7, 1), "event record");
+  // r = W_down^T dy: rows of dy gathered by token against W_down^T [I, H]
+  HIP_TRY(mark(8, 0), "event record");
+  g.a = (const uint8_t*)dy;
+  g.w0 = (const uint8_t*)WdT;
+  g.out = R;
+  HIP_TRY(launch_gemm_tiled(F_BF16, false, 2, g, st), "down input-gradient launch");
+  HIP_TRY(mark(8, 1), "event record");
   BwdSlot sl{};
   sl.G = relu2 ? nullptr : G;
   sl.U = U;
   sl.R = R;
-  sl.dy = (const uint16_t*)dy;
   sl.topk_w = topk_w;
   sl.gather = gather;
   sl.indptr = indptr;
   sl.E = E;
   sl.k = k;
   sl.I = I;
-  sl.H = H;
   sl.act = d.activation;
   sl.limit = act_limit(d);
   sl.Hb = Hb;
-  sl.DG = DG;
-  sl.DU = DU;
-  sl.DO = DO;
+  sl.DGU = DGU;
   sl.dw = d_topk_w;
+  HIP_TRY(mark(9, 0), "event record");
   HIP_TRY(launch_bwd_slot(sl, S, st), "activation backward launch");
-  // da = W_gate^T dg + W_up^T du
-  BwdNN nn2 = nn;
-  nn2.a_gather = nullptr;
-  nn2.gather_div = 1;
-  nn2.a0 = relu2 ? DU : DG;
-  nn2.b0 = (const uint16_t*)(relu2 ? w->w_up : w->w_gate);
-  nn2.a1 = DU;
-  nn2.b1 = (const uint16_t*)w->w_up;
-  nn2.K = I;
-  nn2.N = H;
-  nn2.out = DA;
-  HIP_TRY(launch_bwd_nn(nn2, relu2 ? 1 : 2, max_tiles, st), "gate/up input-gradient launch");
+  HIP_TRY(mark(9, 1), "event record");
+  // da = [dg | du] [W_gate^T ; W_up^T] (K = 2 I; for ReLU^2 dg is zero)
+  HIP_TRY(mark(10, 0), "event record");
+  g.a = (const uint8_t*)DGU;
+  g.gather = nullptr;
+  g.gather_div = 1;
+  g.w0 = (const uint8_t*)WguT;
+  g.N = H;
+  g.K = 2 * I;
+  g.out = DA;
+  HIP_TRY(launch_gemm_tiled(F_BF16, false, 2, g, st), "gate/up input-gradient launch");
+  HIP_TRY(mark(10, 1), "event record");
   BwdDx bx{DA, inv, T, k, H, (uint16_t*)dx};
+  HIP_TRY(mark(11, 0), "event record");
   HIP_TRY(launch_bwd_dx(bx, st), "input-gradient combine launch");
-  // weight gradients over each expert's rows
-  BwdTN tn{};
-  tn.indptr = indptr;
-  tn.a = DO;
-  tn.b = Hb;
-  tn.M = H;
-  tn.N = I;
-  tn.out = d_w_down;
-  HIP_TRY(launch_bwd_tn(tn, E, st), "down weight-gradient launch");
-  tn.b = (const uint16_t*)x;
-  tn.b_gather = gather;
-  tn.gather_div = k;
-  tn.M = I;
-  tn.N = H;
+  HIP_TRY(mark(11, 1), "event record");
+  // weight gradients: the per-slot operands feature-major (slots contiguous)
+  BwdTranspose ta{};
+  ta.R = S;
+  ta.out_ld = b.ldo;
+  ta.gather_div = k;
+  ta.in = (const uint16_t*)dy;          // w dy, gathered by token
+  ta.in_ld = H;
+  ta.C = H;
+  ta.gather = gather;
+  ta.scale = topk_w;
+  ta.out = DOT;
+  HIP_TRY(mark(12, 0), "event record");
+  HIP_TRY(launch_bwd_transpose(ta, 1, st), "slot transpose launch");
+  ta.in = Hb;                           // h
+  ta.in_ld = I;
+  ta.C = I;
+  ta.gather = nullptr;
+  ta.scale = nullptr;
+  ta.out = HbT;
+  HIP_TRY(launch_bwd_transpose(ta, 1, st), "slot transpose launch");
+  BwdWgrad wg{};
+  wg.indptr = indptr;
+  wg.a = DOT;
+  wg.lda = b.ldo;
+  wg.b = HbT;
+  wg.ldb = b.ldo;
+  wg.M = H;
+  wg.N = I;
+  wg.out = d_w_down;
+  HIP_TRY(launch_bwd_wgrad(wg, E, st), "down weight-gradient launch");
+  HIP_TRY(mark(12, 1), "event record");
+  HIP_TRY(mark(13, 0), "event record");
+  ta.in = (const uint16_t*)x;           // x, gathered by token
+  ta.in_ld = H;
+  ta.C = H;
+  ta.gather = gather;
+  ta.out = XgT;
+  HIP_TRY(launch_bwd_transpose(ta, 1, st), "slot transpose launch");
+  ta.in = DGU;                          // dg | du
+  ta.in_ld = 2 * I;
+  ta.C = 2 * I;
+  ta.gather = nullptr;
+  ta.out = DGUT;
+  HIP_TRY(launch_bwd_transpose(ta, 1, st), "slot transpose launch");
+  wg.b = XgT;
+  wg.M = I;
+  wg.N = H;
   if (!relu2) {
-    tn.a = DG;
-    tn.out = d_w_gate;
-    HIP_TRY(launch_bwd_tn(tn, E, st), "gate weight-gradient launch");
+    wg.a = DGUT;
+    wg.out = d_w_gate;
+    HIP_TRY(launch_bwd_wgrad(wg, E, st), "gate weight-gradient launch");
   }
-  tn.a = DU;
-  tn.out = d_w_up;
-  HIP_TRY(launch_bwd_tn(tn, E, st), "up weight-gradient launch");
+  wg.a = DGUT + (size_t)I * b.ldo;
+  wg.out = d_w_up;
+  HIP_TRY(launch_bwd_wgrad(wg, E, st), "up weight-gradient launch");
+  HIP_TRY(mark(13, 1), "event record");
   return MOE_OK;
 }
 
@@ -1268,7 +1339,7 @@ int moe_config_model_params(double* host_theta20) {
 
 int moe_workspace_set_stage_events(moe_ws* ws, int stage, void* ev_begin, void* ev_end) {
   if (!ws) return fail(MOE_EINVAL, "workspace is NULL");
-  if (stage < 0 || stage > 6) return fail(MOE_EINVAL, "stage must be in [0, 6]");
+  if (stage < 0 || stage > 13) return fail(MOE_EINVAL, "stage must be in [0, 13]");
   ws->stage_ev[stage][0] = (hipEvent_t)ev_begin;
   ws->stage_ev[stage][1] = (hipEvent_t)ev_end;
   return MOE_OK;
