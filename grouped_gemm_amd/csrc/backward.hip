@@ -146,73 +146,181 @@ __global__ void __launch_bounds__(BT) k_bwd_transpose(BwdTranspose p) {
 
 // ---------------------------------------------------------------------------
 // Weight-gradient GEMM with the slot dimension contiguous in both operands:
-//   out[e][m, n] = sum over s in [indptr[e], indptr[e+1]) of a[m, s] * b[n, s]
-// a [M, lda], b [N, ldb] bf16 (feature-major copies of the per-slot rows).
-// Work item = (expert, 128 x 128 output block); four waves as 2 x 2, each
-// 64 x 64 from fragments loaded straight from memory (16 bytes per lane per
-// fragment, one 32-slot MFMA depth per step, the next step's fragments in
-// flight during the current step's MFMAs).  Slot chunks that straddle the
-// group's ends are masked on the a side; experts without rows write zeros.
+//   out[e][m, n] = sum over s in [row0, row1) of a[m, s] * b[n, s]
+// for one work chunk (an expert's rows or a piece of them); a [M, lda],
+// b [N, ldb] bf16 (feature-major copies of the per-slot rows).  Work item =
+// (chunk, 128 x 128 output block); four waves as 2 x 2, each 64 x 64.  Per
+// step of 32 slots the workgroup copies the 128 a rows and 128 b rows
+// (64 bytes each) into a ring of WG_NS LDS stages with asynchronous
+// global->LDS loads, so the next steps' loads are in flight while this
+// step's MFMAs run; 16-byte chunks are XOR-swizzled by row so the fragment
+// reads (16 rows, same chunk) are free of bank conflicts.  Slot chunks that
+// straddle the range's ends are masked on the a side after the LDS read.
+namespace {
+
+constexpr int WG_NS = 4;              // ring stages (2 workgroups per CU)
+constexpr int WG_STAGE = 16384;       // a: 128 rows x 64 B, then b
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+DEVI void dma16(const void* src, uint8_t* lds_block) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_block, 16, 0, 0);
+}
+// byte offset of (row, 16-byte chunk) in a swizzled [rows][64 B] block
+DEVI int swz64(int row, int chunk) { return row * 64 + 16 * (chunk ^ ((row >> 1) & 3)); }
+// wait until at most n of this wave's asynchronous loads are pending
+DEVI void wait_vm_steps(int n) {
+  switch (n) {
+    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
+// workgroup barrier without __syncthreads()'s fence, which would also wait
+// for the ring's loads in flight (each wave waits for its own first)
+DEVI void raw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+}  // namespace
+
 __global__ void __launch_bounds__(BT) k_bwd_wgrad(BwdWgrad p) {
-  const int e = blockIdx.z, m0 = blockIdx.y * 128, n0 = blockIdx.x * 128;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[WG_NS * WG_STAGE];
+  // work chunk: a group's whole row range, or one piece of it (split K)
+  const int z = blockIdx.z;
+  if (z >= p.chunks[0]) return;
+  const int4 ch = ((const int4*)(p.chunks + 4))[z];   // expert, first row, end row, partial
+  const int e = ch.x, s0 = ch.y, s1 = ch.z;
+  const int m0 = blockIdx.y * 128, n0 = blockIdx.x * 128;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int s0 = p.indptr[e], s1 = p.indptr[e + 1];
-  const int g8 = (lane >> 4) * 8, l16 = lane & 15;
-  const uint16_t* arow[4];
-  const uint16_t* brow[4];
+  const int g = lane >> 4, l16 = lane & 15;
+  const int sb = s0 & ~31;                 // first 32-aligned step
+  const int steps = s1 > s0 ? (s1 - sb + 31) / 32 : 0;
+  // this lane's DMA sources: in each of the wave's two 16-row blocks of a
+  // and of b, row lane/4 of the block and the chunk that lands at LDS
+  // position lane (its swizzled place)
+  const uint16_t* asrc[2];
+  const uint16_t* bsrc[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    arow[i] = p.a + (size_t)(m0 + wm * 64 + i * 16 + l16) * p.lda;
-    brow[i] = p.b + (size_t)(n0 + wn * 64 + i * 16 + l16) * p.ldb;
+  for (int j = 0; j < 2; ++j) {
+    const int row = (wave * 2 + j) * 16 + (lane >> 2);
+    const int chunk = (lane & 3) ^ ((row >> 1) & 3);
+    asrc[j] = p.a + (size_t)(m0 + row) * p.lda + sb + chunk * 8;
+    bsrc[j] = p.b + (size_t)(n0 + row) * p.ldb + sb + chunk * 8;
   }
+  auto issue = [&](int st) {
+    uint8_t* stg = ring + (st % WG_NS) * WG_STAGE;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dma16(asrc[j] + st * 32, stg + (wave * 2 + j) * 1024);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dma16(bsrc[j] + st * 32, stg + 8192 + (wave * 2 + j) * 1024);
+  };
   f32x4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  const int sb = s0 & ~31;                 // first 32-aligned step
-  const int steps = s1 > s0 ? (s1 - sb + 31) / 32 : 0;
-  u16x8 fa[4], fb[4], na[4], nb[4];
-  auto load = [&](int st, u16x8* A, u16x8* B) {
-    const int c = sb + st * 32 + g8;        // this lane's 8 slots
+  for (int q = 0; q < WG_NS - 1 && q < steps; ++q) issue(q);
+  for (int st = 0; st < steps; ++st) {
+    const int later = steps - 1 - st < WG_NS - 2 ? steps - 1 - st : WG_NS - 2;
+    wait_vm_steps(4 * later);   // this step's stage has landed (this wave's part)
+    raw_barrier();              // ... and every wave's; the previous stage is free
+    if (st + WG_NS - 1 < steps) issue(st + WG_NS - 1);
+    const uint8_t* stg = ring + (st % WG_NS) * WG_STAGE;
+    u16x8 fa[4], fb[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      A[i] = *(const u16x8*)(arow[i] + c);
-      B[i] = *(const u16x8*)(brow[i] + c);
-    }
-    if (c < s0 || c + 8 > s1) {            // a chunk at the group's ends
+    for (int i = 0; i < 4; ++i) fa[i] = *(const u16x8*)(stg + swz64(wm * 64 + i * 16 + l16, g));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[j] = *(const u16x8*)(stg + 8192 + swz64(wn * 64 + j * 16 + l16, g));
+    const int c = sb + st * 32 + 8 * g;      // this lane's 8 slots
+    if (c < s0 || c + 8 > s1) {             // a chunk at the range's ends
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-          if (c + q < s0 || c + q >= s1) A[i][q] = 0;
+          if (c + q < s0 || c + q >= s1) fa[i][q] = 0;
     }
-  };
-  if (steps > 0) load(0, fa, fb);
-  for (int st = 0; st < steps; ++st) {
-    if (st + 1 < steps) load(st + 1, na, nb);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(as_bf16x8(fa[i]), as_bf16x8(fb[j]), acc[i][j]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      fa[i] = na[i];
-      fb[i] = nb[i];
-    }
   }
-  float* out = p.out + (size_t)e * p.M * p.N;
+  float* out = ch.w < 0 ? p.out + (size_t)e * p.M * p.N : p.partial + (size_t)ch.w * p.M * p.N;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int m = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + r;
+      const int m = m0 + wm * 64 + i * 16 + g * 4 + r;
       float* o = out + (size_t)m * p.N + n0 + wn * 64 + l16;
 #pragma unroll
       for (int j = 0; j < 4; ++j) o[j * 16] = acc[i][j][r];
     }
+}
+
+// Work chunks of the weight-gradient GEMM, from the group offsets: each
+// expert's rows in pieces of at most `piece` rows (one piece, possibly
+// empty, for an expert without rows).  Entry i: (expert, first row, end row,
+// partial index), partial index -1 for an expert's first piece (written to
+// the output) and consecutive indices for the rest; per expert its piece
+// count and first partial index.  One 256-thread block, a thread per
+// expert, exclusive scans of the piece and partial counts in LDS (E <= 256).
+__global__ void __launch_bounds__(256) k_bwd_chunks(const int32_t* indptr, int E, int piece,
+                                                    int32_t* chunks, int32_t* nch, int32_t* pbase,
+                                                    int32_t* multi) {
+  __shared__ int sp[256], sq[256], sm[256];
+  const int e = threadIdx.x;
+  int s0 = 0, s1 = 0, pieces = 0;
+  if (e < E) {
+    s0 = indptr[e];
+    s1 = indptr[e + 1];
+    pieces = s1 > s0 ? (s1 - s0 + piece - 1) / piece : 1;
+  }
+  sp[e] = pieces;
+  sq[e] = pieces > 0 ? pieces - 1 : 0;
+  sm[e] = pieces > 1;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {      // inclusive scans
+    const int a = e >= o ? sp[e - o] : 0, b = e >= o ? sq[e - o] : 0, c = e >= o ? sm[e - o] : 0;
+    __syncthreads();
+    sp[e] += a;
+    sq[e] += b;
+    sm[e] += c;
+    __syncthreads();
+  }
+  if (pieces > 1) multi[sm[e]] = e;         // experts split in pieces, from multi[1]
+  if (e == 255) multi[0] = sm[255];
+  if (e < E) {
+    const int first = sp[e] - pieces, pfirst = sq[e] - (pieces - 1);
+    nch[e] = pieces;
+    pbase[e] = pfirst;
+    int4* tab = (int4*)(chunks + 4);
+    for (int c = 0; c < pieces; ++c) {
+      const int a = s0 + c * piece, b = a + piece < s1 ? a + piece : s1;
+      tab[first + c] = make_int4(e, a, b > a ? b : a, c == 0 ? -1 : pfirst + c - 1);
+    }
+  }
+  if (e == 255) chunks[0] = sp[255];
+}
+
+// out[e] += partial pieces 1.. of expert e, in piece order (a fixed order,
+// so the sum is reproducible), for the experts the chunk table lists as
+// split.  Four elements per thread.
+__global__ void __launch_bounds__(BT) k_bwd_wgrad_reduce(BwdWgrad p) {
+  const size_t MN = (size_t)p.M * p.N;
+  const size_t i = ((size_t)blockIdx.x * BT + threadIdx.x) * 4;
+  if (i >= MN) return;
+  const int nm = p.multi[0];
+  for (int q = 0; q < nm; ++q) {
+    const int e = p.multi[1 + q], n = p.nch[e];
+    f32x4* o = (f32x4*)(p.out + e * MN + i);
+    f32x4 a = *o;
+    for (int c = 0; c < n - 1; ++c) a += *(const f32x4*)(p.partial + (size_t)(p.pbase[e] + c) * MN + i);
+    *o = a;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -304,9 +412,24 @@ hipError_t launch_bwd_transpose(const BwdTranspose& a, int nz, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_wgrad(const BwdWgrad& a, int E, hipStream_t st) {
-  if (a.M % 128 || a.N % 128 || E <= 0 || a.lda % 8 || a.ldb % 8) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_bwd_wgrad, dim3(a.N / 128, a.M / 128, E), dim3(BT), 0, st, a);
+hipError_t launch_bwd_chunks(const int32_t* indptr, int E, int piece, int32_t* chunks,
+                             int32_t* nch, int32_t* pbase, int32_t* multi, hipStream_t st) {
+  if (E <= 0 || piece <= 0) return hipErrorInvalidValue;
+  if (E > 256) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_bwd_chunks, dim3(1), dim3(256), 0, st, indptr, E, piece, chunks, nch, pbase,
+                     multi);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_wgrad(const BwdWgrad& a, int E, int max_chunks, hipStream_t st) {
+  if (a.M % 128 || a.N % 128 || E <= 0 || max_chunks <= 0 || a.lda % 8 || a.ldb % 8)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_bwd_wgrad, dim3(a.N / 128, a.M / 128, max_chunks), dim3(BT), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || max_chunks == E) return e;   // one piece per expert: nothing to add
+  const size_t MN = (size_t)a.M * a.N;
+  hipLaunchKernelGGL(k_bwd_wgrad_reduce, dim3((unsigned)((MN / 4 + BT - 1) / BT)), dim3(BT), 0,
+                     st, a);
   return hipGetLastError();
 }
 

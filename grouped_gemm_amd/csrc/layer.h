@@ -279,14 +279,21 @@ struct BwdTranspose {
 // (zeros for experts without rows).  M, N multiples of 128; lda, ldb
 // multiples of 8 and at least the rows rounded up to 32, that padding
 // finite.
+// Work comes from a chunk table (launch_bwd_chunks): each expert's rows in
+// pieces; an expert's first piece writes out[e], the others partial
+// buffers that a second pass adds to out[e] in piece order.
 struct BwdWgrad {
   const uint16_t* a;
   long lda;
   const uint16_t* b;
   long ldb;
-  const int32_t* indptr;
+  const int32_t* chunks;   // [0]: count; from [4]: (expert, row0, row1, partial) per chunk
+  const int32_t* nch;      // [E] pieces per expert
+  const int32_t* pbase;    // [E] first partial index per expert
+  const int32_t* multi;    // [0]: count; from [1]: the experts in more than one piece
   int M, N;
   float* out;
+  float* partial;          // [partials, M, N]
 };
 // Per-slot pass of the backward (see backward.hip).
 struct BwdSlot {
@@ -317,7 +324,10 @@ struct RouterBwd {
   float* ds;               // [T, E]
 };
 hipError_t launch_bwd_transpose(const BwdTranspose& a, int nz, hipStream_t st);
-hipError_t launch_bwd_wgrad(const BwdWgrad& a, int E, hipStream_t st);
+hipError_t launch_bwd_chunks(const int32_t* indptr, int E, int piece, int32_t* chunks,
+                             int32_t* nch, int32_t* pbase, int32_t* multi, hipStream_t st);
+// max_chunks: the grid's bound on chunks (E when every expert is one piece)
+hipError_t launch_bwd_wgrad(const BwdWgrad& a, int E, int max_chunks, hipStream_t st);
 hipError_t launch_bwd_slot(const BwdSlot& a, int max_rows, hipStream_t st);
 hipError_t launch_bwd_dx(const BwdDx& a, hipStream_t st);
 hipError_t launch_router_bwd(const RouterBwd& a, hipStream_t st);

@@ -710,9 +710,20 @@ int moe_dispatch_noalloc(const int32_t* topk_ids, int T, int k, int E, int32_t* 
 namespace {
 
 struct BwdScratch {
-  size_t G, U, R, Hb, DGU, DA, WdT, WguT, XgT, DOT, HbT, DGUT, total;
-  long ldo;   // feature-major rows: slots padded to a multiple of 64
+  size_t G, U, R, Hb, DGU, DA, WdT, WguT, XgT, DOT, HbT, DGUT, chunks, nch, pbase, multi, partial,
+      total;
+  long ldo;        // feature-major rows: slots padded to a multiple of 64
+  int piece;       // rows per weight-gradient work chunk
+  int max_chunks;  // bound on the chunks
 };
+
+// Weight gradients of shapes with few 128 x 128 output blocks per expert
+// split each expert's rows into pieces of 1024 (so that a hot expert's
+// rows spread over many workgroups); larger shapes keep one piece per expert.
+int bwd_piece(const moe_layer_desc& d) {
+  const long tiles = (long)(d.hidden / 128) * (d.inter / 128);
+  return tiles < 256 ? 1024 : (1 << 30);
+}
 
 BwdScratch bwd_scratch(const moe_layer_desc& d) {
   const size_t S = (size_t)d.max_tokens * d.top_k, I = d.inter, H = d.hidden, E = d.num_experts;
@@ -737,6 +748,14 @@ BwdScratch bwd_scratch(const moe_layer_desc& d) {
   b.DOT = take(H * L * 2);            // w dy, feature-major [H, ldo]
   b.HbT = take(I * L * 2);            // h, feature-major [I, ldo]
   b.DGUT = take(2 * I * L * 2);       // dg | du, feature-major [2 I, ldo]
+  b.piece = bwd_piece(d);
+  const size_t extra = b.piece < (1 << 30) ? (S + b.piece - 1) / b.piece : 0;
+  b.max_chunks = (int)(E + extra);
+  b.chunks = take(4 * (4 + 4 * (size_t)b.max_chunks));
+  b.nch = take(4 * E);
+  b.pbase = take(4 * E);
+  b.multi = take(4 * (E + 1));
+  b.partial = take(extra * H * I * 4);
   b.total = off;
   return b;
 }
@@ -927,8 +946,17 @@ int moe_expert_backward(moe_ws* ws, const moe_weights* w, const void* x, const i
   ta.scale = nullptr;
   ta.out = HbT;
   HIP_TRY(launch_bwd_transpose(ta, 1, st), "slot transpose launch");
+  int32_t* chunks = (int32_t*)(sc + b.chunks);
+  int32_t* nch = (int32_t*)(sc + b.nch);
+  int32_t* pbase = (int32_t*)(sc + b.pbase);
+  int32_t* multi = (int32_t*)(sc + b.multi);
+  HIP_TRY(launch_bwd_chunks(indptr, E, b.piece, chunks, nch, pbase, multi, st), "chunk table launch");
   BwdWgrad wg{};
-  wg.indptr = indptr;
+  wg.chunks = chunks;
+  wg.nch = nch;
+  wg.pbase = pbase;
+  wg.multi = multi;
+  wg.partial = (float*)(sc + b.partial);
   wg.a = DOT;
   wg.lda = b.ldo;
   wg.b = HbT;
@@ -936,7 +964,7 @@ int moe_expert_backward(moe_ws* ws, const moe_weights* w, const void* x, const i
   wg.M = H;
   wg.N = I;
   wg.out = d_w_down;
-  HIP_TRY(launch_bwd_wgrad(wg, E, st), "down weight-gradient launch");
+  HIP_TRY(launch_bwd_wgrad(wg, E, b.max_chunks, st), "down weight-gradient launch");
   HIP_TRY(mark(12, 1), "event record");
   HIP_TRY(mark(13, 0), "event record");
   ta.in = (const uint16_t*)x;           // x, gathered by token
@@ -957,11 +985,11 @@ int moe_expert_backward(moe_ws* ws, const moe_weights* w, const void* x, const i
   if (!relu2) {
     wg.a = DGUT;
     wg.out = d_w_gate;
-    HIP_TRY(launch_bwd_wgrad(wg, E, st), "gate weight-gradient launch");
+    HIP_TRY(launch_bwd_wgrad(wg, E, b.max_chunks, st), "gate weight-gradient launch");
   }
   wg.a = DGUT + (size_t)I * b.ldo;
   wg.out = d_w_up;
-  HIP_TRY(launch_bwd_wgrad(wg, E, st), "up weight-gradient launch");
+  HIP_TRY(launch_bwd_wgrad(wg, E, b.max_chunks, st), "up weight-gradient launch");
   HIP_TRY(mark(13, 1), "event record");
   return MOE_OK;
 }
