@@ -284,6 +284,7 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
   const uint8_t* ib_ws = nullptr;          // weight scales (BLK: lane-selected block; MX: wave's matrix)
   uint32_t toff[NTOK];
   uint32_t aoff = 0;
+  const uint8_t* ib_sc = nullptr;          // FP8 1x128: this lane's per-step scale source
 
   const int mrow = wave * 64 + lane;       // metadata row of this lane
   const bool mwave = wave < MW;
@@ -335,6 +336,7 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
       if (GATEUP) s1 = (const uint8_t*)(it.sh ? p.sh_w1s : p.w1s) + so + blk;
       else s1 = NR > 128 ? s0 + (size_t)(K / 128) * 4 : s0;
       ib_ws = (lane & 1) ? s1 : s0;
+      ib_sc = wave == NW - 1 ? ib_ws : ib_a + aoff;
     }
     if constexpr (F == F_MX) {
       const size_t so = it.sh ? 0 : (size_t)it.g * N * (K / 32);
@@ -393,10 +395,9 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
       asm volatile("" : "+v"(wo));
       lds_dma16(ib_w + (size_t)jj * RPI * wrow + wo, st + PC::TOKB + (wave * NWT + jj) * 1024);
     } else if constexpr (F == F_FP8_BLK) {
-      if (wave == NW - 1)   // the step's weight block scales (lanes 0 and 1)
-        lds_dma4(ib_ws, st + PC::TOKB + PC::WTB + (NW - 1) * 256);
-      else
-        lds_dma4(ib_a + aoff, st + PC::TOKB + PC::WTB + wave * 256);
+      // activation scales of the step's rows; the last wave, the step's
+      // weight block scales (lanes 0 and 1)
+      lds_dma4(ib_sc, st + PC::TOKB + PC::WTB + wave * 256);
     } else if constexpr (F == F_MX) {
       if (k == NTOK + NWT)
         lds_dma4(ib_a + aoff, st + PC::TOKB + PC::WTB + wave * 256);
@@ -409,20 +410,27 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
     ib_w += PC::WROWB;
     ib_a += 4;
     ib_ws += 4;
+    ib_sc += 4;
   };
   auto issue = [&](int slot) {
 #pragma unroll
     for (int k = 0; k < NP; ++k) issue_part(slot, k);
-    advance();
   };
 
-  // ---- start: row indices of the first item, then the first D stages
+  // ---- start: row indices of the first item, then the first D stages.
+  // The bases point at the stage to issue next: begin_item sets them to an
+  // item's first step, advance() moves them on after a stage whose item
+  // has more steps (after an item's last stage they stay where they are, so
+  // the loads past the last item read valid addresses again).
   meta_rows(0);
   wait_vm(0);
   raw_barrier();
   begin_item(0);
   meta_rows(1);
-  for (int q = 0; q < D; ++q) issue(q);
+  for (int q = 0; q < D; ++q) {
+    issue(q);
+    if (q + 1 < ns) advance();
+  }
 
   f32x4 acc[NM][RT][TT];
 #pragma unroll
@@ -449,12 +457,11 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
     // loads issued with an item start among the stages ahead are not
     // counted either (the wait then also covers a few loads of the next
     // stage, once per item).
-    {
-      const int ahead = min(D - 1, nq - 1 - q);
-      if (ahead == 0) wait_vm_c<0>();
-      else if (ahead == NSTAGE - 2) wait_vm_c<(NSTAGE - 2) * LOADS>();
-      else wait_vm_ab<LOADS, 0, NSTAGE - 3>(ahead, false);
-    }
+    // Every step issues one stage, also past the last item (then it loads
+    // the last issued stage's addresses again into the slot no remaining
+    // step reads), so D - 1 stages always follow stage q.
+    if (D == NSTAGE - 1) wait_vm_c<(NSTAGE - 2) * LOADS>();
+    else wait_vm_ab<LOADS, 0, NSTAGE - 3>(D - 1, false);
     raw_barrier();
     // the stage this step issues (into the slot every wave has finished
     // reading: the barrier above), spread over the MFMA groups below
@@ -470,16 +477,26 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
         si = 0;
         ++ji;
       }
-      // MX weights (half the bytes per row) measure faster issued at once
-      if constexpr (!SPREAD) {
+    }
+    // MX weights (half the bytes per row) measure faster issued at once
+    if constexpr (!SPREAD) {
 #pragma unroll
-        for (int k = 0; k < NP; ++k) issue_part(islot, k);
-      }
+      for (int k = 0; k < NP; ++k) issue_part(islot, k);
     }
     const uint8_t* st = lds + cs * PC::STAGE;
     cs = cs + 1 == NSTAGE ? 0 : cs + 1;
     // every fragment of the step is read from LDS up front, so the reads
     // overlap each other and the MFMAs wait only for their own operands
+    // (the step's scales first, then the token fragments, then the weight
+    // fragments in MFMA group order)
+    float sa_raw[TT], sw_raw[NM];
+    if constexpr (F == F_FP8_BLK) {
+      const float* scl = (const float*)(st + PC::TOKB + PC::WTB);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) sw_raw[m] = scl[(NW - 1) * 64 + (GATEUP ? m : (wrow0 / 128))];
+#pragma unroll
+      for (int t = 0; t < TT; ++t) sa_raw[t] = scl[trow0 + t * 16 + r16];
+    }
     i32x8 bfr[TT];
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
@@ -512,14 +529,9 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
       // (activation scale x weight block scale).  Products of one weight
       // row tile go to one of two register sets, and the scaling of one
       // set runs while the MFMAs of the other are in flight.
-      const float* scl = (const float*)(st + PC::TOKB + PC::WTB);
+      // (the scale products are formed after the first MFMA groups, so
+      // those wait only for their fragments)
       float sc[NM][TT];
-#pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        const float wsc = scl[(NW - 1) * 64 + (GATEUP ? m : (wrow0 / 128))];
-#pragma unroll
-        for (int t = 0; t < TT; ++t) sc[m][t] = scl[trow0 + t * 16 + r16] * wsc;
-      }
       constexpr int NC = NM * RT;
       f32x4 d[2][TT];
       constexpr int PPC = (NP + NC - 1) / NC;   // DMA parts per MFMA group
@@ -529,15 +541,19 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
 #pragma unroll
       for (int c = 0; c <= NC; ++c) {
         if (c < NC) {
-          if (iss) {
 #pragma unroll
-            for (int k = c * PPC; k < (c + 1) * PPC && k < NP; ++k) issue_part(islot, k);
-          }
+          for (int k = c * PPC; k < (c + 1) * PPC && k < NP; ++k) issue_part(islot, k);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int t = 0; t < TT; ++t)
             d[c & 1][t] = mfma_f8(afr[c / RT][c % RT], bfr[t], (f32x4){0.f, 0.f, 0.f, 0.f});
           __builtin_amdgcn_sched_barrier(0);
+        }
+        if (c == 1) {
+#pragma unroll
+          for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int t = 0; t < TT; ++t) sc[m][t] = sa_raw[t] * sw_raw[m];
         }
         if (c > 0) {
           const int pc = c - 1, pm = pc / RT, prt = pc % RT;
@@ -559,7 +575,7 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           const int c = m * RT + rt;
-          if (SPREAD && iss) {
+          if (SPREAD) {
 #pragma unroll
             for (int k = c * PPC; k < (c + 1) * PPC && k < NP; ++k) issue_part(islot, k);
           }
@@ -574,7 +590,7 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
           __builtin_amdgcn_sched_barrier(0);
         }
     }
-    if (iss) advance();
+    if (iss && si != 0) advance();
     if (++s < ns) continue;
 
     // ------------------------------------------------------------ epilogue
@@ -803,6 +819,9 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
 #pragma unroll
         for (int t = 0; t < TT; ++t) acc[m][rt][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
+  // the stages issued past the last item land before the workgroup's LDS is
+  // released
+  wait_vm_c<0>();
 }
 
 // Tile shape of each row-block height (per format and op):
