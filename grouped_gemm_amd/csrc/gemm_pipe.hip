@@ -217,7 +217,10 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
   const int n_items = ldu(p.meta + META_NTILES) * nblk;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave % WM, wn = wave / WM;
+  // waves w and w + NW/2 share a SIMD; with two row halves (WM = 2) they
+  // hold different halves, so a block whose rows end in the first half
+  // leaves each SIMD one wave of MFMA work
+  const int wm = wave / WN, wn = wave % WN;
   const int r16 = lane & 15, lg = lane >> 4;
   const uint32_t wrow = (uint32_t)row_bytes<WB>(K), xrow = (uint32_t)K;   // token rows: e4m3
   const int ns = K / 128;
@@ -285,6 +288,7 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
   uint32_t toff[NTOK];
   uint32_t aoff = 0;
   const uint8_t* ib_sc = nullptr;          // FP8 1x128: this lane's per-step scale source
+  int m_even = 0, m_odd = 0;               // rows of the last begun items, by parity
 
   const int mrow = wave * 64 + lane;       // metadata row of this lane
   const bool mwave = wave < MW;
@@ -307,6 +311,8 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
   // per-channel weight scales
   auto begin_item = [&](int j) {
     const It it = info(j);
+    if (j & 1) m_odd = it.M;
+    else m_even = it.M;
     const int32_t* ix = idx_l + (j & 1) * RB;
     const bool gat = p.gather != nullptr;
     ib_tok = gat ? p.a : p.a + (size_t)it.m0 * xrow;
@@ -485,110 +491,132 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
     }
     const uint8_t* st = lds + cs * PC::STAGE;
     cs = cs + 1 == NSTAGE ? 0 : cs + 1;
-    // every fragment of the step is read from LDS up front, so the reads
-    // overlap each other and the MFMAs wait only for their own operands
-    // (the step's scales first, then the token fragments, then the weight
-    // fragments in MFMA group order)
-    float sa_raw[TT], sw_raw[NM];
-    if constexpr (F == F_FP8_BLK) {
-      const float* scl = (const float*)(st + PC::TOKB + PC::WTB);
-#pragma unroll
-      for (int m = 0; m < NM; ++m) sw_raw[m] = scl[(NW - 1) * 64 + (GATEUP ? m : (wrow0 / 128))];
-#pragma unroll
-      for (int t = 0; t < TT; ++t) sa_raw[t] = scl[trow0 + t * 16 + r16];
-    }
-    i32x8 bfr[TT];
-#pragma unroll
-    for (int t = 0; t < TT; ++t) {
-      const int row = trow0 + t * 16 + r16;
-      const i32x4 lo = *(const i32x4*)(st + swz128(row, lg));
-      const i32x4 hi = *(const i32x4*)(st + swz128(row, lg + 4));
-      bfr[t] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    }
-    i32x8 afr[NM][RT];
-    int sw[NM][RT];
-#pragma unroll
-    for (int m = 0; m < NM; ++m)
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int R = m * NBC + wrow0 + rt * 16 + r16;     // LDS weight row of this lane
-        sw[m][rt] = 0;
-        if constexpr (WB == 8) {
-          const i32x4 lo = *(const i32x4*)(st + PC::TOKB + swz128(R, lg));
-          const i32x4 hi = *(const i32x4*)(st + PC::TOKB + swz128(R, lg + 4));
-          afr[m][rt] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        } else {
-          const i32x4 qv = *(const i32x4*)(st + PC::TOKB + swz64(R, lg));
-          afr[m][rt] = (i32x8){qv[0], qv[1], qv[2], qv[3], 0, 0, 0, 0};
-          sw[m][rt] = (st + PC::TOKB + PC::WTB + PC::ASB)[R * 4 + lg];
-        }
-      }
-    if constexpr (F == F_FP8_BLK) {
-      // 128x128 block scaling: each K step is one scale block, so every
-      // product is formed unscaled and then added with its row's
-      // (activation scale x weight block scale).  Products of one weight
-      // row tile go to one of two register sets, and the scaling of one
-      // set runs while the MFMAs of the other are in flight.
-      // (the scale products are formed after the first MFMA groups, so
-      // those wait only for their fragments)
-      float sc[NM][TT];
-      constexpr int NC = NM * RT;
-      f32x4 d[2][TT];
-      constexpr int PPC = (NP + NC - 1) / NC;   // DMA parts per MFMA group
-      // a wave issuing its MFMA groups goes first, so the other wave of the
-      // SIMD fills the gaps with its LDS reads and scaling (measured ~2%)
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int c = 0; c <= NC; ++c) {
-        if (c < NC) {
-#pragma unroll
-          for (int k = c * PPC; k < (c + 1) * PPC && k < NP; ++k) issue_part(islot, k);
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int t = 0; t < TT; ++t)
-            d[c & 1][t] = mfma_f8(afr[c / RT][c % RT], bfr[t], (f32x4){0.f, 0.f, 0.f, 0.f});
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if (c == 1) {
-#pragma unroll
-          for (int m = 0; m < NM; ++m)
-#pragma unroll
-            for (int t = 0; t < TT; ++t) sc[m][t] = sa_raw[t] * sw_raw[m];
-        }
-        if (c > 0) {
-          const int pc = c - 1, pm = pc / RT, prt = pc % RT;
-#pragma unroll
-          for (int t = 0; t < TT; ++t) acc[pm][prt][t] += d[pc & 1][t] * sc[pm][t];
-        }
-      }
-      __builtin_amdgcn_s_setprio(0);
-    } else {
-      int sbx[TT];
-      if constexpr (F == F_MX) {
-#pragma unroll
-        for (int t = 0; t < TT; ++t) sbx[t] = (st + PC::TOKB + PC::WTB)[(trow0 + t * 16 + r16) * 4 + lg];
-      }
+    // The step's work for the wave's first NT 16-row token tiles (the
+    // others lie past the item's last row and are skipped; the stage is
+    // issued the same way in every variant).  Every fragment is read from
+    // LDS up front, so the reads overlap each other and the MFMAs wait only
+    // for their own operands (the step's scales first, then the token
+    // fragments, then the weight fragments in MFMA group order).
+    auto compute = [&](auto ntc) {
+      constexpr int NT = decltype(ntc)::value;
       constexpr int NC = NM * RT;
       constexpr int PPC = (NP + NC - 1) / NC;   // DMA parts per MFMA group
+      if constexpr (NT == 0) {
+        if constexpr (SPREAD) {
+#pragma unroll
+          for (int k = 0; k < NP; ++k) issue_part(islot, k);
+        }
+        return;
+      } else {
+      float sa_raw[NT], sw_raw[NM];
+      if constexpr (F == F_FP8_BLK) {
+        const float* scl = (const float*)(st + PC::TOKB + PC::WTB);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) sw_raw[m] = scl[(NW - 1) * 64 + (GATEUP ? m : (wrow0 / 128))];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) sa_raw[t] = scl[trow0 + t * 16 + r16];
+      }
+      i32x8 bfr[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int row = trow0 + t * 16 + r16;
+        const i32x4 lo = *(const i32x4*)(st + swz128(row, lg));
+        const i32x4 hi = *(const i32x4*)(st + swz128(row, lg + 4));
+        bfr[t] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+      i32x8 afr[NM][RT];
+      int sw[NM][RT];
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-          const int c = m * RT + rt;
-          if (SPREAD) {
+          const int R = m * NBC + wrow0 + rt * 16 + r16;     // LDS weight row of this lane
+          sw[m][rt] = 0;
+          if constexpr (WB == 8) {
+            const i32x4 lo = *(const i32x4*)(st + PC::TOKB + swz128(R, lg));
+            const i32x4 hi = *(const i32x4*)(st + PC::TOKB + swz128(R, lg + 4));
+            afr[m][rt] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          } else {
+            const i32x4 qv = *(const i32x4*)(st + PC::TOKB + swz64(R, lg));
+            afr[m][rt] = (i32x8){qv[0], qv[1], qv[2], qv[3], 0, 0, 0, 0};
+            sw[m][rt] = (st + PC::TOKB + PC::WTB + PC::ASB)[R * 4 + lg];
+          }
+        }
+      if constexpr (F == F_FP8_BLK) {
+        // 128x128 block scaling: each K step is one scale block, so every
+        // product is formed unscaled and then added with its row's
+        // (activation scale x weight block scale).  Products of one weight
+        // row tile go to one of two register sets, and the scaling of one
+        // set runs while the MFMAs of the other are in flight (the scale
+        // products are formed after the first MFMA groups, so those wait
+        // only for their fragments).
+        float sc[NM][NT];
+        f32x4 d[2][NT];
+        // a wave issuing its MFMA groups goes first, so the other wave of
+        // the SIMD fills the gaps with its LDS reads and scaling
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int c = 0; c <= NC; ++c) {
+          if (c < NC) {
 #pragma unroll
             for (int k = c * PPC; k < (c + 1) * PPC && k < NP; ++k) issue_part(islot, k);
-          }
-          __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int t = 0; t < TT; ++t) {
-            if constexpr (F == F_MX)
-              acc[m][rt][t] = mfma_f4f8_scaled(afr[m][rt], bfr[t], acc[m][rt][t], sw[m][rt], sbx[t]);
-            else
-              acc[m][rt][t] = mfma_f8(afr[m][rt], bfr[t], acc[m][rt][t]);
+            for (int t = 0; t < NT; ++t)
+              d[c & 1][t] = mfma_f8(afr[c / RT][c % RT], bfr[t], (f32x4){0.f, 0.f, 0.f, 0.f});
+            __builtin_amdgcn_sched_barrier(0);
           }
-          __builtin_amdgcn_sched_barrier(0);
+          if (c == 1) {
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+#pragma unroll
+              for (int t = 0; t < NT; ++t) sc[m][t] = sa_raw[t] * sw_raw[m];
+          }
+          if (c > 0) {
+            const int pc = c - 1, pm = pc / RT, prt = pc % RT;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[pm][prt][t] += d[pc & 1][t] * sc[pm][t];
+          }
         }
+        __builtin_amdgcn_s_setprio(0);
+      } else {
+        int sbx[NT];
+        if constexpr (F == F_MX) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t) sbx[t] = (st + PC::TOKB + PC::WTB)[(trow0 + t * 16 + r16) * 4 + lg];
+        }
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            const int c = m * RT + rt;
+            if (SPREAD) {
+#pragma unroll
+              for (int k = c * PPC; k < (c + 1) * PPC && k < NP; ++k) issue_part(islot, k);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+              if constexpr (F == F_MX)
+                acc[m][rt][t] = mfma_f4f8_scaled(afr[m][rt], bfr[t], acc[m][rt][t], sw[m][rt], sbx[t]);
+              else
+                acc[m][rt][t] = mfma_f8(afr[m][rt], bfr[t], acc[m][rt][t]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+      }
+      }
+    };
+    // Blocks split into two row halves: a wave whose half holds no row of
+    // the item (rows are padded to 128 per block, and most of the padding
+    // sits in the blocks of experts with few tokens) only issues its
+    // stage loads.  (Finer variants, per 16-row tile, cost register copies
+    // of the accumulators at every step.)
+    if constexpr (WM > 1) {
+      if (((j & 1) ? m_odd : m_even) <= trow0) compute(std::integral_constant<int, 0>{});
+      else compute(std::integral_constant<int, TT>{});
+    } else {
+      compute(std::integral_constant<int, TT>{});
     }
     if (iss && si != 0) advance();
     if (++s < ns) continue;
