@@ -369,8 +369,8 @@ __global__ void __launch_bounds__(BT) k_bwd_dx(BwdDx p) {
     a += *(const f32x4*)(p.DA + (size_t)slot * p.H + c);
   }
   uint2 v;
-  v.x = (uint32_t)f32_to_bf16(a[0]) | ((uint32_t)f32_to_bf16(a[1]) << 16);
-  v.y = (uint32_t)f32_to_bf16(a[2]) | ((uint32_t)f32_to_bf16(a[3]) << 16);
+  v.x = pack_bf16x2(a[0], a[1]);
+  v.y = pack_bf16x2(a[2], a[3]);
   *(uint2*)(p.dx + (size_t)t * p.H + c) = v;
 }
 

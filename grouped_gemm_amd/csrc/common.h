@@ -43,11 +43,14 @@ enum Fmt { F_BF16 = 0, F_FP8_CH = 1, F_FP8_BLK = 2, F_MX = 3 };
 DEVI float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // Round to nearest even (finite inputs).
-DEVI uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// Two fp32 -> packed bf16 (lo in bits 0..15), round to nearest even: one
+// gfx950 pair conversion.
+DEVI uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
+DEVI uint16_t f32_to_bf16(float f) { return (uint16_t)pack_bf16x2(f, 0.0f); }
 
 // Two fp32 -> two OCP e4m3 codes (RNE).  The hardware conversion is exact
 // round-to-nearest-even inside the finite range; inputs are clamped to

@@ -205,8 +205,8 @@ struct DecodeItem {
 #pragma unroll
           for (int i = 0; i < 4; ++i) h[i] = gated_act<ACT>(a.act_limit, v0[i], v1[i]);
           if constexpr (F == F_BF16) {
-            const uint32_t lo = (uint32_t)f32_to_bf16(h[0]) | ((uint32_t)f32_to_bf16(h[1]) << 16);
-            const uint32_t hi = (uint32_t)f32_to_bf16(h[2]) | ((uint32_t)f32_to_bf16(h[3]) << 16);
+            const uint32_t lo = pack_bf16x2(h[0], h[1]);
+            const uint32_t hi = pack_bf16x2(h[2], h[3]);
             *(uint2*)((uint16_t*)a.h + (size_t)slot * a.I + n0) = make_uint2(lo, hi);
           } else {
             *(f32x4*)(a.h + (size_t)slot * a.I + n0) = h;
@@ -224,8 +224,8 @@ struct DecodeItem {
         } else {
           const float w = slot < a.T * a.k ? w_l[flat] : 1.0f;
           const f32x4 vw = v0 * w;
-          const uint32_t lo = (uint32_t)f32_to_bf16(vw[0]) | ((uint32_t)f32_to_bf16(vw[1]) << 16);
-          const uint32_t hi = (uint32_t)f32_to_bf16(vw[2]) | ((uint32_t)f32_to_bf16(vw[3]) << 16);
+          const uint32_t lo = pack_bf16x2(vw[0], vw[1]);
+          const uint32_t hi = pack_bf16x2(vw[2], vw[3]);
           *(uint2*)(a.out_slot + (size_t)slot * a.H + n0) = make_uint2(lo, hi);
         }
       }
@@ -418,7 +418,7 @@ __global__ void __launch_bounds__(DL_THREADS) k_decode_layer(DecodeArgs a) {
             uint32_t o[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-              o[i] = (uint32_t)f32_to_bf16(acc[2 * i]) | ((uint32_t)f32_to_bf16(acc[2 * i + 1]) << 16);
+              o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
             uint4* dst = (uint4*)(a.y + (size_t)tok * a.H + nb * 16);
             dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
             dst[1] = make_uint4(o[4], o[5], o[6], o[7]);

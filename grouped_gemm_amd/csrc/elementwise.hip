@@ -223,7 +223,7 @@ __global__ void __launch_bounds__(256) k_combine(CombineArgs c) {
     uint32_t p[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      p[i] = (uint32_t)f32_to_bf16(acc[2 * i]) | ((uint32_t)f32_to_bf16(acc[2 * i + 1]) << 16);
+      p[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
     *(uint4*)(c.y + (size_t)t * H + 8 * ch) = make_uint4(p[0], p[1], p[2], p[3]);
   }
 }

@@ -175,6 +175,29 @@ struct PipeCfg {
   static_assert(RT % 2 == 0 || BM < 128 || (GATEUP && F != F_FP8_BLK), "regrouped stores pair 16-channel tiles");
 };
 
+// Regrouping of two 16-channel MFMA output tiles (a: channels 0..15, b:
+// channels 16..31 of a 32-channel half; the lanes of 16-lane row g hold one
+// dword of channels 4g..4g+3 of each) into the layout where row g holds
+// channels 8g..8g+7 as two dwords (.x: 8g..8g+3, .y: 8g+4..8g+7).  Rows 0/1
+// take a's dwords of rows 0,1 / 2,3, rows 2/3 take b's.  Two gfx950 lane
+// swaps: the 32-lane swap exchanges a's rows 2,3 with b's rows 0,1, then
+// the 16-lane swap exchanges odd rows of the first result with even rows of
+// the second.  Every lane of the wave takes part.
+DEVI uint2 regroup32(uint32_t a, uint32_t b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  const auto q = __builtin_amdgcn_permlane16_swap(r[0], r[1], false, false);
+  return make_uint2(q[0], q[1]);
+}
+
+// Maximum over the four 16-lane rows (lanes l, l^16, l^32, l^48), in every
+// lane: a lane swap with itself pairs lane l with l^32, then with l^16.
+DEVI float max_over_rows(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+
 // byte offset of (row, 16-byte chunk) in a swizzled [rows][128 B] block
 DEVI int swz128(int row, int chunk) { return row * 128 + 16 * (chunk ^ (row & 7)); }
 // byte offset of (row, chunk) in a swizzled [rows][64 B] block
@@ -648,11 +671,9 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
     if constexpr (!GATEUP) {
       if (REGROUP && p.row_w) {
         // Weighted bf16 slot rows.  The MFMA layout gives a lane 4 channels
-        // of each 16-channel tile (16 rows x 32 B per store); four shuffles
+        // of each 16-channel tile (16 rows x 32 B per store); two lane swaps
         // per dword regroup them so lane lg holds channels 8lg..8lg+7 of
         // each 32-channel half, and each 16-byte store covers 16 rows x 64 B.
-        const int sA = r16 + 32 * (lg & 1), sB = sA + 16;   // lanes holding its channels
-        const bool hiq = lg >= 2;                            // second 16-channel tile of the half
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
           const int r = trow0 + t * 16 + r16;
@@ -662,18 +683,17 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) {
             const f32x4 vw = acc[0][rt][t] * w;
-            pk[rt][0] = (uint32_t)f32_to_bf16(vw[0]) | ((uint32_t)f32_to_bf16(vw[1]) << 16);
-            pk[rt][1] = (uint32_t)f32_to_bf16(vw[2]) | ((uint32_t)f32_to_bf16(vw[3]) << 16);
+            pk[rt][0] = pack_bf16x2(vw[0], vw[1]);
+            pk[rt][1] = pack_bf16x2(vw[2], vw[3]);
           }
 #pragma unroll
           for (int h = 0; h < RT / 2; ++h) {
             uint32_t o[4];
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
-              const uint32_t a0 = __shfl(pk[2 * h][x], sA, 64), a1 = __shfl(pk[2 * h + 1][x], sA, 64);
-              const uint32_t b0 = __shfl(pk[2 * h][x], sB, 64), b1 = __shfl(pk[2 * h + 1][x], sB, 64);
-              o[x] = hiq ? a1 : a0;
-              o[2 + x] = hiq ? b1 : b0;
+              const uint2 q = regroup32(pk[2 * h][x], pk[2 * h + 1][x]);
+              o[x] = q.x;
+              o[2 + x] = q.y;
             }
             if (r < M)
               *(uint4*)((uint16_t*)p.out + (size_t)slot * N + c0 + 32 * h + 8 * lg) =
@@ -693,8 +713,8 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
           if (p.row_w) {
             const float w = slot < p.row_w_n ? rwj[r] : 1.0f;
             const f32x4 vw = v * w;
-            const uint32_t lo = (uint32_t)f32_to_bf16(vw[0]) | ((uint32_t)f32_to_bf16(vw[1]) << 16);
-            const uint32_t hi = (uint32_t)f32_to_bf16(vw[2]) | ((uint32_t)f32_to_bf16(vw[3]) << 16);
+            const uint32_t lo = pack_bf16x2(vw[0], vw[1]);
+            const uint32_t hi = pack_bf16x2(vw[2], vw[3]);
             *(uint2*)((uint16_t*)p.out + (size_t)slot * N + n0) = make_uint2(lo, hi);
           } else {
             *(f32x4*)((float*)p.out + (size_t)slot * N + n0) = v;
@@ -738,8 +758,7 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
           for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(acc[0][rt][t][i]));
-          mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+          mx = max_over_rows(mx);
           if (lg == 0) amax_l[wn * BM + trow0 + t * 16 + r16] = mx;
         }
         // LDS-only exchange: the stage loads in flight must not be waited for
@@ -749,8 +768,6 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
         // codes regrouped as in the down projection's store: lane lg writes
         // channels 8lg..8lg+7 of each 32-channel half (16 rows x 32 B per
         // store instead of 16 rows x 16 B)
-        const int sA = r16 + 32 * (lg & 1), sB = sA + 16;
-        const bool hiq = lg >= 2;
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
           const int r = trow0 + t * 16 + r16;
@@ -768,9 +785,8 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
           uint8_t* orow = (uint8_t*)p.out + (size_t)(m0 + r) * N;
 #pragma unroll
           for (int hh = 0; hh < RT / 2; ++hh) {
-            const uint32_t a0 = __shfl(cd[2 * hh], sA, 64), a1 = __shfl(cd[2 * hh + 1], sA, 64);
-            const uint32_t b0 = __shfl(cd[2 * hh], sB, 64), b1 = __shfl(cd[2 * hh + 1], sB, 64);
-            if (r < M) *(uint2*)(orow + c0 + 32 * hh + 8 * lg) = make_uint2(hiq ? a1 : a0, hiq ? b1 : b0);
+            const uint2 q = regroup32(cd[2 * hh], cd[2 * hh + 1]);
+            if (r < M) *(uint2*)(orow + c0 + 32 * hh + 8 * lg) = q;
           }
           if (r < M && wn == 0 && lg == 0) ((float*)p.out_scale)[(size_t)(m0 + r) * (N / 128) + nb] = sc;
         }
@@ -782,8 +798,7 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
           for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(acc[0][rt][t][i]));
-          mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+          mx = max_over_rows(mx);
           if (lg == 0) amax_l[wn * BM + trow0 + t * 16 + r16] = mx;
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -819,8 +834,7 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
             for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
               for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(acc[0][2 * gp + qq][t][i]));
-            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            mx = max_over_rows(mx);
             int ex = mx > 0.f ? ilog2_floor(mx) - 8 : -127;
             ex = ex < -127 ? -127 : (ex > 127 ? 127 : ex);
             const float inv = __builtin_ldexpf(1.0f, -ex);

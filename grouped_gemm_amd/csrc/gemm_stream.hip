@@ -193,8 +193,8 @@ __global__ void __launch_bounds__(WAVES * 64) k_gemm_stream(GemmArgs p) {
             for (int i = 0; i < 4; ++i)
               h[i] = gated_act<ACT>(p.act_limit, v0[i], v1[i]);
             if (F == F_BF16) {
-              uint32_t lo = (uint32_t)f32_to_bf16(h[0]) | ((uint32_t)f32_to_bf16(h[1]) << 16);
-              uint32_t hi = (uint32_t)f32_to_bf16(h[2]) | ((uint32_t)f32_to_bf16(h[3]) << 16);
+              uint32_t lo = pack_bf16x2(h[0], h[1]);
+              uint32_t hi = pack_bf16x2(h[2], h[3]);
               *(uint2*)((uint16_t*)p.out + (size_t)slot * N + n0) = make_uint2(lo, hi);
             } else {
               *(f32x4*)((float*)p.out + (size_t)slot * N + n0) = h;

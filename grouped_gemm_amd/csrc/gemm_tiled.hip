@@ -301,8 +301,8 @@ __global__ void __launch_bounds__(THREADS) k_gemm_tiled(GemmArgs p) {
 #pragma unroll
           for (int rt = 0; rt < RTW; ++rt) {
             f32x4 h = acc[0][rt][t];
-            uint32_t lo = (uint32_t)f32_to_bf16(h[0]) | ((uint32_t)f32_to_bf16(h[1]) << 16);
-            uint32_t hi = (uint32_t)f32_to_bf16(h[2]) | ((uint32_t)f32_to_bf16(h[3]) << 16);
+            uint32_t lo = pack_bf16x2(h[0], h[1]);
+            uint32_t hi = pack_bf16x2(h[2], h[3]);
             *(uint2*)(orow + nw0 + rt * 16 + 4 * lg) = make_uint2(lo, hi);
           }
         }

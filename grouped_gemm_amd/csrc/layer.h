@@ -181,8 +181,8 @@ DEVI void store_down(const GemmArgs& p, int slot, int n0, f32x4 v) {
   if (p.row_w) {
     const float w = slot < p.row_w_n ? p.row_w[p.row_w_idx[slot]] : 1.0f;
     v = v * w;
-    uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-    uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    uint32_t lo = pack_bf16x2(v[0], v[1]);
+    uint32_t hi = pack_bf16x2(v[2], v[3]);
     *(uint2*)((uint16_t*)p.out + (size_t)slot * p.N + n0) = make_uint2(lo, hi);
   } else {
     *(f32x4*)((float*)p.out + (size_t)slot * p.N + n0) = v;
