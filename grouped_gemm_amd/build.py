@@ -53,6 +53,15 @@ def build(verbose: bool = False) -> str:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("link failed")
     os.replace(tmp, OUT)
+    # the rate probes (a standalone program; the library does not use it)
+    diag = os.path.join(HERE, "diag_rates")
+    cmd = [HIPCC, *FLAGS, "-mllvm", "-amdgpu-mfma-vgpr-form", os.path.join(CSRC, "diag_rates.hip"), "-o", diag + ".tmp"]
+    cmd = [c for c in cmd if c not in ("-fPIC", "-fvisibility=hidden")]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed on diag_rates.hip")
+    os.replace(diag + ".tmp", diag)
     if verbose:
         print("built", OUT)
     return OUT
