@@ -215,6 +215,15 @@ DEVI f32x4 mfma_f4f8_scaled(const i32x8& a, const i32x8& b, f32x4 c, int sa, int
 DEVI f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+// Two bf16 16x16x32 products over a 128-byte row chunk read as two 16-byte
+// halves per lane (dwords 0..3: K elements 8g..8g+7, dwords 4..7: 32+8g..;
+// g = lane / 16), the same lane layout as one 16x16x128 FP8 product's.
+DEVI f32x4 mfma_bf16_pair(const i32x8& a, const i32x8& b, f32x4 c) {
+  const i32x4 alo = {a[0], a[1], a[2], a[3]}, ahi = {a[4], a[5], a[6], a[7]};
+  const i32x4 blo = {b[0], b[1], b[2], b[3]}, bhi = {b[4], b[5], b[6], b[7]};
+  c = mfma_bf16(__builtin_bit_cast(bf16x8, alo), __builtin_bit_cast(bf16x8, blo), c);
+  return mfma_bf16(__builtin_bit_cast(bf16x8, ahi), __builtin_bit_cast(bf16x8, bhi), c);
+}
 
 // ---------------------------------------------------------------- fragments
 // One K step = 128 elements.  Per-lane operand bytes per step: fp8 32,

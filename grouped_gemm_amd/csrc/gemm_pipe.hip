@@ -144,7 +144,10 @@ template <int F, bool GATEUP, int BM, int NR, int WM, int NW>
 struct PipeCfg {
   static constexpr int WN = NW / WM;
   static constexpr int WB = FmtBits<F>::W;             // 8 or 4
-  static constexpr int WROWB = 128 * WB / 8;           // weight bytes per row per step
+  // a K step is 128 bytes of a row: 128 elements of the 8- and 4-bit
+  // formats (64 bytes of e2m1 weights), 64 of bf16
+  static constexpr int KE = F == F_BF16 ? 64 : 128;    // K elements per step
+  static constexpr int WROWB = KE * WB / 8;            // weight bytes per row per step
   static constexpr int TOKB = BM * 128;                // token bytes per stage
   static constexpr int WTB = NR * WROWB;               // weight bytes per stage
   static constexpr bool ASC = F == F_FP8_BLK || F == F_MX;   // per-step scale slots
@@ -245,8 +248,9 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
   // leaves each SIMD one wave of MFMA work
   const int wm = wave / WN, wn = wave % WN;
   const int r16 = lane & 15, lg = lane >> 4;
-  const uint32_t wrow = (uint32_t)row_bytes<WB>(K), xrow = (uint32_t)K;   // token rows: e4m3
-  const int ns = K / 128;
+  // token rows: e4m3 codes, or bf16
+  const uint32_t wrow = (uint32_t)row_bytes<WB>(K), xrow = (uint32_t)row_bytes<FmtBits<F>::X>(K);
+  const int ns = K / PC::KE;
   // activation-scale bytes per token row
   const uint32_t srow = F == F_FP8_BLK ? (uint32_t)(K / 128) * 4 : (uint32_t)(K / 32);
 
@@ -288,12 +292,12 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
   // rows of one wave belong to one matrix (gate or up) and its DMA
   // instructions differ by a whole number of row groups, so one lane offset
   // serves all of them; the rest is a wave-uniform base.
-  constexpr int RPI = WB == 8 ? 8 : 16;                  // weight rows per DMA instruction
+  constexpr int RPI = PC::WROWB == 128 ? 8 : 16;         // weight rows per DMA instruction
   static_assert(!GATEUP || NBC % (NWT * RPI) == 0, "a wave's weight rows lie in one matrix");
   const int wr0 = wave * NWT * RPI;                      // first weight row of this wave
   const bool wup = GATEUP && wr0 >= NBC;                 // wave loads up rows
   uint32_t woff;
-  if constexpr (WB == 8) woff = (uint32_t)(lane >> 3) * wrow + 16 * ((lane & 7) ^ ((lane >> 3) & 7));
+  if constexpr (PC::WROWB == 128) woff = (uint32_t)(lane >> 3) * wrow + 16 * ((lane & 7) ^ ((lane >> 3) & 7));
   else woff = (uint32_t)(lane >> 2) * wrow + 16 * ((lane & 3) ^ ((lane >> 3) & 3));
   const size_t wrel = (size_t)(wup ? wr0 - NBC : wr0) * wrow;   // wave's rows in its matrix
   uint32_t wsoff = 0;        // MX: e8m0 scale row of this lane's weight row
@@ -555,7 +559,7 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
         for (int rt = 0; rt < RT; ++rt) {
           const int R = m * NBC + wrow0 + rt * 16 + r16;     // LDS weight row of this lane
           sw[m][rt] = 0;
-          if constexpr (WB == 8) {
+          if constexpr (PC::WROWB == 128) {
             const i32x4 lo = *(const i32x4*)(st + PC::TOKB + swz128(R, lg));
             const i32x4 hi = *(const i32x4*)(st + PC::TOKB + swz128(R, lg + 4));
             afr[m][rt] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -622,6 +626,8 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
             for (int t = 0; t < NT; ++t) {
               if constexpr (F == F_MX)
                 acc[m][rt][t] = mfma_f4f8_scaled(afr[m][rt], bfr[t], acc[m][rt][t], sw[m][rt], sbx[t]);
+              else if constexpr (F == F_BF16)
+                acc[m][rt][t] = mfma_bf16_pair(afr[m][rt], bfr[t], acc[m][rt][t]);
               else
                 acc[m][rt][t] = mfma_f8(afr[m][rt], bfr[t], acc[m][rt][t]);
             }
@@ -995,6 +1001,10 @@ hipError_t launch_gemm_pipe(int fmt, bool gateup, int family, const GemmArgs& g,
       return gateup ? launch_pipe_t<F_FP8_BLK, true>(family, g, st) : launch_pipe_t<F_FP8_BLK, false>(family, g, st);
     case F_MX:
       return gateup ? launch_pipe_t<F_MX, true>(family, g, st) : launch_pipe_t<F_MX, false>(family, g, st);
+    case F_BF16:
+      // plain op only (fp32 rows, or weighted bf16 rows): the backward's
+      // grouped GEMMs
+      return gateup ? hipErrorInvalidValue : launch_pipe_t<F_BF16, false>(family, g, st);
   }
   return hipErrorInvalidValue;
 }

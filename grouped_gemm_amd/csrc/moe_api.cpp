@@ -808,12 +808,13 @@ int moe_expert_backward(moe_ws* ws, const moe_weights* w, const void* x, const i
   };
   char* sc = (char*)scratch;
   const int E = d.num_experts, k = d.top_k, H = d.hidden, I = d.inter, S = T * k;
-  // dispatch of the given routing, block table for 64-row blocks
+  // dispatch of the given routing, block table for 128-row blocks (the
+  // pipelined grouped GEMM's eight-wave configuration)
   DispatchArgs a = dispatch_args(ws, T);
   a.scores = nullptr;
   a.ids_in = topk_ids;
   a.shared = 0;
-  a.force_cfg = 2;
+  a.force_cfg = 3;
   a.cm.on = 0;
   a.fq = QuantArgs{};
   HIP_TRY(launch_dispatch(a, st), "dispatch launch");
@@ -835,8 +836,8 @@ int moe_expert_backward(moe_ws* ws, const moe_weights* w, const void* x, const i
   uint16_t* DOT = (uint16_t*)(sc + b.DOT);
   uint16_t* HbT = (uint16_t*)(sc + b.HbT);
   uint16_t* DGUT = (uint16_t*)(sc + b.DGUT);
-  // the active experts' weights, transposed so that the forward's tiled
-  // grouped GEMM (weights [N, K], K contiguous) computes the input gradients
+  // the active experts' weights, transposed so that the forward's grouped
+  // GEMM (weights [N, K], K contiguous) computes the input gradients
   HIP_TRY(mark(7, 0), "event record");
   BwdTranspose tr{};
   tr.counts = counts;
@@ -865,7 +866,8 @@ int moe_expert_backward(moe_ws* ws, const moe_weights* w, const void* x, const i
   tr.in = (const uint16_t*)w->w_up;
   tr.out_col0 = I;
   HIP_TRY(launch_bwd_transpose(tr, E, st), "weight transpose launch");
-  // g and u recomputed by the forward's tiled bf16 grouped GEMM (64-row blocks)
+  // g and u recomputed by the pipelined bf16 grouped GEMM (128-row blocks,
+  // plain op: fp32 rows)
   GemmArgs g = gemm_args(ws);
   g.E = E;
   g.N = I;
@@ -876,22 +878,22 @@ int moe_expert_backward(moe_ws* ws, const moe_weights* w, const void* x, const i
   g.max_groups = E < S ? E : S;
   g.max_rows = S;
   g.max_group_rows = T;
-  g.cfg_self = 2;
+  g.cfg_self = 3;
   if (!relu2) {
     g.w0 = (const uint8_t*)w->w_gate;
     g.out = G;
-    HIP_TRY(launch_gemm_tiled(F_BF16, false, 2, g, st), "gate recompute launch");
+    HIP_TRY(launch_gemm_pipe(F_BF16, false, 1, g, st), "gate recompute launch");
   }
   g.w0 = (const uint8_t*)w->w_up;
   g.out = U;
-  HIP_TRY(launch_gemm_tiled(F_BF16, false, 2, g, st), "up recompute launch");
+  HIP_TRY(launch_gemm_pipe(F_BF16, false, 1, g, st), "up recompute launch");
   HIP_TRY(mark(7, 1), "event record");
   // r = W_down^T dy: rows of dy gathered by token against W_down^T [I, H]
   HIP_TRY(mark(8, 0), "event record");
   g.a = (const uint8_t*)dy;
   g.w0 = (const uint8_t*)WdT;
   g.out = R;
-  HIP_TRY(launch_gemm_tiled(F_BF16, false, 2, g, st), "down input-gradient launch");
+  HIP_TRY(launch_gemm_pipe(F_BF16, false, 1, g, st), "down input-gradient launch");
   HIP_TRY(mark(8, 1), "event record");
   BwdSlot sl{};
   sl.G = relu2 ? nullptr : G;
@@ -920,7 +922,7 @@ int moe_expert_backward(moe_ws* ws, const moe_weights* w, const void* x, const i
   g.N = H;
   g.K = 2 * I;
   g.out = DA;
-  HIP_TRY(launch_gemm_tiled(F_BF16, false, 2, g, st), "gate/up input-gradient launch");
+  HIP_TRY(launch_gemm_pipe(F_BF16, false, 1, g, st), "gate/up input-gradient launch");
   HIP_TRY(mark(10, 1), "event record");
   BwdDx bx{DA, inv, T, k, H, (uint16_t*)dx};
   HIP_TRY(mark(11, 0), "event record");
