@@ -149,13 +149,16 @@ __global__ void __launch_bounds__(BT) k_bwd_transpose(BwdTranspose p) {
 //   out[e][m, n] = sum over s in [row0, row1) of a[m, s] * b[n, s]
 // for one work chunk (an expert's rows or a piece of them); a [M, lda],
 // b [N, ldb] bf16 (feature-major copies of the per-slot rows).  Work item =
-// (chunk, 128 x 128 output block); four waves as 2 x 2, each 64 x 64.  Per
-// step of 32 slots the workgroup copies the 128 a rows and 128 b rows
-// (64 bytes each) into a ring of WG_NS LDS stages with asynchronous
-// global->LDS loads, so the next steps' loads are in flight while this
-// step's MFMAs run; 16-byte chunks are XOR-swizzled by row so the fragment
-// reads (16 rows, same chunk) are free of bank conflicts.  Slot chunks that
-// straddle the range's ends are masked on the a side after the LDS read.
+// (chunk, 128 x 128 output block), one per workgroup; blockIdx.z walks the
+// chunks longest first (a permutation from launch_bwd_chunks), so that the
+// in-order dispatch of workgroups starts the long items early and the
+// short ones fill the tail.  Four waves as 2 x 2, each 64 x 64.  Per step
+// of 32 slots the workgroup copies the 128 a rows and 128 b rows (64 bytes
+// each) into a ring of WG_NS LDS stages with asynchronous global->LDS
+// loads, so the next steps' loads are in flight while this step's MFMAs
+// run; 16-byte chunks are XOR-swizzled by row so the fragment reads (16
+// rows, same chunk) are free of bank conflicts.  Slot chunks that straddle
+// the range's ends are masked on the a side after the LDS read.
 namespace {
 
 constexpr int WG_NS = 4;              // ring stages (2 workgroups per CU)
@@ -189,8 +192,8 @@ DEVI void raw_barrier() {
 __global__ void __launch_bounds__(BT) k_bwd_wgrad(BwdWgrad p) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring[WG_NS * WG_STAGE];
   // work chunk: a group's whole row range, or one piece of it (split K)
-  const int z = blockIdx.z;
-  if (z >= p.chunks[0]) return;
+  if ((int)blockIdx.z >= p.chunks[0]) return;
+  const int z = p.order[blockIdx.z];
   const int4 ch = ((const int4*)(p.chunks + 4))[z];   // expert, first row, end row, partial
   const int e = ch.x, s0 = ch.y, s1 = ch.z;
   const int m0 = blockIdx.y * 128, n0 = blockIdx.x * 128;
@@ -249,6 +252,9 @@ __global__ void __launch_bounds__(BT) k_bwd_wgrad(BwdWgrad p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(as_bf16x8(fa[i]), as_bf16x8(fb[j]), acc[i][j]);
   }
+  // Lane: rows m0 + wm 64 + 16 i + 4 g + r of column n0 + wn 64 + 16 j + l16.
+  // Each store covers 64 contiguous bytes of four rows (measured faster than
+  // one 16-byte store per lane with the operands swapped).
   float* out = ch.w < 0 ? p.out + (size_t)e * p.M * p.N : p.partial + (size_t)ch.w * p.M * p.N;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -266,12 +272,15 @@ __global__ void __launch_bounds__(BT) k_bwd_wgrad(BwdWgrad p) {
 // empty, for an expert without rows).  Entry i: (expert, first row, end row,
 // partial index), partial index -1 for an expert's first piece (written to
 // the output) and consecutive indices for the rest; per expert its piece
-// count and first partial index.  One 256-thread block, a thread per
-// expert, exclusive scans of the piece and partial counts in LDS (E <= 256).
+// count and first partial index; and a permutation of the chunks by
+// decreasing length in steps of 32 rows (lengths from 63 steps up share a
+// bucket; the order within a bucket is arbitrary and does not affect any
+// result).  One 256-thread block, a thread per expert, exclusive scans of
+// the piece and partial counts in LDS (E <= 256).
 __global__ void __launch_bounds__(256) k_bwd_chunks(const int32_t* indptr, int E, int piece,
                                                     int32_t* chunks, int32_t* nch, int32_t* pbase,
-                                                    int32_t* multi) {
-  __shared__ int sp[256], sq[256], sm[256];
+                                                    int32_t* multi, int32_t* order) {
+  __shared__ int sp[256], sq[256], sm[256], hist[64];
   const int e = threadIdx.x;
   int s0 = 0, s1 = 0, pieces = 0;
   if (e < E) {
@@ -282,6 +291,7 @@ __global__ void __launch_bounds__(256) k_bwd_chunks(const int32_t* indptr, int E
   sp[e] = pieces;
   sq[e] = pieces > 0 ? pieces - 1 : 0;
   sm[e] = pieces > 1;
+  if (e < 64) hist[e] = 0;
   __syncthreads();
   for (int o = 1; o < 256; o <<= 1) {      // inclusive scans
     const int a = e >= o ? sp[e - o] : 0, b = e >= o ? sq[e - o] : 0, c = e >= o ? sm[e - o] : 0;
@@ -293,8 +303,16 @@ __global__ void __launch_bounds__(256) k_bwd_chunks(const int32_t* indptr, int E
   }
   if (pieces > 1) multi[sm[e]] = e;         // experts split in pieces, from multi[1]
   if (e == 255) multi[0] = sm[255];
+  // bucket 63 - min(steps, 63) of a piece: longest first
+  auto bucket = [&](int c) {
+    const int a = s0 + c * piece, b = a + piece < s1 ? a + piece : s1;
+    const int steps = b > a ? (b - (a & ~31) + 31) >> 5 : 0;
+    return 63 - (steps < 63 ? steps : 63);
+  };
+  for (int c = 0; c < pieces; ++c) atomicAdd(&hist[bucket(c)], 1);
+  const int first = sp[e] - pieces;
   if (e < E) {
-    const int first = sp[e] - pieces, pfirst = sq[e] - (pieces - 1);
+    const int pfirst = sq[e] - (pieces - 1);
     nch[e] = pieces;
     pbase[e] = pfirst;
     int4* tab = (int4*)(chunks + 4);
@@ -304,6 +322,17 @@ __global__ void __launch_bounds__(256) k_bwd_chunks(const int32_t* indptr, int E
     }
   }
   if (e == 255) chunks[0] = sp[255];
+  __syncthreads();
+  if (e == 0) {                              // bucket starts
+    int acc = 0;
+    for (int k = 0; k < 64; ++k) {
+      const int n = hist[k];
+      hist[k] = acc;
+      acc += n;
+    }
+  }
+  __syncthreads();
+  for (int c = 0; c < pieces; ++c) order[atomicAdd(&hist[bucket(c)], 1)] = first + c;
 }
 
 // out[e] += partial pieces 1.. of expert e, in piece order (a fixed order,
@@ -413,11 +442,12 @@ hipError_t launch_bwd_transpose(const BwdTranspose& a, int nz, hipStream_t st) {
 }
 
 hipError_t launch_bwd_chunks(const int32_t* indptr, int E, int piece, int32_t* chunks,
-                             int32_t* nch, int32_t* pbase, int32_t* multi, hipStream_t st) {
+                             int32_t* nch, int32_t* pbase, int32_t* multi, int32_t* order,
+                             hipStream_t st) {
   if (E <= 0 || piece <= 0) return hipErrorInvalidValue;
   if (E > 256) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_bwd_chunks, dim3(1), dim3(256), 0, st, indptr, E, piece, chunks, nch, pbase,
-                     multi);
+                     multi, order);
   return hipGetLastError();
 }
 

@@ -281,7 +281,8 @@ struct BwdTranspose {
 // finite.
 // Work comes from a chunk table (launch_bwd_chunks): each expert's rows in
 // pieces; an expert's first piece writes out[e], the others partial
-// buffers that a second pass adds to out[e] in piece order.
+// buffers that a second pass adds to out[e] in piece order.  The grid
+// takes the chunks in `order`, longest first.
 struct BwdWgrad {
   const uint16_t* a;
   long lda;
@@ -291,6 +292,7 @@ struct BwdWgrad {
   const int32_t* nch;      // [E] pieces per expert
   const int32_t* pbase;    // [E] first partial index per expert
   const int32_t* multi;    // [0]: count; from [1]: the experts in more than one piece
+  const int32_t* order;    // chunk indices, longest chunk first
   int M, N;
   float* out;
   float* partial;          // [partials, M, N]
@@ -325,7 +327,8 @@ struct RouterBwd {
 };
 hipError_t launch_bwd_transpose(const BwdTranspose& a, int nz, hipStream_t st);
 hipError_t launch_bwd_chunks(const int32_t* indptr, int E, int piece, int32_t* chunks,
-                             int32_t* nch, int32_t* pbase, int32_t* multi, hipStream_t st);
+                             int32_t* nch, int32_t* pbase, int32_t* multi, int32_t* order,
+                             hipStream_t st);
 // max_chunks: the grid's bound on chunks (E when every expert is one piece)
 hipError_t launch_bwd_wgrad(const BwdWgrad& a, int E, int max_chunks, hipStream_t st);
 hipError_t launch_bwd_slot(const BwdSlot& a, int max_rows, hipStream_t st);

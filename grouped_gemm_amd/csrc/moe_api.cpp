@@ -710,19 +710,26 @@ int moe_dispatch_noalloc(const int32_t* topk_ids, int T, int k, int E, int32_t* 
 namespace {
 
 struct BwdScratch {
-  size_t G, U, R, Hb, DGU, DA, WdT, WguT, XgT, DOT, HbT, DGUT, chunks, nch, pbase, multi, partial,
-      total;
+  size_t G, U, R, Hb, DGU, DA, WdT, WguT, XgT, DOT, HbT, DGUT, chunks, nch, pbase, multi, order,
+      partial, total;
   long ldo;        // feature-major rows: slots padded to a multiple of 64
   int piece;       // rows per weight-gradient work chunk
   int max_chunks;  // bound on the chunks
 };
 
-// Weight gradients of shapes with few 128 x 128 output blocks per expert
-// split each expert's rows into pieces of 1024 (so that a hot expert's
-// rows spread over many workgroups); larger shapes keep one piece per expert.
+// Weight-gradient work chunks: each expert's rows in pieces of at most
+// `piece` rows; one piece keeps piece / 32 steps of every output block in
+// one workgroup.  The chunks are dispatched longest first, so a piece no
+// longer than one workgroup slot's average share of all the steps (S / 32
+// steps times the 128 x 128 blocks per expert, over two workgroups on each
+// of 256 CUs) bounds the tail; splitting less saves the partial buffers and
+// their reduction.  At least 1024 rows, a multiple of 32.
 int bwd_piece(const moe_layer_desc& d) {
+  const long S = (long)d.max_tokens * d.top_k;
   const long tiles = (long)(d.hidden / 128) * (d.inter / 128);
-  return tiles < 256 ? 1024 : (1 << 30);
+  const long share = S * tiles / 512;
+  const long piece = share < 1024 ? 1024 : (share + 31) / 32 * 32;
+  return piece < (1 << 30) ? (int)piece : (1 << 30);
 }
 
 BwdScratch bwd_scratch(const moe_layer_desc& d) {
@@ -755,6 +762,7 @@ BwdScratch bwd_scratch(const moe_layer_desc& d) {
   b.nch = take(4 * E);
   b.pbase = take(4 * E);
   b.multi = take(4 * (E + 1));
+  b.order = take(4 * (size_t)b.max_chunks);
   b.partial = take(extra * H * I * 4);
   b.total = off;
   return b;
@@ -952,12 +960,15 @@ int moe_expert_backward(moe_ws* ws, const moe_weights* w, const void* x, const i
   int32_t* nch = (int32_t*)(sc + b.nch);
   int32_t* pbase = (int32_t*)(sc + b.pbase);
   int32_t* multi = (int32_t*)(sc + b.multi);
-  HIP_TRY(launch_bwd_chunks(indptr, E, b.piece, chunks, nch, pbase, multi, st), "chunk table launch");
+  int32_t* order = (int32_t*)(sc + b.order);
+  HIP_TRY(launch_bwd_chunks(indptr, E, b.piece, chunks, nch, pbase, multi, order, st),
+          "chunk table launch");
   BwdWgrad wg{};
   wg.chunks = chunks;
   wg.nch = nch;
   wg.pbase = pbase;
   wg.multi = multi;
+  wg.order = order;
   wg.partial = (float*)(sc + b.partial);
   wg.a = DOT;
   wg.lda = b.ldo;
@@ -987,7 +998,7 @@ int moe_expert_backward(moe_ws* ws, const moe_weights* w, const void* x, const i
   if (!relu2) {
     wg.a = DGUT;
     wg.out = d_w_gate;
-    HIP_TRY(launch_bwd_wgrad(wg, E, b.max_chunks, st), "gate weight-gradient launch");
+      HIP_TRY(launch_bwd_wgrad(wg, E, b.max_chunks, st), "gate weight-gradient launch");
   }
   wg.a = DGUT + (size_t)I * b.ldo;
   wg.out = d_w_up;
