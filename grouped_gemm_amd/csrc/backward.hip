@@ -145,32 +145,82 @@ __global__ void __launch_bounds__(BT) k_bwd_transpose(BwdTranspose p) {
 }
 
 // ---------------------------------------------------------------------------
-// Weight-gradient GEMM with the slot dimension contiguous in both operands:
-//   out[e][m, n] = sum over s in [row0, row1) of a[m, s] * b[n, s]
-// for one work chunk (an expert's rows or a piece of them); a [M, lda],
-// b [N, ldb] bf16 (feature-major copies of the per-slot rows).  Work item =
-// (chunk, 128 x 128 output block), one per workgroup; blockIdx.z walks the
-// chunks longest first (a permutation from launch_bwd_chunks), so that the
-// in-order dispatch of workgroups starts the long items early and the
-// short ones fill the tail.  Four waves as 2 x 2, each 64 x 64.  Per step
-// of 32 slots the workgroup copies the 128 a rows and 128 b rows (64 bytes
-// each) into a ring of WG_NS LDS stages with asynchronous global->LDS
-// loads, so the next steps' loads are in flight while this step's MFMAs
-// run; 16-byte chunks are XOR-swizzled by row so the fragment reads (16
-// rows, same chunk) are free of bank conflicts.  Slot chunks that straddle
-// the range's ends are masked on the a side after the LDS read.
+// Weight-gradient GEMM over each group's slots:
+//   out[e][m, n] = sum over s in [row0, row1) of a[s, m] * b[row_b(s), n]
+// with the operands as the per-slot pass and the inputs store them: a
+// [slots, lda] bf16, b [rows, ldb] bf16, row_b(s) = b_tok[s] (the token of
+// slot s, for x) or s.  Work item = (chunk, 128 x 128 output block), one per
+// workgroup; blockIdx.z walks the chunks longest first (a permutation from
+// launch_bwd_chunks), so that the in-order dispatch of workgroups starts
+// the long items early and the short ones fill the tail.  Four waves as
+// 2 x 2, each 64 x 64.  Per step of 32 slots the workgroup copies the 32
+// slot rows of its 128 columns of a and of b (256 bytes each) into a ring
+// of WG_NS LDS stages with asynchronous global->LDS loads, so the next
+// steps' loads are in flight while this step's MFMAs run.  The MFMA wants
+// 8 consecutive slots per lane for one column: LDS transpose reads
+// (ds_read_b64_tr_b16) give them straight from the slot rows.  Within each
+// 16-lane group, lane i of such a read receives element i % 4 of the 8-byte
+// pieces addressed by lanes i / 4, i / 4 + 4, i / 4 + 8 and i / 4 + 12; with
+// lane j addressing slot row kb + j / 4 at columns 4 (j % 4) .. + 3 of a
+// 16-column block, lane i ends with slots kb .. kb + 3 of column i.  The
+// 32-byte blocks of a row are XOR-swizzled by the row so that the eight
+// rows a half-wave reads sit in distinct banks.  Slots outside the range
+// are masked on the a side after the LDS read (their rows are loaded from
+// a valid row of the range).
 namespace {
 
 constexpr int WG_NS = 4;              // ring stages (2 workgroups per CU)
-constexpr int WG_STAGE = 16384;       // a: 128 rows x 64 B, then b
+constexpr int WG_STAGE = 16384;       // a: 32 slots x 256 B, then b
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 DEVI void dma16(const void* src, uint8_t* lds_block) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_block, 16, 0, 0);
 }
-// byte offset of (row, 16-byte chunk) in a swizzled [rows][64 B] block
-DEVI int swz64(int row, int chunk) { return row * 64 + 16 * (chunk ^ ((row >> 1) & 3)); }
+// 32-byte block swizzle of slot row r (distinct over rows 0-3 and 8-11)
+DEVI int blk_swz(int r) { return (r & 3) | (((r >> 3) & 1) << 2); }
+// The step's 16 transpose reads: for each of the 8 LDS addresses (byte
+// offsets) the rows at it and 4 rows (1024 bytes) further.  One asm block
+// that waits for its own reads before it ends, so every output is written
+// when the block returns.  (The builtin form makes the compiler wait for
+// every asynchronous global->LDS load in flight before each read, as it
+// cannot tell them apart; the ring's own waits and barrier already cover
+// the stage read here.)
+struct Frags { i32x2 v[16]; };
+DEVI Frags read_tr16(const uint32_t (&ad)[8]) {
+  Frags f;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16\n"
+      "ds_read_b64_tr_b16 %1, %16 offset:1024\n"
+      "ds_read_b64_tr_b16 %2, %17\n"
+      "ds_read_b64_tr_b16 %3, %17 offset:1024\n"
+      "ds_read_b64_tr_b16 %4, %18\n"
+      "ds_read_b64_tr_b16 %5, %18 offset:1024\n"
+      "ds_read_b64_tr_b16 %6, %19\n"
+      "ds_read_b64_tr_b16 %7, %19 offset:1024\n"
+      "ds_read_b64_tr_b16 %8, %20\n"
+      "ds_read_b64_tr_b16 %9, %20 offset:1024\n"
+      "ds_read_b64_tr_b16 %10, %21\n"
+      "ds_read_b64_tr_b16 %11, %21 offset:1024\n"
+      "ds_read_b64_tr_b16 %12, %22\n"
+      "ds_read_b64_tr_b16 %13, %22 offset:1024\n"
+      "ds_read_b64_tr_b16 %14, %23\n"
+      "ds_read_b64_tr_b16 %15, %23 offset:1024\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(f.v[0]), "=&v"(f.v[1]), "=&v"(f.v[2]), "=&v"(f.v[3]), "=&v"(f.v[4]),
+        "=&v"(f.v[5]), "=&v"(f.v[6]), "=&v"(f.v[7]), "=&v"(f.v[8]), "=&v"(f.v[9]),
+        "=&v"(f.v[10]), "=&v"(f.v[11]), "=&v"(f.v[12]), "=&v"(f.v[13]), "=&v"(f.v[14]),
+        "=&v"(f.v[15])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]),
+        "v"(ad[7])
+      : "memory");
+  return f;
+}
+DEVI u16x8 join_frag(i32x2 lo, i32x2 hi) {
+  const i32x4 v = {lo[0], lo[1], hi[0], hi[1]};
+  return __builtin_bit_cast(u16x8, v);
+}
 // wait until at most n of this wave's asynchronous loads are pending
 DEVI void wait_vm_steps(int n) {
   switch (n) {
@@ -185,6 +235,18 @@ DEVI void raw_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+}
+// eight consecutive token indices from index i through the scalar cache
+// (the table comes from an earlier launch; the pointer goes through an
+// integer so that the compiler keeps the constant address space)
+struct Tok8 { int v[8]; };
+DEVI Tok8 tok8(const int32_t* tok, int i) {
+  typedef const __attribute__((address_space(4))) int cint;
+  const cint* t = (const cint*)(uintptr_t)(tok + i);
+  Tok8 r;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) r.v[k] = __builtin_amdgcn_readfirstlane(t[k]);
+  return r;
 }
 
 }  // namespace
@@ -203,49 +265,73 @@ __global__ void __launch_bounds__(BT) k_bwd_wgrad(BwdWgrad p) {
   const int g = lane >> 4, l16 = lane & 15;
   const int sb = s0 & ~31;                 // first 32-aligned step
   const int steps = s1 > s0 ? (s1 - sb + 31) / 32 : 0;
-  // this lane's DMA sources: in each of the wave's two 16-row blocks of a
-  // and of b, row lane/4 of the block and the chunk that lands at LDS
-  // position lane (its swizzled place)
-  const uint16_t* asrc[2];
-  const uint16_t* bsrc[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = (wave * 2 + j) * 16 + (lane >> 2);
-    const int chunk = (lane & 3) ^ ((row >> 1) & 3);
-    asrc[j] = p.a + (size_t)(m0 + row) * p.lda + sb + chunk * 8;
-    bsrc[j] = p.b + (size_t)(n0 + row) * p.ldb + sb + chunk * 8;
-  }
+  // DMA: per stage this wave loads slot rows 8 wave + 4 jj + lane / 16
+  // (jj = 0, 1) of a and of b, 16 bytes each; lane's LDS place is 16-byte
+  // piece lane % 16 of its row, holding source piece 2 (q ^ swz) + lane % 2
+  // of the row's 128 columns, q = (lane % 16) / 2
+  const int lrow = lane >> 4;
+  const int cp = lane & 15;
+  const int csrc = 2 * ((cp >> 1) ^ (lrow | ((wave & 1) << 2))) + (cp & 1);
+  const uint16_t* a_col = p.a + m0 + 8 * csrc;
+  const uint16_t* b_col = p.b + n0 + 8 * csrc;
+  Tok8 tk{};
+  if (p.b_tok && steps > 0) tk = tok8(p.b_tok, sb + wave * 8);
   auto issue = [&](int st) {
-    uint8_t* stg = ring + (st % WG_NS) * WG_STAGE;
+    uint8_t* stg = ring + (st % WG_NS) * WG_STAGE + wave * 2048;
+    const int sr = sb + st * 32 + wave * 8;        // this wave's first slot row
 #pragma unroll
-    for (int j = 0; j < 2; ++j) dma16(asrc[j] + st * 32, stg + (wave * 2 + j) * 1024);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) dma16(bsrc[j] + st * 32, stg + 8192 + (wave * 2 + j) * 1024);
+    for (int jj = 0; jj < 2; ++jj) {
+      const int s = sr + 4 * jj + lrow;
+      const bool in = s < s1;
+      const int ar = in ? s : s1 - 1;
+      int br = ar;
+      if (p.b_tok) {
+        const int* t = tk.v + 4 * jj;
+        const int tv = lrow == 0 ? t[0] : lrow == 1 ? t[1] : lrow == 2 ? t[2] : t[3];
+        br = in ? tv : 0;
+      }
+      dma16(a_col + (size_t)ar * p.lda, stg + jj * 1024);
+      dma16(b_col + (size_t)br * p.ldb, stg + 8192 + jj * 1024);
+    }
+    // the next stage's token indices (only read after the next barrier)
+    if (p.b_tok && st + 1 < steps) tk = tok8(p.b_tok, sr + 32);
   };
   f32x4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  // fragment reads: lane reads slot rows 8 g + l16 / 4 (+ 4) of the
+  // fragment's 32-byte block, 8-byte part l16 % 4
+  const int r0 = 8 * g + (l16 >> 2);
+  const int hsw = blk_swz(r0);             // the same for r0 + 4
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_void*)ring;
+  const uint32_t foff = ring_lds + r0 * 256 + 8 * (l16 & 3);
   for (int q = 0; q < WG_NS - 1 && q < steps; ++q) issue(q);
   for (int st = 0; st < steps; ++st) {
     const int later = steps - 1 - st < WG_NS - 2 ? steps - 1 - st : WG_NS - 2;
     wait_vm_steps(4 * later);   // this step's stage has landed (this wave's part)
     raw_barrier();              // ... and every wave's; the previous stage is free
     if (st + WG_NS - 1 < steps) issue(st + WG_NS - 1);
-    const uint8_t* stg = ring + (st % WG_NS) * WG_STAGE;
+    const uint32_t so = foff + (st % WG_NS) * WG_STAGE;
+    uint32_t ad[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ad[i] = so + 32 * ((4 * wm + i) ^ hsw);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ad[4 + j] = so + 8192 + 32 * ((4 * wn + j) ^ hsw);
+    const Frags fr = read_tr16(ad);
     u16x8 fa[4], fb[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = *(const u16x8*)(stg + swz64(wm * 64 + i * 16 + l16, g));
+    for (int i = 0; i < 4; ++i) fa[i] = join_frag(fr.v[2 * i], fr.v[2 * i + 1]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) fb[j] = *(const u16x8*)(stg + 8192 + swz64(wn * 64 + j * 16 + l16, g));
+    for (int j = 0; j < 4; ++j) fb[j] = join_frag(fr.v[8 + 2 * j], fr.v[9 + 2 * j]);
     const int c = sb + st * 32 + 8 * g;      // this lane's 8 slots
     if (c < s0 || c + 8 > s1) {             // a chunk at the range's ends
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-          if (c + q < s0 || c + q >= s1) fa[i][q] = 0;
+        for (int k = 0; k < 8; ++k)
+          if (c + k < s0 || c + k >= s1) fa[i][k] = 0;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -355,7 +441,8 @@ __global__ void __launch_bounds__(BT) k_bwd_wgrad_reduce(BwdWgrad p) {
 // ---------------------------------------------------------------------------
 // Per-slot pass: h = bf16(act(g, u)), dw = <r, h> (fixed-order block
 // reduction), dg = bf16(w r dact/dg) and du = bf16(w r dact/du) side by
-// side in one row of 2 I.  One workgroup per slot.
+// side in one row of 2 I; and the weight gradients' slot rows
+// wdy = bf16(w dy_t) and tok = t.  One workgroup per slot.
 __global__ void __launch_bounds__(BT) k_bwd_slot(BwdSlot p) {
   __shared__ float red[BT];
   const int s = blockIdx.x;
@@ -363,6 +450,17 @@ __global__ void __launch_bounds__(BT) k_bwd_slot(BwdSlot p) {
   const int tid = threadIdx.x;
   const int pos = p.gather[s];                 // t * k + j
   const float w = p.topk_w[pos];
+  const int tkn = pos / p.k;
+  if (tid == 0) p.tok[s] = tkn;
+  for (int c = tid * 8; c < p.H; c += BT * 8) {
+    const u16x8 v = *(const u16x8*)(p.dy + (size_t)tkn * p.H + c);
+    uint4 o;
+    o.x = pack_bf16x2(w * bf16_to_f32(v[0]), w * bf16_to_f32(v[1]));
+    o.y = pack_bf16x2(w * bf16_to_f32(v[2]), w * bf16_to_f32(v[3]));
+    o.z = pack_bf16x2(w * bf16_to_f32(v[4]), w * bf16_to_f32(v[5]));
+    o.w = pack_bf16x2(w * bf16_to_f32(v[6]), w * bf16_to_f32(v[7]));
+    *(uint4*)(p.WDY + (size_t)s * p.H + c) = o;
+  }
   const int I = p.I;
   float part = 0.0f;
   for (int n = tid; n < I; n += BT) {
@@ -452,7 +550,8 @@ hipError_t launch_bwd_chunks(const int32_t* indptr, int E, int piece, int32_t* c
 }
 
 hipError_t launch_bwd_wgrad(const BwdWgrad& a, int E, int max_chunks, hipStream_t st) {
-  if (a.M % 128 || a.N % 128 || E <= 0 || max_chunks <= 0 || a.lda % 8 || a.ldb % 8)
+  if (a.M % 128 || a.N % 128 || E <= 0 || max_chunks <= 0 || a.lda % 8 || a.ldb % 8 ||
+      (uintptr_t)a.a % 16 || (uintptr_t)a.b % 16)
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_bwd_wgrad, dim3(a.N / 128, a.M / 128, max_chunks), dim3(BT), 0, st, a);
   hipError_t e = hipGetLastError();

@@ -275,19 +275,20 @@ struct BwdTranspose {
   const int32_t* counts;
 };
 // Weight-gradient GEMM: out[e][m, n] = sum over s in [indptr[e],
-// indptr[e+1]) of a[m * lda + s] * b[n * ldb + s]; out fp32 [E, M, N]
-// (zeros for experts without rows).  M, N multiples of 128; lda, ldb
-// multiples of 8 and at least the rows rounded up to 32, that padding
-// finite.
+// indptr[e+1]) of a[s * lda + m] * b[row_b(s) * ldb + n], row_b(s) =
+// b_tok[s] when b_tok is set, else s; out fp32 [E, M, N] (zeros for experts
+// without rows).  M, N multiples of 128; lda, ldb multiples of 8; a and b
+// 16-byte aligned; b_tok readable 32 entries past the last slot.
 // Work comes from a chunk table (launch_bwd_chunks): each expert's rows in
 // pieces; an expert's first piece writes out[e], the others partial
 // buffers that a second pass adds to out[e] in piece order.  The grid
 // takes the chunks in `order`, longest first.
 struct BwdWgrad {
-  const uint16_t* a;
+  const uint16_t* a;       // [slots, lda]
   long lda;
-  const uint16_t* b;
+  const uint16_t* b;       // [rows, ldb]
   long ldb;
+  const int32_t* b_tok;    // [slots + 32] b's row of each slot, or NULL
   const int32_t* chunks;   // [0]: count; from [4]: (expert, row0, row1, partial) per chunk
   const int32_t* nch;      // [E] pieces per expert
   const int32_t* pbase;    // [E] first partial index per expert
@@ -310,6 +311,10 @@ struct BwdSlot {
   uint16_t* Hb;            // [rows, I] bf16 h
   uint16_t* DGU;           // [rows, 2 I] bf16: dg, then du
   float* dw;               // [T, k]
+  const uint16_t* dy;      // [T, H] bf16
+  int H;
+  uint16_t* WDY;           // [rows, H] bf16 w dy_t
+  int32_t* tok;            // [rows] t of each slot
 };
 struct BwdDx {
   const float* DA;         // [rows, H]

@@ -710,9 +710,8 @@ int moe_dispatch_noalloc(const int32_t* topk_ids, int T, int k, int E, int32_t* 
 namespace {
 
 struct BwdScratch {
-  size_t G, U, R, Hb, DGU, DA, WdT, WguT, XgT, DOT, HbT, DGUT, chunks, nch, pbase, multi, order,
-      partial, total;
-  long ldo;        // feature-major rows: slots padded to a multiple of 64
+  size_t G, U, R, Hb, DGU, DA, WdT, WguT, WDY, tok, chunks, nch, pbase, multi, order, partial,
+      total;
   int piece;       // rows per weight-gradient work chunk
   int max_chunks;  // bound on the chunks
 };
@@ -735,8 +734,6 @@ int bwd_piece(const moe_layer_desc& d) {
 BwdScratch bwd_scratch(const moe_layer_desc& d) {
   const size_t S = (size_t)d.max_tokens * d.top_k, I = d.inter, H = d.hidden, E = d.num_experts;
   BwdScratch b{};
-  b.ldo = (long)((S + 63) / 64 * 64);
-  const size_t L = (size_t)b.ldo;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -751,10 +748,8 @@ BwdScratch bwd_scratch(const moe_layer_desc& d) {
   b.DA = take(S * H * 4);
   b.WdT = take(E * I * H * 2);        // W_down transposed: [E, I, H]
   b.WguT = take(E * H * 2 * I * 2);   // W_gate | W_up transposed: [E, H, 2 I]
-  b.XgT = take(H * L * 2);            // gathered x, feature-major [H, ldo]
-  b.DOT = take(H * L * 2);            // w dy, feature-major [H, ldo]
-  b.HbT = take(I * L * 2);            // h, feature-major [I, ldo]
-  b.DGUT = take(2 * I * L * 2);       // dg | du, feature-major [2 I, ldo]
+  b.WDY = take(S * H * 2);            // w dy_t per slot [S, H]
+  b.tok = take(4 * (S + 32));         // token of each slot, 32 entries of slack
   b.piece = bwd_piece(d);
   const size_t extra = b.piece < (1 << 30) ? (S + b.piece - 1) / b.piece : 0;
   b.max_chunks = (int)(E + extra);
@@ -840,10 +835,8 @@ int moe_expert_backward(moe_ws* ws, const moe_weights* w, const void* x, const i
   float* DA = (float*)(sc + b.DA);
   uint16_t* WdT = (uint16_t*)(sc + b.WdT);
   uint16_t* WguT = (uint16_t*)(sc + b.WguT);
-  uint16_t* XgT = (uint16_t*)(sc + b.XgT);
-  uint16_t* DOT = (uint16_t*)(sc + b.DOT);
-  uint16_t* HbT = (uint16_t*)(sc + b.HbT);
-  uint16_t* DGUT = (uint16_t*)(sc + b.DGUT);
+  uint16_t* WDY = (uint16_t*)(sc + b.WDY);
+  int32_t* tok = (int32_t*)(sc + b.tok);
   // the active experts' weights, transposed so that the forward's grouped
   // GEMM (weights [N, K], K contiguous) computes the input gradients
   HIP_TRY(mark(7, 0), "event record");
@@ -918,6 +911,10 @@ int moe_expert_backward(moe_ws* ws, const moe_weights* w, const void* x, const i
   sl.Hb = Hb;
   sl.DGU = DGU;
   sl.dw = d_topk_w;
+  sl.dy = (const uint16_t*)dy;
+  sl.H = H;
+  sl.WDY = WDY;
+  sl.tok = tok;
   HIP_TRY(mark(9, 0), "event record");
   HIP_TRY(launch_bwd_slot(sl, S, st), "activation backward launch");
   HIP_TRY(mark(9, 1), "event record");
@@ -936,26 +933,8 @@ int moe_expert_backward(moe_ws* ws, const moe_weights* w, const void* x, const i
   HIP_TRY(mark(11, 0), "event record");
   HIP_TRY(launch_bwd_dx(bx, st), "input-gradient combine launch");
   HIP_TRY(mark(11, 1), "event record");
-  // weight gradients: the per-slot operands feature-major (slots contiguous)
-  BwdTranspose ta{};
-  ta.R = S;
-  ta.out_ld = b.ldo;
-  ta.gather_div = k;
-  ta.in = (const uint16_t*)dy;          // w dy, gathered by token
-  ta.in_ld = H;
-  ta.C = H;
-  ta.gather = gather;
-  ta.scale = topk_w;
-  ta.out = DOT;
+  // weight gradients over each expert's slots, from the slot rows as stored
   HIP_TRY(mark(12, 0), "event record");
-  HIP_TRY(launch_bwd_transpose(ta, 1, st), "slot transpose launch");
-  ta.in = Hb;                           // h
-  ta.in_ld = I;
-  ta.C = I;
-  ta.gather = nullptr;
-  ta.scale = nullptr;
-  ta.out = HbT;
-  HIP_TRY(launch_bwd_transpose(ta, 1, st), "slot transpose launch");
   int32_t* chunks = (int32_t*)(sc + b.chunks);
   int32_t* nch = (int32_t*)(sc + b.nch);
   int32_t* pbase = (int32_t*)(sc + b.pbase);
@@ -970,37 +949,29 @@ int moe_expert_backward(moe_ws* ws, const moe_weights* w, const void* x, const i
   wg.multi = multi;
   wg.order = order;
   wg.partial = (float*)(sc + b.partial);
-  wg.a = DOT;
-  wg.lda = b.ldo;
-  wg.b = HbT;
-  wg.ldb = b.ldo;
+  wg.a = WDY;                           // dW_down[e] = sum (w dy_t) h^T
+  wg.lda = H;
+  wg.b = Hb;
+  wg.ldb = I;
+  wg.b_tok = nullptr;
   wg.M = H;
   wg.N = I;
   wg.out = d_w_down;
   HIP_TRY(launch_bwd_wgrad(wg, E, b.max_chunks, st), "down weight-gradient launch");
   HIP_TRY(mark(12, 1), "event record");
   HIP_TRY(mark(13, 0), "event record");
-  ta.in = (const uint16_t*)x;           // x, gathered by token
-  ta.in_ld = H;
-  ta.C = H;
-  ta.gather = gather;
-  ta.out = XgT;
-  HIP_TRY(launch_bwd_transpose(ta, 1, st), "slot transpose launch");
-  ta.in = DGU;                          // dg | du
-  ta.in_ld = 2 * I;
-  ta.C = 2 * I;
-  ta.gather = nullptr;
-  ta.out = DGUT;
-  HIP_TRY(launch_bwd_transpose(ta, 1, st), "slot transpose launch");
-  wg.b = XgT;
+  wg.b = (const uint16_t*)x;            // dW_gate[e] = sum dg x_t^T, dW_up[e] = sum du x_t^T
+  wg.ldb = H;
+  wg.b_tok = tok;
+  wg.a = DGU;
+  wg.lda = 2 * I;
   wg.M = I;
   wg.N = H;
   if (!relu2) {
-    wg.a = DGUT;
     wg.out = d_w_gate;
       HIP_TRY(launch_bwd_wgrad(wg, E, b.max_chunks, st), "gate weight-gradient launch");
   }
-  wg.a = DGUT + (size_t)I * b.ldo;
+  wg.a = DGU + I;
   wg.out = d_w_up;
   HIP_TRY(launch_bwd_wgrad(wg, E, b.max_chunks, st), "up weight-gradient launch");
   HIP_TRY(mark(13, 1), "event record");
