@@ -140,6 +140,45 @@ DEVI void raw_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// K-major weight fragments: for each of RT LDS addresses the transpose
+// reads of K rows +0, +4 (2048 bytes on), +32 and +36.  One asm block that
+// waits for its own reads before it ends, so every output is written when
+// it returns (the builtin form makes the compiler wait for every
+// asynchronous global->LDS load in flight before each read, as it cannot
+// tell them from the stage read here, which the ring's waits and barrier
+// already cover).
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+template <int RT> struct KnFrags { i32x2 v[4 * RT]; };
+template <int RT> DEVI KnFrags<RT> read_kn_frags(const uint32_t (&ad)[RT]);
+template <> DEVI KnFrags<4> read_kn_frags<4>(const uint32_t (&ad)[4]) {
+  KnFrags<4> f;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16\n"
+      "ds_read_b64_tr_b16 %1, %16 offset:2048\n"
+      "ds_read_b64_tr_b16 %2, %16 offset:16384\n"
+      "ds_read_b64_tr_b16 %3, %16 offset:18432\n"
+      "ds_read_b64_tr_b16 %4, %17\n"
+      "ds_read_b64_tr_b16 %5, %17 offset:2048\n"
+      "ds_read_b64_tr_b16 %6, %17 offset:16384\n"
+      "ds_read_b64_tr_b16 %7, %17 offset:18432\n"
+      "ds_read_b64_tr_b16 %8, %18\n"
+      "ds_read_b64_tr_b16 %9, %18 offset:2048\n"
+      "ds_read_b64_tr_b16 %10, %18 offset:16384\n"
+      "ds_read_b64_tr_b16 %11, %18 offset:18432\n"
+      "ds_read_b64_tr_b16 %12, %19\n"
+      "ds_read_b64_tr_b16 %13, %19 offset:2048\n"
+      "ds_read_b64_tr_b16 %14, %19 offset:16384\n"
+      "ds_read_b64_tr_b16 %15, %19 offset:18432\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(f.v[0]), "=&v"(f.v[1]), "=&v"(f.v[2]), "=&v"(f.v[3]), "=&v"(f.v[4]),
+        "=&v"(f.v[5]), "=&v"(f.v[6]), "=&v"(f.v[7]), "=&v"(f.v[8]), "=&v"(f.v[9]),
+        "=&v"(f.v[10]), "=&v"(f.v[11]), "=&v"(f.v[12]), "=&v"(f.v[13]), "=&v"(f.v[14]),
+        "=&v"(f.v[15])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+      : "memory");
+  return f;
+}
+
 template <int F, bool GATEUP, int BM, int NR, int WM, int NW>
 struct PipeCfg {
   static constexpr int WN = NW / WM;
@@ -229,9 +268,18 @@ constexpr int pipe_lds_bytes() {
 // registers) plus a fixed 32-bit per-lane offset.
 // ACT: the gate/up epilogue's activation (ACT_*; the down projection
 // ignores it).
-template <int F, bool GATEUP, int BM, int NR, int WM, int NW, int ACT>
+// WT: bf16 plain op with K-major weights (GemmArgs::w_kn): a stage's weight
+// tile is 64 K rows of the item's 256 channels (512 bytes each, 32-byte
+// blocks XOR-swizzled by row), and the weight fragments come from LDS
+// transpose reads (ds_read_b64_tr_b16: within each 16-lane group, lane i
+// receives element i % 4 of the 8-byte pieces addressed by lanes i / 4 + 4 k;
+// lane j addressing K row kb + j / 4 at channels 4 (j % 4) .. + 3 of a
+// 16-channel block, lane i gets K rows kb .. kb + 3 of channel i).
+template <int F, bool GATEUP, int BM, int NR, int WM, int NW, int ACT, bool WT = false>
 DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
   using PC = PipeCfg<F, GATEUP, BM, NR, WM, NW>;
+  static_assert(!WT || (F == F_BF16 && !GATEUP && NR == 256 && PC::NWT * NW * 2 == 64),
+                "K-major weights: bf16 plain op, 256-channel items, 64 K rows per stage");
   constexpr int WB = PC::WB, WN = PC::WN, NSTAGE = PC::NSTAGE;
   constexpr int NM = GATEUP ? 2 : 1;
   constexpr int RT = PC::RT, TT = PC::TT, NBC = PC::NBC, RB = PC::RB;
@@ -300,6 +348,24 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
   if constexpr (PC::WROWB == 128) woff = (uint32_t)(lane >> 3) * wrow + 16 * ((lane & 7) ^ ((lane >> 3) & 7));
   else woff = (uint32_t)(lane >> 2) * wrow + 16 * ((lane & 3) ^ ((lane >> 3) & 3));
   const size_t wrel = (size_t)(wup ? wr0 - NBC : wr0) * wrow;   // wave's rows in its matrix
+  // K-major weights: this wave loads K rows 8 wave + 2 jj + lane / 32 of a
+  // step (jj < NWT), 16-byte piece lane % 32 of the row's 512 bytes; the
+  // piece at LDS position q (32-byte block q / 2) holds source block
+  // (q / 2) ^ swz(row), swz(row) = (row & 3) | ((row >> 3) & 1) << 2, whose
+  // row & 3 follows the parity of jj
+  const uint32_t krow = (uint32_t)N * 2;                 // bytes per K row
+  uint32_t woff_kn[2] = {0, 0};
+  if constexpr (WT) {
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int r = 2 * par + (lane >> 5);
+      const int sw = (r & 3) | ((wave & 1) << 2);
+      const int q = lane & 31;
+      woff_kn[par] = (uint32_t)(lane >> 5) * krow + 16 * (2 * ((q >> 1) ^ sw) + (q & 1));
+    }
+  }
+  const int ks_w1 = WT ? p.w_k0 / PC::KE : 1 << 30;      // first step from w1
+  const uint8_t* ib_w1 = nullptr;                        // K-major: the item's w1 base
   uint32_t wsoff = 0;        // MX: e8m0 scale row of this lane's weight row
   if constexpr (F == F_MX) {
     const int R0 = wave * 64 + lane;
@@ -356,9 +422,15 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
       ib_a = gat ? (const uint8_t*)p.a_scale : (const uint8_t*)p.a_scale + (size_t)it.m0 * srow;
       aoff = rm * srow;
     }
-    const size_t wexp = (size_t)it.g * N * wrow;
-    const uint8_t* wm0 = wup ? (it.sh ? p.sh_w1 : p.w1 + wexp) : (it.sh ? p.sh_w0 : p.w0 + wexp);
-    ib_w = wm0 + (size_t)it.cbase * wrow + wrel;
+    if constexpr (WT) {
+      const size_t c0 = (size_t)it.cbase * 2 + (size_t)wave * 8 * krow;
+      ib_w = (ks_w1 == 0 ? p.w1 : p.w0 + (size_t)it.g * p.w_k0 * krow) + c0;
+      ib_w1 = p.w1 ? p.w1 + (size_t)it.g * (K - p.w_k0) * krow + c0 : ib_w;
+    } else {
+      const size_t wexp = (size_t)it.g * N * wrow;
+      const uint8_t* wm0 = wup ? (it.sh ? p.sh_w1 : p.w1 + wexp) : (it.sh ? p.sh_w0 : p.w0 + wexp);
+      ib_w = wm0 + (size_t)it.cbase * wrow + wrel;
+    }
     if constexpr (F == F_FP8_BLK) {
       // lane 0: block of the gate (down: first 128 rows), lane 1: up (down:
       // the second 128 rows when the item has them)
@@ -424,9 +496,15 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
       const int jj = k - NTOK;
       // the offset is re-materialised as a 32-bit value, so the loads take
       // the scalar base + 32-bit lane offset form
-      uint32_t wo = woff;
-      asm volatile("" : "+v"(wo));
-      lds_dma16(ib_w + (size_t)jj * RPI * wrow + wo, st + PC::TOKB + (wave * NWT + jj) * 1024);
+      if constexpr (WT) {
+        uint32_t wo = woff_kn[jj & 1];
+        asm volatile("" : "+v"(wo));
+        lds_dma16(ib_w + (size_t)jj * 2 * krow + wo, st + PC::TOKB + (wave * NWT + jj) * 1024);
+      } else {
+        uint32_t wo = woff;
+        asm volatile("" : "+v"(wo));
+        lds_dma16(ib_w + (size_t)jj * RPI * wrow + wo, st + PC::TOKB + (wave * NWT + jj) * 1024);
+      }
     } else if constexpr (F == F_FP8_BLK) {
       // activation scales of the step's rows; the last wave, the step's
       // weight block scales (lanes 0 and 1)
@@ -438,9 +516,12 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
         lds_dma4(ib_ws + wsoff, st + PC::TOKB + PC::WTB + PC::ASB + wave * 256);
     }
   };
-  auto advance = [&]() {
+  // next_step: the step of the stage issued next (K-major weights switch
+  // to w1 at step ks_w1)
+  auto advance = [&](int next_step) {
     ib_tok += 128;
-    ib_w += PC::WROWB;
+    if constexpr (WT) ib_w = next_step == ks_w1 ? ib_w1 : ib_w + (size_t)PC::KE * krow;
+    else ib_w += PC::WROWB;
     ib_a += 4;
     ib_ws += 4;
     ib_sc += 4;
@@ -462,7 +543,7 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
   meta_rows(1);
   for (int q = 0; q < D; ++q) {
     issue(q);
-    if (q + 1 < ns) advance();
+    if (q + 1 < ns) advance(q + 1);
   }
 
   f32x4 acc[NM][RT][TT];
@@ -553,6 +634,25 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
       }
       i32x8 afr[NM][RT];
       int sw[NM][RT];
+      if constexpr (WT) {
+        // K rows 8 lg + r16 / 4 (+4, +32, +36) of channel block
+        // (wrow0 + 16 rt) / 16, 8-byte part r16 % 4: K elements 8 lg .. + 7
+        // and 32 + 8 lg .. + 7 of channel wrow0 + 16 rt + r16, the token
+        // fragments' K order
+        const int r0 = 8 * lg + (r16 >> 2);
+        const int sw0 = (r0 & 3) | (((r0 >> 3) & 1) << 2);   // the same for r0 + 4, + 32, + 36
+        const uint32_t wl = (uint32_t)(uintptr_t)(lds_void*)(st + PC::TOKB) + r0 * 512 + 8 * (r16 & 3);
+        uint32_t ad[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) ad[rt] = wl + 32 * (((wrow0 >> 4) + rt) ^ sw0);
+        const KnFrags<RT> f = read_kn_frags<RT>(ad);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          sw[0][rt] = 0;
+          const i32x2 a = f.v[4 * rt], b = f.v[4 * rt + 1], c = f.v[4 * rt + 2], d = f.v[4 * rt + 3];
+          afr[0][rt] = (i32x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+        }
+      } else
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -647,7 +747,7 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
     } else {
       compute(std::integral_constant<int, TT>{});
     }
-    if (iss && si != 0) advance();
+    if (iss && si != 0) advance(si);
     if (++s < ns) continue;
 
     // ------------------------------------------------------------ epilogue
@@ -938,7 +1038,8 @@ __global__ void __launch_bounds__(256) k_gemm_pipe(GemmArgs p) {
 }
 
 // Configuration 3 (128-row blocks).
-template <int F, bool GATEUP, int ACT>
+// WT: K-major bf16 weights (GemmArgs::w_kn), N a multiple of 256.
+template <int F, bool GATEUP, int ACT, bool WT = false>
 __global__ void __launch_bounds__(Pipe8Waves<F>::NW * 64) k_gemm_pipe8(GemmArgs p) {
   using SH = PipeShapes<F, GATEUP>;
   constexpr int WM = Pipe8Waves<F>::WM, NW = Pipe8Waves<F>::NW;
@@ -948,7 +1049,8 @@ __global__ void __launch_bounds__(Pipe8Waves<F>::NW * 64) k_gemm_pipe8(GemmArgs 
     __shared__ __attribute__((aligned(1024))) uint8_t lds[SH::LDS8];
     const int cfg = p.meta[META_CFG];
     if (cfg != 3 || (p.cfg_self >= 0 && cfg != p.cfg_self)) return;
-    if (GATEUP || p.N % 256 == 0) pipe_body<F, GATEUP, 128, 256, WM, NW, ACT>(p, lds);
+    if constexpr (WT) pipe_body<F, GATEUP, 128, 256, WM, NW, ACT, true>(p, lds);
+    else if (GATEUP || p.N % 256 == 0) pipe_body<F, GATEUP, 128, 256, WM, NW, ACT>(p, lds);
     else if constexpr (!GATEUP) pipe_body<F, GATEUP, 128, 128, WM, NW, ACT>(p, lds);
   }
 }
@@ -985,6 +1087,15 @@ hipError_t launch_pipe_t(int family, const GemmArgs& g, hipStream_t st) {
       return hipGetLastError();
     });
   } else {
+    if constexpr (F == F_BF16) {
+      if (g.w_kn) {   // K-major weights: configuration 3 only, 256-channel items
+        if (family != 1 || g.cfg_self != 3 || g.N % 256 || g.w_k0 <= 0 || g.w_k0 > g.K ||
+            g.w_k0 % 64 || (g.w_k0 < g.K && !g.w1) || g.sh_w0)
+          return hipErrorInvalidValue;
+        hipLaunchKernelGGL((k_gemm_pipe8<F, false, ACT_SWIGLU, true>), dim3(grid), b8, 0, st, g);
+        return hipGetLastError();
+      }
+    }
     if (family == 0) hipLaunchKernelGGL((k_gemm_pipe<F, false, ACT_SWIGLU>), dim3(grid), dim3(256), 0, st, g);
     else hipLaunchKernelGGL((k_gemm_pipe8<F, false, ACT_SWIGLU>), dim3(grid), b8, 0, st, g);
     return hipGetLastError();

@@ -174,6 +174,10 @@ struct GemmArgs {
   int act;
   float act_limit;
   int grid_cap;           // streaming kernel: most workgroups (0: one per work item)
+  // bf16 plain op only: w_kn = 1 takes the weights K-major as stored for
+  // the forward's other side: w0 [E, w_k0, N] supplies K rows 0 .. w_k0 - 1
+  // and w1 [E, K - w_k0, N] the rest (w_k0 == K: w0 alone)
+  int w_kn, w_k0;
 };
 
 // Store four consecutive down-projection outputs of one row.

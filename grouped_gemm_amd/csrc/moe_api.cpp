@@ -746,8 +746,10 @@ BwdScratch bwd_scratch(const moe_layer_desc& d) {
   b.Hb = take(S * I * 2);
   b.DGU = take(S * 2 * I * 2);
   b.DA = take(S * H * 4);
-  b.WdT = take(E * I * H * 2);        // W_down transposed: [E, I, H]
-  b.WguT = take(E * H * 2 * I * 2);   // W_gate | W_up transposed: [E, H, 2 I]
+  // transposed weights, only where the input-gradient GEMM cannot read the
+  // stored ones K-major (its 256-channel items need N % 256 == 0)
+  b.WdT = I % 256 ? take(E * I * H * 2) : 0;         // W_down transposed: [E, I, H]
+  b.WguT = H % 256 ? take(E * H * 2 * I * 2) : 0;    // W_gate | W_up transposed: [E, H, 2 I]
   b.WDY = take(S * H * 2);            // w dy_t per slot [S, H]
   b.tok = take(4 * (S + 32));         // token of each slot, 32 entries of slack
   b.piece = bwd_piece(d);
@@ -837,8 +839,11 @@ int moe_expert_backward(moe_ws* ws, const moe_weights* w, const void* x, const i
   uint16_t* WguT = (uint16_t*)(sc + b.WguT);
   uint16_t* WDY = (uint16_t*)(sc + b.WDY);
   int32_t* tok = (int32_t*)(sc + b.tok);
-  // the active experts' weights, transposed so that the forward's grouped
-  // GEMM (weights [N, K], K contiguous) computes the input gradients
+  // The input gradients contract the stored weights along their N axis:
+  // the pipelined grouped GEMM reads them K-major as stored (w_kn) when the
+  // output width is a multiple of 256; otherwise the active experts'
+  // weights are first transposed to the forward's [N, K] layout.
+  const bool kn_r = I % 256 == 0, kn_da = H % 256 == 0;
   HIP_TRY(mark(7, 0), "event record");
   BwdTranspose tr{};
   tr.counts = counts;
@@ -851,7 +856,7 @@ int moe_expert_backward(moe_ws* ws, const moe_weights* w, const void* x, const i
   tr.out_zstride = (long)I * H;
   tr.R = H;
   tr.C = I;
-  HIP_TRY(launch_bwd_transpose(tr, E, st), "weight transpose launch");
+  if (!kn_r) HIP_TRY(launch_bwd_transpose(tr, E, st), "weight transpose launch");
   tr.in_ld = H;                         // [I, H] per expert -> [H, 2 I] halves
   tr.in_zstride = (long)I * H;
   tr.out = WguT;
@@ -863,10 +868,10 @@ int moe_expert_backward(moe_ws* ws, const moe_weights* w, const void* x, const i
   // the gate half holds finite values
   tr.in = (const uint16_t*)(relu2 ? w->w_up : w->w_gate);
   tr.out_col0 = 0;
-  HIP_TRY(launch_bwd_transpose(tr, E, st), "weight transpose launch");
+  if (!kn_da) HIP_TRY(launch_bwd_transpose(tr, E, st), "weight transpose launch");
   tr.in = (const uint16_t*)w->w_up;
   tr.out_col0 = I;
-  HIP_TRY(launch_bwd_transpose(tr, E, st), "weight transpose launch");
+  if (!kn_da) HIP_TRY(launch_bwd_transpose(tr, E, st), "weight transpose launch");
   // g and u recomputed by the pipelined bf16 grouped GEMM (128-row blocks,
   // plain op: fp32 rows)
   GemmArgs g = gemm_args(ws);
@@ -889,10 +894,13 @@ int moe_expert_backward(moe_ws* ws, const moe_weights* w, const void* x, const i
   g.out = U;
   HIP_TRY(launch_gemm_pipe(F_BF16, false, 1, g, st), "up recompute launch");
   HIP_TRY(mark(7, 1), "event record");
-  // r = W_down^T dy: rows of dy gathered by token against W_down^T [I, H]
+  // r = W_down^T dy: rows of dy gathered by token against W_down [H, I]
+  // read K-major (or its transpose [I, H])
   HIP_TRY(mark(8, 0), "event record");
   g.a = (const uint8_t*)dy;
-  g.w0 = (const uint8_t*)WdT;
+  g.w0 = kn_r ? (const uint8_t*)w->w_down : (const uint8_t*)WdT;
+  g.w_kn = kn_r;
+  g.w_k0 = H;
   g.out = R;
   HIP_TRY(launch_gemm_pipe(F_BF16, false, 1, g, st), "down input-gradient launch");
   HIP_TRY(mark(8, 1), "event record");
@@ -923,7 +931,15 @@ int moe_expert_backward(moe_ws* ws, const moe_weights* w, const void* x, const i
   g.a = (const uint8_t*)DGU;
   g.gather = nullptr;
   g.gather_div = 1;
-  g.w0 = (const uint8_t*)WguT;
+  if (kn_da) {            // K rows 0 .. I - 1 from W_gate [I, H], the rest from W_up
+    g.w0 = (const uint8_t*)(relu2 ? w->w_up : w->w_gate);
+    g.w1 = (const uint8_t*)w->w_up;
+  } else {
+    g.w0 = (const uint8_t*)WguT;
+    g.w1 = nullptr;
+  }
+  g.w_kn = kn_da;
+  g.w_k0 = I;
   g.N = H;
   g.K = 2 * I;
   g.out = DA;
