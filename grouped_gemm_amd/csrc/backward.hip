@@ -149,74 +149,91 @@ __global__ void __launch_bounds__(BT) k_bwd_transpose(BwdTranspose p) {
 //   out[e][m, n] = sum over s in [row0, row1) of a[s, m] * b[row_b(s), n]
 // with the operands as the per-slot pass and the inputs store them: a
 // [slots, lda] bf16, b [rows, ldb] bf16, row_b(s) = b_tok[s] (the token of
-// slot s, for x) or s.  Work item = (chunk, 128 x 128 output block), one per
-// workgroup; blockIdx.z walks the chunks longest first (a permutation from
-// launch_bwd_chunks), so that the in-order dispatch of workgroups starts
-// the long items early and the short ones fill the tail.  Four waves as
-// 2 x 2, each 64 x 64.  Per step of 32 slots the workgroup copies the 32
-// slot rows of its 128 columns of a and of b (256 bytes each) into a ring
-// of WG_NS LDS stages with asynchronous global->LDS loads, so the next
-// steps' loads are in flight while this step's MFMAs run.  The MFMA wants
-// 8 consecutive slots per lane for one column: LDS transpose reads
-// (ds_read_b64_tr_b16) give them straight from the slot rows.  Within each
-// 16-lane group, lane i of such a read receives element i % 4 of the 8-byte
-// pieces addressed by lanes i / 4, i / 4 + 4, i / 4 + 8 and i / 4 + 12; with
-// lane j addressing slot row kb + j / 4 at columns 4 (j % 4) .. + 3 of a
-// 16-column block, lane i ends with slots kb .. kb + 3 of column i.  The
-// 32-byte blocks of a row are XOR-swizzled by the row so that the eight
-// rows a half-wave reads sit in distinct banks.  Slots outside the range
-// are masked on the a side after the LDS read (their rows are loaded from
-// a valid row of the range).
+// slot s, for x) or s.  Work item = (chunk, 128 x 64 WN output block), one
+// per workgroup; blockIdx.z walks the chunks longest first (a permutation
+// from launch_bwd_chunks), so that the in-order dispatch of workgroups
+// starts the long items early and the short ones fill the tail.  2 x WN
+// waves, each 64 x 64 (WN = 4 where N allows: 256 columns per item read
+// three quarters of the operand bytes per MFMA that 128 columns do).  Per
+// step of 32 slots the workgroup copies the 32 slot rows of its columns of
+// a and of b into a ring of LDS stages with asynchronous global->LDS loads,
+// so the next steps' loads are in flight while this step's MFMAs run.  The
+// MFMA wants 8 consecutive slots per lane for one column: LDS transpose
+// reads (ds_read_b64_tr_b16) give them straight from the slot rows.  Within
+// each 16-lane group, lane i of such a read receives element i % 4 of the
+// 8-byte pieces addressed by lanes i / 4, i / 4 + 4, i / 4 + 8 and
+// i / 4 + 12; with lane j addressing slot row kb + j / 4 at columns
+// 4 (j % 4) .. + 3 of a 16-column block, lane i ends with slots kb .. kb + 3
+// of column i.  The 32-byte blocks of a row are XOR-swizzled by the row so
+// that the eight rows a half-wave reads sit in distinct banks.  Slots
+// outside the range are masked on the a side after the LDS read (their
+// rows are loaded from a valid row of the range).
 namespace {
-
-constexpr int WG_NS = 4;              // ring stages (2 workgroups per CU)
-constexpr int WG_STAGE = 16384;       // a: 32 slots x 256 B, then b
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// ring geometry per WN: a stage holds a (32 slots x 256 B) then b (32 slots
+// x 128 WN bytes); 2 workgroups per CU
+template <int WN> struct WgCfg {
+  static constexpr int NWV = 2 * WN;                 // waves
+  static constexpr int BROW = 128 * WN;              // b bytes per slot row
+  static constexpr int STAGE = 8192 + 32 * BROW;
+  static constexpr int NS = WN == 2 ? 4 : 3;         // stages
+  static constexpr int IA = 8 / NWV;                 // a loads per wave per stage (4 rows each)
+  static constexpr int RPB = 1024 / BROW;            // b rows per load
+  static constexpr int IB = 32 / RPB / NWV;          // b loads per wave per stage
+  static constexpr int LOADS = IA + IB;
+  static_assert(IA * NWV * 4 == 32 && IB * NWV * RPB == 32, "whole loads per wave");
+};
 
 DEVI void dma16(const void* src, uint8_t* lds_block) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_block, 16, 0, 0);
 }
 // 32-byte block swizzle of slot row r (distinct over rows 0-3 and 8-11)
 DEVI int blk_swz(int r) { return (r & 3) | (((r >> 3) & 1) << 2); }
-// The step's 16 transpose reads: for each of the 8 LDS addresses (byte
-// offsets) the rows at it and 4 rows (1024 bytes) further.  One asm block
-// that waits for its own reads before it ends, so every output is written
-// when the block returns.  (The builtin form makes the compiler wait for
-// every asynchronous global->LDS load in flight before each read, as it
-// cannot tell them apart; the ring's own waits and barrier already cover
-// the stage read here.)
+// The step's 16 transpose reads: for each of the 4 a addresses the rows at
+// it and 4 rows (1024 bytes) further, for each of the 4 b addresses the
+// rows at it and 4 rows (BOFF bytes) further.  One asm block that waits for
+// its own reads before it ends, so every output is written when the block
+// returns.  (The builtin form makes the compiler wait for every
+// asynchronous global->LDS load in flight before each read, as it cannot
+// tell them apart; the ring's own waits and barrier already cover the
+// stage read here.)
 struct Frags { i32x2 v[16]; };
-DEVI Frags read_tr16(const uint32_t (&ad)[8]) {
+#define WG_TR_READS(BOFF)                                                                     \
+  asm volatile(                                                                               \
+      "ds_read_b64_tr_b16 %0, %16\n"                                                          \
+      "ds_read_b64_tr_b16 %1, %16 offset:1024\n"                                              \
+      "ds_read_b64_tr_b16 %2, %17\n"                                                          \
+      "ds_read_b64_tr_b16 %3, %17 offset:1024\n"                                              \
+      "ds_read_b64_tr_b16 %4, %18\n"                                                          \
+      "ds_read_b64_tr_b16 %5, %18 offset:1024\n"                                              \
+      "ds_read_b64_tr_b16 %6, %19\n"                                                          \
+      "ds_read_b64_tr_b16 %7, %19 offset:1024\n"                                              \
+      "ds_read_b64_tr_b16 %8, %20\n"                                                          \
+      "ds_read_b64_tr_b16 %9, %20 offset:" #BOFF "\n"                                         \
+      "ds_read_b64_tr_b16 %10, %21\n"                                                         \
+      "ds_read_b64_tr_b16 %11, %21 offset:" #BOFF "\n"                                        \
+      "ds_read_b64_tr_b16 %12, %22\n"                                                         \
+      "ds_read_b64_tr_b16 %13, %22 offset:" #BOFF "\n"                                        \
+      "ds_read_b64_tr_b16 %14, %23\n"                                                         \
+      "ds_read_b64_tr_b16 %15, %23 offset:" #BOFF "\n"                                        \
+      "s_waitcnt lgkmcnt(0)"                                                                  \
+      : "=&v"(f.v[0]), "=&v"(f.v[1]), "=&v"(f.v[2]), "=&v"(f.v[3]), "=&v"(f.v[4]),            \
+        "=&v"(f.v[5]), "=&v"(f.v[6]), "=&v"(f.v[7]), "=&v"(f.v[8]), "=&v"(f.v[9]),            \
+        "=&v"(f.v[10]), "=&v"(f.v[11]), "=&v"(f.v[12]), "=&v"(f.v[13]), "=&v"(f.v[14]),       \
+        "=&v"(f.v[15])                                                                        \
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]),   \
+        "v"(ad[7])                                                                            \
+      : "memory")
+template <int WN> DEVI Frags read_tr16(const uint32_t (&ad)[8]) {
   Frags f;
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %16\n"
-      "ds_read_b64_tr_b16 %1, %16 offset:1024\n"
-      "ds_read_b64_tr_b16 %2, %17\n"
-      "ds_read_b64_tr_b16 %3, %17 offset:1024\n"
-      "ds_read_b64_tr_b16 %4, %18\n"
-      "ds_read_b64_tr_b16 %5, %18 offset:1024\n"
-      "ds_read_b64_tr_b16 %6, %19\n"
-      "ds_read_b64_tr_b16 %7, %19 offset:1024\n"
-      "ds_read_b64_tr_b16 %8, %20\n"
-      "ds_read_b64_tr_b16 %9, %20 offset:1024\n"
-      "ds_read_b64_tr_b16 %10, %21\n"
-      "ds_read_b64_tr_b16 %11, %21 offset:1024\n"
-      "ds_read_b64_tr_b16 %12, %22\n"
-      "ds_read_b64_tr_b16 %13, %22 offset:1024\n"
-      "ds_read_b64_tr_b16 %14, %23\n"
-      "ds_read_b64_tr_b16 %15, %23 offset:1024\n"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(f.v[0]), "=&v"(f.v[1]), "=&v"(f.v[2]), "=&v"(f.v[3]), "=&v"(f.v[4]),
-        "=&v"(f.v[5]), "=&v"(f.v[6]), "=&v"(f.v[7]), "=&v"(f.v[8]), "=&v"(f.v[9]),
-        "=&v"(f.v[10]), "=&v"(f.v[11]), "=&v"(f.v[12]), "=&v"(f.v[13]), "=&v"(f.v[14]),
-        "=&v"(f.v[15])
-      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]),
-        "v"(ad[7])
-      : "memory");
+  if constexpr (WN == 2) WG_TR_READS(1024);
+  else WG_TR_READS(2048);
   return f;
 }
+#undef WG_TR_READS
 DEVI u16x8 join_frag(i32x2 lo, i32x2 hi) {
   const i32x4 v = {lo[0], lo[1], hi[0], hi[1]};
   return __builtin_bit_cast(u16x8, v);
@@ -226,6 +243,7 @@ DEVI void wait_vm_steps(int n) {
   switch (n) {
     case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
     case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
     default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
   }
 }
@@ -236,65 +254,112 @@ DEVI void raw_barrier() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
-// eight consecutive token indices from index i through the scalar cache
+// Eight consecutive token indices from index i through the scalar cache
 // (the table comes from an earlier launch; the pointer goes through an
-// integer so that the compiler keeps the constant address space)
-struct Tok8 { int v[8]; };
+// integer so that the compiler keeps the constant address space).  A
+// lane-dependent pick among them must stay a chain of register selects:
+// folded into an indexed read, it becomes a private array that the
+// compiler places in LDS, whose writes then wait for every asynchronous
+// load in flight.
+struct Tok8 { int t0, t1, t2, t3, t4, t5, t6, t7; };
 DEVI Tok8 tok8(const int32_t* tok, int i) {
   typedef const __attribute__((address_space(4))) int cint;
   const cint* t = (const cint*)(uintptr_t)(tok + i);
-  Tok8 r;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) r.v[k] = __builtin_amdgcn_readfirstlane(t[k]);
-  return r;
+  return Tok8{__builtin_amdgcn_readfirstlane(t[0]), __builtin_amdgcn_readfirstlane(t[1]),
+              __builtin_amdgcn_readfirstlane(t[2]), __builtin_amdgcn_readfirstlane(t[3]),
+              __builtin_amdgcn_readfirstlane(t[4]), __builtin_amdgcn_readfirstlane(t[5]),
+              __builtin_amdgcn_readfirstlane(t[6]), __builtin_amdgcn_readfirstlane(t[7])};
+}
+// value k of a Tok8 (k a compile-time constant after unrolling)
+DEVI int tok_at(const Tok8& t, int k) {
+  switch (k) {
+    case 0: return t.t0;
+    case 1: return t.t1;
+    case 2: return t.t2;
+    case 3: return t.t3;
+    case 4: return t.t4;
+    case 5: return t.t5;
+    case 6: return t.t6;
+    default: return t.t7;
+  }
 }
 
 }  // namespace
 
-__global__ void __launch_bounds__(BT) k_bwd_wgrad(BwdWgrad p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[WG_NS * WG_STAGE];
+template <int WN>
+__global__ void __launch_bounds__(128 * WN) k_bwd_wgrad(BwdWgrad p) {
+  using C = WgCfg<WN>;
+  constexpr int NS = C::NS, STAGE = C::STAGE, BROW = C::BROW, IA = C::IA, IB = C::IB, RPB = C::RPB;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * STAGE];
   // work chunk: a group's whole row range, or one piece of it (split K)
   if ((int)blockIdx.z >= p.chunks[0]) return;
   const int z = p.order[blockIdx.z];
   const int4 ch = ((const int4*)(p.chunks + 4))[z];   // expert, first row, end row, partial
   const int e = ch.x, s0 = ch.y, s1 = ch.z;
-  const int m0 = blockIdx.y * 128, n0 = blockIdx.x * 128;
+  const int m0 = blockIdx.y * 128, n0 = blockIdx.x * 64 * WN;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int g = lane >> 4, l16 = lane & 15;
   const int sb = s0 & ~31;                 // first 32-aligned step
   const int steps = s1 > s0 ? (s1 - sb + 31) / 32 : 0;
-  // DMA: per stage this wave loads slot rows 8 wave + 4 jj + lane / 16
-  // (jj = 0, 1) of a and of b, 16 bytes each; lane's LDS place is 16-byte
-  // piece lane % 16 of its row, holding source piece 2 (q ^ swz) + lane % 2
-  // of the row's 128 columns, q = (lane % 16) / 2
-  const int lrow = lane >> 4;
-  const int cp = lane & 15;
-  const int csrc = 2 * ((cp >> 1) ^ (lrow | ((wave & 1) << 2))) + (cp & 1);
-  const uint16_t* a_col = p.a + m0 + 8 * csrc;
-  const uint16_t* b_col = p.b + n0 + 8 * csrc;
-  Tok8 tk{};
-  if (p.b_tok && steps > 0) tk = tok8(p.b_tok, sb + wave * 8);
-  auto issue = [&](int st) {
-    uint8_t* stg = ring + (st % WG_NS) * WG_STAGE + wave * 2048;
-    const int sr = sb + st * 32 + wave * 8;        // this wave's first slot row
+  // DMA: per stage this wave loads a slot rows 4 (IA wave + ia) + lane / 16
+  // and b slot rows RPB (IB wave + ib) + lane / (64 / RPB), 16 bytes each;
+  // a lane's LDS place is 16-byte piece q of its row, holding source piece
+  // 2 ((q / 2) ^ swz(row)) + q % 2 of the row's columns
+  auto src_piece = [&](int row, int q) { return 2 * ((q >> 1) ^ blk_swz(row)) + (q & 1); };
+  uint32_t aoff[IA], boff[IB];
+  int arow[IA], brow[IB];
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int s = sr + 4 * jj + lrow;
+  for (int ia = 0; ia < IA; ++ia) {
+    arow[ia] = 4 * (IA * wave + ia) + (lane >> 4);
+    aoff[ia] = 16 * src_piece(arow[ia], lane & 15);
+  }
+#pragma unroll
+  for (int ib = 0; ib < IB; ++ib) {
+    brow[ib] = RPB * (IB * wave + ib) + lane / (64 / RPB);
+    boff[ib] = 16 * src_piece(brow[ib], lane % (64 / RPB));
+  }
+  const uint8_t* a_col = (const uint8_t*)(p.a + m0);
+  const uint8_t* b_col = (const uint8_t*)(p.b + n0);
+  const int tbase = RPB * IB * wave;       // this wave's first b row in a stage
+  Tok8 tk{};
+  if (p.b_tok && steps > 0) tk = tok8(p.b_tok, sb + tbase);
+  auto issue = [&](int st) {
+    uint8_t* stg = ring + (st % NS) * STAGE;
+    const int sr = sb + st * 32;           // the stage's first slot row
+#pragma unroll
+    for (int ia = 0; ia < IA; ++ia) {
+      const int s = sr + arow[ia];
+      const int r = s < s1 ? s : s1 - 1;
+      dma16(a_col + (size_t)r * p.lda * 2 + aoff[ia], stg + (IA * wave + ia) * 1024);
+    }
+#pragma unroll
+    for (int ib = 0; ib < IB; ++ib) {
+      const int s = sr + brow[ib];
       const bool in = s < s1;
-      const int ar = in ? s : s1 - 1;
-      int br = ar;
+      int r = in ? s : s1 - 1;
       if (p.b_tok) {
-        const int* t = tk.v + 4 * jj;
-        const int tv = lrow == 0 ? t[0] : lrow == 1 ? t[1] : lrow == 2 ? t[2] : t[3];
-        br = in ? tv : 0;
+        // row brow[ib] - tbase of the wave's rows: index RPB ib + sub,
+        // sub = lane / (64 / RPB) (a select over registers, not an indexed
+        // array, which would go to scratch)
+        // (each candidate passes through an empty asm as a register value,
+        // so the selects cannot be folded into one indexed load)
+        const int sub = lane / (64 / RPB);
+        int tv = tok_at(tk, RPB * ib);
+        asm("" : "+s"(tv));
+#pragma unroll
+        for (int c = 1; c < RPB; ++c) {
+          int vc = tok_at(tk, RPB * ib + c);
+          asm("" : "+s"(vc));
+          tv = sub == c ? vc : tv;
+        }
+        r = in ? tv : 0;
       }
-      dma16(a_col + (size_t)ar * p.lda, stg + jj * 1024);
-      dma16(b_col + (size_t)br * p.ldb, stg + 8192 + jj * 1024);
+      dma16(b_col + (size_t)r * p.ldb * 2 + boff[ib], stg + 8192 + (IB * wave + ib) * 1024);
     }
     // the next stage's token indices (only read after the next barrier)
-    if (p.b_tok && st + 1 < steps) tk = tok8(p.b_tok, sr + 32);
+    if (p.b_tok && st + 1 < steps) tk = tok8(p.b_tok, sr + 32 + tbase);
   };
   f32x4 acc[4][4];
 #pragma unroll
@@ -306,20 +371,21 @@ __global__ void __launch_bounds__(BT) k_bwd_wgrad(BwdWgrad p) {
   const int r0 = 8 * g + (l16 >> 2);
   const int hsw = blk_swz(r0);             // the same for r0 + 4
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_void*)ring;
-  const uint32_t foff = ring_lds + r0 * 256 + 8 * (l16 & 3);
-  for (int q = 0; q < WG_NS - 1 && q < steps; ++q) issue(q);
+  const uint32_t fa_off = ring_lds + r0 * 256 + 8 * (l16 & 3);
+  const uint32_t fb_off = ring_lds + 8192 + r0 * BROW + 8 * (l16 & 3);
+  for (int q = 0; q < NS - 1 && q < steps; ++q) issue(q);
   for (int st = 0; st < steps; ++st) {
-    const int later = steps - 1 - st < WG_NS - 2 ? steps - 1 - st : WG_NS - 2;
-    wait_vm_steps(4 * later);   // this step's stage has landed (this wave's part)
-    raw_barrier();              // ... and every wave's; the previous stage is free
-    if (st + WG_NS - 1 < steps) issue(st + WG_NS - 1);
-    const uint32_t so = foff + (st % WG_NS) * WG_STAGE;
+    const int later = steps - 1 - st < NS - 2 ? steps - 1 - st : NS - 2;
+    wait_vm_steps(C::LOADS * later);   // this step's stage has landed (this wave's part)
+    raw_barrier();                     // ... and every wave's; the previous stage is free
+    if (st + NS - 1 < steps) issue(st + NS - 1);
+    const uint32_t so = (st % NS) * STAGE;
     uint32_t ad[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ad[i] = so + 32 * ((4 * wm + i) ^ hsw);
+    for (int i = 0; i < 4; ++i) ad[i] = fa_off + so + 32 * ((4 * wm + i) ^ hsw);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ad[4 + j] = so + 8192 + 32 * ((4 * wn + j) ^ hsw);
-    const Frags fr = read_tr16(ad);
+    for (int j = 0; j < 4; ++j) ad[4 + j] = fb_off + so + 32 * ((4 * wn + j) ^ hsw);
+    const Frags fr = read_tr16<WN>(ad);
     u16x8 fa[4], fb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) fa[i] = join_frag(fr.v[2 * i], fr.v[2 * i + 1]);
@@ -553,7 +619,10 @@ hipError_t launch_bwd_wgrad(const BwdWgrad& a, int E, int max_chunks, hipStream_
   if (a.M % 128 || a.N % 128 || E <= 0 || max_chunks <= 0 || a.lda % 8 || a.ldb % 8 ||
       (uintptr_t)a.a % 16 || (uintptr_t)a.b % 16)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_bwd_wgrad, dim3(a.N / 128, a.M / 128, max_chunks), dim3(BT), 0, st, a);
+  if (a.N % 256 == 0)   // 128 x 256 items, eight waves
+    hipLaunchKernelGGL(k_bwd_wgrad<4>, dim3(a.N / 256, a.M / 128, max_chunks), dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_bwd_wgrad<2>, dim3(a.N / 128, a.M / 128, max_chunks), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || max_chunks == E) return e;   // one piece per expert: nothing to add
   const size_t MN = (size_t)a.M * a.N;

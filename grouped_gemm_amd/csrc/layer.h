@@ -282,7 +282,7 @@ struct BwdTranspose {
 // indptr[e+1]) of a[s * lda + m] * b[row_b(s) * ldb + n], row_b(s) =
 // b_tok[s] when b_tok is set, else s; out fp32 [E, M, N] (zeros for experts
 // without rows).  M, N multiples of 128; lda, ldb multiples of 8; a and b
-// 16-byte aligned; b_tok readable 32 entries past the last slot.
+// 16-byte aligned; b_tok readable 64 entries past the last slot.
 // Work comes from a chunk table (launch_bwd_chunks): each expert's rows in
 // pieces; an expert's first piece writes out[e], the others partial
 // buffers that a second pass adds to out[e] in piece order.  The grid
@@ -292,7 +292,7 @@ struct BwdWgrad {
   long lda;
   const uint16_t* b;       // [rows, ldb]
   long ldb;
-  const int32_t* b_tok;    // [slots + 32] b's row of each slot, or NULL
+  const int32_t* b_tok;    // [slots + 64] b's row of each slot, or NULL
   const int32_t* chunks;   // [0]: count; from [4]: (expert, row0, row1, partial) per chunk
   const int32_t* nch;      // [E] pieces per expert
   const int32_t* pbase;    // [E] first partial index per expert

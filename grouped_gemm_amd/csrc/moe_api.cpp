@@ -751,7 +751,7 @@ BwdScratch bwd_scratch(const moe_layer_desc& d) {
   b.WdT = I % 256 ? take(E * I * H * 2) : 0;         // W_down transposed: [E, I, H]
   b.WguT = H % 256 ? take(E * H * 2 * I * 2) : 0;    // W_gate | W_up transposed: [E, H, 2 I]
   b.WDY = take(S * H * 2);            // w dy_t per slot [S, H]
-  b.tok = take(4 * (S + 32));         // token of each slot, 32 entries of slack
+  b.tok = take(4 * (S + 64));         // token of each slot, 64 entries of slack
   b.piece = bwd_piece(d);
   const size_t extra = b.piece < (1 << 30) ? (S + b.piece - 1) / b.piece : 0;
   b.max_chunks = (int)(E + extra);
