@@ -86,6 +86,20 @@ def test_expert_backward_matches_oracle(name, act, L, T):
     _check(sh, T, seed=act)
 
 
+# Widths that are multiples of 256: the input gradients read the stored
+# weights K-major (no transposes) and every weight gradient runs 128 x 256
+# items; I = 384 above covers the transposed-weight fallback and 128 x 128
+# items.
+WIDE = ms.small_shape("tiny", hidden=512, inter=256, experts=8, top_k=2)
+
+
+@pytest.mark.parametrize("T", [3, 150])
+@pytest.mark.parametrize("name,act,L", [ACTS[0], ACTS[4]], ids=["swiglu", "relu2"])
+def test_expert_backward_kmajor_weights_matches_oracle(name, act, L, T):
+    say(f"backward K-major weights {name} T={T}")
+    _check(WIDE.with_(activation=act, act_limit=L), T, seed=T + 3)
+
+
 def test_expert_backward_skewed_routing_and_repeatable():
     """Most tokens on two experts (several 64-row blocks with a ragged tail),
     three experts without tokens; two runs give identical bits."""
