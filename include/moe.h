@@ -339,11 +339,11 @@ MOE_API int moe_workspace_set_fused_decode(moe_ws* ws, int enable);
  * moe_layer_forward.  Stages: 0 routing + dispatch, 1 input quantisation,
  * 2 gate/up grouped GEMM, 3 intermediate requantisation, 4 down grouped
  * GEMM, 5 combine, 6 the single-launch decode layer (which replaces stages
- * 0-5 when it runs); moe_expert_backward: 7 weight transposes and gate/up
- * recomputation, 8 down input gradient (one launch), 9 per-slot pass, 10
- * gate/up input gradient (one launch), 11 input gradient combine, 12 down
- * weight gradient with its operand transposes, 13 gate and up weight
- * gradients with theirs.  NULL events clear the stage.  While any forward stage has
+ * 0-5 when it runs); moe_expert_backward: 7 gate/up recomputation (and the
+ * weight transposes of shapes whose hidden or inter size is not a multiple
+ * of 256), 8 down input gradient (one launch), 9 per-slot pass, 10 gate/up
+ * input gradient (one launch), 11 input gradient combine, 12 down weight
+ * gradient, 13 gate and up weight gradients.  NULL events clear the stage.  While any forward stage has
  * events, moe_layer_forward runs its eager path (no graph replay). */
 MOE_API int moe_workspace_set_stage_events(moe_ws* ws, int stage, void* ev_begin, void* ev_end);
 
