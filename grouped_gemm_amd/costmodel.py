@@ -170,7 +170,7 @@ def families(f: int) -> list:
     FP8 one for 32/64-row blocks and one for 128-row blocks; for MXFP4 one
     for every tiled configuration."""
     if f == 0:
-        return [1, 2, 4]
+        return [1, 2, 4, 8]
     if f == 3:
         return [1, 14]
     return [1, 6, 8]
@@ -199,6 +199,8 @@ def candidate_mask(th: np.ndarray, T: int, E: int, k: int, shared: int, H: int, 
     for sel in range(1, 1 << len(fams)):
         # every configuration a launched kernel serves is a candidate
         mask = sum(fam for i, fam in enumerate(fams) if (sel >> i) & 1) & ((1 << ncfg) - 1)
+        if mask == 0:      # only launches of configurations this record lacks
+            continue
         cost = sum(w * min(p[c] for c in range(ncfg) if (mask >> c) & 1)
                    for w, p in zip(ROUTING_PRIOR, preds))
         cost += LAUNCH_US * (launches(mask, f) - 1)

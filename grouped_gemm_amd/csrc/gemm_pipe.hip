@@ -846,7 +846,33 @@ DEVI void pipe_body(const GemmArgs& p, uint8_t* lds) {
             for (int i = 0; i < 4; ++i)
               acc[0][rt][t][i] = gated_act<ACT>(L, acc[0][rt][t][i], acc[1][rt][t][i]);
       }
-      if constexpr (F == F_FP8_CH) {
+      if constexpr (F == F_BF16) {
+        // bf16 intermediate rows, regrouped as in the down projection's
+        // store (16 rows x 64 B per 16-byte store)
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+          const int r = trow0 + t * 16 + r16;
+          uint32_t pk[RT][2];
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            pk[rt][0] = pack_bf16x2(acc[0][rt][t][0], acc[0][rt][t][1]);
+            pk[rt][1] = pack_bf16x2(acc[0][rt][t][2], acc[0][rt][t][3]);
+          }
+#pragma unroll
+          for (int h = 0; h < RT / 2; ++h) {
+            uint32_t o[4];
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+              const uint2 q = regroup32(pk[2 * h][x], pk[2 * h + 1][x]);
+              o[x] = q.x;
+              o[2 + x] = q.y;
+            }
+            if (r < M)
+              *(uint4*)((uint16_t*)p.out + (size_t)(m0 + r) * N + c0 + 32 * h + 8 * lg) =
+                  make_uint4(o[0], o[1], o[2], o[3]);
+          }
+        }
+      } else if constexpr (F == F_FP8_CH) {
   #pragma unroll
         for (int t = 0; t < TT; ++t) {
           const int r = trow0 + t * 16 + r16;
@@ -1079,7 +1105,16 @@ hipError_t launch_pipe_t(int family, const GemmArgs& g, hipStream_t st) {
   // one kernel holds every tiled configuration for this format: family 1
   // (configuration 3) is the same launch as family 0
   if (PipeShapes<F, GATEUP>::ONE_KERNEL) family = 0;
-  if constexpr (GATEUP) {
+  if constexpr (GATEUP && F == F_BF16) {
+    // bf16 gate/up: 128-row blocks only (the 32/64-row blocks run the
+    // tiled kernel)
+    if (family != 1 || g.N % 128) return hipErrorInvalidValue;
+    return with_act(g.act, [&](auto a) {
+      constexpr int ACT = decltype(a)::value;
+      hipLaunchKernelGGL((k_gemm_pipe8<F, true, ACT>), dim3(grid), b8, 0, st, g);
+      return hipGetLastError();
+    });
+  } else if constexpr (GATEUP) {
     return with_act(g.act, [&](auto a) {
       constexpr int ACT = decltype(a)::value;
       if (family == 0) hipLaunchKernelGGL((k_gemm_pipe<F, true, ACT>), dim3(grid), dim3(256), 0, st, g);
@@ -1113,9 +1148,9 @@ hipError_t launch_gemm_pipe(int fmt, bool gateup, int family, const GemmArgs& g,
     case F_MX:
       return gateup ? launch_pipe_t<F_MX, true>(family, g, st) : launch_pipe_t<F_MX, false>(family, g, st);
     case F_BF16:
-      // plain op only (fp32 rows, or weighted bf16 rows): the backward's
-      // grouped GEMMs
-      return gateup ? hipErrorInvalidValue : launch_pipe_t<F_BF16, false>(family, g, st);
+      // 128-row blocks of the layer (gate/up with bf16 intermediate rows,
+      // down with weighted bf16 rows) and the backward's grouped GEMMs
+      return gateup ? launch_pipe_t<F_BF16, true>(family, g, st) : launch_pipe_t<F_BF16, false>(family, g, st);
   }
   return hipErrorInvalidValue;
 }

@@ -43,7 +43,7 @@ int hip_fail(hipError_t e, const char* what) {
 // tiled with row blocks of cfg_rows(cfg).  bf16 stops at 64-row blocks (a
 // 128-row bf16 token tile would not leave registers for the accumulators).
 constexpr int kNumCfgs = 4;
-int num_cfgs(int fmt) { return fmt == F_BF16 ? 3 : kNumCfgs; }
+int num_cfgs(int) { return kNumCfgs; }
 
 int fmt_of(const moe_layer_desc& d) {
   if (d.w_format == MOE_W_BF16 && d.a_format == MOE_A_BF16) return F_BF16;
@@ -239,7 +239,8 @@ int launch_families(int fmt, int* fam) {
   if (fmt == F_BF16) {
     fam[1] = 2;
     fam[2] = 4;
-    return 3;
+    fam[3] = 8;
+    return 4;
   }
   if (fmt == F_MX) {
     fam[1] = 14;
@@ -267,7 +268,7 @@ CostModel cost_model(const moe_ws* ws, int T) {
   double t[2][kNumCfgs];
   for (int i = 0; i < 2; ++i)
     for (int c = 0; c < nc; ++c) t[i][c] = cost_model_time(th, h[i], c, ws->fmt, d.hidden, d.inter, T, cus);
-  int fam[3];
+  int fam[4];
   const int nf = launch_families(ws->fmt, fam);
   int best = 0;
   double best_cost = 0.0;
@@ -280,6 +281,7 @@ CostModel cost_model(const moe_ws* ws, int T) {
         ++nl;
       }
     mask &= (1 << nc) - 1;
+    if (!mask) continue;
     double cost = 0.0;
     for (int i = 0; i < 2; ++i) {
       double mn = 0.0;
@@ -435,7 +437,10 @@ hipError_t run_gemm_c(const moe_ws* ws, bool gateup, GemmArgs g, void* tiled_out
   for (int c = 1; c < num_cfgs(ws->fmt); ++c) {
     if (!((cand.mask >> c) & 1)) continue;
     g.cfg_self = c;
-    hipError_t e = launch_gemm_tiled(ws->fmt, gateup, c, g, st);
+    // bf16: 32/64-row blocks on the tiled kernel, 128-row blocks on the
+    // pipelined one
+    hipError_t e = c == 3 ? launch_gemm_pipe(ws->fmt, gateup, 1, g, st)
+                          : launch_gemm_tiled(ws->fmt, gateup, c, g, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

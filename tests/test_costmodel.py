@@ -111,7 +111,7 @@ def test_bounding_histograms_are_routings(T, E, k, shared):
 
 
 def test_candidate_mask_valid(th):
-    for f, ncfg in ((0, 3), (1, 4), (2, 4), (3, 4)):
+    for f, ncfg in ((0, 4), (1, 4), (2, 4), (3, 4)):
         for T in (1, 2, 16, 17, 64, 512, 8192):
             m = cm.candidate_mask(th, T, 128, 8, 0, 2048, 768, f, ncfg)
             assert 0 < m < (1 << ncfg)

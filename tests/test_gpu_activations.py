@@ -56,7 +56,7 @@ def test_activation_every_config_matches_oracle(act, name, base, T):
     ws.set_graphs(False)
     ids, w = oracle.route(B.scores, sh.top_k, sh.score_fn)
     ref = oracle.layer_forward(W, B.x_bits, ids, w)
-    ncfg = 3 if sh.w_format == ms.W_BF16 else 4
+    ncfg = 4
     for cfg in range(ncfg):
         say("activation", act, name, "T", T, "cfg", cfg)
         ws.force_config(cfg)

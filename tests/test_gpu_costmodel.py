@@ -54,7 +54,7 @@ def _zero_weights(sh):
 def _expected(th, sh, T, counts, mask, cus):
     """The model's pick within the mask, and whether a near tie makes
     another member equally valid."""
-    ncfg = 3 if sh.w_format == ms.W_BF16 else 4
+    ncfg = 4
     st = cm.hist_stats([int(c) for c in counts])
     t = {c: cm.predict_stats(th, st, c, sh.hidden, sh.inter, sh.w_format, T, cus)
          for c in range(ncfg) if (mask >> c) & 1}
@@ -68,7 +68,7 @@ def test_device_choice_is_the_models(name):
     sh = ms.CONFIGS[name]
     th = np.array(g.config_model_params())
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    ncfg = 3 if sh.w_format == ms.W_BF16 else 4
+    ncfg = 4
     dW = _zero_weights(sh)
     ws = workspace(sh, max(TOKENS))
     ws.set_graphs(False)

@@ -147,7 +147,7 @@ def test_grouped_gemm_prefill_size_every_config(fmt, op):
     sh = ms.LayerShape("t", 9, 256, N, E, 1, w_format=w_format, a_format=a_format)
     ws = workspace(sh, R)
     a_dev = dev(a.view(np.int16) if a.dtype == np.uint16 else a)
-    ncfg = 3 if fmt == "bf16" else 4
+    ncfg = 4
     for cfg in [-1] + list(range(ncfg)):
         ws.force_config(cfg)
         d_out_scale = None

@@ -277,7 +277,7 @@ def test_layer_every_config_matches_oracle(name, sh, T):
     ws.set_graphs(False)
     ids, w = oracle.route(B.scores, sh.top_k, sh.score_fn)
     ref = oracle.layer_forward(W, B.x_bits, ids, w)
-    ncfg = 3 if sh.w_format == ms.W_BF16 else 4
+    ncfg = 4
     outs = []
     for cfg in range(ncfg):
         ws.force_config(cfg)

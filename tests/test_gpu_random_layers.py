@@ -31,7 +31,7 @@ def _case(i):
     if base == "dsv3":
         kw["shared_inter"] = I
     sh = ms.small_shape(base, **kw)
-    ncfg = 3 if sh.w_format == ms.W_BF16 else 4
+    ncfg = 4
     cfg = int(rng.integers(-1, ncfg))   # -1: the device's own choice
     return sh, T, cfg
 

@@ -71,7 +71,7 @@ def test_layer_block_table_every_config(name, sh, T):
     ids, _ = oracle.route(B.scores, sh.top_k, sh.score_fn)
     counts, _, _, _ = oracle.dispatch(ids, sh.experts)
     counts_all = np.concatenate([counts, [T] if sh.shared else []]).astype(np.int32)
-    ncfg = 3 if sh.w_format == ms.W_BF16 else 4
+    ncfg = 4
     for cfg in [-1] + list(range(ncfg)):
         ws.force_config(cfg)
         run_layer(ws, dW, B.x_bits, B.scores)
