@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libmoe.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["route_dispatch.hip", "elementwise.hip", "gemm_stream.hip", "gemm_tiled.hip",
+SOURCES = ["route_dispatch.hip", "elementwise.hip", "gemm_stream.hip",
            "gemm_pipe.hip", "decode_layer.hip", "backward.hip", "moe_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

@@ -166,11 +166,8 @@ def bounding_histograms(T: int, E: int, k: int, shared: int) -> list:
 
 def families(f: int) -> list:
     """The configurations each kernel launch serves (bit c: configuration c):
-    the streaming kernel; for bf16 one launch per tiled configuration; for
-    FP8 one for 32/64-row blocks and one for 128-row blocks; for MXFP4 one
-    for every tiled configuration."""
-    if f == 0:
-        return [1, 2, 4, 8]
+    the streaming kernel; for bf16 and FP8 one for 32/64-row blocks and one
+    for 128-row blocks; for MXFP4 one for every tiled configuration."""
     if f == 3:
         return [1, 14]
     return [1, 6, 8]

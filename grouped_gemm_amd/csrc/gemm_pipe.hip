@@ -1105,16 +1105,7 @@ hipError_t launch_pipe_t(int family, const GemmArgs& g, hipStream_t st) {
   // one kernel holds every tiled configuration for this format: family 1
   // (configuration 3) is the same launch as family 0
   if (PipeShapes<F, GATEUP>::ONE_KERNEL) family = 0;
-  if constexpr (GATEUP && F == F_BF16) {
-    // bf16 gate/up: 128-row blocks only (the 32/64-row blocks run the
-    // tiled kernel)
-    if (family != 1 || g.N % 128) return hipErrorInvalidValue;
-    return with_act(g.act, [&](auto a) {
-      constexpr int ACT = decltype(a)::value;
-      hipLaunchKernelGGL((k_gemm_pipe8<F, true, ACT>), dim3(grid), b8, 0, st, g);
-      return hipGetLastError();
-    });
-  } else if constexpr (GATEUP) {
+  if constexpr (GATEUP) {
     return with_act(g.act, [&](auto a) {
       constexpr int ACT = decltype(a)::value;
       if (family == 0) hipLaunchKernelGGL((k_gemm_pipe<F, true, ACT>), dim3(grid), dim3(256), 0, st, g);
@@ -1148,8 +1139,6 @@ hipError_t launch_gemm_pipe(int fmt, bool gateup, int family, const GemmArgs& g,
     case F_MX:
       return gateup ? launch_pipe_t<F_MX, true>(family, g, st) : launch_pipe_t<F_MX, false>(family, g, st);
     case F_BF16:
-      // 128-row blocks of the layer (gate/up with bf16 intermediate rows,
-      // down with weighted bf16 rows) and the backward's grouped GEMMs
       return gateup ? launch_pipe_t<F_BF16, true>(family, g, st) : launch_pipe_t<F_BF16, false>(family, g, st);
   }
   return hipErrorInvalidValue;

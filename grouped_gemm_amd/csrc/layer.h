@@ -250,7 +250,6 @@ hipError_t launch_indptr_table(const int32_t* user_indptr, int cap, const Dispat
                                hipStream_t st);
 // Streaming (decode) grouped GEMM; fmt = Fmt, gateup = fused SwiGLU op.
 hipError_t launch_gemm_stream(int fmt, bool gateup, const GemmArgs& g, hipStream_t st);
-hipError_t launch_gemm_tiled(int fmt, bool gateup, int cfg, const GemmArgs& g, hipStream_t st);
 // Pipelined grouped GEMM (FP8 and MX formats).  Family 0 covers the tiled
 // configurations 1 and 2 (row blocks of 32/64, four waves), family 1
 // configuration 3 (128-row blocks, eight waves); g.cfg_self = -1 runs

@@ -236,12 +236,6 @@ void add_groups(HistStats& h, long c, long m) {
 // blocks and one for 128-row blocks; MXFP4 one for every tiled one.
 int launch_families(int fmt, int* fam) {
   fam[0] = 1;
-  if (fmt == F_BF16) {
-    fam[1] = 2;
-    fam[2] = 4;
-    fam[3] = 8;
-    return 4;
-  }
   if (fmt == F_MX) {
     fam[1] = 14;
     return 2;
@@ -422,27 +416,15 @@ hipError_t run_gemm_c(const moe_ws* ws, bool gateup, GemmArgs g, void* tiled_out
     g.out = tiled_out;
     g.out_scale = tiled_scale;
   }
-  if (ws->fmt != F_BF16) {
-    g.cfg_self = ws->force_cfg > 0 ? ws->force_cfg : -1;   // any tiled configuration
-    // MXFP4 runs every tiled configuration in one kernel (four-wave blocks
-    // throughout), so it takes one launch whichever of them the device picks
-    if (ws->fmt == F_MX) return launch_gemm_pipe(ws->fmt, gateup, 0, g, st);
-    if (cand.small) {
-      hipError_t e = launch_gemm_pipe(ws->fmt, gateup, 0, g, st);
-      if (e != hipSuccess) return e;
-    }
-    if (cand.big) return launch_gemm_pipe(ws->fmt, gateup, 1, g, st);
-    return hipSuccess;
-  }
-  for (int c = 1; c < num_cfgs(ws->fmt); ++c) {
-    if (!((cand.mask >> c) & 1)) continue;
-    g.cfg_self = c;
-    // bf16: 32/64-row blocks on the tiled kernel, 128-row blocks on the
-    // pipelined one
-    hipError_t e = c == 3 ? launch_gemm_pipe(ws->fmt, gateup, 1, g, st)
-                          : launch_gemm_tiled(ws->fmt, gateup, c, g, st);
+  g.cfg_self = ws->force_cfg > 0 ? ws->force_cfg : -1;   // any tiled configuration
+  // MXFP4 runs every tiled configuration in one kernel (four-wave blocks
+  // throughout), so it takes one launch whichever of them the device picks
+  if (ws->fmt == F_MX) return launch_gemm_pipe(ws->fmt, gateup, 0, g, st);
+  if (cand.small) {
+    hipError_t e = launch_gemm_pipe(ws->fmt, gateup, 0, g, st);
     if (e != hipSuccess) return e;
   }
+  if (cand.big) return launch_gemm_pipe(ws->fmt, gateup, 1, g, st);
   return hipSuccess;
 }
 
