@@ -47,7 +47,7 @@ METRIC = ("MoE layer µs + active TFLOP/s / HBM GB/s (FP8 W8A8) at 32, 128, 8192
 # figure is only reported while the kernel sources still hash to the value
 # they had when the counters were taken.
 TRAFFIC = {
-    ("mixtral", 128, 2): {"bytes": 962571266, "src_sha": "c5d8a894f3136ad9"},
+    ("mixtral", 128, 2): {"bytes": 962571010, "src_sha": "094c15288b0b6928"},
 }
 KERNEL_SRC = ["grouped_gemm_amd/csrc/gemm_pipe.hip", "grouped_gemm_amd/csrc/common.h",
               "grouped_gemm_amd/csrc/layer.h"]

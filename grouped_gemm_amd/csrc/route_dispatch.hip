@@ -239,6 +239,9 @@ DEVI int config_rule(int mx, int active, int rows, int tiles32, int I, int num_c
 // at fixed fields (a per-lane configuration index would make the compiler
 // index them through scratch memory).
 DEVI int pick_config(const DispatchArgs& d, const HistStats& h) {
+  // one candidate (the host launched one kernel family): nothing to weigh
+  if (d.cm.on && d.cm.mask && !(d.cm.mask & (d.cm.mask - 1)) && d.cm.mask < (1 << d.num_cfgs))
+    return __builtin_ctz((unsigned)d.cm.mask);
   if (d.cm.on && d.cm.mask) {
     int best = -1;
     double bt = 0.0;
