@@ -223,6 +223,34 @@ def test_layer_full_size(name, T, mode):
     assert tok_err.max() <= 2 * tol_for(sh), int(toks[np.argmax(tok_err)])
 
 
+FULL_BF16 = [("qwen", 8192), ("mixtral", 128), ("dsv3", 256)]
+
+
+@pytest.mark.parametrize("name,T", FULL_BF16, ids=[f"{n}-T{t}" for n, t in FULL_BF16])
+def test_layer_full_size_bf16(name, T):
+    """Full-size shapes with bf16 weights and activations (bench.py --bf16)
+    on the configuration the device picks, every token against the oracle
+    within the bf16 tolerance, each token on its own too."""
+    sh = ms.CONFIGS[name].with_(w_format=ms.W_BF16, a_format=ms.A_BF16)
+    say("layer full bf16", name, T)
+    B = ms.gen_batch(sh, T)
+    ids_ref, _ = oracle.route(B.scores, sh.top_k, sh.score_fn)
+    active = sorted(set(np.unique(ids_ref).tolist()))
+    W = ms.gen_weights(sh, experts=active)
+    ws = workspace(sh, T)
+    y = run_layer(ws, dev_weights(W), B.x_bits, B.scores)
+    say("  device configuration", ws.last_config())
+    ids, w = check_routing(sh, T, ws_routing(ws, sh, T), B.scores)
+    ref = oracle.layer_forward(W, B.x_bits, ids, w)
+    yt = bf16_to_f64(y)
+    err = relerr(yt, ref)
+    tok_err = per_token_relerr(yt, ref)
+    say("  relerr", err, "worst token", float(tok_err.max()))
+    assert np.all(np.isfinite(yt))
+    assert err <= tol_for(sh)
+    assert tok_err.max() <= 2 * tol_for(sh), int(np.argmax(tok_err))
+
+
 def test_decode_graph_cache_stays_bounded_with_rotating_buffers():
     """Decode calls whose x / scores / y buffers change from call to call
     (as under a caching allocator) replay one graph per token count: the
