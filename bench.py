@@ -259,7 +259,7 @@ def config_sweep(name, T, act=0, rounds=3, calls=30):
     import grouped_gemm_amd as g
     sh, B, W, dW, ws, x, s, y, n_active = setup(name, T, act=act)
     ws.set_graphs(False)
-    ncfg = 3 if sh.w_format == 0 else 4
+    ncfg = 4
     st = torch.cuda.Stream()
 
     def median_us(n):
@@ -295,7 +295,7 @@ def config_sweep(name, T, act=0, rounds=3, calls=30):
             "fastest_config": fastest, "auto_over_fastest": round(best[-1] / best[fastest] - 1, 4)}
 
 
-def config_sweep_many(name, tokens, act=0, rounds=3, calls=20):
+def config_sweep_many(name, tokens, act=0, rounds=3, calls=20, bf16=False):
     """config_sweep at several token counts of one workload with one weight
     draw (every expert), also reporting the routing histogram each point ran
     (the data the tile-configuration cost model is fitted to)."""
@@ -304,6 +304,8 @@ def config_sweep_many(name, tokens, act=0, rounds=3, calls=20):
     import moe_synth as ms
     import oracle
     sh = ms.CONFIGS[name].with_(activation=act)
+    if bf16:   # the same shape with bf16 weights and activations
+        sh = sh.with_(w_format=ms.W_BF16, a_format=ms.A_BF16)
     t0 = time.time()
     W = ms.gen_weights(sh)
     log(f"[sweep] {name}: all {sh.experts} experts drawn in {time.time() - t0:.1f}s")
@@ -312,7 +314,7 @@ def config_sweep_many(name, tokens, act=0, rounds=3, calls=20):
           for n in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
                     "sh_gate", "sh_up", "sh_down", "ss_gate", "ss_up", "ss_down")}
     del W
-    ncfg = 3 if sh.w_format == 0 else 4
+    ncfg = 4
     st = torch.cuda.Stream()
     out = []
     for T in tokens:
@@ -530,7 +532,8 @@ def main():
     sh0 = ms.CONFIGS[args.workload]
     if args.config_sweep:
         if args.sweep_tokens:
-            config_sweep_many(args.workload, [int(t) for t in args.sweep_tokens.split(",")], act)
+            config_sweep_many(args.workload, [int(t) for t in args.sweep_tokens.split(",")], act,
+                              bf16=args.bf16)
             return
         for T in ([args.tokens] if args.tokens else list(sh0.tokens)):
             print(json.dumps(config_sweep(args.workload, T, act)), flush=True)

@@ -351,6 +351,8 @@ def emit_header(th: np.ndarray, path: str, source: str) -> None:
 HERE = os.path.dirname(os.path.abspath(__file__))
 SWEEP = os.path.join(HERE, "costmodel_sweep_gfx950.jsonl")
 CHECK = os.path.join(HERE, "costmodel_check_gfx950.jsonl")   # held-out points, model deployed
+# bf16 layers, a format the fit never saw (same kernel families as FP8)
+CHECK_BF16 = os.path.join(HERE, "costmodel_check_bf16_gfx950.jsonl")
 HEADER = os.path.join(HERE, "csrc", "costmodel_params.h")
 
 
@@ -371,4 +373,8 @@ if __name__ == "__main__":
     if os.path.exists(CHECK):
         chk = load(CHECK)
         print("held-out points, measured: model", measured_regret(chk, "auto_us"),
+              "rule", measured_regret(chk, "rule_us"))
+    if os.path.exists(CHECK_BF16):
+        chk = load(CHECK_BF16)
+        print("bf16 layers, measured: model", measured_regret(chk, "auto_us"),
               "rule", measured_regret(chk, "rule_us"))

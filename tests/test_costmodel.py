@@ -132,3 +132,15 @@ def test_fitted_model_regret(recs, th):
     assert deployed["mean"] < static["mean"]
     assert lowo["_mean"] < rule["mean"]
     assert lowo["_mean"] < static["mean"]
+
+
+def test_bf16_layers_measured_regret():
+    """bf16 layers (never in the fit) on the model's choice: the recorded
+    sweep's regret against the fastest forced configuration stays small and
+    below the fixed histogram rule's."""
+    recs = cm.load(cm.CHECK_BF16)
+    assert len(recs) == 16 and all(r["w_format"] == 0 for r in recs)
+    model = cm.measured_regret(recs, "auto_us")
+    rule = cm.measured_regret(recs, "rule_us")
+    assert model["mean"] <= 0.03 and model["max"] <= 0.11
+    assert model["mean"] < rule["mean"]
